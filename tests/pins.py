@@ -1,0 +1,343 @@
+"""Independent pins of the fp64 oracle.
+
+Each pin checks the oracle against something other than itself: the unrolled
+closed form of the recurrence, the LTI convolution-kernel view (by FFT), the
+worked example on the ozercemkelahmet.com page, the pages' small/large step
+size limits, a library convolution (torch conv1d) and library sigmoid /
+softplus (scipy.special.expit, numpy.logaddexp). Every pin takes an oracle
+handle so that the same checks can be run on deliberately broken copies of
+the oracle (tests/test_oracle_mutants.py) to show that they catch mistakes.
+
+The pins never call the HIP library.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+from scipy.special import expit
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+# ---------------------------------------------------------------------------
+# small independent helpers (library routines, not the oracle's code)
+
+def lib_softplus(v):
+    return np.logaddexp(0.0, v)
+
+
+def lib_silu(v):
+    return v * expit(v)
+
+
+def lib_conv_silu(x, conv_w, conv_b, conv_state):
+    """u = SiLU(causal depthwise conv) through torch.nn.functional.conv1d.
+    x [B,L,D], conv_w [D,K], conv_state [B,D,K-1] history (oldest first)."""
+    Bsz, L, D = x.shape
+    K = conv_w.shape[1]
+    xt = torch.from_numpy(np.ascontiguousarray(np.transpose(x, (0, 2, 1)))).double()  # [B,D,L]
+    hist = torch.zeros(Bsz, D, K - 1, dtype=torch.float64) if conv_state is None \
+        else torch.from_numpy(np.asarray(conv_state, dtype=np.float64))
+    full = torch.cat([hist, xt], dim=2)
+    w = torch.from_numpy(np.asarray(conv_w, dtype=np.float64)).unsqueeze(1)  # [D,1,K]
+    b = None if conv_b is None else torch.from_numpy(np.asarray(conv_b, dtype=np.float64))
+    c = torch.nn.functional.conv1d(full, w, b, groups=D)  # [B,D,L]
+    u = torch.nn.functional.silu(c)
+    return np.transpose(u.numpy(), (0, 2, 1)), np.transpose(c.numpy(), (0, 2, 1))
+
+
+def closed_form(x, delta, A, B, C, conv_w=None, conv_b=None, delta_bias=None, D=None, z=None,
+                ssm_state=None, conv_state=None):
+    """Unrolled solution of the recurrence, evaluated by brute force O(L^2 D N):
+    y_t = sum_n C_t[n] (prod_{k<=t} Abar_k[n] h0[n] + sum_{s<=t} prod_{s<k<=t} Abar_k[n] Delta_s B_s[n] u_s)
+          + D u_t, then times SiLU(z_t), with prod Abar = exp(A * sum of Delta)."""
+    x = np.asarray(x, np.float64)
+    Bsz, L, Dn = x.shape
+    N = A.shape[1]
+    if conv_w is not None:
+        u, _ = lib_conv_silu(x, conv_w, conv_b, conv_state)
+    else:
+        u = x
+    v = np.asarray(delta, np.float64) + (0.0 if delta_bias is None else np.asarray(delta_bias, np.float64))
+    dt = lib_softplus(v)                                   # [B,L,D]
+    cum = np.cumsum(dt, axis=1)                            # sum_{k<=t}
+    y = np.zeros((Bsz, L, Dn))
+    h_final = np.zeros((Bsz, Dn, N))
+    h0 = np.zeros((Bsz, Dn, N)) if ssm_state is None else np.asarray(ssm_state, np.float64)
+    for b in range(Bsz):
+        for t in range(L):
+            # contribution of the initial state: exp(A * cum_t)
+            hv = np.exp(A * cum[b, t][:, None]) * h0[b]                       # [D,N]
+            for s in range(t + 1):
+                decay = np.exp(A * (cum[b, t] - cum[b, s])[:, None])            # [D,N]
+                hv = hv + decay * (dt[b, s] * u[b, s])[:, None] * B[b, s][None, :]
+            y[b, t] = (hv * C[b, t][None, :]).sum(axis=1)
+            if t == L - 1:
+                h_final[b] = hv
+    if D is not None:
+        y = y + np.asarray(D, np.float64)[None, None, :] * u
+    if z is not None:
+        y = y * lib_silu(np.asarray(z, np.float64))
+    return y, h_final
+
+
+def relerr(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    scale = max(np.max(np.abs(b)), math.sqrt(np.mean(b * b)) if b.size else 0.0, 1e-300)
+    return float(np.max(np.abs(a - b)) / scale) if b.size else 0.0
+
+
+def rand_case(rng, Bsz, L, D, N, K=4, conv=True, gate=True, skip=True, bias=True, states=False):
+    c = dict(
+        x=rng.standard_normal((Bsz, L, D)),
+        delta=rng.standard_normal((Bsz, L, D)),
+        A=-rng.uniform(0.2, 3.0, (D, N)),
+        B=rng.standard_normal((Bsz, L, N)),
+        C=rng.standard_normal((Bsz, L, N)),
+    )
+    if conv:
+        c["conv_w"] = rng.uniform(-0.5, 0.5, (D, K))
+        c["conv_b"] = rng.uniform(-0.2, 0.2, D)
+    if bias:
+        c["delta_bias"] = rng.uniform(-2.0, 0.5, D)
+    if skip:
+        c["D"] = rng.standard_normal(D)
+    if gate:
+        c["z"] = rng.standard_normal((Bsz, L, D))
+    if states:
+        c["ssm_state"] = rng.standard_normal((Bsz, D, N))
+        if conv:
+            c["conv_state"] = rng.standard_normal((Bsz, D, K - 1))
+    return c
+
+
+# ---------------------------------------------------------------------------
+# pins
+
+def pin_closed_form(orc, seed=1, shape=(2, 9, 3, 4), states=True):
+    """The recurrence against its unrolled closed form (brute force)."""
+    rng = np.random.default_rng(seed)
+    c = rand_case(rng, *shape, states=states)
+    y, h, _ = orc.conv_scan_fwd(**c)
+    y_ref, h_ref = closed_form(**c)
+    assert relerr(y, y_ref) < 1e-12, relerr(y, y_ref)
+    if states:
+        assert relerr(h, h_ref) < 1e-12, relerr(h, h_ref)
+
+
+def pin_lti_fft(orc, seed=2, Bsz=1, L=64, D=3, N=5):
+    """With Delta, B, C fixed over time the scan is a causal convolution of u with
+    K_j[d] = sum_n C[n] Abar[d,n]^j Delta[d] B[n]; evaluated with numpy.fft."""
+    rng = np.random.default_rng(seed)
+    A = -rng.uniform(0.05, 1.0, (D, N))
+    Bv = rng.standard_normal(N)
+    Cv = rng.standard_normal(N)
+    dpre = rng.uniform(-3.0, 0.0, D)
+    x = rng.standard_normal((Bsz, L, D))
+    delta = np.broadcast_to(dpre, (Bsz, L, D)).copy()
+    Bm = np.broadcast_to(Bv, (Bsz, L, N)).copy()
+    Cm = np.broadcast_to(Cv, (Bsz, L, N)).copy()
+    Dsk = rng.standard_normal(D)
+    y, _, _ = orc.conv_scan_fwd(x, delta, A, Bm, Cm, D=Dsk)
+    dt = lib_softplus(dpre)
+    j = np.arange(L)
+    Ab = np.exp(dt[:, None] * A)                                           # [D,N]
+    Kj = ((Cv * Bv)[None, None, :] * Ab[None, :, :] ** j[:, None, None]).sum(-1) * dt[None, :]  # [L,D]
+    nfft = 2 * L
+    Kf = np.fft.rfft(Kj, n=nfft, axis=0)
+    for b in range(Bsz):
+        yf = np.fft.irfft(np.fft.rfft(x[b], n=nfft, axis=0) * Kf, n=nfft, axis=0)[:L]
+        ref = yf + Dsk[None, :] * x[b]
+        assert relerr(y[b], ref) < 1e-12, relerr(y[b], ref)
+
+
+def load_worked_example():
+    with open(os.path.join(HERE, "golden", "worked_example.json")) as f:
+        return json.load(f)
+
+
+def pin_worked_example(orc):
+    """The scalar walk-through of the ozercemkelahmet.com page, with delta = ln 2."""
+    g = load_worked_example()
+    inp = g["inputs"]
+    u = np.array(inp["u"], np.float64)[None, :, None]
+    L = u.shape[1]
+    delta = np.array(inp["delta_pre_softplus"], np.float64)[None, :, None]
+    A = np.array([[inp["A"]]])
+    Bm = np.full((1, L, 1), inp["B"])
+    Cm = np.full((1, L, 1), inp["C"])
+    y, h, _ = orc.conv_scan_fwd(u, delta, A, Bm, Cm, D=np.array([inp["D"]]),
+                                ssm_state=np.zeros((1, 1, 1)))
+    want = np.array(g["expected"]["y_over_ln2"]) * math.log(2.0)
+    assert np.max(np.abs(y[0, :, 0] - want)) <= 4e-16 * np.max(np.abs(want)), (y[0, :, 0], want)
+    assert abs(h[0, 0, 0] - g["expected"]["final_state_over_ln2"] * math.log(2.0)) < 1e-15
+
+
+def pin_selective_walkthrough(orc):
+    """Same walk-through with a selective step size: large on the salient inputs
+    (steps 1 and 4), tiny elsewhere. The state is rewritten on the salient steps
+    and kept across the quiet ones, as the page describes."""
+    u = np.array([1.0, 0.0, 0.0, 5.0, 0.0])[None, :, None]
+    pre = np.array([20.0, -20.0, -20.0, 20.0, -20.0])[None, :, None]
+    dt = lib_softplus(pre[0, :, 0])
+    y, _, _ = orc.conv_scan_fwd(u, pre, np.array([[-1.0]]), np.ones((1, 5, 1)), np.ones((1, 5, 1)))
+    y = y[0, :, 0]
+    assert abs(y[0] - dt[0]) < 1e-12 * dt[0]
+    assert abs(y[1] - y[0]) < 1e-7 * y[0] and abs(y[2] - y[0]) < 1e-7 * y[0]
+    assert abs(y[3] - (math.exp(-dt[3]) * y[2] + dt[3] * 5.0)) < 1e-12 * y[3]
+    assert abs(y[3] - dt[3] * 5.0) < 1e-6 * y[3]
+
+
+def pin_small_step_keeps_state(orc, seed=3, shape=(2, 16, 4, 6)):
+    """Delta -> 0 (pre-softplus -30): Abar -> 1 and the write term vanishes, so the
+    state is kept: h_L = h_0 and y_t = C_t . h_0 + D u_t (times the gate)."""
+    rng = np.random.default_rng(seed)
+    c = rand_case(rng, *shape, bias=False, states=True)
+    c["delta"] = np.full_like(c["delta"], -30.0)
+    y, h, _ = orc.conv_scan_fwd(**c)
+    assert relerr(h, c["ssm_state"]) < 1e-11
+    u, _ = lib_conv_silu(c["x"], c["conv_w"], c["conv_b"], c["conv_state"])
+    ref = np.einsum("bln,bdn->bld", c["C"], c["ssm_state"]) + c["D"] * u
+    ref = ref * lib_silu(c["z"])
+    assert relerr(y, ref) < 1e-11, relerr(y, ref)
+
+
+def pin_large_step_forgets(orc, seed=4, shape=(2, 12, 3, 4)):
+    """Large Delta (pre-softplus +50, A <= -1): Abar ~ e^-50, the old state is
+    forgotten and h_t = Delta_t B_t u_t."""
+    rng = np.random.default_rng(seed)
+    c = rand_case(rng, *shape, bias=False, states=True)
+    c["A"] = -np.broadcast_to(np.arange(1, shape[3] + 1, dtype=np.float64), (shape[2], shape[3])).copy()
+    c["delta"] = np.full_like(c["delta"], 50.0)
+    y, h, _ = orc.conv_scan_fwd(**c)
+    u, _ = lib_conv_silu(c["x"], c["conv_w"], c["conv_b"], c["conv_state"])
+    dt = lib_softplus(50.0)
+    h_ref = dt * u[:, -1, :, None] * c["B"][:, -1, None, :]
+    assert relerr(h, h_ref) < 1e-12
+    ref = dt * u * np.einsum("bln,bln->bl", c["C"], c["B"])[:, :, None] + c["D"] * u
+    ref = ref * lib_silu(c["z"])
+    assert relerr(y, ref) < 1e-12
+
+
+def _readout_u(orc, x, conv_w, conv_b=None, conv_state=None):
+    """Observe u through the skip path: C = 0, D = 1, no gate -> y = u."""
+    Bsz, L, D = x.shape
+    N = 2
+    y, _, cs = orc.conv_scan_fwd(x, np.zeros((Bsz, L, D)), -np.ones((D, N)), np.zeros((Bsz, L, N)),
+                                 np.zeros((Bsz, L, N)), conv_w=conv_w, conv_b=conv_b, D=np.ones(D),
+                                 conv_state=conv_state)
+    return y, cs
+
+
+def pin_conv_impulse(orc, seed=5, L=10, D=3, t0=3):
+    """A unit impulse at t0 through the causal conv: pre-SiLU value at t0+j is
+    conv_w[d, K-1-j] + bias (only current and past positions contribute)."""
+    rng = np.random.default_rng(seed)
+    w = rng.uniform(-0.5, 0.5, (D, 4))
+    bias = rng.uniform(-0.2, 0.2, D)
+    x = np.zeros((1, L, D))
+    x[0, t0, :] = 1.0
+    y, _ = _readout_u(orc, x, w, bias)
+    c = np.tile(bias, (L, 1))
+    for j in range(4):
+        c[t0 + j] += w[:, 3 - j]
+    assert relerr(y[0], lib_silu(c)) < 1e-14
+    # identity filter: u = SiLU(x)
+    x2 = rng.standard_normal((1, L, D))
+    w2 = np.zeros((D, 4))
+    w2[:, 3] = 1.0
+    y2, _ = _readout_u(orc, x2, w2)
+    assert relerr(y2, lib_silu(x2)) < 1e-14
+
+
+def pin_conv_library(orc, seed=6, shape=(2, 11, 5)):
+    """Conv front end with history against torch.nn.functional.conv1d, and the
+    returned conv history equals the last K-1 inputs."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape)
+    w = rng.uniform(-0.5, 0.5, (shape[2], 4))
+    bias = rng.uniform(-0.2, 0.2, shape[2])
+    hist = rng.standard_normal((shape[0], shape[2], 3))
+    y, cs = _readout_u(orc, x, w, bias, hist)
+    u, _ = lib_conv_silu(x, w, bias, hist)
+    assert relerr(y, u) < 1e-14
+    assert np.array_equal(cs, np.transpose(x[:, -3:, :], (0, 2, 1)))
+
+
+def pin_gate_and_skip(orc, seed=7, shape=(1, 8, 4, 3)):
+    """z = 0 gives 0; the gate multiplies by SiLU(z); C = 0 leaves D*u*SiLU(z)."""
+    rng = np.random.default_rng(seed)
+    c = rand_case(rng, *shape)
+    y_g, _, _ = orc.conv_scan_fwd(**c)
+    c0 = dict(c)
+    c0["z"] = np.zeros_like(c["z"])
+    y0, _, _ = orc.conv_scan_fwd(**c0)
+    assert np.all(y0 == 0.0)
+    cu = dict(c)
+    cu.pop("z")
+    y_u, _, _ = orc.conv_scan_fwd(**cu)
+    assert relerr(y_g, y_u * lib_silu(c["z"])) < 1e-14
+    cc = dict(c)
+    cc["C"] = np.zeros_like(c["C"])
+    y_c, _, _ = orc.conv_scan_fwd(**cc)
+    u, _ = lib_conv_silu(c["x"], c["conv_w"], c["conv_b"], None)
+    assert relerr(y_c, c["D"] * u * lib_silu(c["z"])) < 1e-14
+
+
+def pin_softplus_sum(orc, seed=8, L=40, D=3):
+    """With A = 0 the decay is 1 and, for N = 1, B = C = 1, u = 1, the output is the
+    running sum of the step sizes: checks softplus (with bias) over a wide range."""
+    rng = np.random.default_rng(seed)
+    pre = rng.uniform(-40.0, 40.0, (1, L, D))
+    bias = rng.uniform(-1.0, 1.0, D)
+    y, _, _ = orc.conv_scan_fwd(np.ones((1, L, D)), pre, np.zeros((D, 1)), np.ones((1, L, 1)),
+                                np.ones((1, L, 1)), delta_bias=bias)
+    ref = np.cumsum(lib_softplus(pre + bias), axis=1)
+    assert relerr(y, ref) < 1e-13
+
+
+def pin_state_handoff(orc, seed=9, shape=(2, 23, 3, 4), splits=(1, 7, 16, 22)):
+    """Processing a sequence in two chunks, passing (ssm_state, conv_state) from
+    the first to the second, gives the same outputs as one pass."""
+    rng = np.random.default_rng(seed)
+    c = rand_case(rng, *shape, states=True)
+    y, h, cs = orc.conv_scan_fwd(**c)
+    for L1 in splits:
+        def part(sl, st_h, st_c):
+            d = dict(c)
+            for k in ("x", "delta", "z", "B", "C"):
+                d[k] = c[k][:, sl]
+            d["ssm_state"], d["conv_state"] = st_h, st_c
+            return orc.conv_scan_fwd(**d)
+        y1, h1, c1 = part(slice(0, L1), c["ssm_state"], c["conv_state"])
+        y2, h2, c2 = part(slice(L1, None), h1, c1)
+        assert relerr(np.concatenate([y1, y2], axis=1), y) < 1e-13
+        assert relerr(h2, h) < 1e-13 and np.array_equal(c2, cs)
+
+
+def pin_step_matches_scan(orc, seed=10, shape=(3, 6, 4, 5)):
+    """L decode steps from a carried state reproduce the full-sequence pass."""
+    rng = np.random.default_rng(seed)
+    c = rand_case(rng, *shape, states=True)
+    y, h, cs = orc.conv_scan_fwd(**c)
+    hs, css = c["ssm_state"], c["conv_state"]
+    ys = []
+    for t in range(shape[1]):
+        yt, hs, css = orc.step(c["x"][:, t], c["delta"][:, t], c["A"], c["B"][:, t], c["C"][:, t], hs,
+                               conv_w=c["conv_w"], conv_b=c["conv_b"], delta_bias=c["delta_bias"],
+                               D=c["D"], z=c["z"][:, t], conv_state=css)
+        ys.append(yt)
+    assert relerr(np.stack(ys, axis=1), y) < 1e-13
+    assert relerr(hs, h) < 1e-13 and np.array_equal(css, cs)
+
+
+ALL_PINS = [
+    pin_closed_form, pin_lti_fft, pin_worked_example, pin_selective_walkthrough,
+    pin_small_step_keeps_state, pin_large_step_forgets, pin_conv_impulse, pin_conv_library,
+    pin_gate_and_skip, pin_softplus_sum, pin_state_handoff, pin_step_matches_scan,
+]
