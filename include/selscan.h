@@ -1,0 +1,127 @@
+/*
+ * libselscan: selective-scan (S6) forward path and single-token decode step
+ * for AMD Instinct MI355X (gfx950), as hand-written HIP kernels behind a C ABI.
+ *
+ * The operation (per batch row b, channel d, state index n, time t):
+ *
+ *   c_t   = conv_b[d] + sum_{k<K} conv_w[d,k] * x_{t-(K-1)+k}   causal depthwise conv,
+ *                                                               conv_w[d,K-1] multiplies x_t,
+ *                                                               history from conv_state or zeros
+ *   u_t   = SiLU(c_t) = c_t / (1 + exp(-c_t))
+ *   Dt_t  = softplus(delta_t + delta_bias[d])
+ *   h_t   = exp(Dt_t * A[d,n]) * h_{t-1} + Dt_t * B_t[n] * u_t
+ *   y_t   = (sum_n C_t[n] * h_t[n] + Dskip[d] * u_t) * SiLU(z_t)
+ *
+ * Sources: ai360xpert.com "Mamba", section "The selection mechanism" (step size
+ * as softplus of an affine map of the input; A_bar = exp(Delta A); B_bar ~ Delta B);
+ * ozercemkelahmet.com "Mamba", "A minimal selective scan in PyTorch" (state per
+ * (batch, channel, state index), zero initial state, h = dA*h + dB*x, output read
+ * from the updated state), "Deployment notes" (long prompts processed in chunks
+ * that pass the state on; every sequence carries a same-sized state), "Step 5"
+ * (inference keeps only the fixed-size state); bembew.net "Overview of Mamba (SSM)
+ * Model", "How the Mamba Block Works" (depthwise conv and SiLU before the SSM,
+ * SiLU gate multiplying its output). The D*u skip is not on the pages and is part
+ * of the computation implemented here.
+ *
+ * Layout: every tensor is contiguous row-major. x, delta, z, y: [B,L,D] with d
+ * fastest; B, C: [B,L,N] with n fastest (shared by all channels); A: [D,N];
+ * conv_w: [D,K]; conv_b, delta_bias, Dskip: [D]; ssm_state: [B,D,N];
+ * conv_state: [B,D,K-1] (oldest input first). x, delta, z, B, C and y have the
+ * I/O dtype (fp32 or bf16); parameters and states are fp32. All arithmetic is fp32.
+ *
+ * Ownership and ordering: every pointer in ss_args is a DEVICE pointer owned by
+ * the caller. The library allocates no device memory; the workspace of
+ * ss_conv_scan_fwd is supplied by the caller (size from ss_workspace_bytes).
+ * All work is enqueued on `stream` (a hipStream_t, NULL = the default stream)
+ * and is asynchronous: the library never synchronises, and inputs, outputs and
+ * workspace must stay valid until the stream has executed the work. Calls that
+ * share a workspace must be ordered on one stream.
+ *
+ * Errors: every call returns an ss_status. Arguments are validated on the host
+ * before anything is enqueued, so a rejected call writes nothing. Rejected:
+ * NULL required pointers, non-positive sizes, unsupported d_state / d_conv /
+ * dtype, pointers not aligned to their element type (4 bytes for fp32 and for
+ * bf16 x/delta/z/y/B/C rows, see below), a too-small workspace, y overlapping an
+ * input. Launch failures return SS_ERR_HIP; ss_last_error() gives the detail
+ * (per calling thread). Faults inside a kernel surface at the caller's next
+ * synchronisation. NaN/Inf inputs propagate and are not checked. Results are
+ * deterministic for a given shape (no floating-point atomics).
+ */
+#ifndef SELSCAN_H
+#define SELSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SS_VERSION 1
+
+typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
+
+typedef enum {
+    SS_OK = 0,
+    SS_ERR_INVALID_ARG = 1,   /* NULL pointer, bad size, misalignment, aliasing */
+    SS_ERR_UNSUPPORTED = 2,   /* d_state / d_conv / dtype outside the built set */
+    SS_ERR_WORKSPACE = 3,     /* workspace NULL or smaller than ss_workspace_bytes */
+    SS_ERR_HIP = 4            /* a HIP runtime call or launch failed */
+} ss_status;
+
+typedef struct {
+    int64_t  batch;     /* B (streams for ss_step), >= 1                                  */
+    int64_t  seqlen;    /* L >= 1 for ss_conv_scan_fwd; ignored by ss_step (one token)     */
+    int64_t  d_inner;   /* D >= 1 channels                                                 */
+    int32_t  d_state;   /* N in {4, 8, 16, 32, 64}                                         */
+    int32_t  d_conv;    /* K; 4 is the only width built                                    */
+    int32_t  io_dtype;  /* ss_dtype of x, delta, z, B, C, y                                */
+    int32_t  reserved;  /* must be 0                                                       */
+} ss_dims;
+
+typedef struct {
+    const void*  x;          /* [B,L,D] io, input to the conv (pre-conv activations)        */
+    const float* conv_w;     /* [D,K] or NULL: NULL means no conv and no SiLU (u = x);
+                                then conv_state must be NULL                                 */
+    const float* conv_b;     /* [D] or NULL (zero)                                          */
+    const void*  delta;      /* [B,L,D] io, pre-softplus step input                          */
+    const float* delta_bias; /* [D] or NULL (zero); added inside the softplus               */
+    const float* A;          /* [D,N] (negative for a decaying state; not checked)          */
+    const void*  B;          /* [B,L,N] io                                                  */
+    const void*  C;          /* [B,L,N] io                                                  */
+    const float* Dskip;      /* [D] or NULL (zero)                                          */
+    const void*  z;          /* [B,L,D] io or NULL (no gate)                                */
+    void*        y;          /* [B,L,D] io, OUT; must not overlap any input                 */
+    float*       ssm_state;  /* [B,D,N] IN/OUT, or NULL: zero initial state, final not
+                                returned. Required by ss_step.                               */
+    float*       conv_state; /* [B,D,K-1] IN/OUT, or NULL: zero history, final not
+                                returned. Required by ss_step when conv_w != NULL.           */
+} ss_args;
+
+/* Bytes of device workspace ss_conv_scan_fwd needs for these dims (0 is
+ * possible). Returns 0 also for invalid dims; ss_conv_scan_fwd then rejects them. */
+size_t ss_workspace_bytes(const ss_dims* dims);
+
+/* Full-sequence forward: y = gate(scan(conv(x))) for every (b, t, d), reading
+ * the initial state from ssm_state / conv_state when given and overwriting them
+ * with the state after token L-1 (so a long sequence can be processed in
+ * pieces, passing the state on). `workspace` is device memory of at least
+ * ss_workspace_bytes(dims) bytes (may be NULL when that is 0); its contents on
+ * entry do not matter. */
+ss_status ss_conv_scan_fwd(const ss_dims* dims, const ss_args* args,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* One decode step for every stream b: the same computation for a single token
+ * (x, delta, z, y: [B,D]; B, C: [B,N]) from the carried state, updating
+ * ssm_state [B,D,N] and conv_state [B,D,K-1] in place. dims->seqlen is ignored. */
+ss_status ss_step(const ss_dims* dims, const ss_args* args, void* stream);
+
+const char* ss_status_str(ss_status s);
+const char* ss_last_error(void);   /* detail of the calling thread's last failure */
+int         ss_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SELSCAN_H */

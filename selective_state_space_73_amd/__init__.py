@@ -1,0 +1,175 @@
+"""Python binding of libselscan (selective-scan S6 forward + decode step on gfx950).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their data pointers and torch's current HIP stream are passed to
+the C ABI declared in include/selscan.h, and every step of the computation
+runs in the library's HIP kernels. There is no CPU fallback: importing the
+package without a built ``libselscan.so`` raises.
+
+Names follow the C ABI: ``ss_conv_scan_fwd``, ``ss_step``,
+``ss_workspace_bytes``, ``ss_version``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libselscan.so")
+
+SS_F32, SS_BF16 = 0, 1
+STATUS = {0: "SS_OK", 1: "SS_ERR_INVALID_ARG", 2: "SS_ERR_UNSUPPORTED", 3: "SS_ERR_WORKSPACE", 4: "SS_ERR_HIP"}
+
+
+class ss_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("d_inner", ctypes.c_int64),
+                ("d_state", ctypes.c_int32), ("d_conv", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+_vp = ctypes.c_void_p
+
+
+class ss_args(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("x", "conv_w", "conv_b", "delta", "delta_bias", "A", "B", "C", "Dskip",
+                                   "z", "y", "ssm_state", "conv_state")]
+
+
+class SelscanError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.ss_workspace_bytes.argtypes = [ctypes.POINTER(ss_dims)]
+    lib.ss_workspace_bytes.restype = ctypes.c_size_t
+    lib.ss_conv_scan_fwd.argtypes = [ctypes.POINTER(ss_dims), ctypes.POINTER(ss_args), _vp, ctypes.c_size_t, _vp]
+    lib.ss_conv_scan_fwd.restype = ctypes.c_int
+    lib.ss_step.argtypes = [ctypes.POINTER(ss_dims), ctypes.POINTER(ss_args), _vp]
+    lib.ss_step.restype = ctypes.c_int
+    lib.ss_status_str.argtypes = [ctypes.c_int]
+    lib.ss_status_str.restype = ctypes.c_char_p
+    lib.ss_last_error.argtypes = []
+    lib.ss_last_error.restype = ctypes.c_char_p
+    lib.ss_version.argtypes = []
+    lib.ss_version.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def ss_version() -> int:
+    return lib.ss_version()
+
+
+def _check(status: int):
+    if status != 0:
+        raise SelscanError(status, lib.ss_last_error().decode())
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SS_F32
+    if t.dtype == torch.bfloat16:
+        return SS_BF16
+    raise TypeError(f"I/O tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor], shape=None, dtype=None, name="") -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def make_dims(batch: int, seqlen: int, d_inner: int, d_state: int, io_dtype: int, d_conv: int = 4) -> ss_dims:
+    return ss_dims(batch, seqlen, d_inner, d_state, d_conv, io_dtype, 0)
+
+
+def ss_workspace_bytes(dims: ss_dims) -> int:
+    return int(lib.ss_workspace_bytes(ctypes.byref(dims)))
+
+
+def _stream_handle(stream) -> Optional[int]:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream or None
+
+
+def _build_args(x, delta, A, B, C, conv_w, conv_b, delta_bias, D, z, y, ssm_state, conv_state,
+                lead, dims: ss_dims):
+    io = x.dtype
+    Dn, N, K = dims.d_inner, dims.d_state, dims.d_conv
+    lead_bd = lead[:1] + (Dn,)
+    return ss_args(
+        x=_ptr(x, lead + (Dn,), io, "x"), conv_w=_ptr(conv_w, (Dn, K), torch.float32, "conv_w"),
+        conv_b=_ptr(conv_b, (Dn,), torch.float32, "conv_b"), delta=_ptr(delta, lead + (Dn,), io, "delta"),
+        delta_bias=_ptr(delta_bias, (Dn,), torch.float32, "delta_bias"), A=_ptr(A, (Dn, N), torch.float32, "A"),
+        B=_ptr(B, lead + (N,), io, "B"), C=_ptr(C, lead + (N,), io, "C"), Dskip=_ptr(D, (Dn,), torch.float32, "D"),
+        z=_ptr(z, lead + (Dn,), io, "z"), y=_ptr(y, lead + (Dn,), io, "y"),
+        ssm_state=_ptr(ssm_state, lead_bd + (N,), torch.float32, "ssm_state"),
+        conv_state=_ptr(conv_state, lead_bd + (K - 1,), torch.float32, "conv_state"))
+
+
+def ss_conv_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, *,
+                     conv_w: Optional[torch.Tensor] = None, conv_b: Optional[torch.Tensor] = None,
+                     delta_bias: Optional[torch.Tensor] = None, D: Optional[torch.Tensor] = None,
+                     z: Optional[torch.Tensor] = None, ssm_state: Optional[torch.Tensor] = None,
+                     conv_state: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Full-sequence forward. x/delta/z: [B,L,D]; B/C: [B,L,N] (float32 or bfloat16, one dtype);
+    A [D,N], conv_w [D,4], conv_b/delta_bias/D [D] float32; ssm_state [B,D,N] and conv_state [B,D,3]
+    float32, updated in place when given. Returns y [B,L,D] in the I/O dtype. Asynchronous on the
+    current stream."""
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, d_inner]")
+    Bsz, L, Dn = x.shape
+    dims = make_dims(Bsz, L, Dn, A.shape[1] if A.dim() == 2 else 0, _io_dtype(x))
+    if y is None:
+        y = torch.empty_like(x)
+    args = _build_args(x, delta, A, B, C, conv_w, conv_b, delta_bias, D, z, y, ssm_state, conv_state,
+                       (Bsz, L), dims)
+    need = ss_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
+    _check(lib.ss_conv_scan_fwd(ctypes.byref(dims), ctypes.byref(args), workspace.data_ptr() if need else None,
+                                workspace.numel(), _stream_handle(stream)))
+    return y
+
+
+def ss_step(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+            ssm_state: torch.Tensor, *, conv_state: Optional[torch.Tensor] = None,
+            conv_w: Optional[torch.Tensor] = None, conv_b: Optional[torch.Tensor] = None,
+            delta_bias: Optional[torch.Tensor] = None, D: Optional[torch.Tensor] = None,
+            z: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step. x/delta/z: [S,D]; B/C: [S,N]; ssm_state [S,D,N] and conv_state [S,D,3]
+    float32, updated in place. Returns y [S,D]."""
+    if x.dim() != 2:
+        raise ValueError("x must be [streams, d_inner]")
+    S, Dn = x.shape
+    dims = make_dims(S, 1, Dn, A.shape[1] if A.dim() == 2 else 0, _io_dtype(x))
+    if y is None:
+        y = torch.empty_like(x)
+    args = _build_args(x, delta, A, B, C, conv_w, conv_b, delta_bias, D, z, y, ssm_state, conv_state, (S,), dims)
+    _check(lib.ss_step(ctypes.byref(dims), ctypes.byref(args), _stream_handle(stream)))
+    return y
+
+
+__all__ = ["ss_conv_scan_fwd", "ss_step", "ss_workspace_bytes", "ss_version", "make_dims", "ss_dims", "ss_args",
+           "SelscanError", "SS_F32", "SS_BF16", "LIB_PATH", "lib"]

@@ -1,0 +1,238 @@
+// C ABI of libselscan: argument validation, workspace layout, launch dispatch.
+// Declared in include/selscan.h. Nothing here touches the device before all
+// arguments have been validated, so a rejected call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "selscan.h"
+#include "selscan_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ss_status fail(ss_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+constexpr int64_t kMaxGridYZ = 65535;
+constexpr int64_t kMinChunk = 256;        // shortest chunk worth a separate aggregate
+constexpr int64_t kTargetGroups = 512;    // workgroups (of 4 waves) the scan aims to launch
+
+bool supported_n(int n) { return n == 4 || n == 8 || n == 16 || n == 32 || n == 64; }
+
+size_t io_size(int dt) { return dt == SS_BF16 ? 2 : 4; }
+
+// Chunk count for the full-sequence scan. One chunk when batch x channel
+// workgroups already fill the GPU; otherwise enough chunks (each at least
+// kMinChunk tokens) to reach about kTargetGroups workgroups.
+// SELSCAN_CHUNKS=<n> overrides the count (tuning only).
+int choose_chunks(const ss_dims& d) {
+    const int64_t col_groups = (d.d_inner + selscan::kScanThreads - 1) / selscan::kScanThreads;
+    const int64_t base = d.batch * col_groups;
+    int64_t nc = 1;
+    static const int64_t env = [] {
+        const char* e = std::getenv("SELSCAN_CHUNKS");
+        return e ? std::atoll(e) : int64_t(0);
+    }();
+    if (env > 0) {
+        nc = env;
+    } else if (base < 256) {
+        nc = (kTargetGroups + base - 1) / base;
+    }
+    const int64_t max_by_len = d.seqlen / kMinChunk > 0 ? d.seqlen / kMinChunk : 1;
+    if (env <= 0 && nc > max_by_len) nc = max_by_len;
+    if (nc > d.seqlen) nc = d.seqlen;
+    if (nc > kMaxGridYZ) nc = kMaxGridYZ;
+    if (nc < 1) nc = 1;
+    // equalise: every chunk has ceil(L / nc) tokens except the last
+    const int64_t len = (d.seqlen + nc - 1) / nc;
+    return (int)((d.seqlen + len - 1) / len);
+}
+
+struct Layout {
+    int nchunks = 1;
+    int64_t chunk_len = 0;
+    size_t off_S = 0, off_sdt = 0, off_h0 = 0, off_c0 = 0, total = 0;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+Layout layout(const ss_dims& d) {
+    Layout l;
+    l.nchunks = choose_chunks(d);
+    l.chunk_len = (d.seqlen + l.nchunks - 1) / l.nchunks;
+    const size_t B = (size_t)d.batch, D = (size_t)d.d_inner, N = (size_t)d.d_state;
+    size_t off = 0;
+    if (l.nchunks > 1) {
+        const size_t na = (size_t)(l.nchunks - 1);
+        l.off_S = off;   off = align256(off + B * na * D * N * sizeof(float));
+        l.off_sdt = off; off = align256(off + B * na * D * sizeof(float));
+        l.off_h0 = off;  off = align256(off + B * D * N * sizeof(float));
+        l.off_c0 = off;  off = align256(off + B * D * (size_t)(d.d_conv - 1) * sizeof(float));
+    }
+    l.total = off;
+    return l;
+}
+
+ss_status check_dims(const ss_dims* d, bool step) {
+    if (!d) return fail(SS_ERR_INVALID_ARG, "dims is NULL");
+    if (d->reserved != 0) return fail(SS_ERR_INVALID_ARG, "dims.reserved must be 0");
+    if (d->batch < 1 || d->batch > kMaxGridYZ)
+        return fail(SS_ERR_INVALID_ARG, "batch %lld outside [1, %lld]", (long long)d->batch, (long long)kMaxGridYZ);
+    if (!step && d->seqlen < 1) return fail(SS_ERR_INVALID_ARG, "seqlen %lld < 1", (long long)d->seqlen);
+    if (d->d_inner < 1 || d->d_inner > (int64_t(1) << 30))
+        return fail(SS_ERR_INVALID_ARG, "d_inner %lld outside [1, 2^30]", (long long)d->d_inner);
+    if (!supported_n(d->d_state)) return fail(SS_ERR_UNSUPPORTED, "d_state %d not in {4,8,16,32,64}", d->d_state);
+    if (d->d_conv != 4) return fail(SS_ERR_UNSUPPORTED, "d_conv %d: only 4 is built", d->d_conv);
+    if (d->io_dtype != SS_F32 && d->io_dtype != SS_BF16)
+        return fail(SS_ERR_UNSUPPORTED, "io_dtype %d unknown", d->io_dtype);
+    if (!step) {
+        const double elems = (double)d->batch * (double)d->seqlen * (double)d->d_inner;
+        if (elems > 9.0e18 / 64) return fail(SS_ERR_INVALID_ARG, "tensor too large");
+    }
+    return SS_OK;
+}
+
+struct Range { const void* p; size_t bytes; const char* name; };
+
+bool overlap(const Range& a, const Range& b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.bytes, b0 = (uintptr_t)b.p, b1 = b0 + b.bytes;
+    return a0 < b1 && b0 < a1;
+}
+
+ss_status check_args(const ss_dims& d, const ss_args* a, bool step) {
+    if (!a) return fail(SS_ERR_INVALID_ARG, "args is NULL");
+    const int64_t L = step ? 1 : d.seqlen;
+    const size_t es = io_size(d.io_dtype);
+    const size_t BLD = (size_t)d.batch * (size_t)L * (size_t)d.d_inner;
+    const size_t BLN = (size_t)d.batch * (size_t)L * (size_t)d.d_state;
+    const size_t D = (size_t)d.d_inner, N = (size_t)d.d_state, K = (size_t)d.d_conv;
+    const size_t BD = (size_t)d.batch * D;
+    struct Req { const void* p; const char* name; };
+    const Req req[] = {{a->x, "x"}, {a->delta, "delta"}, {a->A, "A"}, {a->B, "B"}, {a->C, "C"}, {a->y, "y"}};
+    for (const Req& r : req)
+        if (!r.p) return fail(SS_ERR_INVALID_ARG, "%s is NULL", r.name);
+    if (step && !a->ssm_state) return fail(SS_ERR_INVALID_ARG, "ss_step needs ssm_state");
+    if (step && a->conv_w && !a->conv_state) return fail(SS_ERR_INVALID_ARG, "ss_step with conv_w needs conv_state");
+    if (!a->conv_w && a->conv_state) return fail(SS_ERR_INVALID_ARG, "conv_state given without conv_w");
+
+    const Range in[] = {
+        {a->x, BLD * es, "x"}, {a->delta, BLD * es, "delta"}, {a->z, BLD * es, "z"},
+        {a->B, BLN * es, "B"}, {a->C, BLN * es, "C"}, {a->A, D * N * 4, "A"},
+        {a->conv_w, D * K * 4, "conv_w"}, {a->conv_b, D * 4, "conv_b"},
+        {a->delta_bias, D * 4, "delta_bias"}, {a->Dskip, D * 4, "Dskip"},
+        {a->ssm_state, BD * N * 4, "ssm_state"}, {a->conv_state, BD * (K - 1) * 4, "conv_state"},
+    };
+    for (const Range& r : in)
+        if (r.p && ((uintptr_t)r.p & 3u)) return fail(SS_ERR_INVALID_ARG, "%s not 4-byte aligned", r.name);
+    if ((uintptr_t)a->y & 3u) return fail(SS_ERR_INVALID_ARG, "y not 4-byte aligned");
+    if (a->ssm_state && ((uintptr_t)a->ssm_state & 15u))
+        return fail(SS_ERR_INVALID_ARG, "ssm_state not 16-byte aligned");
+    const Range yr{a->y, BLD * es, "y"};
+    for (const Range& r : in)
+        if (overlap(yr, r)) return fail(SS_ERR_INVALID_ARG, "y overlaps %s", r.name);
+    if (overlap(Range{a->ssm_state, BD * N * 4, "ssm_state"}, Range{a->conv_state, BD * (K - 1) * 4, "conv_state"}))
+        return fail(SS_ERR_INVALID_ARG, "ssm_state overlaps conv_state");
+    for (int i = 0; i < 10; ++i) {
+        if (overlap(Range{a->ssm_state, BD * N * 4, "ssm_state"}, in[i]))
+            return fail(SS_ERR_INVALID_ARG, "ssm_state overlaps %s", in[i].name);
+        if (overlap(Range{a->conv_state, BD * (K - 1) * 4, "conv_state"}, in[i]))
+            return fail(SS_ERR_INVALID_ARG, "conv_state overlaps %s", in[i].name);
+    }
+    return SS_OK;
+}
+
+selscan::LaunchScan make_launch(const ss_dims& d, const ss_args& a, void* stream) {
+    selscan::LaunchScan p{};
+    p.batch = d.batch; p.L = d.seqlen; p.D = d.d_inner; p.N = d.d_state; p.bf16 = d.io_dtype == SS_BF16;
+    p.x = a.x; p.conv_w = a.conv_w; p.conv_b = a.conv_b; p.delta = a.delta; p.delta_bias = a.delta_bias;
+    p.A = a.A; p.B = a.B; p.C = a.C; p.Dskip = a.Dskip; p.z = a.z; p.y = a.y;
+    p.ssm_state = a.ssm_state; p.conv_state = a.conv_state;
+    p.stream = stream;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ss_workspace_bytes(const ss_dims* dims) {
+    if (check_dims(dims, false) != SS_OK) return 0;
+    return layout(*dims).total;
+}
+
+ss_status ss_conv_scan_fwd(const ss_dims* dims, const ss_args* args, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    ss_status s = check_dims(dims, false);
+    if (s != SS_OK) return s;
+    s = check_args(*dims, args, false);
+    if (s != SS_OK) return s;
+    const Layout l = layout(*dims);
+    if (l.total > 0 && (!workspace || workspace_bytes < l.total))
+        return fail(SS_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, l.total);
+    if (workspace && ((uintptr_t)workspace & 255u))
+        return fail(SS_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+    const Range wr{workspace, l.total, "workspace"};
+    const Range others[] = {{args->x, 1, "x"}, {args->y, 1, "y"}, {args->B, 1, "B"}, {args->C, 1, "C"},
+                            {args->delta, 1, "delta"}, {args->ssm_state, 1, "ssm_state"}};
+    for (const Range& r : others)
+        if (overlap(wr, r)) return fail(SS_ERR_INVALID_ARG, "workspace overlaps %s", r.name);
+
+    selscan::LaunchScan p = make_launch(*dims, *args, stream);
+    char* ws = static_cast<char*>(workspace);
+    p.nchunks = l.nchunks;
+    p.chunk_len = l.chunk_len;
+    if (l.nchunks > 1) {
+        p.ws_S = reinterpret_cast<float*>(ws + l.off_S);
+        p.ws_sdt = reinterpret_cast<float*>(ws + l.off_sdt);
+        p.ws_h0 = reinterpret_cast<float*>(ws + l.off_h0);
+        p.ws_c0 = reinterpret_cast<float*>(ws + l.off_c0);
+    }
+    const hipError_t e = selscan::launch_scan(p);
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return SS_OK;
+}
+
+ss_status ss_step(const ss_dims* dims, const ss_args* args, void* stream) {
+    ss_status s = check_dims(dims, true);
+    if (s != SS_OK) return s;
+    s = check_args(*dims, args, true);
+    if (s != SS_OK) return s;
+    ss_dims one = *dims;
+    one.seqlen = 1;
+    selscan::LaunchScan p = make_launch(one, *args, stream);
+    const hipError_t e = selscan::launch_step(p);
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return SS_OK;
+}
+
+const char* ss_status_str(ss_status s) {
+    switch (s) {
+        case SS_OK: return "ok";
+        case SS_ERR_INVALID_ARG: return "invalid argument";
+        case SS_ERR_UNSUPPORTED: return "unsupported configuration";
+        case SS_ERR_WORKSPACE: return "workspace missing or too small";
+        case SS_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* ss_last_error(void) { return g_last_error.c_str(); }
+
+int ss_version(void) { return SS_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// Internal interface between the C-ABI layer and the HIP kernels of libselscan.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace selscan {
+
+constexpr int kScanThreads = 256;   // channels per workgroup of the scan kernels (4 waves)
+constexpr int kStepThreads = 256;   // channels per workgroup of the decode-step kernel
+constexpr int kScanTile = 64;       // tokens of B/C staged in LDS at a time
+
+// Everything a launch needs, already validated by the C-ABI layer.
+struct LaunchScan {
+    int64_t batch, L, D;
+    int N;
+    bool bf16;
+    const void* x; const float* conv_w; const float* conv_b; const void* delta; const float* delta_bias;
+    const float* A; const void* B; const void* C; const float* Dskip; const void* z; void* y;
+    float* ssm_state; float* conv_state;
+    // chunking and workspace (scan only)
+    int nchunks; int64_t chunk_len;
+    float* ws_S;    // [B, nchunks-1, D, N]
+    float* ws_sdt;  // [B, nchunks-1, D]
+    float* ws_h0;   // [B, D, N]
+    float* ws_c0;   // [B, D, K-1]
+    void* stream;
+};
+
+hipError_t launch_scan(const LaunchScan& p);
+hipError_t launch_step(const LaunchScan& p);
+
+}  // namespace selscan

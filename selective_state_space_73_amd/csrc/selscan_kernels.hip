@@ -1,0 +1,420 @@
+// HIP kernels of libselscan for gfx950 (CDNA4, wave64).
+//
+// The selective scan (S6) forward path: causal depthwise conv1d + SiLU,
+// softplus step size, exp(Delta A) decay, Euler write term Delta B u, readout
+// C.h + D u, SiLU(z) gate (ai360xpert.com "Mamba", "The selection mechanism";
+// ozercemkelahmet.com "Mamba", "A minimal selective scan in PyTorch"; bembew.net
+// "Overview of Mamba (SSM) Model", "How the Mamba Block Works").
+//
+// Mapping: one lane owns one (batch row, channel) pair and keeps its N state
+// values in VGPRs for a run of consecutive tokens (a chunk). Loads of x, delta,
+// z and stores of y are coalesced along d. B_t and C_t are the same for every
+// channel: each workgroup stages them through LDS in fp32 tiles and every wave
+// reads them back as broadcasts.
+//
+// Long sequences with few channels are split into chunks so the grid fills the
+// GPU. The recurrence h_t = a_t h_{t-1} + b_t is associative in the pair (a, b)
+// (ai360xpert.com "Mamba", "Why this breaks the parallel form": the scan exploits
+// associativity; ozercemkelahmet.com "Deployment notes": chunks pass the state).
+// A first pass computes each chunk's end state from zero, S_c, and its summed
+// step size, so that the chunk's total decay is exp(A * sum Delta); the main pass
+// folds these aggregates of all earlier chunks into its carry-in and then runs
+// the chunk with the exact initial state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "selscan_internal.h"
+
+namespace selscan {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// elementwise pieces (fp32)
+
+__device__ __forceinline__ float exp2_fast(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ __forceinline__ float log2_fast(float v) { return __builtin_amdgcn_logf(v); }
+__device__ __forceinline__ float rcp_fast(float v) { return __builtin_amdgcn_rcpf(v); }
+
+// SiLU(v) = v / (1 + e^-v)
+__device__ __forceinline__ float silu(float v) {
+    return v * rcp_fast(1.0f + exp2_fast(-kLog2e * v));
+}
+
+// softplus(v) = max(v,0) + log1p(e^-|v|). log1p(e) is taken as log(1+e) plus the
+// rounding error of 1+e, which keeps relative accuracy when e is small.
+__device__ __forceinline__ float softplus(float v) {
+    const float e = exp2_fast(-kLog2e * __builtin_fabsf(v));
+    const float s = 1.0f + e;
+    const float corr = e - (s - 1.0f);
+    const float lp = __builtin_fmaf(log2_fast(s), kLn2, corr);
+    return __builtin_fmaxf(v, 0.0f) + lp;
+}
+
+template <typename T> struct IO;
+template <> struct IO<float> {
+    static __device__ __forceinline__ float cvt(float v) { return v; }
+    static __device__ __forceinline__ float ld(const float* p) { return *p; }
+    static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+};
+template <> struct IO<uint16_t> {   // bfloat16 bits
+    static __device__ __forceinline__ float cvt(uint16_t v) {
+        return __builtin_bit_cast(float, static_cast<uint32_t>(v) << 16);
+    }
+    static __device__ __forceinline__ float ld(const uint16_t* p) {
+        return __builtin_bit_cast(float, static_cast<uint32_t>(*p) << 16);
+    }
+    static __device__ __forceinline__ void st(uint16_t* p, float v) {
+        *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));   // round to nearest even
+    }
+};
+
+// ---------------------------------------------------------------------------
+// The chunk pass. MAIN = true: full forward over the chunk with outputs.
+// MAIN = false: aggregate pass (end state from the chunk's initial state, and the
+// summed step size), no outputs.
+
+struct ScanArgs {
+    int64_t L;            // sequence length
+    int64_t chunk_len;    // tokens per chunk
+    int D;                // channels
+    int nchunks;
+};
+
+template <typename T, int N, bool CONV, bool GATE, bool MAIN>
+__global__ void __launch_bounds__(kScanThreads)
+k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
+       const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
+       const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
+       const T* __restrict__ z, T* __restrict__ y,
+       float* __restrict__ ssm_state,        // MAIN: IN (nchunks==1) and OUT (last chunk); AGG: IN
+       float* __restrict__ conv_state,       // MAIN: IN (nchunks==1) and OUT (last chunk); AGG: IN
+       float* __restrict__ ws_S,             // [B, nchunks-1, D, N] chunk end states (chunk 0 includes h0)
+       float* __restrict__ ws_sdt,           // [B, nchunks-1, D] summed step sizes
+       float* __restrict__ ws_h0,            // [B, D, N] copy of the initial state (nchunks > 1)
+       float* __restrict__ ws_c0,            // [B, D, K-1] copy of the initial conv history (nchunks > 1)
+       ScanArgs sa) {
+    const int D = sa.D;
+    const int d_raw = blockIdx.x * kScanThreads + threadIdx.x;
+    // lanes past the last channel work on the last channel: they compute and store
+    // bit-identical values, so no store needs a branch
+    const int d = d_raw < D ? d_raw : D - 1;
+    const int c = blockIdx.y;
+    const int b = blockIdx.z;
+    const int64_t t0 = (int64_t)c * sa.chunk_len;
+    const int64_t t1 = (t0 + sa.chunk_len < sa.L) ? t0 + sa.chunk_len : sa.L;
+    const int nagg = sa.nchunks - 1;
+    const bool multi = sa.nchunks > 1;
+
+    // per-channel parameters
+    float A2[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) A2[n] = A[(int64_t)d * N + n] * kLog2e;
+    const float dbias = delta_bias ? delta_bias[d] : 0.0f;
+    const float dsk = Dskip ? Dskip[d] : 0.0f;
+    float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 1.f, cb = 0.f;
+    if (CONV) {
+        w0 = conv_w[d * 4 + 0]; w1 = conv_w[d * 4 + 1]; w2 = conv_w[d * 4 + 2]; w3 = conv_w[d * 4 + 3];
+        cb = conv_b ? conv_b[d] : 0.0f;
+    }
+
+    // initial state of this chunk
+    float h[N];
+    const int64_t bd = (int64_t)b * D + d;
+    if (c == 0) {
+        // with several chunks the main pass reads the copy the aggregate pass made,
+        // because the last chunk overwrites ssm_state
+        const float* src = (ssm_state && MAIN && multi) ? ws_h0 : ssm_state;
+#pragma unroll
+        for (int n = 0; n < N; ++n) h[n] = src ? src[bd * N + n] : 0.0f;
+        if (!MAIN && multi && ssm_state) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) ws_h0[bd * N + n] = h[n];
+        }
+    } else {
+        // aggregate pass: chunks after the first start from zero. Main pass: fold
+        // the aggregates of chunks 0..c-1 into the carry-in.
+#pragma unroll
+        for (int n = 0; n < N; ++n) h[n] = 0.0f;
+        for (int cc = 0; MAIN && cc < c; ++cc) {
+            const int64_t ai = ((int64_t)b * nagg + cc) * D + d;
+            const float sdt = ws_sdt[ai];
+#pragma unroll
+            for (int n = 0; n < N; ++n)
+                h[n] = __builtin_fmaf(exp2_fast(sdt * A2[n]), h[n], ws_S[ai * N + n]);
+        }
+    }
+
+    // conv history x_{t0-3}, x_{t0-2}, x_{t0-1}: from x where t0-k >= 0, else from
+    // the initial history (the main pass of a multi-chunk call reads the copy the
+    // aggregate pass made, because the last chunk overwrites conv_state)
+    float x3 = 0.f, x2 = 0.f, x1 = 0.f;
+    if (CONV) {
+        const float* hsrc = conv_state ? ((MAIN && multi) ? ws_c0 : conv_state) : nullptr;
+        float xh[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int64_t tt = t0 - 3 + j;
+            xh[j] = tt >= 0 ? IO<T>::ld(x + ((int64_t)b * sa.L + tt) * D + d)
+                            : (hsrc ? hsrc[bd * 3 + (3 + tt)] : 0.0f);
+        }
+        x3 = xh[0]; x2 = xh[1]; x1 = xh[2];
+        if (!MAIN && multi && c == 0 && conv_state) {
+            ws_c0[bd * 3 + 0] = conv_state[bd * 3 + 0];
+            ws_c0[bd * 3 + 1] = conv_state[bd * 3 + 1];
+            ws_c0[bd * 3 + 2] = conv_state[bd * 3 + 2];
+        }
+    }
+
+    // Token loop. B_t/C_t are staged through LDS in tiles of R tokens (double
+    // buffered, one barrier per tile) and read back as wave-uniform broadcasts.
+    // x/delta/z are prefetched U tokens ahead as raw bits and widened at use.
+    // Rows past the chunk end are clamped to its last row: loaded, never used.
+    constexpr int U = 4;
+    constexpr int R = kScanTile;
+    constexpr int NB = MAIN ? 2 * N : N;                // staged values per token
+    __shared__ float sbc[2][R][NB];
+    const int64_t row0 = (int64_t)b * sa.L;
+    const int tid = threadIdx.x;
+
+    // cooperative tile load: element e of the tile is (row e / N, state e % N)
+    constexpr int TILE_ELEMS = R * N;
+    constexpr int PER_THREAD = (TILE_ELEMS + kScanThreads - 1) / kScanThreads;
+    T tb[PER_THREAD], tc[PER_THREAD];
+    auto tile_fetch = [&](int64_t tbase) {
+#pragma unroll
+        for (int k = 0; k < PER_THREAD; ++k) {
+            const int e = tid + k * kScanThreads;
+            const int r = (e < TILE_ELEMS ? e : TILE_ELEMS - 1) / N;
+            const int n = (e < TILE_ELEMS ? e : TILE_ELEMS - 1) % N;
+            const int64_t t = (tbase + r < t1) ? tbase + r : t1 - 1;
+            tb[k] = Bm[(row0 + t) * N + n];
+            if (MAIN) tc[k] = Cm[(row0 + t) * N + n];
+        }
+    };
+    auto tile_store = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < PER_THREAD; ++k) {
+            const int e = tid + k * kScanThreads;
+            if (e < TILE_ELEMS) {
+                sbc[buf][e / N][e % N] = IO<T>::cvt(tb[k]);
+                if (MAIN) sbc[buf][e / N][N + e % N] = IO<T>::cvt(tc[k]);
+            }
+        }
+    };
+
+    float sdt = 0.0f;
+    T px[U], pd[U], pz[U];
+    auto load_group = [&](int64_t tg) {
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int64_t t = (tg + i < t1) ? tg + i : t1 - 1;
+            const int64_t ri = (row0 + t) * D + d;
+            px[i] = x[ri];
+            pd[i] = delta[ri];
+            if (MAIN && GATE) pz[i] = z[ri];
+        }
+    };
+
+    if (t0 < t1) {
+        tile_fetch(t0);
+        tile_store(0);
+        load_group(t0);
+    }
+    __syncthreads();
+    int buf = 0;
+    for (int64_t tt = t0; tt < t1; tt += R) {
+        const bool more = tt + R < t1;
+        if (more) tile_fetch(tt + R);
+        const int64_t tend = (tt + R < t1) ? tt + R : t1;
+        for (int64_t tg = tt; tg < tend; tg += U) {
+            T cx[U], cd[U], cz[U];
+#pragma unroll
+            for (int i = 0; i < U; ++i) { cx[i] = px[i]; cd[i] = pd[i]; cz[i] = pz[i]; }
+            if (tg + U < t1) load_group(tg + U);
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const int64_t t = tg + i;
+                if (t >= tend) break;
+                const float* bct = sbc[buf][t - tt];
+                const float xt = IO<T>::cvt(cx[i]);
+                float u;
+                if (CONV) {
+                    const float cv = __builtin_fmaf(w3, xt, __builtin_fmaf(w2, x1, __builtin_fmaf(w1, x2, __builtin_fmaf(w0, x3, cb))));
+                    x3 = x2; x2 = x1; x1 = xt;
+                    u = silu(cv);
+                } else {
+                    u = xt;
+                }
+                const float dt = softplus(IO<T>::cvt(cd[i]) + dbias);
+                const float wv = dt * u;
+#pragma unroll
+                for (int n = 0; n < N; ++n) {
+                    const float a = exp2_fast(dt * A2[n]);
+                    h[n] = __builtin_fmaf(a, h[n], wv * bct[n]);
+                }
+                if (MAIN) {
+                    float ya = dsk * u, yb = 0.0f;
+#pragma unroll
+                    for (int n = 0; n < N; n += 2) {
+                        ya = __builtin_fmaf(bct[N + n], h[n], ya);
+                        yb = __builtin_fmaf(bct[N + n + 1], h[n + 1], yb);
+                    }
+                    float yv = ya + yb;
+                    if (GATE) yv *= silu(IO<T>::cvt(cz[i]));
+                    // lanes past the last channel were clamped to it and store the same value
+                    IO<T>::st(y + (row0 + t) * D + d, yv);
+                } else {
+                    sdt += dt;
+                }
+            }
+        }
+        if (more) tile_store(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+    }
+
+    if (MAIN) {
+        if (c == sa.nchunks - 1) {
+            if (ssm_state) {
+#pragma unroll
+                for (int n = 0; n < N; ++n) ssm_state[bd * N + n] = h[n];
+            }
+            if (CONV && conv_state) {
+                conv_state[bd * 3 + 0] = x3; conv_state[bd * 3 + 1] = x2; conv_state[bd * 3 + 2] = x1;
+            }
+        }
+    } else {
+        const int64_t ai = ((int64_t)b * nagg + c) * D + d;
+        ws_sdt[ai] = sdt;
+#pragma unroll
+        for (int n = 0; n < N; ++n) ws_S[ai * N + n] = h[n];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode step: one lane per (stream, channel); both states read and written in place.
+
+template <typename T, int N, bool CONV, bool GATE>
+__global__ void __launch_bounds__(kStepThreads)
+k_step(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
+       const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
+       const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
+       const T* __restrict__ z, T* __restrict__ y, float* __restrict__ ssm_state,
+       float* __restrict__ conv_state, int D) {
+    const int d = blockIdx.x * kStepThreads + threadIdx.x;
+    const int s = blockIdx.y;
+    if (d >= D) return;
+    const int64_t sd = (int64_t)s * D + d;
+
+    float h[N];
+    const float4* hp = reinterpret_cast<const float4*>(ssm_state + sd * N);
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+        const float4 v = hp[q];
+        h[4 * q + 0] = v.x; h[4 * q + 1] = v.y; h[4 * q + 2] = v.z; h[4 * q + 3] = v.w;
+    }
+    const float xt = IO<T>::ld(x + sd);
+    float u;
+    if (CONV) {
+        float* cs = conv_state + sd * 3;
+        const float x3 = cs[0], x2 = cs[1], x1 = cs[2];
+        const float cb = conv_b ? conv_b[d] : 0.0f;
+        const float cv = __builtin_fmaf(conv_w[d * 4 + 3], xt, __builtin_fmaf(conv_w[d * 4 + 2], x1,
+                         __builtin_fmaf(conv_w[d * 4 + 1], x2, __builtin_fmaf(conv_w[d * 4 + 0], x3, cb))));
+        cs[0] = x2; cs[1] = x1; cs[2] = xt;
+        u = silu(cv);
+    } else {
+        u = xt;
+    }
+    const float dt = softplus(IO<T>::ld(delta + sd) + (delta_bias ? delta_bias[d] : 0.0f));
+    const float wv = dt * u;
+    const T* Bs = Bm + (int64_t)s * N;
+    const T* Cs = Cm + (int64_t)s * N;
+    float ya = (Dskip ? Dskip[d] : 0.0f) * u, yb = 0.0f;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const float a = exp2_fast(dt * (A[(int64_t)d * N + n] * kLog2e));
+        h[n] = __builtin_fmaf(a, h[n], wv * IO<T>::ld(Bs + n));
+        if (n & 1) yb = __builtin_fmaf(IO<T>::ld(Cs + n), h[n], yb);
+        else       ya = __builtin_fmaf(IO<T>::ld(Cs + n), h[n], ya);
+    }
+    float yv = ya + yb;
+    if (GATE) yv *= silu(IO<T>::ld(z + sd));
+    IO<T>::st(y + sd, yv);
+    float4* hw = reinterpret_cast<float4*>(ssm_state + sd * N);
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) hw[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+
+template <typename T, int N, bool CONV, bool GATE>
+static hipError_t launch_scan_t(const LaunchScan& p) {
+    const T* x = static_cast<const T*>(p.x);
+    const T* dl = static_cast<const T*>(p.delta);
+    const T* z = static_cast<const T*>(p.z);
+    T* y = static_cast<T*>(p.y);
+    hipStream_t st = static_cast<hipStream_t>(p.stream);
+    ScanArgs sa{p.L, p.chunk_len, (int)p.D, p.nchunks};
+    const unsigned gx = (unsigned)((p.D + kScanThreads - 1) / kScanThreads);
+    if (p.nchunks > 1) {
+        hipLaunchKernelGGL((k_scan<T, N, CONV, GATE, false>), dim3(gx, p.nchunks - 1, (unsigned)p.batch),
+                           dim3(kScanThreads), 0, st, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
+                           static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip, z, y, p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, sa);
+    }
+    hipLaunchKernelGGL((k_scan<T, N, CONV, GATE, true>), dim3(gx, p.nchunks, (unsigned)p.batch),
+                       dim3(kScanThreads), 0, st, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
+                       static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip, z, y, p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, sa);
+    return hipGetLastError();
+}
+
+template <typename T, int N, bool CONV, bool GATE>
+static hipError_t launch_step_t(const LaunchScan& p) {
+    hipStream_t st = static_cast<hipStream_t>(p.stream);
+    const unsigned gx = (unsigned)((p.D + kStepThreads - 1) / kStepThreads);
+    hipLaunchKernelGGL((k_step<T, N, CONV, GATE>), dim3(gx, (unsigned)p.batch), dim3(kStepThreads), 0, st,
+                       static_cast<const T*>(p.x), p.conv_w, p.conv_b, static_cast<const T*>(p.delta),
+                       p.delta_bias, p.A, static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip,
+                       static_cast<const T*>(p.z), static_cast<T*>(p.y), p.ssm_state, p.conv_state, (int)p.D);
+    return hipGetLastError();
+}
+
+template <typename T, int N>
+static hipError_t dispatch_flags(const LaunchScan& p, bool step) {
+    const bool conv = p.conv_w != nullptr, gate = p.z != nullptr;
+    if (step) {
+        if (conv && gate) return launch_step_t<T, N, true, true>(p);
+        if (conv) return launch_step_t<T, N, true, false>(p);
+        if (gate) return launch_step_t<T, N, false, true>(p);
+        return launch_step_t<T, N, false, false>(p);
+    }
+    if (conv && gate) return launch_scan_t<T, N, true, true>(p);
+    if (conv) return launch_scan_t<T, N, true, false>(p);
+    if (gate) return launch_scan_t<T, N, false, true>(p);
+    return launch_scan_t<T, N, false, false>(p);
+}
+
+template <typename T>
+static hipError_t dispatch_n(const LaunchScan& p, bool step) {
+    switch (p.N) {
+        case 4: return dispatch_flags<T, 4>(p, step);
+        case 8: return dispatch_flags<T, 8>(p, step);
+        case 16: return dispatch_flags<T, 16>(p, step);
+        case 32: return dispatch_flags<T, 32>(p, step);
+        case 64: return dispatch_flags<T, 64>(p, step);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_scan(const LaunchScan& p) {
+    return p.bf16 ? dispatch_n<uint16_t>(p, false) : dispatch_n<float>(p, false);
+}
+
+hipError_t launch_step(const LaunchScan& p) {
+    return p.bf16 ? dispatch_n<uint16_t>(p, true) : dispatch_n<float>(p, true);
+}
+
+}  // namespace selscan

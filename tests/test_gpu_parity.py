@@ -1,0 +1,229 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on the
+same seeded inputs. Tolerances: max relative error 1e-4 for fp32 I/O, 2e-2 for
+bf16 I/O (fp32 state in both); conv history must match exactly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import TOL, gpu_fwd, host, maxrel, oracle_fwd, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ss():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_73_amd as mod
+    return mod
+
+
+def _check_fwd(ss, spec, *, seed=None, shape=None, states=False, flags=None, dsel=None, label=""):
+    shape = shape or {}
+    inp = W.gen_scan_inputs(spec, seed=seed, **shape)
+    Bsz, L, Dn = inp["x"].shape
+    N = inp["A"].shape[1]
+    st = W.gen_states(Bsz, Dn, N) if states else None
+    g = to_dev(inp, spec.io_dtype)
+    hs = torch.from_numpy(st["ssm_state"]).cuda() if states else None
+    cs = torch.from_numpy(st["conv_state"]).cuda() if states else None
+    y = gpu_fwd(ss, g, hs, cs, flags)
+    torch.cuda.synchronize()
+    yr, hr, cr = oracle_fwd(inp, st["ssm_state"] if states else None, st["conv_state"] if states else None,
+                            flags, dsel)
+    yg = host(y) if dsel is None else host(y[:, :, torch.as_tensor(dsel, device=y.device)])
+    tol = TOL[spec.io_dtype]
+    e = maxrel(yg, yr)
+    print(f"{label} y maxrel {e:.3e}", flush=True)
+    assert e <= tol, (label, e)
+    if states:
+        hg = host(hs) if dsel is None else host(hs)[:, dsel]
+        eh = maxrel(hg, hr)
+        assert eh <= tol, (label, "ssm_state", eh)
+        if (flags or {}).get("conv", True):
+            cg = host(cs) if dsel is None else host(cs)[:, dsel]
+            assert np.array_equal(cg.astype(np.float64), cr), (label, "conv_state")
+    return e
+
+
+# ----------------------------------------------------------------------------- workloads
+
+@pytest.mark.parametrize("states", [False, True])
+def test_tiny_full(ss, states):
+    _check_fwd(ss, W.WORKLOADS["tiny"], states=states, label="tiny")
+
+
+@pytest.mark.parametrize("states", [False, True])
+def test_block_full(ss, states):
+    _check_fwd(ss, W.WORKLOADS["block"], states=states, label="block")
+
+
+def test_train_full_size_sampled_channels(ss):
+    # the full batch/sequence on the GPU, the oracle on 96 channels spread over d
+    dsel = np.unique(np.concatenate([np.arange(0, 5120, 61), [0, 1, 63, 64, 255, 256, 5119]]))
+    _check_fwd(ss, W.WORKLOADS["train"], states=True, dsel=dsel, label="train")
+
+
+def test_long_full_size_sampled_channels(ss):
+    # chunked path: the full 131072-token sequence, the oracle on 12 channels
+    dsel = np.array([0, 1, 2, 63, 64, 255, 256, 1000, 1023, 1024, 2046, 2047])
+    _check_fwd(ss, W.WORKLOADS["long"], states=True, dsel=dsel, label="long")
+
+
+def test_decode_full_shape_sampled(ss):
+    """Decode shapes (64 streams x 8192 channels, N=16, bf16 token inputs, fp32
+    states) for 2 layers x 20 steps from N(0,1) states, one ss_step per
+    layer-step; the oracle follows 6 streams x 40 channels of each layer."""
+    spec = W.DECODE
+    S, Dn, N = spec.streams, spec.d_inner, spec.d_state
+    steps = 20
+    s_sel = np.array([0, 1, 17, 31, 62, 63])
+    d_sel = np.unique(np.concatenate([np.arange(0, Dn, 211), [0, 1, 255, 256, 8191]]))
+    for layer in (0, 31):
+        par = W.gen_decode_layer_params(spec, layer)
+        st = W.gen_states(S, Dn, N, seed=1000 + layer)
+        gp = {k: torch.from_numpy(v).cuda() for k, v in par.items()}
+        hs = torch.from_numpy(st["ssm_state"]).cuda()
+        cs = torch.from_numpy(st["conv_state"]).cuda()
+        hr = st["ssm_state"][s_sel][:, d_sel].astype(np.float64)
+        cr = st["conv_state"][s_sel][:, d_sel].astype(np.float64)
+        worst = 0.0
+        for step in range(steps):
+            si = W.gen_decode_step_inputs(spec, layer, step % spec.pool)
+            gs = {k: torch.from_numpy(v).cuda().to(torch.bfloat16) for k, v in si.items()}
+            y = ss.ss_step(gs["x"], gs["delta"], gp["A"], gs["B"], gs["C"], hs, conv_state=cs, conv_w=gp["conv_w"],
+                           conv_b=gp["conv_b"], delta_bias=gp["delta_bias"], D=gp["D"], z=gs["z"])
+            yr, hr, cr = oracle.step(si["x"][s_sel][:, d_sel], si["delta"][s_sel][:, d_sel], par["A"][d_sel],
+                                     si["B"][s_sel], si["C"][s_sel], hr, conv_w=par["conv_w"][d_sel],
+                                     conv_b=par["conv_b"][d_sel], delta_bias=par["delta_bias"][d_sel],
+                                     D=par["D"][d_sel], z=si["z"][s_sel][:, d_sel], conv_state=cr)
+            yg = host(y)[s_sel][:, d_sel]
+            worst = max(worst, maxrel(yg, yr))
+        torch.cuda.synchronize()
+        eh = maxrel(host(hs)[s_sel][:, d_sel], hr)
+        print(f"decode layer {layer}: y maxrel {worst:.3e} state maxrel {eh:.3e}", flush=True)
+        assert worst <= TOL["bf16"] and eh <= TOL["bf16"]
+        assert np.array_equal(host(cs)[s_sel][:, d_sel].astype(np.float64), cr)
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+EDGE_SHAPES = [
+    dict(batch=1, seqlen=1, d_inner=8, d_state=4),          # single token
+    dict(batch=2, seqlen=2, d_inner=5, d_state=4),          # shorter than the conv window
+    dict(batch=3, seqlen=67, d_inner=70, d_state=8),        # ragged L and D (not multiples of 4/64/256)
+    dict(batch=1, seqlen=131, d_inner=257, d_state=16),     # one channel past a workgroup
+    dict(batch=2, seqlen=200, d_inner=64, d_state=32),
+    dict(batch=1, seqlen=150, d_inner=33, d_state=64),
+]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "B{batch}L{seqlen}D{d_inner}N{d_state}".format(**s))
+def test_edge_shapes(ss, io, shape):
+    spec = W.ScanSpec("edge", 1, 1, 1, 4, io_dtype=io, delta_mode="bias", seed=4242)
+    _check_fwd(ss, spec, shape=shape, states=True, label=f"edge {shape} {io}")
+
+
+@pytest.mark.parametrize("flags", [dict(conv=False), dict(gate=False), dict(skip=False), dict(bias=False),
+                                   dict(conv=False, gate=False, skip=False, bias=False)],
+                         ids=lambda f: "-".join(f"no_{k}" for k in f))
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_optional_pieces(ss, flags, io):
+    spec = W.ScanSpec("flags", 2, 90, 72, 16, io_dtype=io, delta_mode="bias", seed=99)
+    _check_fwd(ss, spec, states=True, flags=flags, label=f"flags {flags} {io}")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [dict(batch=1, seqlen=4096, d_inner=64, d_state=16),
+                                   dict(batch=2, seqlen=3001, d_inner=100, d_state=8)],
+                         ids=["chunked_even", "chunked_ragged"])
+def test_chunked_path(ss, io, shape):
+    """Few channels and a long sequence select the chunked scan (aggregate pass +
+    carry-in); it must agree with the oracle including the returned state."""
+    dims = ss.make_dims(shape["batch"], shape["seqlen"], shape["d_inner"], shape["d_state"], 0)
+    assert ss.ss_workspace_bytes(dims) > 0, "shape does not select the chunked path"
+    spec = W.ScanSpec("chunk", 1, 1, 1, 4, io_dtype=io, delta_mode="bias", seed=7)
+    _check_fwd(ss, spec, shape=shape, states=True, label=f"chunked {shape} {io}")
+
+
+# ----------------------------------------------------------------------------- properties
+
+def test_split_handoff_matches_one_pass(ss):
+    """Processing a sequence in two calls that pass (ssm_state, conv_state) on gives
+    the one-pass result (the chunk hand-off of the deployment notes)."""
+    spec = W.ScanSpec("split", 2, 1, 1, 16, io_dtype="f32", delta_mode="bias", seed=5)
+    inp = W.gen_scan_inputs(spec, batch=2, seqlen=2500, d_inner=96)
+    st = W.gen_states(2, 96, 16)
+    g = to_dev(inp, "f32")
+    h1, c1 = torch.from_numpy(st["ssm_state"]).cuda(), torch.from_numpy(st["conv_state"]).cuda()
+    y_all = gpu_fwd(ss, g, h1, c1)
+    for L1 in (1, 3, 700, 2047):
+        h2, c2 = torch.from_numpy(st["ssm_state"]).cuda(), torch.from_numpy(st["conv_state"]).cuda()
+        parts = []
+        for sl in (slice(0, L1), slice(L1, None)):
+            gp = dict(g)
+            for k in ("x", "delta", "z", "B", "C"):
+                gp[k] = g[k][:, sl].contiguous()
+            parts.append(gpu_fwd(ss, gp, h2, c2))
+        y_split = torch.cat(parts, dim=1)
+        # both results are within fp32 rounding of each other (chunk boundaries differ)
+        e_y, e_h = maxrel(host(y_split), host(y_all)), maxrel(host(h2), host(h1))
+        assert e_y <= TOL["f32"] and e_h <= TOL["f32"], (L1, e_y, e_h)
+        assert torch.equal(c2, c1)
+    yr, hr, cr = oracle_fwd(inp, st["ssm_state"], st["conv_state"])
+    e = maxrel(host(y_all), yr)
+    assert e <= TOL["f32"], e
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_steps_match_scan(ss, io):
+    """L calls of ss_step from a carried state reproduce ss_conv_scan_fwd (recurrent
+    vs parallel mode on a short input)."""
+    spec = W.ScanSpec("steps", 3, 1, 1, 16, io_dtype=io, delta_mode="bias", seed=11)
+    inp = W.gen_scan_inputs(spec, batch=3, seqlen=24, d_inner=130)
+    st = W.gen_states(3, 130, 16)
+    g = to_dev(inp, io)
+    h_s, c_s = torch.from_numpy(st["ssm_state"]).cuda(), torch.from_numpy(st["conv_state"]).cuda()
+    y_scan = gpu_fwd(ss, g, h_s, c_s)
+    h, c = torch.from_numpy(st["ssm_state"]).cuda(), torch.from_numpy(st["conv_state"]).cuda()
+    ys = []
+    for t in range(24):
+        ys.append(ss.ss_step(g["x"][:, t].contiguous(), g["delta"][:, t].contiguous(), g["A"],
+                             g["B"][:, t].contiguous(), g["C"][:, t].contiguous(), h, conv_state=c,
+                             conv_w=g["conv_w"], conv_b=g["conv_b"], delta_bias=g["delta_bias"], D=g["D"],
+                             z=g["z"][:, t].contiguous()))
+    y_step = torch.stack(ys, dim=1)
+    e_y, e_h = maxrel(host(y_step), host(y_scan)), maxrel(host(h), host(h_s))
+    assert e_y <= TOL[io] and e_h <= TOL["f32"], (e_y, e_h)
+    assert torch.equal(c, c_s)
+
+
+def test_bitwise_deterministic(ss):
+    spec = W.ScanSpec("det", 1, 1, 1, 16, io_dtype="bf16", delta_mode="direct", seed=3)
+    inp = W.gen_scan_inputs(spec, batch=1, seqlen=8192, d_inner=256)
+    g = to_dev(inp, "bf16")
+    outs = []
+    for _ in range(3):
+        h = torch.zeros(1, 256, 16, device="cuda")
+        outs.append((gpu_fwd(ss, g, h), h))
+    for y, h in outs[1:]:
+        assert torch.equal(y, outs[0][0]) and torch.equal(h, outs[0][1])
+
+
+def test_selective_walkthrough_on_gpu(ss):
+    """The scalar walk-through (ozercemkelahmet.com, 'A worked example') on the GPU:
+    delta = softplus(0) = ln 2 halves the state each step (fp32, no conv/gate)."""
+    import json, os, math
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")))
+    u = torch.tensor(g["inputs"]["u"], dtype=torch.float32, device="cuda").view(1, 5, 1)
+    zeros = torch.zeros(1, 5, 1, device="cuda")
+    ones = torch.ones(1, 5, 4, device="cuda")
+    # N = 4 identical state rows with A = -1 and B = 1; C = 1/4 so the readout is one row's value
+    A = -torch.ones(1, 4, device="cuda")
+    y = ss.ss_conv_scan_fwd(u, zeros, A, ones, ones / 4)
+    want = np.array(g["expected"]["y_over_ln2"]) * math.log(2.0)
+    e = maxrel(host(y)[0, :, 0], want)
+    assert e <= 1e-6, e
