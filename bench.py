@@ -1,0 +1,342 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective-scan (S6) forward path and decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|train|block]
+                    [--no-decode] [--no-cpu]
+
+A step is one ss_conv_scan_fwd call over the whole workload (conv1d + SiLU,
+softplus step, discretisation, scan, C.h + D.u readout, SiLU(z) gate), with
+inputs resident in HBM. The default workload is the long sequence: batch 1,
+L = 131072, d_inner 2048, d_state 16, bf16 x/delta/z/B/C, fp32 state and
+parameters. Prints one JSON line:
+
+* value: Gelem/s = B*L*D*N / step time, whole step (all kernels of the call).
+* roofline: the main scan kernel, timed live with HIP events recorded around
+  that kernel on its own stream; it is bound by VALU issue, so achieved is its
+  algorithmic VALU slots per launch / its average duration against the chip's
+  VALU slot rate (see slots_per_row below). The same kernel's HBM view
+  (algorithmic bytes / duration vs 8 TB/s) is given as hbm_view.
+* decode: 64 streams x 32 layers x 256 token steps (d_inner 8192, d_state 16),
+  one ss_step per layer and token, timed end to end eagerly and replayed from
+  HIP graphs (one graph per token step over the 32 layers); its roofline is
+  the step kernel's algorithmic bytes / average duration against 8 TB/s.
+* cpu_baseline: the fp64 oracle on a channel sample of the same workload, on
+  the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E
+VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9     # CUs x SIMDs x lanes x clock: 39.3e12 fp32 lane-ops/s (no packed fp32)
+METRIC = "selective-scan fwd Gelem(B·L·D·N)/s + achieved HBM GB/s vs peak; decode tokens/s"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def slots_per_row(N: int) -> int:
+    """Algorithmic fp32 VALU issue slots per (b, t, d) row, one slot per add/mul/fma/max
+    and two per exp/log/reciprocal (gfx950 issues transcendentals at half rate):
+    conv 4; SiLU(conv) 7 (scale, exp, add, rcp, mul); softplus 9 (bias add, scale,
+    exp, add, log, max, add... ); Delta*u 1; per state index 6 (Delta*A, exp,
+    Delta*u*B, state fma, readout fma); D*u 1; SiLU(z) 7 and the gate product 1."""
+    return 30 + 6 * N
+
+
+class Hip:
+    """The few HIP runtime calls the bench needs for events (ctypes)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def scan_bytes(spec: W.ScanSpec) -> int:
+    """Algorithmic HBM bytes of one forward call: x, delta, z read and y written at the
+    I/O size, B and C read, parameters read once, fp32 state and conv history read and
+    written. The per-token state is never materialised and is not counted."""
+    es = 2 if spec.io_dtype == "bf16" else 4
+    Bz, L, D, N = spec.batch, spec.seqlen, spec.d_inner, spec.d_state
+    rows = Bz * L * D
+    return (rows * 4 * es + Bz * L * N * 2 * es + D * (N + 4 + 3) * 4
+            + 2 * Bz * D * (N + 3) * 4)
+
+
+def decode_bytes(spec: W.DecodeSpec) -> int:
+    """Algorithmic HBM bytes of one layer-step: per (stream, channel) the fp32 state
+    (N) and conv history (3) read and written, x/delta/z read and y written (bf16);
+    B and C per stream; the layer's parameters once."""
+    S, D, N = spec.streams, spec.d_inner, spec.d_state
+    return S * D * (2 * (N + 3) * 4 + 4 * 2) + S * N * 2 * 2 + D * (N + 4 + 3) * 4
+
+
+def run_scan(ss, torch, hip, spec, steps, warmup, want_sample):
+    t0 = time.time()
+    inp = W.gen_scan_inputs(spec)
+    log(f"[bench] generated {spec.name} inputs in {time.time() - t0:.1f}s")
+    sample = None
+    if want_sample:
+        # channel sample kept on the host for the CPU baseline (every 2nd channel;
+        # the baseline itself times a prefix of it sized to about 12 s)
+        dsel = np.arange(0, spec.d_inner, 2)
+        sample = dict(dsel=dsel, x=np.ascontiguousarray(inp["x"][:, :, dsel]),
+                      delta=np.ascontiguousarray(inp["delta"][:, :, dsel]),
+                      z=np.ascontiguousarray(inp["z"][:, :, dsel]), B=inp["B"], C=inp["C"],
+                      A=inp["A"][dsel], conv_w=inp["conv_w"][dsel], conv_b=inp["conv_b"][dsel],
+                      delta_bias=inp["delta_bias"][dsel], D=inp["D"][dsel])
+    tdt = torch.bfloat16 if spec.io_dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    g = {}
+    for k in list(inp.keys()):
+        v = torch.from_numpy(inp.pop(k)).to(dev)
+        g[k] = v.to(tdt) if k in ("x", "delta", "z", "B", "C") else v
+    del inp
+    Bz, L, D, N = spec.batch, spec.seqlen, spec.d_inner, spec.d_state
+    h = torch.zeros(Bz, D, N, device=dev)
+    cs = torch.zeros(Bz, D, 3, device=dev)
+    y = torch.empty(Bz, L, D, dtype=tdt, device=dev)
+    dims = ss.make_dims(Bz, L, D, N, ss.SS_BF16 if spec.io_dtype == "bf16" else ss.SS_F32)
+    ws = torch.empty(max(ss.ss_workspace_bytes(dims), 1), dtype=torch.uint8, device=dev)
+
+    def call():
+        ss.ss_conv_scan_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], conv_w=g["conv_w"], conv_b=g["conv_b"],
+                            delta_bias=g["delta_bias"], D=g["D"], z=g["z"], ssm_state=h, conv_state=cs, y=y,
+                            workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [[hip.event() for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(steps):
+        ss.ss_time_next_call(*ev[i])
+        call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    nchunk_agg = ss.ss_workspace_bytes(dims) > 0
+    main_ms = [hip.elapsed_ms(e[2], e[3]) for e in ev]
+    agg_ms = [hip.elapsed_ms(e[0], e[1]) for e in ev] if nchunk_agg else [0.0] * steps
+    for e in ev:
+        for x in e:
+            hip.destroy(x)
+    return dict(wall_s=wall, main_ms=float(np.mean(main_ms)), agg_ms=float(np.mean(agg_ms)),
+                main_ms_min=float(np.min(main_ms)), sample=sample)
+
+
+def run_decode(ss, torch, hip, spec: W.DecodeSpec, token_steps: int):
+    dev = torch.device("cuda:0")
+    S, D, N, Lyr = spec.streams, spec.d_inner, spec.d_state, spec.layers
+    t0 = time.time()
+    params, states, convs, ys, pool = [], [], [], [], []
+    for layer in range(Lyr):
+        p = {k: torch.from_numpy(v).to(dev) for k, v in W.gen_decode_layer_params(spec, layer).items()}
+        params.append(p)
+        states.append(torch.zeros(S, D, N, device=dev))
+        convs.append(torch.zeros(S, D, 3, device=dev))
+        ys.append(torch.empty(S, D, dtype=torch.bfloat16, device=dev))
+        slots = []
+        for slot in range(spec.pool):
+            si = W.gen_decode_step_inputs(spec, layer, slot)
+            slots.append({k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in si.items()})
+        pool.append(slots)
+    log(f"[bench] generated decode inputs in {time.time() - t0:.1f}s")
+    dims = ss.make_dims(S, 1, D, N, ss.SS_BF16)
+    # argument blocks built once (marshalling), then the C ABI is called directly
+    args = [[ss.ss_args(x=pool[l][k]["x"].data_ptr(), conv_w=params[l]["conv_w"].data_ptr(),
+                        conv_b=params[l]["conv_b"].data_ptr(), delta=pool[l][k]["delta"].data_ptr(),
+                        delta_bias=params[l]["delta_bias"].data_ptr(), A=params[l]["A"].data_ptr(),
+                        B=pool[l][k]["B"].data_ptr(), C=pool[l][k]["C"].data_ptr(), Dskip=params[l]["D"].data_ptr(),
+                        z=pool[l][k]["z"].data_ptr(), y=ys[l].data_ptr(), ssm_state=states[l].data_ptr(),
+                        conv_state=convs[l].data_ptr()) for k in range(spec.pool)] for l in range(Lyr)]
+    dims_ref = ctypes.byref(dims)
+
+    def token_step(step, stream_handle, events=None):
+        k = step % spec.pool
+        for l in range(Lyr):
+            if events is not None:
+                ss.lib.ss_time_next_call(None, None, events[l][0], events[l][1])
+            rc = ss.lib.ss_step(dims_ref, ctypes.byref(args[l][k]), stream_handle)
+            if rc != 0:
+                raise RuntimeError(ss.lib.ss_last_error().decode())
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream or None
+    for s in range(4):
+        token_step(s, sh)
+    torch.cuda.synchronize()
+
+    # eager, with the step kernel timed by events on a sample of token steps
+    timed_steps = list(range(0, token_steps, max(1, token_steps // 16)))
+    evs = {s: [[hip.event(), hip.event()] for _ in range(Lyr)] for s in timed_steps}
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(token_steps):
+        token_step(s, sh, evs.get(s))
+    torch.cuda.synchronize()
+    eager_s = time.perf_counter() - t_start
+    kms = [hip.elapsed_ms(a, b) for s in timed_steps for a, b in evs[s]]
+    for s in timed_steps:
+        for a, b in evs[s]:
+            hip.destroy(a)
+            hip.destroy(b)
+
+    # graphs: one per pool slot, each capturing the 32 layer calls of one token step
+    graphs = []
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        for k in range(spec.pool):
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph, stream=cap):
+                token_step(k, torch.cuda.current_stream().cuda_stream)
+            graphs.append(gph)
+    torch.cuda.synchronize()
+    for s in range(4):
+        graphs[s % spec.pool].replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(token_steps):
+        graphs[s % spec.pool].replay()
+    torch.cuda.synchronize()
+    graph_s = time.perf_counter() - t_start
+    del graphs
+    return dict(eager_s=eager_s, graph_s=graph_s, kernel_ms=float(np.mean(kms)), kernel_ms_min=float(np.min(kms)),
+                kernel_samples=len(kms))
+
+
+def cpu_baseline(sample, spec, target_s=12.0):
+    """Time the fp64 oracle (as it stands) on host cores over a channel sample of
+    the workload: a short calibration run, then enough channels for about
+    target_s seconds (all tokens of each channel)."""
+    import oracle
+    orc = oracle.default()
+    nthreads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+
+    def run(k):
+        sl = slice(0, k)
+        t0 = time.perf_counter()
+        orc.conv_scan_fwd(sample["x"][:, :, sl], sample["delta"][:, :, sl], sample["A"][sl], sample["B"],
+                          sample["C"], conv_w=sample["conv_w"][sl], conv_b=sample["conv_b"][sl],
+                          delta_bias=sample["delta_bias"][sl], D=sample["D"][sl], z=sample["z"][:, :, sl],
+                          nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    avail = len(sample["dsel"])
+    k0 = min(avail, max(nthreads, 8))
+    t_cal = run(k0)
+    k = int(min(avail, max(k0, k0 * target_s / max(t_cal, 1e-3))))
+    k = max(nthreads, (k // nthreads) * nthreads) if k >= nthreads else k
+    k = min(k, avail)
+    dt = run(k)
+    elems = spec.batch * spec.seqlen * k * spec.d_state
+    return {"value": round(elems / dt / 1e9, 4), "unit": "Gelem/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{k} of {spec.d_inner} channels (every 2nd from channel 0), all {spec.batch}x{spec.seqlen} "
+                      f"tokens, d_state {spec.d_state}, fp64 OpenMP over channels, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long", choices=["long", "train", "block", "tiny"])
+    ap.add_argument("--decode-steps", type=int, default=W.DECODE.steps)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_73_amd as ss
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    hip = Hip()
+    spec = W.WORKLOADS[a.workload]
+    log(f"[bench] workload {spec}")
+    r = run_scan(ss, torch, hip, spec, a.steps, a.warmup, not a.no_cpu)
+    Bz, L, D, N = spec.batch, spec.seqlen, spec.d_inner, spec.d_state
+    rows = Bz * L * D
+    ms_step = r["wall_s"] / a.steps * 1e3
+    gelem = rows * N / (ms_step / 1e3) / 1e9
+    nbytes = scan_bytes(spec)
+    main_s = r["main_ms"] / 1e3
+    slots = rows * slots_per_row(N)
+    out = {
+        "metric": METRIC, "value": round(gelem, 2), "unit": "Gelem/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{spec.name}: batch {Bz}, L={L}, d_inner {D}, d_state {N}, d_conv 4, "
+                               f"{spec.io_dtype} x/delta/z/B/C/y, fp32 state and parameters",
+                   "batch": Bz, "seq_len": L, "d_inner": D, "d_state": N, "io_dtype": spec.io_dtype},
+        "hbm_gbps_step": round(nbytes / (ms_step / 1e3) / 1e9, 1),
+        "roofline": {"kernel": "k_scan main pass", "bound": "alu",
+                     "achieved": round(slots / main_s / 1e12, 3), "peak": round(VALU_SLOTS_PER_S / 1e12, 3),
+                     "unit": "Tslot/s", "frac": round(slots / main_s / VALU_SLOTS_PER_S, 4),
+                     "traffic": None, "kernel_ms": round(r["main_ms"], 4),
+                     "slots_per_row": slots_per_row(N), "rows_per_launch": rows},
+        "hbm_view": {"achieved": round(nbytes / main_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / main_s / 1e9 / PEAK_HBM_GBS, 4), "bytes_per_launch": nbytes},
+        "aggregate_kernel_ms": round(r["agg_ms"], 4),
+    }
+    if not a.no_decode:
+        dspec = W.DECODE
+        dr = run_decode(ss, torch, hip, dspec, a.decode_steps)
+        tokens = dspec.streams * a.decode_steps
+        dbytes = decode_bytes(dspec)
+        ks = dr["kernel_ms"] / 1e3
+        out["decode"] = {
+            "workload": f"{dspec.streams} streams x {dspec.layers} layers x {a.decode_steps} token steps, "
+                        f"d_inner {dspec.d_inner}, d_state {dspec.d_state}, bf16 token inputs, fp32 states",
+            "tokens_per_s_graph": round(tokens / dr["graph_s"], 1),
+            "tokens_per_s_eager": round(tokens / dr["eager_s"], 1),
+            "ms_per_token_step_graph": round(dr["graph_s"] / a.decode_steps * 1e3, 4),
+            "roofline": {"kernel": "k_step", "bound": "hbm", "achieved": round(dbytes / ks / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dbytes / ks / 1e9 / PEAK_HBM_GBS, 4),
+                         "traffic": None, "kernel_us": round(dr["kernel_ms"] * 1e3, 3),
+                         "bytes_per_launch": dbytes},
+            "hbm_gbps_end_to_end_graph": round(dbytes * dspec.layers * a.decode_steps / dr["graph_s"] / 1e9, 1),
+        }
+    if not a.no_cpu and r["sample"] is not None:
+        out["cpu_baseline"] = cpu_baseline(r["sample"], spec)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

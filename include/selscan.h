@@ -40,9 +40,8 @@
  * Errors: every call returns an ss_status. Arguments are validated on the host
  * before anything is enqueued, so a rejected call writes nothing. Rejected:
  * NULL required pointers, non-positive sizes, unsupported d_state / d_conv /
- * dtype, pointers not aligned to their element type (4 bytes for fp32 and for
- * bf16 x/delta/z/y/B/C rows, see below), a too-small workspace, y overlapping an
- * input. Launch failures return SS_ERR_HIP; ss_last_error() gives the detail
+ * dtype, pointers not 4-byte aligned (ssm_state: 16 bytes; workspace: 256
+ * bytes), a too-small workspace, y or a state overlapping an input. Launch failures return SS_ERR_HIP; ss_last_error() gives the detail
  * (per calling thread). Faults inside a kernel surface at the caller's next
  * synchronisation. NaN/Inf inputs propagate and are not checked. Results are
  * deterministic for a given shape (no floating-point atomics).
@@ -115,6 +114,15 @@ ss_status ss_conv_scan_fwd(const ss_dims* dims, const ss_args* args,
  * (x, delta, z, y: [B,D]; B, C: [B,N]) from the carried state, updating
  * ssm_state [B,D,N] and conv_state [B,D,K-1] in place. dims->seqlen is ignored. */
 ss_status ss_step(const ss_dims* dims, const ss_args* args, void* stream);
+
+/* Profiling support for benchmarks: events (hipEvent_t handles created by the
+ * caller) that the NEXT ss_conv_scan_fwd or ss_step call made on this thread
+ * records around its kernels, at the kernels' own start and end on the call's
+ * stream: agg_start/agg_stop around the chunk-aggregate kernel (left unrecorded
+ * when the call launches none), main_start/main_stop around the main scan or
+ * decode-step kernel. Any pointer may be NULL. The setting is consumed by that
+ * next call, also when it fails. Always returns SS_OK. */
+ss_status ss_time_next_call(void* agg_start, void* agg_stop, void* main_start, void* main_stop);
 
 const char* ss_status_str(ss_status s);
 const char* ss_last_error(void);   /* detail of the calling thread's last failure */

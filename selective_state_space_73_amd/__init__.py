@@ -60,6 +60,8 @@ def _load() -> ctypes.CDLL:
     lib.ss_last_error.restype = ctypes.c_char_p
     lib.ss_version.argtypes = []
     lib.ss_version.restype = ctypes.c_int
+    lib.ss_time_next_call.argtypes = [_vp, _vp, _vp, _vp]
+    lib.ss_time_next_call.restype = ctypes.c_int
     return lib
 
 
@@ -68,6 +70,12 @@ lib = _load()
 
 def ss_version() -> int:
     return lib.ss_version()
+
+
+def ss_time_next_call(agg_start=None, agg_stop=None, main_start=None, main_stop=None) -> None:
+    """Arm hipEvent_t handles (ints) to be recorded around the kernels of the next
+    ss_conv_scan_fwd / ss_step call on this thread (profiling)."""
+    lib.ss_time_next_call(agg_start, agg_stop, main_start, main_stop)
 
 
 def _check(status: int):
@@ -171,5 +179,5 @@ def ss_step(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tens
     return y
 
 
-__all__ = ["ss_conv_scan_fwd", "ss_step", "ss_workspace_bytes", "ss_version", "make_dims", "ss_dims", "ss_args",
+__all__ = ["ss_conv_scan_fwd", "ss_step", "ss_workspace_bytes", "ss_version", "ss_time_next_call", "make_dims", "ss_dims", "ss_args",
            "SelscanError", "SS_F32", "SS_BF16", "LIB_PATH", "lib"]

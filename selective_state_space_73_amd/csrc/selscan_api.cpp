@@ -16,6 +16,17 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local void* g_events[4] = {nullptr, nullptr, nullptr, nullptr};   // see ss_time_next_call
+
+void take_events(selscan::LaunchScan& p) {
+    p.ev_agg[0] = g_events[0]; p.ev_agg[1] = g_events[1];
+    p.ev_main[0] = g_events[2]; p.ev_main[1] = g_events[3];
+    for (void*& e : g_events) e = nullptr;
+}
+
+void drop_events() {
+    for (void*& e : g_events) e = nullptr;
+}
 
 ss_status fail(ss_status s, const char* fmt, ...) {
     char buf[512];
@@ -178,21 +189,25 @@ size_t ss_workspace_bytes(const ss_dims* dims) {
 ss_status ss_conv_scan_fwd(const ss_dims* dims, const ss_args* args, void* workspace,
                            size_t workspace_bytes, void* stream) {
     ss_status s = check_dims(dims, false);
-    if (s != SS_OK) return s;
-    s = check_args(*dims, args, false);
-    if (s != SS_OK) return s;
+    if (s == SS_OK) s = check_args(*dims, args, false);
+    if (s != SS_OK) { drop_events(); return s; }
     const Layout l = layout(*dims);
-    if (l.total > 0 && (!workspace || workspace_bytes < l.total))
+    if (l.total > 0 && (!workspace || workspace_bytes < l.total)) {
+        drop_events();
         return fail(SS_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, l.total);
-    if (workspace && ((uintptr_t)workspace & 255u))
+    }
+    if (workspace && ((uintptr_t)workspace & 255u)) {
+        drop_events();
         return fail(SS_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+    }
     const Range wr{workspace, l.total, "workspace"};
     const Range others[] = {{args->x, 1, "x"}, {args->y, 1, "y"}, {args->B, 1, "B"}, {args->C, 1, "C"},
                             {args->delta, 1, "delta"}, {args->ssm_state, 1, "ssm_state"}};
     for (const Range& r : others)
-        if (overlap(wr, r)) return fail(SS_ERR_INVALID_ARG, "workspace overlaps %s", r.name);
+        if (overlap(wr, r)) { drop_events(); return fail(SS_ERR_INVALID_ARG, "workspace overlaps %s", r.name); }
 
     selscan::LaunchScan p = make_launch(*dims, *args, stream);
+    take_events(p);
     char* ws = static_cast<char*>(workspace);
     p.nchunks = l.nchunks;
     p.chunk_len = l.chunk_len;
@@ -209,14 +224,19 @@ ss_status ss_conv_scan_fwd(const ss_dims* dims, const ss_args* args, void* works
 
 ss_status ss_step(const ss_dims* dims, const ss_args* args, void* stream) {
     ss_status s = check_dims(dims, true);
-    if (s != SS_OK) return s;
-    s = check_args(*dims, args, true);
-    if (s != SS_OK) return s;
+    if (s == SS_OK) s = check_args(*dims, args, true);
+    if (s != SS_OK) { drop_events(); return s; }
     ss_dims one = *dims;
     one.seqlen = 1;
     selscan::LaunchScan p = make_launch(one, *args, stream);
+    take_events(p);
     const hipError_t e = selscan::launch_step(p);
     if (e != hipSuccess) return fail(SS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return SS_OK;
+}
+
+ss_status ss_time_next_call(void* agg_start, void* agg_stop, void* main_start, void* main_stop) {
+    g_events[0] = agg_start; g_events[1] = agg_stop; g_events[2] = main_start; g_events[3] = main_stop;
     return SS_OK;
 }
 

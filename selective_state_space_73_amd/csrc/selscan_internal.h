@@ -6,7 +6,8 @@
 namespace selscan {
 
 constexpr int kScanThreads = 256;   // channels per workgroup of the scan kernels (4 waves)
-constexpr int kStepThreads = 256;   // channels per workgroup of the decode-step kernel
+constexpr int kStepThreads = 256;   // lanes per workgroup of the decode-step kernel (4 per channel)
+constexpr int kStepStreams = 4;     // streams each lane quad of the decode-step kernel handles
 constexpr int kScanTile = 64;       // tokens of B/C staged in LDS at a time
 
 // Everything a launch needs, already validated by the C-ABI layer.
@@ -24,6 +25,8 @@ struct LaunchScan {
     float* ws_h0;   // [B, D, N]
     float* ws_c0;   // [B, D, K-1]
     void* stream;
+    void* ev_agg[2];   // optional hipEvent_t pair recorded around the aggregate kernel
+    void* ev_main[2];  // optional hipEvent_t pair recorded around the main kernel
 };
 
 hipError_t launch_scan(const LaunchScan& p);

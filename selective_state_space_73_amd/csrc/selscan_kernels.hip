@@ -20,6 +20,7 @@
 // step size, so that the chunk's total decay is exp(A * sum Delta); the main pass
 // folds these aggregates of all earlier chunks into its carry-in and then runs
 // the chunk with the exact initial state.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -169,28 +170,37 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 
     // Token loop. B_t/C_t are staged through LDS in tiles of R tokens (double
     // buffered, one barrier per tile) and read back as wave-uniform broadcasts.
-    // x/delta/z are prefetched U tokens ahead as raw bits and widened at use.
-    // Rows past the chunk end are clamped to its last row: loaded, never used.
+    // x/delta/z are prefetched one U-token group ahead as raw bits (two buffers
+    // used alternately) and widened at use. Full tiles run without per-token
+    // branches; only a chunk's last, partial tile goes token by token.
     constexpr int U = 4;
     constexpr int R = kScanTile;
+    static_assert(R % (2 * U) == 0, "a tile holds whole pairs of groups");
     constexpr int NB = MAIN ? 2 * N : N;                // staged values per token
     __shared__ float sbc[2][R][NB];
-    const int64_t row0 = (int64_t)b * sa.L;
     const int tid = threadIdx.x;
+    const int nrows = (int)(t1 - t0);
+    const int64_t rowbase = (int64_t)b * sa.L + t0;     // global row of the chunk's first token
+    const T* xb = x + rowbase * D;
+    const T* db = delta + rowbase * D;
+    const T* zb = (MAIN && GATE) ? z + rowbase * D : nullptr;
+    T* yb = MAIN ? y + rowbase * D : nullptr;
+    const T* Bb = Bm + rowbase * N;
+    const T* Cb = MAIN ? Cm + rowbase * N : nullptr;
 
     // cooperative tile load: element e of the tile is (row e / N, state e % N)
     constexpr int TILE_ELEMS = R * N;
     constexpr int PER_THREAD = (TILE_ELEMS + kScanThreads - 1) / kScanThreads;
     T tb[PER_THREAD], tc[PER_THREAD];
-    auto tile_fetch = [&](int64_t tbase) {
+    auto tile_fetch = [&](int r0) {
 #pragma unroll
         for (int k = 0; k < PER_THREAD; ++k) {
-            const int e = tid + k * kScanThreads;
-            const int r = (e < TILE_ELEMS ? e : TILE_ELEMS - 1) / N;
-            const int n = (e < TILE_ELEMS ? e : TILE_ELEMS - 1) % N;
-            const int64_t t = (tbase + r < t1) ? tbase + r : t1 - 1;
-            tb[k] = Bm[(row0 + t) * N + n];
-            if (MAIN) tc[k] = Cm[(row0 + t) * N + n];
+            const int e0 = tid + k * kScanThreads;
+            const int e = e0 < TILE_ELEMS ? e0 : TILE_ELEMS - 1;
+            const int r = (r0 + e / N < nrows) ? r0 + e / N : nrows - 1;
+            const int64_t off = (int64_t)r * N + e % N;
+            tb[k] = Bb[off];
+            if (MAIN) tc[k] = Cb[off];
         }
     };
     auto tile_store = [&](int buf) {
@@ -205,69 +215,97 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     };
 
     float sdt = 0.0f;
-    T px[U], pd[U], pz[U];
-    auto load_group = [&](int64_t tg) {
+    // Per-token work in two phases. prologue(): the conv, SiLU, softplus and gate of
+    // one token (a long dependent chain, run for a whole group of tokens first so the
+    // chains of different tokens overlap). update(): the N-wide state update and
+    // readout of one token, with its B/C row read from LDS up front.
+    struct Pro { float u, dt, wv, g; };
+    auto prologue = [&](T xraw, T draw, T zraw) -> Pro {
+        Pro p;
+        const float xt = IO<T>::cvt(xraw);
+        if (CONV) {
+            const float cv = __builtin_fmaf(w3, xt, __builtin_fmaf(w2, x1, __builtin_fmaf(w1, x2, __builtin_fmaf(w0, x3, cb))));
+            x3 = x2; x2 = x1; x1 = xt;
+            p.u = silu(cv);
+        } else {
+            p.u = xt;
+        }
+        p.dt = softplus(IO<T>::cvt(draw) + dbias);
+        p.wv = p.dt * p.u;
+        p.g = (MAIN && GATE) ? silu(IO<T>::cvt(zraw)) : 1.0f;
+        return p;
+    };
+    auto update = [&](const Pro& p, const float* bct, int r) {
+        float bv[N], cv[N], a[N];
+#pragma unroll
+        for (int n = 0; n < N; ++n) bv[n] = bct[n];
+        if (MAIN) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) cv[n] = bct[N + n];
+        }
+#pragma unroll
+        for (int n = 0; n < N; ++n) a[n] = exp2_fast(p.dt * A2[n]);
+#pragma unroll
+        for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(a[n], h[n], p.wv * bv[n]);
+        if (MAIN) {
+            float ya = dsk * p.u, yc = 0.0f;
+#pragma unroll
+            for (int n = 0; n < N; n += 2) {
+                ya = __builtin_fmaf(cv[n], h[n], ya);
+                yc = __builtin_fmaf(cv[n + 1], h[n + 1], yc);
+            }
+            const float yv = (ya + yc) * p.g;
+            // lanes past the last channel were clamped to it and store the same value
+            IO<T>::st(yb + (int64_t)r * D + d, yv);
+        } else {
+            sdt += p.dt;
+        }
+    };
+    auto token = [&](T xraw, T draw, T zraw, const float* bct, int r) {
+        const Pro p = prologue(xraw, draw, zraw);
+        update(p, bct, r);
+    };
+    auto group = [&](const T* gx, const T* gd, const T* gz, const float* tile_rows, int r0) {
+        Pro p[U];
+#pragma unroll
+        for (int i = 0; i < U; ++i) p[i] = prologue(gx[i], gd[i], gz[i]);
+#pragma unroll
+        for (int i = 0; i < U; ++i) update(p[i], tile_rows + i * NB, r0 + i);
+    };
+    T gx0[U], gd0[U], gz0[U], gx1[U], gd1[U], gz1[U];
+    auto load_group = [&](int r0, T* gx, T* gd, T* gz) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            const int64_t t = (tg + i < t1) ? tg + i : t1 - 1;
-            const int64_t ri = (row0 + t) * D + d;
-            px[i] = x[ri];
-            pd[i] = delta[ri];
-            if (MAIN && GATE) pz[i] = z[ri];
+            const int r = (r0 + i < nrows) ? r0 + i : nrows - 1;
+            const int64_t off = (int64_t)r * D;
+            gx[i] = xb[off + d];
+            gd[i] = db[off + d];
+            if (MAIN && GATE) gz[i] = zb[off + d];
         }
     };
 
-    if (t0 < t1) {
-        tile_fetch(t0);
+    int buf = 0;
+    if (nrows > 0) {
+        tile_fetch(0);
         tile_store(0);
-        load_group(t0);
+        load_group(0, gx0, gd0, gz0);
     }
     __syncthreads();
-    int buf = 0;
-    for (int64_t tt = t0; tt < t1; tt += R) {
-        const bool more = tt + R < t1;
+    for (int tt = 0; tt < nrows; tt += R) {
+        const bool more = tt + R < nrows;
         if (more) tile_fetch(tt + R);
-        const int64_t tend = (tt + R < t1) ? tt + R : t1;
-        for (int64_t tg = tt; tg < tend; tg += U) {
-            T cx[U], cd[U], cz[U];
-#pragma unroll
-            for (int i = 0; i < U; ++i) { cx[i] = px[i]; cd[i] = pd[i]; cz[i] = pz[i]; }
-            if (tg + U < t1) load_group(tg + U);
-#pragma unroll
-            for (int i = 0; i < U; ++i) {
-                const int64_t t = tg + i;
-                if (t >= tend) break;
-                const float* bct = sbc[buf][t - tt];
-                const float xt = IO<T>::cvt(cx[i]);
-                float u;
-                if (CONV) {
-                    const float cv = __builtin_fmaf(w3, xt, __builtin_fmaf(w2, x1, __builtin_fmaf(w1, x2, __builtin_fmaf(w0, x3, cb))));
-                    x3 = x2; x2 = x1; x1 = xt;
-                    u = silu(cv);
-                } else {
-                    u = xt;
-                }
-                const float dt = softplus(IO<T>::cvt(cd[i]) + dbias);
-                const float wv = dt * u;
-#pragma unroll
-                for (int n = 0; n < N; ++n) {
-                    const float a = exp2_fast(dt * A2[n]);
-                    h[n] = __builtin_fmaf(a, h[n], wv * bct[n]);
-                }
-                if (MAIN) {
-                    float ya = dsk * u, yb = 0.0f;
-#pragma unroll
-                    for (int n = 0; n < N; n += 2) {
-                        ya = __builtin_fmaf(bct[N + n], h[n], ya);
-                        yb = __builtin_fmaf(bct[N + n + 1], h[n + 1], yb);
-                    }
-                    float yv = ya + yb;
-                    if (GATE) yv *= silu(IO<T>::cvt(cz[i]));
-                    // lanes past the last channel were clamped to it and store the same value
-                    IO<T>::st(y + (row0 + t) * D + d, yv);
-                } else {
-                    sdt += dt;
-                }
+        const float* tile = &sbc[buf][0][0];
+        if (tt + R <= nrows) {
+            for (int g = 0; g < R; g += 2 * U) {
+                load_group(tt + g + U, gx1, gd1, gz1);
+                group(gx0, gd0, gz0, tile + g * NB, tt + g);
+                load_group(tt + g + 2 * U, gx0, gd0, gz0);
+                group(gx1, gd1, gz1, tile + (g + U) * NB, tt + g + U);
+            }
+        } else {
+            for (int r = tt; r < nrows; ++r) {
+                const int64_t off = (int64_t)r * D + d;
+                token(xb[off], db[off], (MAIN && GATE) ? zb[off] : T(0), tile + (r - tt) * NB, r);
             }
         }
         if (more) tile_store(buf ^ 1);
@@ -294,7 +332,54 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 }
 
 // ---------------------------------------------------------------------------
-// Decode step: one lane per (stream, channel); both states read and written in place.
+// Decode step. Four lanes (a quad) per (stream, channel): lane q holds state
+// entries [q*N/4, (q+1)*N/4), so every state load and store of a wave is one
+// contiguous, nontemporal vector access. The conv taps and the readout are
+// summed across the quad with DPP; lane q < 3 holds conv history entry q and
+// lane 3 the new input, so the shifted history is one quad rotation away.
+
+typedef float vf4 __attribute__((ext_vector_type(4)));
+
+// DPP quad permutations: xor-1, xor-2 and "take lane q+1" (lane 3 keeps its own)
+constexpr int kQuadXor1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);
+constexpr int kQuadXor2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);
+constexpr int kQuadNext = 1 | (2 << 2) | (3 << 4) | (3 << 6);
+
+template <int CTRL>
+__device__ __forceinline__ float quad_dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+    v += quad_dpp<kQuadXor1>(v);
+    return v + quad_dpp<kQuadXor2>(v);
+}
+
+template <int NQ>
+__device__ __forceinline__ void ld_nt(const float* p, float* v) {
+    if constexpr (NQ % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < NQ / 4; ++k) {
+            const vf4 t = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(p) + k);
+            v[4 * k] = t.x; v[4 * k + 1] = t.y; v[4 * k + 2] = t.z; v[4 * k + 3] = t.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) v[k] = __builtin_nontemporal_load(p + k);
+    }
+}
+template <int NQ>
+__device__ __forceinline__ void st_nt(float* p, const float* v) {
+    if constexpr (NQ % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < NQ / 4; ++k) {
+            const vf4 t = {v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+            __builtin_nontemporal_store(t, reinterpret_cast<vf4*>(p) + k);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) __builtin_nontemporal_store(v[k], p + k);
+    }
+}
 
 template <typename T, int N, bool CONV, bool GATE>
 __global__ void __launch_bounds__(kStepThreads)
@@ -302,50 +387,72 @@ k_step(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
        const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
        const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
        const T* __restrict__ z, T* __restrict__ y, float* __restrict__ ssm_state,
-       float* __restrict__ conv_state, int D) {
-    const int d = blockIdx.x * kStepThreads + threadIdx.x;
-    const int s = blockIdx.y;
-    if (d >= D) return;
-    const int64_t sd = (int64_t)s * D + d;
+       float* __restrict__ conv_state, int D, int S) {
+    constexpr int NQ = N / 4;
+    constexpr int SPT = kStepStreams;         // streams handled by each quad (same channel)
+    const int q = threadIdx.x & 3;
+    const int d = blockIdx.x * (kStepThreads / 4) + (threadIdx.x >> 2);
+    const int s0 = blockIdx.y * SPT;
+    if (d >= D) return;                       // whole quads leave together
 
-    float h[N];
-    const float4* hp = reinterpret_cast<const float4*>(ssm_state + sd * N);
+    // channel parameters, shared by the SPT streams
+    float aq[NQ];
 #pragma unroll
-    for (int q = 0; q < N / 4; ++q) {
-        const float4 v = hp[q];
-        h[4 * q + 0] = v.x; h[4 * q + 1] = v.y; h[4 * q + 2] = v.z; h[4 * q + 3] = v.w;
-    }
-    const float xt = IO<T>::ld(x + sd);
-    float u;
-    if (CONV) {
-        float* cs = conv_state + sd * 3;
-        const float x3 = cs[0], x2 = cs[1], x1 = cs[2];
-        const float cb = conv_b ? conv_b[d] : 0.0f;
-        const float cv = __builtin_fmaf(conv_w[d * 4 + 3], xt, __builtin_fmaf(conv_w[d * 4 + 2], x1,
-                         __builtin_fmaf(conv_w[d * 4 + 1], x2, __builtin_fmaf(conv_w[d * 4 + 0], x3, cb))));
-        cs[0] = x2; cs[1] = x1; cs[2] = xt;
-        u = silu(cv);
-    } else {
-        u = xt;
-    }
-    const float dt = softplus(IO<T>::ld(delta + sd) + (delta_bias ? delta_bias[d] : 0.0f));
-    const float wv = dt * u;
-    const T* Bs = Bm + (int64_t)s * N;
-    const T* Cs = Cm + (int64_t)s * N;
-    float ya = (Dskip ? Dskip[d] : 0.0f) * u, yb = 0.0f;
+    for (int k = 0; k < NQ; ++k) aq[k] = A[(int64_t)d * N + q * NQ + k] * kLog2e;
+    const float wq = CONV ? conv_w[d * 4 + q] : 0.0f;
+    const float cb = (CONV && conv_b) ? conv_b[d] : 0.0f;
+    const float dbias = delta_bias ? delta_bias[d] : 0.0f;
+    const float dsk = Dskip ? Dskip[d] : 0.0f;
+
+    // every stream's loads first (streams past S are clamped to the last one and skipped below)
+    float hq[SPT][NQ], hist[SPT];
+    T braw[SPT][NQ], craw[SPT][NQ], xraw[SPT], draw[SPT], zraw[SPT];
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-        const float a = exp2_fast(dt * (A[(int64_t)d * N + n] * kLog2e));
-        h[n] = __builtin_fmaf(a, h[n], wv * IO<T>::ld(Bs + n));
-        if (n & 1) yb = __builtin_fmaf(IO<T>::ld(Cs + n), h[n], yb);
-        else       ya = __builtin_fmaf(IO<T>::ld(Cs + n), h[n], ya);
-    }
-    float yv = ya + yb;
-    if (GATE) yv *= silu(IO<T>::ld(z + sd));
-    IO<T>::st(y + sd, yv);
-    float4* hw = reinterpret_cast<float4*>(ssm_state + sd * N);
+    for (int j = 0; j < SPT; ++j) {
+        const int s = (s0 + j < S) ? s0 + j : S - 1;
+        const int64_t sd = (int64_t)s * D + d;
+        ld_nt<NQ>(ssm_state + sd * N + q * NQ, hq[j]);
 #pragma unroll
-    for (int q = 0; q < N / 4; ++q) hw[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+        for (int k = 0; k < NQ; ++k) {
+            braw[j][k] = Bm[(int64_t)s * N + q * NQ + k];
+            craw[j][k] = Cm[(int64_t)s * N + q * NQ + k];
+        }
+        xraw[j] = x[sd];
+        draw[j] = delta[sd];
+        zraw[j] = GATE ? z[sd] : T(0);
+        hist[j] = (CONV && q < 3) ? __builtin_nontemporal_load(conv_state + sd * 3 + q) : 0.0f;
+    }
+
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+        if (s0 + j >= S) break;                // uniform across the workgroup
+        const int64_t sd = (int64_t)(s0 + j) * D + d;
+        const float xt = IO<T>::cvt(xraw[j]);
+        float u;
+        if (CONV) {
+            // lane q contributes w[q] * (history q, or the new input on lane 3)
+            const float v = q < 3 ? hist[j] : xt;
+            u = silu(quad_sum(wq * v) + cb);
+            // shifted history (x_{t-2}, x_{t-1}, x_t): lane q takes lane q+1's value
+            const float nh = quad_dpp<kQuadNext>(v);
+            if (q < 3) __builtin_nontemporal_store(nh, conv_state + sd * 3 + q);
+        } else {
+            u = xt;
+        }
+        const float dt = softplus(IO<T>::cvt(draw[j]) + dbias);
+        const float wv = dt * u;
+        float yp = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            const float a = exp2_fast(dt * aq[k]);
+            hq[j][k] = __builtin_fmaf(a, hq[j][k], wv * IO<T>::cvt(braw[j][k]));
+            yp = __builtin_fmaf(IO<T>::cvt(craw[j][k]), hq[j][k], yp);
+        }
+        st_nt<NQ>(ssm_state + sd * N + q * NQ, hq[j]);
+        float yv = quad_sum(yp) + dsk * u;
+        if (GATE) yv *= silu(IO<T>::cvt(zraw[j]));
+        if (q == 0) IO<T>::st(y + sd, yv);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -361,12 +468,14 @@ static hipError_t launch_scan_t(const LaunchScan& p) {
     ScanArgs sa{p.L, p.chunk_len, (int)p.D, p.nchunks};
     const unsigned gx = (unsigned)((p.D + kScanThreads - 1) / kScanThreads);
     if (p.nchunks > 1) {
-        hipLaunchKernelGGL((k_scan<T, N, CONV, GATE, false>), dim3(gx, p.nchunks - 1, (unsigned)p.batch),
-                           dim3(kScanThreads), 0, st, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
+        hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, false>), dim3(gx, p.nchunks - 1, (unsigned)p.batch),
+                              dim3(kScanThreads), 0, st, static_cast<hipEvent_t>(p.ev_agg[0]),
+                              static_cast<hipEvent_t>(p.ev_agg[1]), 0, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
                            static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip, z, y, p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, sa);
     }
-    hipLaunchKernelGGL((k_scan<T, N, CONV, GATE, true>), dim3(gx, p.nchunks, (unsigned)p.batch),
-                       dim3(kScanThreads), 0, st, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
+    hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, true>), dim3(gx, p.nchunks, (unsigned)p.batch),
+                          dim3(kScanThreads), 0, st, static_cast<hipEvent_t>(p.ev_main[0]),
+                          static_cast<hipEvent_t>(p.ev_main[1]), 0, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
                        static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip, z, y, p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, sa);
     return hipGetLastError();
 }
@@ -374,11 +483,14 @@ static hipError_t launch_scan_t(const LaunchScan& p) {
 template <typename T, int N, bool CONV, bool GATE>
 static hipError_t launch_step_t(const LaunchScan& p) {
     hipStream_t st = static_cast<hipStream_t>(p.stream);
-    const unsigned gx = (unsigned)((p.D + kStepThreads - 1) / kStepThreads);
-    hipLaunchKernelGGL((k_step<T, N, CONV, GATE>), dim3(gx, (unsigned)p.batch), dim3(kStepThreads), 0, st,
+    constexpr int per_block = kStepThreads / 4;   // channels per workgroup (a quad each)
+    const unsigned gx = (unsigned)((p.D + per_block - 1) / per_block);
+    const unsigned gy = (unsigned)((p.batch + kStepStreams - 1) / kStepStreams);
+    hipExtLaunchKernelGGL((k_step<T, N, CONV, GATE>), dim3(gx, gy), dim3(kStepThreads), 0, st,
+                          static_cast<hipEvent_t>(p.ev_main[0]), static_cast<hipEvent_t>(p.ev_main[1]), 0,
                        static_cast<const T*>(p.x), p.conv_w, p.conv_b, static_cast<const T*>(p.delta),
                        p.delta_bias, p.A, static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip,
-                       static_cast<const T*>(p.z), static_cast<T*>(p.y), p.ssm_state, p.conv_state, (int)p.D);
+                       static_cast<const T*>(p.z), static_cast<T*>(p.y), p.ssm_state, p.conv_state, (int)p.D, (int)p.batch);
     return hipGetLastError();
 }
 

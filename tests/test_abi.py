@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["ss_workspace_bytes", "ss_conv_scan_fwd", "ss_step", "ss_status_str",
-                                           "ss_last_error", "ss_version"])
+                                           "ss_last_error", "ss_version", "ss_time_next_call"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -103,6 +103,14 @@ def test_y_aliasing_an_input_rejected():
 
 def test_conv_state_without_conv_rejected():
     assert _call(_dims(), _fake_args(conv_w=None)) == 1
+
+
+def test_timing_events_are_consumed_by_a_failing_call():
+    assert ss.lib.ss_time_next_call(None, None, None, None) == 0
+    # a rejected call must not leave the events armed for the next call
+    assert ss.lib.ss_time_next_call(1, 2, 3, 4) == 0
+    assert _call(_dims(), _fake_args(x=None)) == 1
+    assert ss.lib.ss_time_next_call(None, None, None, None) == 0
 
 
 def test_step_requires_states():

@@ -227,3 +227,49 @@ def test_selective_walkthrough_on_gpu(ss):
     want = np.array(g["expected"]["y_over_ln2"]) * math.log(2.0)
     e = maxrel(host(y)[0, :, 0], want)
     assert e <= 1e-6, e
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("S,Dn,N", [(1, 8, 4), (3, 70, 8), (5, 64, 16), (6, 33, 32), (7, 130, 64), (64, 257, 16)],
+                         ids=lambda v: str(v))
+def test_step_edge_shapes(ss, io, S, Dn, N):
+    """ss_step against the oracle for a few steps: stream counts not a multiple of the
+    streams handled per lane quad, ragged channel counts, every d_state."""
+    spec = W.ScanSpec("stepedge", 1, 1, 1, 4, io_dtype=io, delta_mode="bias", seed=77)
+    inp = W.gen_scan_inputs(spec, batch=S, seqlen=5, d_inner=Dn, d_state=N)
+    st = W.gen_states(S, Dn, N, seed=78)
+    g = to_dev(inp, io)
+    h = torch.from_numpy(st["ssm_state"]).cuda()
+    c = torch.from_numpy(st["conv_state"]).cuda()
+    hr, cr = st["ssm_state"].astype(np.float64), st["conv_state"].astype(np.float64)
+    for t in range(5):
+        y = ss.ss_step(g["x"][:, t].contiguous(), g["delta"][:, t].contiguous(), g["A"], g["B"][:, t].contiguous(),
+                       g["C"][:, t].contiguous(), h, conv_state=c, conv_w=g["conv_w"], conv_b=g["conv_b"],
+                       delta_bias=g["delta_bias"], D=g["D"], z=g["z"][:, t].contiguous())
+        yr, hr, cr = oracle.step(inp["x"][:, t], inp["delta"][:, t], inp["A"], inp["B"][:, t], inp["C"][:, t], hr,
+                                 conv_w=inp["conv_w"], conv_b=inp["conv_b"], delta_bias=inp["delta_bias"],
+                                 D=inp["D"], z=inp["z"][:, t], conv_state=cr)
+        e = maxrel(host(y), yr)
+        assert e <= TOL[io], (t, e)
+    torch.cuda.synchronize()
+    eh = maxrel(host(h), hr)
+    assert eh <= TOL["f32"], eh
+    assert np.array_equal(host(c).astype(np.float64), cr)
+
+
+@pytest.mark.parametrize("S,Dn,N", [(4, 64, 16), (3, 70, 8)], ids=str)
+def test_step_without_conv_or_gate(ss, S, Dn, N):
+    spec = W.ScanSpec("stepflags", 1, 1, 1, 4, io_dtype="f32", delta_mode="bias", seed=79)
+    inp = W.gen_scan_inputs(spec, batch=S, seqlen=3, d_inner=Dn, d_state=N)
+    st = W.gen_states(S, Dn, N, seed=80)
+    g = to_dev(inp, "f32")
+    h = torch.from_numpy(st["ssm_state"]).cuda()
+    hr = st["ssm_state"].astype(np.float64)
+    for t in range(3):
+        y = ss.ss_step(g["x"][:, t].contiguous(), g["delta"][:, t].contiguous(), g["A"], g["B"][:, t].contiguous(),
+                       g["C"][:, t].contiguous(), h, D=g["D"])
+        yr, hr, _ = oracle.step(inp["x"][:, t], inp["delta"][:, t], inp["A"], inp["B"][:, t], inp["C"][:, t], hr,
+                                D=inp["D"])
+        assert maxrel(host(y), yr) <= TOL["f32"]
+    torch.cuda.synchronize()
+    assert maxrel(host(h), hr) <= TOL["f32"]
