@@ -48,6 +48,22 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def measured_traffic(key: str):
+    """HBM bytes per dispatch of a kernel from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    passes (profiles/traffic.json), or None when the kernel source has changed since."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            t = json.load(f)
+        with open(os.path.join(ROOT, "selective_state_space_73_amd", "csrc", "selscan_kernels.hip"), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if t.get("kernel_source_sha256") != sha:
+        return None
+    return t.get("traffic_bytes_per_dispatch", {}).get(key)
+
+
 def slots_per_row(N: int) -> int:
     """Algorithmic fp32 VALU issue slots per (b, t, d) row, one slot per add/mul/fma/max
     and two per exp/log/reciprocal (gfx950 issues transcendentals at half rate):
@@ -276,6 +292,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=W.DECODE.steps)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 256 MiB device-to-device copy (a known-size reference for "
+                         "hardware traffic counters)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
@@ -288,6 +307,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     hip = Hip()
+    if a.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     spec = W.WORKLOADS[a.workload]
     log(f"[bench] workload {spec}")
     r = run_scan(ss, torch, hip, spec, a.steps, a.warmup, not a.no_cpu)
@@ -309,7 +334,8 @@ def main():
         "roofline": {"kernel": "k_scan main pass", "bound": "alu",
                      "achieved": round(slots / main_s / 1e12, 3), "peak": round(VALU_SLOTS_PER_S / 1e12, 3),
                      "unit": "Tslot/s", "frac": round(slots / main_s / VALU_SLOTS_PER_S, 4),
-                     "traffic": None, "kernel_ms": round(r["main_ms"], 4),
+                     "traffic": measured_traffic("k_scan_main") if a.workload == "long" else None,
+                     "kernel_ms": round(r["main_ms"], 4),
                      "slots_per_row": slots_per_row(N), "rows_per_launch": rows},
         "hbm_view": {"achieved": round(nbytes / main_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(nbytes / main_s / 1e9 / PEAK_HBM_GBS, 4), "bytes_per_launch": nbytes},
@@ -329,7 +355,7 @@ def main():
             "ms_per_token_step_graph": round(dr["graph_s"] / a.decode_steps * 1e3, 4),
             "roofline": {"kernel": "k_step", "bound": "hbm", "achieved": round(dbytes / ks / 1e9, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dbytes / ks / 1e9 / PEAK_HBM_GBS, 4),
-                         "traffic": None, "kernel_us": round(dr["kernel_ms"] * 1e3, 3),
+                         "traffic": measured_traffic("k_step"), "kernel_us": round(dr["kernel_ms"] * 1e3, 3),
                          "bytes_per_launch": dbytes},
             "hbm_gbps_end_to_end_graph": round(dbytes * dspec.layers * a.decode_steps / dr["graph_s"] / 1e9, 1),
         }
