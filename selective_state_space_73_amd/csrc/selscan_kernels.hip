@@ -193,14 +193,18 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     constexpr int PER_THREAD = (TILE_ELEMS + kScanThreads - 1) / kScanThreads;
     T tb[PER_THREAD], tc[PER_THREAD];
     auto tile_fetch = [&](int r0) {
+        // the tile's rows are contiguous in B and C: one uniform base, a 32-bit offset per element
+        const int rlast = nrows - 1 - r0;
+        const T* Bt = Bb + (int64_t)r0 * N;
+        const T* Ct = MAIN ? Cb + (int64_t)r0 * N : nullptr;
 #pragma unroll
         for (int k = 0; k < PER_THREAD; ++k) {
             const int e0 = tid + k * kScanThreads;
             const int e = e0 < TILE_ELEMS ? e0 : TILE_ELEMS - 1;
-            const int r = (r0 + e / N < nrows) ? r0 + e / N : nrows - 1;
-            const int64_t off = (int64_t)r * N + e % N;
-            tb[k] = Bb[off];
-            if (MAIN) tc[k] = Cb[off];
+            const int r = e / N < rlast ? e / N : rlast;
+            const int off = r * N + e % N;
+            tb[k] = Bt[off];
+            if (MAIN) tc[k] = Ct[off];
         }
     };
     auto tile_store = [&](int buf) {
@@ -256,7 +260,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
             }
             const float yv = (ya + yc) * p.g;
             // lanes past the last channel were clamped to it and store the same value
-            IO<T>::st(yb + (int64_t)r * D + d, yv);
+            IO<T>::st((yb + (int64_t)r * D) + d, yv);
         } else {
             sdt += p.dt;
         }
@@ -278,9 +282,9 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         for (int i = 0; i < U; ++i) {
             const int r = (r0 + i < nrows) ? r0 + i : nrows - 1;
             const int64_t off = (int64_t)r * D;
-            gx[i] = xb[off + d];
-            gd[i] = db[off + d];
-            if (MAIN && GATE) gz[i] = zb[off + d];
+            gx[i] = (xb + off)[d];
+            gd[i] = (db + off)[d];
+            if (MAIN && GATE) gz[i] = (zb + off)[d];
         }
     };
 
@@ -304,8 +308,8 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
             }
         } else {
             for (int r = tt; r < nrows; ++r) {
-                const int64_t off = (int64_t)r * D + d;
-                token(xb[off], db[off], (MAIN && GATE) ? zb[off] : T(0), tile + (r - tt) * NB, r);
+                const int64_t off = (int64_t)r * D;
+                token((xb + off)[d], (db + off)[d], (MAIN && GATE) ? (zb + off)[d] : T(0), tile + (r - tt) * NB, r);
             }
         }
         if (more) tile_store(buf ^ 1);
@@ -329,6 +333,294 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 #pragma unroll
         for (int n = 0; n < N; ++n) ws_S[ai * N + n] = h[n];
     }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk aggregates: for every chunk but the last, its end state S (from its
+// initial state: zero, or the caller's state for chunk 0) and its summed step
+// size. Written in the backward (Horner) form
+//     S_n = sum_t exp(A_n * R_t) * Delta_t * u_t * B_t[n],   R_t = sum_{k>t} Delta_k,
+// which is the unrolled recurrence. The sweep runs backward from the chunk end;
+// a state index n is dropped (wave-uniformly) once exp(A_n * R) < 2^-kAggCutLog2
+// for every lane, because R only grows from there. Rows after every n is dropped
+// only add Delta to the chunk's sum (needed exactly for its decay exp(A*sum))
+// and to a bound M on everything dropped:
+//     |dropped part of S_n| <= 2^-kAggCutLog2 * sum_t |Delta_t u_t| * max_n |B_t[n]|.
+// If 2^-kAggCutLog2 * M exceeds 2^-24 * max_n |S_n| (one unit roundoff of the
+// aggregate) for any lane, the wave recomputes S exactly with the forward
+// recurrence. R is accumulated in fp64.
+
+constexpr int kAggCutLog2 = 40;
+
+template <typename T, int N, bool CONV>
+__global__ void __launch_bounds__(kScanThreads)
+k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
+      const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
+      const T* __restrict__ Bm, const float* __restrict__ ssm_state, const float* __restrict__ conv_state,
+      float* __restrict__ ws_S, float* __restrict__ ws_sdt, float* __restrict__ ws_h0, float* __restrict__ ws_c0,
+      ScanArgs sa) {
+    const int D = sa.D;
+    const int d_raw = blockIdx.x * kScanThreads + threadIdx.x;
+    const int d = d_raw < D ? d_raw : D - 1;      // clamped lanes repeat the last channel
+    const int c = blockIdx.y;                     // chunk, < nchunks - 1
+    const int b = blockIdx.z;
+    const int64_t t0 = (int64_t)c * sa.chunk_len;
+    const int64_t t1 = t0 + sa.chunk_len;         // every chunk but the last is full
+    const int nagg = sa.nchunks - 1;
+    const int64_t row0 = (int64_t)b * sa.L;
+    const int64_t bd = (int64_t)b * D + d;
+
+    float A2[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) A2[n] = A[(int64_t)d * N + n] * kLog2e;
+    const float dbias = delta_bias ? delta_bias[d] : 0.0f;
+    float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 1.f, cb = 0.f;
+    if (CONV) {
+        w0 = conv_w[d * 4 + 0]; w1 = conv_w[d * 4 + 1]; w2 = conv_w[d * 4 + 2]; w3 = conv_w[d * 4 + 3];
+        cb = conv_b ? conv_b[d] : 0.0f;
+    }
+    // the main pass of a multi-chunk call reads copies of the initial states,
+    // because its last chunk overwrites them
+    if (c == 0) {
+        if (ssm_state) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) ws_h0[bd * N + n] = ssm_state[bd * N + n];
+        }
+        if (CONV && conv_state) {
+            ws_c0[bd * 3 + 0] = conv_state[bd * 3 + 0];
+            ws_c0[bd * 3 + 1] = conv_state[bd * 3 + 1];
+            ws_c0[bd * 3 + 2] = conv_state[bd * 3 + 2];
+        }
+    }
+    constexpr int U = 4;
+    constexpr int R = kScanTile;
+    static_assert(R % (2 * U) == 0, "tiles hold whole pairs of groups");
+    constexpr int NB = N + 1;                     // B values and max_n |B| per token
+    __shared__ float sB[2][R][NB];
+    const int tid = threadIdx.x;
+    constexpr int TILE_ELEMS = R * N;
+    constexpr int PER_THREAD = (TILE_ELEMS + kScanThreads - 1) / kScanThreads;
+    static_assert(kScanThreads % N == 0 && 64 % N == 0, "a token's N values sit in consecutive lanes of a wave");
+    T tb[PER_THREAD];
+    // tile with chunk-relative rows [rlo, rlo + R); rows before the chunk start are
+    // clamped to it (they are zero-weight padding)
+    const T* Bc = Bm + (row0 + t0) * N;                   // uniform: B of the chunk's first token
+    auto tile_fetch = [&](int rlo) {
+#pragma unroll
+        for (int k = 0; k < PER_THREAD; ++k) {
+            const int e0 = tid + k * kScanThreads;
+            const int e = e0 < TILE_ELEMS ? e0 : TILE_ELEMS - 1;
+            const int r = rlo + e / N;
+            tb[k] = Bc[(r < 0 ? 0 : r) * N + e % N];
+        }
+    };
+    auto tile_store = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < PER_THREAD; ++k) {
+            const int e = tid + k * kScanThreads;
+            const float v = IO<T>::cvt(tb[k]);
+            float m = __builtin_fabsf(v);
+#pragma unroll
+            for (int o = 1; o < N; o <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o, N));
+            if (e < TILE_ELEMS) {
+                sB[buf][e / N][e % N] = v;
+                if (e % N == 0) sB[buf][e / N][N] = m;
+            }
+        }
+    };
+
+    float S[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) S[n] = 0.0f;
+    double Rsum = 0.0;                            // sum of Delta over the tokens swept so far
+    float M = 0.0f;                               // sum |Delta u| max|B| over swept rows (full mode)
+    float Mh = 0.0f;                              // sum Delta max|B| over rows swept after every n was dropped
+    float xmax = 0.0f;                            // max |x| feeding those rows
+    // state indices are dropped in blocks of four; a block goes once its least
+    // negative exponent A2 * R is below the cut on every lane
+    constexpr int NBLK = N / 4;
+    float A2blk[NBLK];
+#pragma unroll
+    for (int j = 0; j < NBLK; ++j)
+        A2blk[j] = __builtin_fmaxf(__builtin_fmaxf(A2[4 * j], A2[4 * j + 1]), __builtin_fmaxf(A2[4 * j + 2], A2[4 * j + 3]));
+    uint32_t act = (1u << NBLK) - 1u;
+    const float cut = -(float)kAggCutLog2;
+
+    // initial conv history (x_{-3}, x_{-2}, x_{-1}) in registers
+    float hist0 = 0.f, hist1 = 0.f, hist2 = 0.f;
+    if (CONV && conv_state) { hist0 = conv_state[bd * 3 + 0]; hist1 = conv_state[bd * 3 + 1]; hist2 = conv_state[bd * 3 + 2]; }
+
+    // Token indices below are relative to the chunk start (int32). Rows at rel < 0
+    // are zero-weight padding; x at global token < 0 comes from the history.
+    const int clen = (int)(t1 - t0);
+    // lowest chunk-relative row of x this sweep reads from memory: rows down to -(3+U)
+    // are touched (x_{r-3} of the padding rows); below global token 0 nothing exists
+    const int minrel = t0 >= 3 + U ? -(3 + U) : (int)-t0;
+    const T* xrow0 = x + (row0 + t0) * D;                 // uniform: token t0 of this batch row
+    const T* drow0 = delta + (row0 + t0) * D;
+    auto xrel = [&](int r) -> float {                     // x at chunk-relative row r (may be < 0)
+        if (r >= minrel) return IO<T>::cvt(xrow0[(int64_t)r * D + d]);
+        const int64_t tt = t0 + r;                       // < 0 here
+        return tt == -1 ? hist2 : (tt == -2 ? hist1 : (tt == -3 ? hist0 : 0.0f));
+    };
+    // conv window for the token about to be processed (r): xa = x_r, xb = x_{r-1}, xc = x_{r-2}
+    float xa = xrel(clen - 1), xb = xrel(clen - 2), xc = xrel(clen - 3);
+    // prefetch of a group (rows gr-1 .. gr-U): delta of those rows, x of rows gr-4 .. gr-U-3;
+    // two buffers used alternately
+    T pd0[U], px0[U], pd1[U], px1[U];
+    auto load_group = [&](int gr, T* pd, T* px) {
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int r = gr - 1 - i;
+            const int rd = r < 0 ? 0 : r;
+            const int rx = (r - 3) < minrel ? minrel : r - 3;
+            pd[i] = (drow0 + (int64_t)rd * D)[d];
+            px[i] = (xrow0 + (int64_t)rx * D)[d];
+        }
+    };
+    bool cut_seen = false;                                // the window at the switch enters xmax once
+
+    // one group of U rows (gr-1 .. gr-U), B/C row of gr-1 at rowp
+    auto group = [&](int gr, const T* cd, const T* cx, const float* rowp) {
+        // x_{r-3} of each row, and which rows are padding; only the group that reaches
+        // down to rel < 3 needs the selects
+        float xd[U];
+        bool pad[U];
+        if (gr - U < 3) {
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const int r = gr - 1 - i;
+                xd[i] = (r - 3) >= minrel ? IO<T>::cvt(cx[i]) : xrel(r - 3);
+                pad[i] = r < 0;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < U; ++i) { xd[i] = IO<T>::cvt(cx[i]); pad[i] = false; }
+        }
+        if (act) {
+            float dt[U], wv[U];
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                float u;
+                if (CONV) {
+                    const float cv = __builtin_fmaf(w3, xa, __builtin_fmaf(w2, xb, __builtin_fmaf(w1, xc, __builtin_fmaf(w0, xd[i], cb))));
+                    u = silu(cv);
+                } else {
+                    u = xa;
+                }
+                xa = xb; xb = xc; xc = xd[i];
+                dt[i] = pad[i] ? 0.0f : softplus(IO<T>::cvt(cd[i]) + dbias);
+                wv[i] = dt[i] * u;
+            }
+            // suffix sums: fp64 running total, fp32 within the group
+            const float rbase = (float)Rsum;
+            float Rf[U], part = 0.0f;
+#pragma unroll
+            for (int i = 0; i < U; ++i) { Rf[i] = rbase + part; part += dt[i]; }
+            Rsum += (double)part;
+#pragma unroll
+            for (int i = 0; i < U; ++i) M = __builtin_fmaf(__builtin_fabsf(wv[i]), rowp[-i * NB + N], M);
+#pragma unroll
+            for (int j = 0; j < NBLK; ++j) {
+                if ((act >> j) & 1u) {
+#pragma unroll
+                    for (int i = 0; i < U; ++i) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int n = 4 * j + q;
+                            S[n] = __builtin_fmaf(exp2_fast(A2[n] * Rf[i]), wv[i] * rowp[-i * NB + n], S[n]);
+                        }
+                    }
+                    // weights only shrink further back: drop the block once every lane is below the cut
+                    if (!__any(A2blk[j] * (float)Rsum > cut)) act &= ~(1u << j);
+                }
+            }
+        } else {
+            if (!cut_seen) {
+                // the window entering the first row after the cut
+                xmax = __builtin_fmaxf(__builtin_fabsf(xa), __builtin_fmaxf(__builtin_fabsf(xb), __builtin_fabsf(xc)));
+                cut_seen = true;
+            }
+            float part = 0.0f;
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                // each x enters the bound once, as the newest input of the row that loads it
+                xmax = __builtin_fmaxf(xmax, pad[i] ? 0.0f : __builtin_fabsf(xd[i]));
+                const float dtv = pad[i] ? 0.0f : softplus(IO<T>::cvt(cd[i]) + dbias);
+                part += dtv;
+                Mh = __builtin_fmaf(dtv, rowp[-i * NB + N], Mh);
+            }
+            Rsum += (double)part;
+        }
+    };
+
+    const int ntiles = (clen + R - 1) / R;
+    tile_fetch(clen - R);
+    tile_store(0);
+    load_group(clen, pd0, px0);
+    __syncthreads();
+    int buf = 0;
+    for (int k = 0; k < ntiles; ++k) {
+        const int rhi = clen - k * R;                     // tile rows [rhi - R, rhi)
+        if (k + 1 < ntiles) tile_fetch(rhi - 2 * R);
+        const float* tbase = &sB[buf][0][0] - (int64_t)(rhi - R) * NB;   // row r of this tile at tbase + r*NB
+        for (int gr = rhi; gr > rhi - R; gr -= 2 * U) {
+            load_group(gr - U, pd1, px1);
+            group(gr, pd0, px0, tbase + (gr - 1) * NB);
+            load_group(gr - 2 * U, pd0, px0);
+            group(gr - U, pd1, px1, tbase + (gr - U - 1) * NB);
+        }
+        if (k + 1 < ntiles) tile_store(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+    }
+    xmax = cut_seen ? xmax : 0.0f;
+    // rows swept after the cut: |u| <= |c| <= |cb| + sum_k |w_k| max|x| (SiLU(c) shrinks |c|)
+    const float umax = CONV ? __builtin_fabsf(cb) + (__builtin_fabsf(w0) + __builtin_fabsf(w1) + __builtin_fabsf(w2) +
+                                                    __builtin_fabsf(w3)) * xmax
+                            : xmax;
+    const float Rtot = (float)Rsum;
+    if (c == 0 && ssm_state) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) S[n] = __builtin_fmaf(exp2_fast(A2[n] * Rtot), ssm_state[bd * N + n], S[n]);
+    }
+    float smax = 0.0f;
+#pragma unroll
+    for (int n = 0; n < N; ++n) smax = __builtin_fmaxf(smax, __builtin_fabsf(S[n]));
+    const float bound = (M + umax * Mh) * 0x1p-40f;
+    const bool bad = !(bound <= smax * 0x1p-24f);
+    if (__any(bad)) {
+        // exact forward recurrence over the chunk (rare: the dropped part was not negligible)
+        float h[N];
+        const float* src = (c == 0) ? ssm_state : nullptr;
+#pragma unroll
+        for (int n = 0; n < N; ++n) h[n] = src ? src[bd * N + n] : 0.0f;
+        float x3 = xrel(-3), x2 = xrel(-2), x1 = xrel(-1);
+        double sd = 0.0;
+        for (int64_t t = t0; t < t1; ++t) {
+            const float xt = IO<T>::ld(x + (row0 + t) * D + d);
+            float u = xt;
+            if (CONV) {
+                const float cv = __builtin_fmaf(w3, xt, __builtin_fmaf(w2, x1, __builtin_fmaf(w1, x2, __builtin_fmaf(w0, x3, cb))));
+                x3 = x2; x2 = x1; x1 = xt;
+                u = silu(cv);
+            }
+            const float dtv = softplus(IO<T>::ld(delta + (row0 + t) * D + d) + dbias);
+            sd += (double)dtv;
+            const float w = dtv * u;
+            const T* Bt = Bm + (row0 + t) * N;
+#pragma unroll
+            for (int n = 0; n < N; ++n)
+                h[n] = __builtin_fmaf(exp2_fast(dtv * A2[n]), h[n], w * IO<T>::cvt(Bt[n]));
+        }
+#pragma unroll
+        for (int n = 0; n < N; ++n) S[n] = h[n];
+        Rsum = sd;
+    }
+    const int64_t ai = ((int64_t)b * nagg + c) * D + d;
+    ws_sdt[ai] = (float)Rsum;
+#pragma unroll
+    for (int n = 0; n < N; ++n) ws_S[ai * N + n] = S[n];
 }
 
 // ---------------------------------------------------------------------------
@@ -468,10 +760,11 @@ static hipError_t launch_scan_t(const LaunchScan& p) {
     ScanArgs sa{p.L, p.chunk_len, (int)p.D, p.nchunks};
     const unsigned gx = (unsigned)((p.D + kScanThreads - 1) / kScanThreads);
     if (p.nchunks > 1) {
-        hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, false>), dim3(gx, p.nchunks - 1, (unsigned)p.batch),
+        hipExtLaunchKernelGGL((k_agg<T, N, CONV>), dim3(gx, p.nchunks - 1, (unsigned)p.batch),
                               dim3(kScanThreads), 0, st, static_cast<hipEvent_t>(p.ev_agg[0]),
                               static_cast<hipEvent_t>(p.ev_agg[1]), 0, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
-                           static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip, z, y, p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, sa);
+                              static_cast<const T*>(p.B), p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0,
+                              p.ws_c0, sa);
     }
     hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, true>), dim3(gx, p.nchunks, (unsigned)p.batch),
                           dim3(kScanThreads), 0, st, static_cast<hipEvent_t>(p.ev_main[0]),

@@ -273,3 +273,56 @@ def test_step_without_conv_or_gate(ss, S, Dn, N):
         assert maxrel(host(y), yr) <= TOL["f32"]
     torch.cuda.synchronize()
     assert maxrel(host(h), hr) <= TOL["f32"]
+
+
+def _long_chunk_case(ss, inp, io, dsel, label, states=True):
+    Bsz, L, Dn = inp["x"].shape
+    N = inp["A"].shape[1]
+    dims = ss.make_dims(Bsz, L, Dn, N, 0 if io == "f32" else 1)
+    assert ss.ss_workspace_bytes(dims) > 0, "shape does not select the chunked path"
+    st = W.gen_states(Bsz, Dn, N) if states else None
+    g = to_dev(inp, io)
+    hs = torch.from_numpy(st["ssm_state"]).cuda() if states else None
+    cs = torch.from_numpy(st["conv_state"]).cuda() if states else None
+    y = gpu_fwd(ss, g, hs, cs)
+    torch.cuda.synchronize()
+    yr, hr, cr = oracle_fwd(inp, st["ssm_state"] if states else None, st["conv_state"] if states else None,
+                            dsel=dsel)
+    yg = host(y[:, :, torch.as_tensor(dsel, device=y.device)])
+    e = maxrel(yg, yr)
+    print(f"{label} y maxrel {e:.3e}", flush=True)
+    assert e <= TOL[io], (label, e)
+    if states:
+        eh = maxrel(host(hs)[:, dsel], hr)
+        assert eh <= TOL["f32"], (label, "ssm_state", eh)
+
+
+def test_long_chunks_fp32_truncated_aggregates(ss):
+    """Chunks of 1024 tokens with step sizes in [1e-3, 1e-1]: the aggregate pass drops
+    each state index once its weight is below 2^-40; fp32 parity must still hold."""
+    spec = W.ScanSpec("lc", 2, 65536, 1024, 16, io_dtype="f32", delta_mode="direct", seed=123)
+    inp = W.gen_scan_inputs(spec)
+    _long_chunk_case(ss, inp, "f32", np.array([0, 5, 511, 700, 1023]), "long chunks fp32")
+
+
+def test_aggregate_bound_fallback(ss):
+    """Constant step 0.1 makes every state index fall below the cut early in the
+    backward sweep, while the first quarter of every 1024-token chunk carries inputs
+    of magnitude 1e6: the bound on the dropped part then exceeds one unit roundoff
+    of the aggregate, the exact recurrence takes over, and parity holds."""
+    spec = W.ScanSpec("fb", 2, 65536, 1024, 16, io_dtype="f32", delta_mode="direct", seed=124)
+    inp = W.gen_scan_inputs(spec)
+    inp["delta"][:] = np.float32(np.log(np.expm1(0.1)))
+    t = np.arange(65536)
+    head = (t % 1024) < 256
+    inp["x"][:, head, :] *= np.float32(1e6)
+    _long_chunk_case(ss, inp, "f32", np.array([0, 3, 512, 1023]), "bound fallback")
+
+
+def test_chunked_growing_state_channels(ss):
+    """Channels with A > 0 (a growing state) are never dropped by the cut."""
+    spec = W.ScanSpec("grow", 1, 16384, 2048, 16, io_dtype="f32", delta_mode="direct", seed=125)
+    inp = W.gen_scan_inputs(spec)
+    inp["A"][::7] = np.float32(0.002)
+    inp["A"][1::7, :4] = np.float32(0.0)
+    _long_chunk_case(ss, inp, "f32", np.array([0, 1, 7, 8, 14, 2047]), "growing state", states=False)
