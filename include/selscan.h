@@ -70,8 +70,8 @@ typedef enum {
 
 typedef struct {
     int64_t  batch;     /* B (streams for ss_step), >= 1                                  */
-    int64_t  seqlen;    /* L >= 1 for ss_conv_scan_fwd; ignored by ss_step (one token)     */
-    int64_t  d_inner;   /* D >= 1 channels                                                 */
+    int64_t  seqlen;    /* 1 <= L < 2^31 for ss_conv_scan_fwd; ignored by ss_step         */
+    int64_t  d_inner;   /* 1 <= D <= 2^26 channels                                         */
     int32_t  d_state;   /* N in {4, 8, 16, 32, 64}                                         */
     int32_t  d_conv;    /* K; 4 is the only width built                                    */
     int32_t  io_dtype;  /* ss_dtype of x, delta, z, B, C, y                                */

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <climits>
 #include <string>
 
 #include "selscan.h"
@@ -39,7 +40,7 @@ ss_status fail(ss_status s, const char* fmt, ...) {
 }
 
 constexpr int64_t kMaxGridYZ = 65535;
-constexpr int64_t kMinChunk = 256;        // shortest chunk worth a separate aggregate
+constexpr int64_t kMinChunk = 64;         // shortest chunk: one B/C tile
 constexpr int64_t kTargetGroups = 512;    // workgroups (of 4 waves) the scan aims to launch
 
 bool supported_n(int n) { return n == 4 || n == 8 || n == 16 || n == 32 || n == 64; }
@@ -104,8 +105,10 @@ ss_status check_dims(const ss_dims* d, bool step) {
     if (d->batch < 1 || d->batch > kMaxGridYZ)
         return fail(SS_ERR_INVALID_ARG, "batch %lld outside [1, %lld]", (long long)d->batch, (long long)kMaxGridYZ);
     if (!step && d->seqlen < 1) return fail(SS_ERR_INVALID_ARG, "seqlen %lld < 1", (long long)d->seqlen);
-    if (d->d_inner < 1 || d->d_inner > (int64_t(1) << 30))
-        return fail(SS_ERR_INVALID_ARG, "d_inner %lld outside [1, 2^30]", (long long)d->d_inner);
+    if (d->d_inner < 1 || d->d_inner > (int64_t(1) << 26))
+        return fail(SS_ERR_INVALID_ARG, "d_inner %lld outside [1, 2^26]", (long long)d->d_inner);
+    if (!step && d->seqlen > INT32_MAX)
+        return fail(SS_ERR_INVALID_ARG, "seqlen %lld above 2^31-1", (long long)d->seqlen);
     if (!supported_n(d->d_state)) return fail(SS_ERR_UNSUPPORTED, "d_state %d not in {4,8,16,32,64}", d->d_state);
     if (d->d_conv != 4) return fail(SS_ERR_UNSUPPORTED, "d_conv %d: only 4 is built", d->d_conv);
     if (d->io_dtype != SS_F32 && d->io_dtype != SS_BF16)

@@ -6,8 +6,14 @@
 namespace selscan {
 
 constexpr int kScanThreads = 256;   // channels per workgroup of the scan kernels (4 waves)
-constexpr int kStepThreads = 256;   // lanes per workgroup of the decode-step kernel (4 per channel)
-constexpr int kStepStreams = 4;     // streams each lane quad of the decode-step kernel handles
+#ifndef SELSCAN_STEP_THREADS
+#define SELSCAN_STEP_THREADS 256
+#endif
+#ifndef SELSCAN_STEP_STREAMS
+#define SELSCAN_STEP_STREAMS 4
+#endif
+constexpr int kStepThreads = SELSCAN_STEP_THREADS;   // lanes per workgroup of the decode-step kernel (4 per channel)
+constexpr int kStepStreams = SELSCAN_STEP_STREAMS;   // streams each lane quad of the decode-step kernel handles
 constexpr int kScanTile = 64;       // tokens of B/C staged in LDS at a time
 
 // Everything a launch needs, already validated by the C-ABI layer.

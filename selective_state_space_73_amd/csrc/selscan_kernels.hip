@@ -56,6 +56,7 @@ __device__ __forceinline__ float softplus(float v) {
 template <typename T> struct IO;
 template <> struct IO<float> {
     static __device__ __forceinline__ float cvt(float v) { return v; }
+    static __device__ __forceinline__ float bits(float v) { return v; }
     static __device__ __forceinline__ float ld(const float* p) { return *p; }
     static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
 };
@@ -66,8 +67,38 @@ template <> struct IO<uint16_t> {   // bfloat16 bits
     static __device__ __forceinline__ float ld(const uint16_t* p) {
         return __builtin_bit_cast(float, static_cast<uint32_t>(*p) << 16);
     }
-    static __device__ __forceinline__ void st(uint16_t* p, float v) {
-        *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));   // round to nearest even
+    static __device__ __forceinline__ void st(uint16_t* p, float v) { *p = bits(v); }
+    static __device__ __forceinline__ uint16_t bits(float v) {
+        return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));   // round to nearest even
+    }
+};
+
+// Raw buffer access: a uniform base (SGPR resource), a 32-bit per-lane byte offset
+// and a uniform byte offset, so the per-token addressing needs no 64-bit VALU
+// arithmetic. Offsets stay below 2^32 (d_inner <= 2^26 is checked on the host).
+constexpr int kBufDword3 = 0x00020000;            // raw buffer, 32-bit data format (gfx9 family)
+
+template <typename T> struct Buf;
+template <> struct Buf<uint16_t> {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ explicit Buf(const uint16_t* p)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), 0, -1, kBufDword3)) {}
+    __device__ __forceinline__ uint16_t ld(unsigned voff, unsigned soff) const {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    }
+    __device__ __forceinline__ void st(uint16_t v, unsigned voff, unsigned soff) const {
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
+    }
+};
+template <> struct Buf<float> {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ explicit Buf(const float* p)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, -1, kBufDword3)) {}
+    __device__ __forceinline__ float ld(unsigned voff, unsigned soff) const {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    }
+    __device__ __forceinline__ void st(float v, unsigned voff, unsigned soff) const {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
     }
 };
 
@@ -101,6 +132,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     // lanes past the last channel work on the last channel: they compute and store
     // bit-identical values, so no store needs a branch
     const int d = d_raw < D ? d_raw : D - 1;
+    const unsigned du = (unsigned)d;              // zero-extended lane offset: uniform-base addressing
     const int c = blockIdx.y;
     const int b = blockIdx.z;
     const int64_t t0 = (int64_t)c * sa.chunk_len;
@@ -180,6 +212,8 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     __shared__ float sbc[2][R][NB];
     const int tid = threadIdx.x;
     const int nrows = (int)(t1 - t0);
+    const unsigned voff = du * (unsigned)sizeof(T);               // lane byte offset within a token row
+    const unsigned rowb = (unsigned)D * (unsigned)sizeof(T);      // bytes per token row
     const int64_t rowbase = (int64_t)b * sa.L + t0;     // global row of the chunk's first token
     const T* xb = x + rowbase * D;
     const T* db = delta + rowbase * D;
@@ -260,7 +294,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
             }
             const float yv = (ya + yc) * p.g;
             // lanes past the last channel were clamped to it and store the same value
-            IO<T>::st((yb + (int64_t)r * D) + d, yv);
+            Buf<T>(yb + (int64_t)r * D).st(IO<T>::bits(yv), voff, 0u);
         } else {
             sdt += p.dt;
         }
@@ -278,13 +312,17 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     };
     T gx0[U], gd0[U], gz0[U], gx1[U], gd1[U], gz1[U];
     auto load_group = [&](int r0, T* gx, T* gd, T* gz) {
+        // rows r0 .. r0+U-1 relative to one base per group (clamped to the chunk's last row)
+        const int rb = r0 < nrows ? r0 : nrows - 1;
+        const int64_t off = (int64_t)rb * D;
+        const Buf<T> bx(xb + off), bdl(db + off);
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const int r = (r0 + i < nrows) ? r0 + i : nrows - 1;
-            const int64_t off = (int64_t)r * D;
-            gx[i] = (xb + off)[d];
-            gd[i] = (db + off)[d];
-            if (MAIN && GATE) gz[i] = (zb + off)[d];
+            const unsigned so = (unsigned)(r - rb) * rowb;
+            gx[i] = bx.ld(voff, so);
+            gd[i] = bdl.ld(voff, so);
+            if (MAIN && GATE) gz[i] = Buf<T>(zb + off).ld(voff, so);
         }
     };
 
@@ -309,7 +347,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         } else {
             for (int r = tt; r < nrows; ++r) {
                 const int64_t off = (int64_t)r * D;
-                token((xb + off)[d], (db + off)[d], (MAIN && GATE) ? (zb + off)[d] : T(0), tile + (r - tt) * NB, r);
+                token((xb + off)[du], (db + off)[du], (MAIN && GATE) ? (zb + off)[du] : T(0), tile + (r - tt) * NB, r);
             }
         }
         if (more) tile_store(buf ^ 1);
@@ -362,6 +400,7 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     const int D = sa.D;
     const int d_raw = blockIdx.x * kScanThreads + threadIdx.x;
     const int d = d_raw < D ? d_raw : D - 1;      // clamped lanes repeat the last channel
+    const unsigned du = (unsigned)d;              // zero-extended lane offset: uniform-base addressing
     const int c = blockIdx.y;                     // chunk, < nchunks - 1
     const int b = blockIdx.z;
     const int64_t t0 = (int64_t)c * sa.chunk_len;
@@ -474,8 +513,8 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
             const int r = gr - 1 - i;
             const int rd = r < 0 ? 0 : r;
             const int rx = (r - 3) < minrel ? minrel : r - 3;
-            pd[i] = (drow0 + (int64_t)rd * D)[d];
-            px[i] = (xrow0 + (int64_t)rx * D)[d];
+            pd[i] = (drow0 + (int64_t)rd * D)[du];
+            px[i] = (xrow0 + (int64_t)rx * D)[du];
         }
     };
     bool cut_seen = false;                                // the window at the switch enters xmax once

@@ -75,7 +75,8 @@ def test_null_required_pointer_rejected(field):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(batch=0), 1), (dict(seqlen=0), 1), (dict(d_inner=0), 1), (dict(d_state=12), 2),
+    (dict(batch=0), 1), (dict(seqlen=0), 1), (dict(d_inner=0), 1), (dict(d_inner=(1 << 26) + 1), 1),
+    (dict(seqlen=1 << 31), 1), (dict(d_state=12), 2),
     (dict(d_state=128), 2), (dict(d_conv=3), 2), (dict(io_dtype=7), 2),
 ])
 def test_bad_dims_rejected(kw, status):
