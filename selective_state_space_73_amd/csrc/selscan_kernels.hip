@@ -114,8 +114,15 @@ struct ScanArgs {
     int nchunks;
 };
 
+// Register budget of the scan kernel: three waves per SIMD (<= 168 VGPRs) for
+// N <= 16, measured faster than the compiler's own choice (two waves at ~240
+// VGPRs) because more resident waves hide the long per-token dependency chains;
+// larger N needs the registers for the state and keeps one-wave-per-SIMD limits.
+// (Without the conv the compiler's schedule under that cap spills, so it is left free.)
+template <int N, bool CONV> constexpr int scan_waves_per_eu() { return (N <= 16 && CONV) ? 3 : 1; }
+
 template <typename T, int N, bool CONV, bool GATE, bool MAIN>
-__global__ void __launch_bounds__(kScanThreads)
+__global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<N, CONV>())))
 k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
        const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
        const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
