@@ -10,7 +10,8 @@ builds that file with gcc, widens arrays to float64 and marshals pointers.
 
 Pinned by ``tests/test_oracle_pins.py`` (closed form, LTI convolution,
 worked example, limits, conv impulse / library conv, gate and skip,
-softplus through a cumulative sum) and ``tests/test_oracle_mutants.py``.
+softplus through a cumulative sum; for the zero-order-hold variant: Van Loan
+``expm``, equilibrium, composition of steps) and ``tests/test_oracle_mutants.py``.
 """
 from __future__ import annotations
 
@@ -56,10 +57,10 @@ class Oracle:
             path = LIB
         self.path = path
         lib = ctypes.CDLL(path)
-        args = [ctypes.c_int64] * 5 + [_dp] * 13 + [ctypes.c_int]
+        args = [ctypes.c_int64] * 5 + [_dp] * 13 + [ctypes.c_int, ctypes.c_int]
         lib.oracle_conv_scan_fwd.argtypes = args
         lib.oracle_conv_scan_fwd.restype = ctypes.c_int
-        lib.oracle_step.argtypes = [ctypes.c_int64] * 4 + [_dp] * 13 + [ctypes.c_int]
+        lib.oracle_step.argtypes = [ctypes.c_int64] * 4 + [_dp] * 13 + [ctypes.c_int, ctypes.c_int]
         lib.oracle_step.restype = ctypes.c_int
         self._lib = lib
 
@@ -73,8 +74,9 @@ class Oracle:
         return arr, arr.ctypes.data_as(_dp)
 
     def conv_scan_fwd(self, x, delta, A, B, C, *, conv_w=None, conv_b=None, delta_bias=None,
-                      D=None, z=None, ssm_state=None, conv_state=None, nthreads: int = 0):
-        """Full-sequence forward. x/delta/z: [B,L,D]; B/C: [B,L,N]; A: [D,N];
+                      D=None, z=None, ssm_state=None, conv_state=None, zoh: bool = False,
+                      nthreads: int = 0):
+        """Full-sequence forward (zoh=True: zero-order-hold write term instead of Euler). x/delta/z: [B,L,D]; B/C: [B,L,N]; A: [D,N];
         conv_w: [D,K]; conv_b/delta_bias/D: [D]; ssm_state: [B,D,N]; conv_state: [B,D,K-1].
         Returns (y [B,L,D], final ssm_state or None, final conv_state or None), float64."""
         x = np.asarray(x)
@@ -98,13 +100,13 @@ class Oracle:
             y.ctypes.data_as(_dp),
             None if hs is None else hs.ctypes.data_as(_dp),
             None if cs is None else cs.ctypes.data_as(_dp),
-            int(nthreads))
+            int(bool(zoh)), int(nthreads))
         if rc != 0:
             raise ValueError("oracle rejected its arguments")
         return y, hs, cs
 
     def step(self, x, delta, A, B, C, ssm_state, *, conv_w=None, conv_b=None, delta_bias=None,
-             D=None, z=None, conv_state=None, nthreads: int = 0):
+             D=None, z=None, conv_state=None, zoh: bool = False, nthreads: int = 0):
         """One decode step. x/delta/z: [S,D]; B/C: [S,N]; states required (conv_state when conv_w).
         Returns (y [S,D], new ssm_state, new conv_state or None)."""
         x = np.asarray(x)
@@ -113,7 +115,7 @@ class Oracle:
             x[:, None, :], np.asarray(delta)[:, None, :], A, np.asarray(B)[:, None, :],
             np.asarray(C)[:, None, :], conv_w=conv_w, conv_b=conv_b, delta_bias=delta_bias, D=D,
             z=None if z is None else np.asarray(z)[:, None, :], ssm_state=ssm_state,
-            conv_state=conv_state, nthreads=nthreads)
+            conv_state=conv_state, zoh=zoh, nthreads=nthreads)
         return y[:, 0, :], hs, cs
 
 

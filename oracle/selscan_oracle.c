@@ -12,14 +12,18 @@
  *          history from conv_state (or zeros)                 conv_w[d,K-1] multiplies x_t
  *   u_t  = c_t * sigmoid(c_t)                                 SiLU
  *   D_t  = softplus(delta_t + b_delta[d])                     selection of the step size
- *   h_t  = exp(D_t * A[d,n]) * h_{t-1} + D_t * B_t[n] * u_t   discretised recurrence
+ *   h_t  = exp(D_t * A[d,n]) * h_{t-1} + Bbar_t[n] * u_t      discretised recurrence
+ *          Bbar = D_t * B_t[n]                                 (Euler write term), or
+ *          Bbar = (1 - exp(D_t A[d,n])) / (-A[d,n]) * B_t[n]    (zero-order hold; D_t * B when A = 0)
  *   y_t  = sum_n C_t[n] * h_t[n] + Dskip[d] * u_t             readout after the update
  *   out_t = y_t * z_t * sigmoid(z_t)                          SiLU(z) gate
  *
  * Sources (the pages, cited by title and section):
  *  - ai360xpert.com "Mamba", "The selection mechanism": step size is softplus of
  *    an affine function of the input (bias inside the softplus); A_bar = exp(Delta A),
- *    B_bar ~ Delta B (the Euler write term used here).
+ *    B_bar ~ Delta B (the Euler write term, the default); its "Show Me the Code"
+ *    loop and inferensys.com "Mamba" (zero-order hold rule) give the ZOH form
+ *    B_bar = (1 - A_bar)/(-A) B (selected by `zoh`).
  *  - ozercemkelahmet.com "Mamba", "A minimal selective scan in PyTorch": state per
  *    (batch, channel, state index), zero initial state, dA = exp(delta*A),
  *    dB = delta*B, h = dA*h + dB*x, output read from the updated state as sum over n
@@ -61,7 +65,7 @@ static void scan_channel(int64_t L, int64_t D, int64_t N, int64_t K,
                          const double* delta, const double* delta_bias, const double* A,
                          const double* Bm, const double* Cm, const double* Dskip,
                          const double* z, double* y, double* ssm_state, double* conv_state,
-                         int64_t b, int64_t d, double* h) {
+                         int zoh, int64_t b, int64_t d, double* h) {
     double win[ORACLE_MAX_K];            /* win[0..K-2]: x_{t-(K-1)} .. x_{t-1} */
     for (int64_t k = 0; k < K - 1; ++k)
         win[k] = conv_state ? conv_state[(b * D + d) * (K - 1) + k] : 0.0;
@@ -88,8 +92,11 @@ static void scan_channel(int64_t L, int64_t D, int64_t N, int64_t K,
         const double dt = softplus(delta[row] + (delta_bias ? delta_bias[d] : 0.0));
 
         for (int64_t n = 0; n < N; ++n) {
-            const double abar = exp(dt * A[d * N + n]);
-            h[n] = abar * h[n] + dt * Bm[bc + n] * u;
+            const double a = A[d * N + n];
+            const double abar = exp(dt * a);
+            double bcoef = dt;                                   /* Euler: Delta */
+            if (zoh && a != 0.0) bcoef = expm1(dt * a) / a;      /* (1 - exp(Delta a)) / (-a) */
+            h[n] = abar * h[n] + bcoef * Bm[bc + n] * u;
         }
 
         double yt = 0.0;
@@ -112,7 +119,7 @@ int oracle_conv_scan_fwd(int64_t Bsz, int64_t L, int64_t D, int64_t N, int64_t K
                          const double* delta, const double* delta_bias, const double* A,
                          const double* Bm, const double* Cm, const double* Dskip,
                          const double* z, double* y, double* ssm_state, double* conv_state,
-                         int nthreads) {
+                         int zoh, int nthreads) {
     if (Bsz < 0 || L < 0 || D < 0 || N < 1 || N > 1024 || K < 1 || K > ORACLE_MAX_K) return -1;
     if (!x || !delta || !A || !Bm || !Cm || !y) return -1;
     if (!conv_w && conv_state) return -1;
@@ -124,7 +131,7 @@ int oracle_conv_scan_fwd(int64_t Bsz, int64_t L, int64_t D, int64_t N, int64_t K
 #pragma omp for schedule(dynamic, 1)
         for (int64_t i = 0; i < channels; ++i)
             scan_channel(L, D, N, K, x, conv_w, conv_b, delta, delta_bias, A, Bm, Cm, Dskip,
-                         z, y, ssm_state, conv_state, i / D, i % D, h);
+                         z, y, ssm_state, conv_state, zoh, i / D, i % D, h);
     }
     return 0;
 }
@@ -136,10 +143,10 @@ int oracle_step(int64_t Bsz, int64_t D, int64_t N, int64_t K,
                 const double* delta, const double* delta_bias, const double* A,
                 const double* Bm, const double* Cm, const double* Dskip,
                 const double* z, double* y, double* ssm_state, double* conv_state,
-                int nthreads) {
+                int zoh, int nthreads) {
     if (!ssm_state || (conv_w && !conv_state)) return -1;
     return oracle_conv_scan_fwd(Bsz, 1, D, N, K, x, conv_w, conv_b, delta, delta_bias, A,
-                                Bm, Cm, Dskip, z, y, ssm_state, conv_state, nthreads);
+                                Bm, Cm, Dskip, z, y, ssm_state, conv_state, zoh, nthreads);
 }
 
-int oracle_version(void) { return 1; }
+int oracle_version(void) { return 2; }

@@ -4,7 +4,10 @@ Each pin checks the oracle against something other than itself: the unrolled
 closed form of the recurrence, the LTI convolution-kernel view (by FFT), the
 worked example on the ozercemkelahmet.com page, the pages' small/large step
 size limits, a library convolution (torch conv1d) and library sigmoid /
-softplus (scipy.special.expit, numpy.logaddexp). Every pin takes an oracle
+softplus (scipy.special.expit, numpy.logaddexp). The zero-order-hold variant is
+pinned to Van Loan's matrix-exponential form of the exact discretisation
+(scipy.linalg.expm), to the continuous system's equilibrium and to the
+composition property of the exact flow. Every pin takes an oracle
 handle so that the same checks can be run on deliberately broken copies of
 the oracle (tests/test_oracle_mutants.py) to show that they catch mistakes.
 
@@ -18,6 +21,7 @@ import os
 
 import numpy as np
 import torch
+from scipy.linalg import expm
 from scipy.special import expit
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -336,8 +340,93 @@ def pin_step_matches_scan(orc, seed=10, shape=(3, 6, 4, 5)):
     assert relerr(hs, h) < 1e-13 and np.array_equal(css, cs)
 
 
+# ---------------------------------------------------------------------------
+# zero-order hold (inferensys.com "Mamba", the discretization bullet; the
+# ai360xpert.com "Mamba" code section writes the same "simplified ZOH" term)
+
+def inv_softplus(dt):
+    """Pre-activation whose softplus is dt (dt > 0)."""
+    return np.log(np.expm1(np.asarray(dt, np.float64)))
+
+
+def pin_zoh_van_loan(orc, seed=11, shape=(2, 7, 3, 5)):
+    """ZOH is the exact solution of h' = a h + b u over one step of length Delta
+    with u, b held. Van Loan: expm(Delta [[a, b u], [0, 0]]) has the transition
+    exp(a Delta) top-left and the held-input response top-right. Chaining those
+    2x2 transitions from h0 (library expm, no recurrence formula) and reading out
+    C . h must give the oracle's ZOH scan, including a = 0 and a -> 0 states."""
+    rng = np.random.default_rng(seed)
+    Bsz, L, D, N = shape
+    c = rand_case(rng, *shape, states=True)
+    c["A"][:, 0] = 0.0
+    c["A"][:, 1] = -1e-9
+    y, h, _ = orc.conv_scan_fwd(**c, zoh=True)
+    u, _ = lib_conv_silu(c["x"], c["conv_w"], c["conv_b"], c["conv_state"])
+    dt = lib_softplus(c["delta"] + c["delta_bias"])
+    y_ref = np.zeros((Bsz, L, D))
+    h_ref = np.zeros((Bsz, D, N))
+    for b in range(Bsz):
+        for d in range(D):
+            for n in range(N):
+                v = np.array([c["ssm_state"][b, d, n], 1.0])
+                for t in range(L):
+                    gen = np.array([[c["A"][d, n], c["B"][b, t, n] * u[b, t, d]], [0.0, 0.0]])
+                    v = expm(dt[b, t, d] * gen) @ v
+                    y_ref[b, t, d] += c["C"][b, t, n] * v[0]
+                h_ref[b, d, n] = v[0]
+    y_ref = (y_ref + c["D"] * u) * lib_silu(c["z"])
+    assert relerr(y, y_ref) < 1e-12, relerr(y, y_ref)
+    assert relerr(h, h_ref) < 1e-12, relerr(h, h_ref)
+
+
+def pin_zoh_equilibrium(orc, seed=12, L=30, D=3, N=4):
+    """With u and B held, h* = -B u / a is the equilibrium of the continuous
+    system and so a fixed point of its exact discretisation for every step size:
+    a state started there stays there while Delta varies wildly from step to step,
+    and y_t = C_t . h* + D u."""
+    rng = np.random.default_rng(seed)
+    A = -rng.uniform(0.2, 3.0, (D, N))
+    Bv = rng.standard_normal(N)
+    uv = rng.standard_normal(D)
+    hstar = -(uv[:, None] * Bv[None, :]) / A
+    x = np.broadcast_to(uv, (1, L, D)).copy()
+    Bm = np.broadcast_to(Bv, (1, L, N)).copy()
+    Cm = rng.standard_normal((1, L, N))
+    Dsk = rng.standard_normal(D)
+    y, h, _ = orc.conv_scan_fwd(x, rng.uniform(-6.0, 6.0, (1, L, D)), A, Bm, Cm, D=Dsk,
+                                ssm_state=hstar[None], zoh=True)
+    assert relerr(h[0], hstar) < 1e-13, relerr(h[0], hstar)
+    ref = np.einsum("ln,dn->ld", Cm[0], hstar) + Dsk * uv
+    assert relerr(y[0], ref) < 1e-13, relerr(y[0], ref)
+
+
+def pin_zoh_composition(orc, seed=13, D=3, N=4):
+    """The exact flow composes: with u, B held, two ZOH steps of sizes Delta1 and
+    Delta2 reach the same state as one step of Delta1 + Delta2."""
+    rng = np.random.default_rng(seed)
+    A = -rng.uniform(0.2, 3.0, (D, N))
+    Bv = rng.standard_normal(N)
+    uv = rng.standard_normal(D)
+    h0 = rng.standard_normal((1, D, N))
+    d1 = rng.uniform(0.05, 2.0, D)
+    d2 = rng.uniform(0.05, 2.0, D)
+
+    def run(steps):
+        L = len(steps)
+        pre = inv_softplus(np.stack(steps))[None]
+        _, h, _ = orc.conv_scan_fwd(np.broadcast_to(uv, (1, L, D)).copy(), pre, A,
+                                    np.broadcast_to(Bv, (1, L, N)).copy(), np.zeros((1, L, N)),
+                                    ssm_state=h0, zoh=True)
+        return h
+
+    h_two = run([d1, d2])
+    h_one = run([d1 + d2])
+    assert relerr(h_two, h_one) < 1e-12, relerr(h_two, h_one)
+
+
 ALL_PINS = [
     pin_closed_form, pin_lti_fft, pin_worked_example, pin_selective_walkthrough,
     pin_small_step_keeps_state, pin_large_step_forgets, pin_conv_impulse, pin_conv_library,
     pin_gate_and_skip, pin_softplus_sum, pin_state_handoff, pin_step_matches_scan,
+    pin_zoh_van_loan, pin_zoh_equilibrium, pin_zoh_composition,
 ]

@@ -8,6 +8,17 @@ import pytest
 import oracle
 import pins
 
+_UPDATE = """        for (int64_t n = 0; n < N; ++n) {
+            const double a = A[d * N + n];
+            const double abar = exp(dt * a);
+            double bcoef = dt;                                   /* Euler: Delta */
+            if (zoh && a != 0.0) bcoef = expm1(dt * a) / a;      /* (1 - exp(Delta a)) / (-a) */
+            h[n] = abar * h[n] + bcoef * Bm[bc + n] * u;
+        }
+"""
+_READOUT = """        double yt = 0.0;
+        for (int64_t n = 0; n < N; ++n) yt += Cm[bc + n] * h[n];"""
+
 MUTANTS = {
     "conv_taps_reversed": [
         ("c += conv_w[d * K + k] * win[k];", "c += conv_w[d * K + (K - 1 - k)] * win[k];"),
@@ -18,28 +29,19 @@ MUTANTS = {
     "softplus_drops_bias": [("softplus(delta[row] + (delta_bias ? delta_bias[d] : 0.0))",
                              "softplus(delta[row])")],
     "softplus_log1p_dropped": [("return m + log1p(exp(-fabs(v)));", "return m + exp(-fabs(v));")],
-    "decay_sign_flipped": [("exp(dt * A[d * N + n])", "exp(-dt * A[d * N + n])")],
-    "zoh_instead_of_euler": [("h[n] = abar * h[n] + dt * Bm[bc + n] * u;",
-                              "h[n] = abar * h[n] + (1.0 - abar) / (-A[d * N + n]) * Bm[bc + n] * u;")],
-    "write_term_without_delta": [("h[n] = abar * h[n] + dt * Bm[bc + n] * u;",
-                                  "h[n] = abar * h[n] + Bm[bc + n] * u;")],
-    "state_not_carried": [("h[n] = abar * h[n] + dt", "h[n] = abar * 0.0 + dt")],
-    "B_and_C_swapped": [("dt * Bm[bc + n] * u", "dt * Cm[bc + n] * u"),
+    "decay_sign_flipped": [("abar = exp(dt * a);", "abar = exp(-dt * a);")],
+    "zoh_instead_of_euler": [("if (zoh && a != 0.0)", "if (a != 0.0)")],
+    "euler_instead_of_zoh": [("if (zoh && a != 0.0)", "if (0 && a != 0.0)")],
+    "zoh_sign_flipped": [("bcoef = expm1(dt * a) / a;", "bcoef = expm1(dt * a) / (-a);")],
+    "zoh_without_minus_one": [("bcoef = expm1(dt * a) / a;", "bcoef = exp(dt * a) / a;")],
+    "zoh_extra_delta": [("bcoef = expm1(dt * a) / a;", "bcoef = dt * expm1(dt * a) / a;")],
+    "zoh_zero_a_drops_input": [("if (zoh && a != 0.0) bcoef = expm1(dt * a) / a;",
+                                "if (zoh) bcoef = (a != 0.0) ? expm1(dt * a) / a : 0.0;")],
+    "write_term_without_delta": [("double bcoef = dt;", "double bcoef = 1.0;")],
+    "state_not_carried": [("h[n] = abar * h[n] + bcoef", "h[n] = abar * 0.0 + bcoef")],
+    "B_and_C_swapped": [("bcoef * Bm[bc + n] * u", "bcoef * Cm[bc + n] * u"),
                         ("yt += Cm[bc + n] * h[n];", "yt += Bm[bc + n] * h[n];")],
-    "readout_before_update": [
-        ("""        for (int64_t n = 0; n < N; ++n) {
-            const double abar = exp(dt * A[d * N + n]);
-            h[n] = abar * h[n] + dt * Bm[bc + n] * u;
-        }
-
-        double yt = 0.0;
-        for (int64_t n = 0; n < N; ++n) yt += Cm[bc + n] * h[n];""",
-         """        double yt = 0.0;
-        for (int64_t n = 0; n < N; ++n) yt += Cm[bc + n] * h[n];
-        for (int64_t n = 0; n < N; ++n) {
-            const double abar = exp(dt * A[d * N + n]);
-            h[n] = abar * h[n] + dt * Bm[bc + n] * u;
-        }""")],
+    "readout_before_update": [(_UPDATE + "\n" + _READOUT, _READOUT + "\n" + _UPDATE)],
     "skip_dropped": [("yt += (Dskip ? Dskip[d] : 0.0) * u;", "yt += 0.0 * u;")],
     "skip_uses_x": [("yt += (Dskip ? Dskip[d] : 0.0) * u;", "yt += (Dskip ? Dskip[d] : 0.0) * xt;")],
     "gate_sigmoid_not_silu": [("if (z) yt *= silu(z[row]);", "if (z) yt *= 1.0 / (1.0 + exp(-z[row]));")],
