@@ -2,7 +2,7 @@
 """Benchmark of the selective-scan (S6) forward path and decode step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|train|block]
-                    [--no-decode] [--no-cpu]
+                    [--no-decode] [--no-cpu] [--zoh-steps K]
 
 A step is one ss_conv_scan_fwd call over the whole workload (conv1d + SiLU,
 softplus step, discretisation, scan, C.h + D.u readout, SiLU(z) gate), with
@@ -13,9 +13,11 @@ parameters. Prints one JSON line:
 * value: Gelem/s = B*L*D*N / step time, whole step (all kernels of the call).
 * roofline: the main scan kernel, timed live with HIP events recorded around
   that kernel on its own stream; it is bound by VALU issue, so achieved is its
-  algorithmic VALU slots per launch / its average duration against the chip's
-  VALU slot rate (see slots_per_row below). The same kernel's HBM view
-  (algorithmic bytes / duration vs 8 TB/s) is given as hbm_view.
+  algorithmic fp32 VALU instructions per launch / its average duration against
+  the chip's VALU issue rate (see instr_per_row below). The same kernel's HBM
+  view (algorithmic bytes / duration vs 8 TB/s) is given as hbm_view.
+* zoh: the same workload and inputs with the zero-order-hold write term, its
+  step rate and main-kernel roofline on the same model.
 * decode: 64 streams x 32 layers x 256 token steps (d_inner 8192, d_state 16),
   one ss_step per layer and token, timed end to end eagerly and replayed from
   HIP graphs (one graph per token step over the 32 layers); its roofline is
@@ -40,7 +42,10 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E
-VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9     # CUs x SIMDs x lanes x clock: 39.3e12 fp32 lane-ops/s (no packed fp32)
+# fp32 VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3e12 lane-instructions/s
+# (a wave64 instruction holds a SIMD16 for 4 cycles; no packed fp32). Transcendentals
+# issue in one slot too; measured interleaved with fmas they cost 1.3-1.9 slots.
+VALU_INSTR_PER_S = 256 * 4 * 16 * 2.4e9
 METRIC = "selective-scan fwd Gelem(B·L·D·N)/s + achieved HBM GB/s vs peak; decode tokens/s"
 
 
@@ -48,29 +53,33 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def measured_traffic(key: str):
+def measured_traffic(key: str, digest: str):
     """HBM bytes per dispatch of a kernel from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    passes (profiles/traffic.json), or None when the kernel source has changed since."""
-    import hashlib
+    passes (profiles/traffic.json), or None when the kernel sources have changed since."""
     try:
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             t = json.load(f)
-        with open(os.path.join(ROOT, "selective_state_space_73_amd", "csrc", "selscan_kernels.hip"), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
-    if t.get("kernel_source_sha256") != sha:
+    if t.get("kernel_source_sha256") != digest:
         return None
     return t.get("traffic_bytes_per_dispatch", {}).get(key)
 
 
-def slots_per_row(N: int) -> int:
-    """Algorithmic fp32 VALU issue slots per (b, t, d) row, one slot per add/mul/fma/max
-    and two per exp/log/reciprocal (gfx950 issues transcendentals at half rate):
-    conv 4; SiLU(conv) 7 (scale, exp, add, rcp, mul); softplus 9 (bias add, scale,
-    exp, add, log, max, add... ); Delta*u 1; per state index 6 (Delta*A, exp,
-    Delta*u*B, state fma, readout fma); D*u 1; SiLU(z) 7 and the gate product 1."""
-    return 30 + 6 * N
+def instr_per_row(N: int, zoh: bool = False) -> int:
+    """Algorithmic fp32 VALU instructions per (b, t, d) row (one per add/mul/fma/max/
+    compare/select, one per exp/log/reciprocal): conv 4; SiLU(conv) 5 (scale, exp,
+    add, reciprocal, mul); softplus 7 (bias add, scale, exp, add, log, max, add);
+    Delta*u 1; D*u 1; SiLU(z) 5 and the gate product 1 -> 24. Per state index, Euler
+    5 (Delta*A, exp, Delta*u*B, state fma, readout fma). The zero-order hold adds 8:
+    the coefficient (exp(Delta A) - 1) / A as one fma on the decay, its series
+    branch (3 fma and the product with Delta), the compare and select between
+    them, and the product with u*B (which replaces Delta*u*B)."""
+    return 24 + (13 if zoh else 5) * N
+
+
+def trans_per_row(N: int) -> int:
+    return 6 + N
 
 
 class Hip:
@@ -119,7 +128,9 @@ def decode_bytes(spec: W.DecodeSpec) -> int:
     return S * D * (2 * (N + 3) * 4 + 4 * 2) + S * N * 2 * 2 + D * (N + 4 + 3) * 4
 
 
-def run_scan(ss, torch, hip, spec, steps, warmup, want_sample):
+def prepare_scan(torch, spec, want_sample):
+    """Seeded inputs of the workload, resident in HBM; plus a host channel sample for
+    the CPU baseline."""
     t0 = time.time()
     inp = W.gen_scan_inputs(spec)
     log(f"[bench] generated {spec.name} inputs in {time.time() - t0:.1f}s")
@@ -140,17 +151,26 @@ def run_scan(ss, torch, hip, spec, steps, warmup, want_sample):
         v = torch.from_numpy(inp.pop(k)).to(dev)
         g[k] = v.to(tdt) if k in ("x", "delta", "z", "B", "C") else v
     del inp
+    return g, sample
+
+
+def run_scan(ss, torch, hip, spec, g, steps, warmup, zoh=False):
+    """Time `steps` whole forward calls (wall clock between synchronisations) and,
+    with events recorded at the kernels' own start and end, each kernel."""
+    tdt = g["x"].dtype
+    dev = g["x"].device
     Bz, L, D, N = spec.batch, spec.seqlen, spec.d_inner, spec.d_state
     h = torch.zeros(Bz, D, N, device=dev)
     cs = torch.zeros(Bz, D, 3, device=dev)
     y = torch.empty(Bz, L, D, dtype=tdt, device=dev)
-    dims = ss.make_dims(Bz, L, D, N, ss.SS_BF16 if spec.io_dtype == "bf16" else ss.SS_F32)
+    dims = ss.make_dims(Bz, L, D, N, ss.SS_BF16 if spec.io_dtype == "bf16" else ss.SS_F32,
+                        discretization=ss.SS_ZOH if zoh else ss.SS_EULER)
     ws = torch.empty(max(ss.ss_workspace_bytes(dims), 1), dtype=torch.uint8, device=dev)
 
     def call():
         ss.ss_conv_scan_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], conv_w=g["conv_w"], conv_b=g["conv_b"],
                             delta_bias=g["delta_bias"], D=g["D"], z=g["z"], ssm_state=h, conv_state=cs, y=y,
-                            workspace=ws)
+                            workspace=ws, zoh=zoh)
 
     for _ in range(warmup):
         call()
@@ -170,7 +190,7 @@ def run_scan(ss, torch, hip, spec, steps, warmup, want_sample):
         for x in e:
             hip.destroy(x)
     return dict(wall_s=wall, main_ms=float(np.mean(main_ms)), agg_ms=float(np.mean(agg_ms)),
-                main_ms_min=float(np.min(main_ms)), sample=sample)
+                main_ms_min=float(np.min(main_ms)))
 
 
 def run_decode(ss, torch, hip, spec: W.DecodeSpec, token_steps: int):
@@ -292,6 +312,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=W.DECODE.steps)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--zoh-steps", type=int, default=10,
+                    help="timed calls of the zero-order-hold variant on the same inputs (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known-size reference for "
                          "hardware traffic counters)")
@@ -313,16 +335,19 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    from selective_state_space_73_amd import build as ss_build
+    digest = ss_build.kernel_digest()
     spec = W.WORKLOADS[a.workload]
     log(f"[bench] workload {spec}")
-    r = run_scan(ss, torch, hip, spec, a.steps, a.warmup, not a.no_cpu)
+    g, sample = prepare_scan(torch, spec, not a.no_cpu)
+    r = run_scan(ss, torch, hip, spec, g, a.steps, a.warmup)
     Bz, L, D, N = spec.batch, spec.seqlen, spec.d_inner, spec.d_state
     rows = Bz * L * D
     ms_step = r["wall_s"] / a.steps * 1e3
     gelem = rows * N / (ms_step / 1e3) / 1e9
     nbytes = scan_bytes(spec)
     main_s = r["main_ms"] / 1e3
-    slots = rows * slots_per_row(N)
+    instrs = rows * instr_per_row(N)
     out = {
         "metric": METRIC, "value": round(gelem, 2), "unit": "Gelem/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -332,15 +357,31 @@ def main():
                    "batch": Bz, "seq_len": L, "d_inner": D, "d_state": N, "io_dtype": spec.io_dtype},
         "hbm_gbps_step": round(nbytes / (ms_step / 1e3) / 1e9, 1),
         "roofline": {"kernel": "k_scan main pass", "bound": "alu",
-                     "achieved": round(slots / main_s / 1e12, 3), "peak": round(VALU_SLOTS_PER_S / 1e12, 3),
-                     "unit": "Tslot/s", "frac": round(slots / main_s / VALU_SLOTS_PER_S, 4),
-                     "traffic": measured_traffic("k_scan_main") if a.workload == "long" else None,
-                     "kernel_ms": round(r["main_ms"], 4),
-                     "slots_per_row": slots_per_row(N), "rows_per_launch": rows},
+                     "achieved": round(instrs / main_s / 1e12, 3), "peak": round(VALU_INSTR_PER_S / 1e12, 3),
+                     "unit": "T fp32 VALU instr/s", "frac": round(instrs / main_s / VALU_INSTR_PER_S, 4),
+                     "traffic": measured_traffic("k_scan_main", digest) if a.workload == "long" else None,
+                     "kernel_ms": round(r["main_ms"], 4), "valu_instr_per_row": instr_per_row(N),
+                     "of_which_transcendental": trans_per_row(N), "rows_per_launch": rows},
         "hbm_view": {"achieved": round(nbytes / main_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(nbytes / main_s / 1e9 / PEAK_HBM_GBS, 4), "bytes_per_launch": nbytes},
         "aggregate_kernel_ms": round(r["agg_ms"], 4),
     }
+    if a.zoh_steps > 0:
+        rz = run_scan(ss, torch, hip, spec, g, a.zoh_steps, a.warmup, zoh=True)
+        zms = rz["wall_s"] / a.zoh_steps * 1e3
+        zinstr = rows * instr_per_row(N, zoh=True)
+        out["zoh"] = {
+            "workload": "same inputs, zero-order-hold write term (exp(Delta A) - 1) / A",
+            "value": round(rows * N / (zms / 1e3) / 1e9, 2), "unit": "Gelem/s", "ms_per_step": round(zms, 4),
+            "roofline": {"kernel": "k_scan main pass (ZOH)", "bound": "alu",
+                         "achieved": round(zinstr / (rz["main_ms"] / 1e3) / 1e12, 3),
+                         "peak": round(VALU_INSTR_PER_S / 1e12, 3), "unit": "T fp32 VALU instr/s",
+                         "frac": round(zinstr / (rz["main_ms"] / 1e3) / VALU_INSTR_PER_S, 4),
+                         "traffic": measured_traffic("k_scan_main_zoh", digest) if a.workload == "long" else None,
+                         "kernel_ms": round(rz["main_ms"], 4), "valu_instr_per_row": instr_per_row(N, zoh=True),
+                         "of_which_transcendental": trans_per_row(N), "rows_per_launch": rows},
+            "aggregate_kernel_ms": round(rz["agg_ms"], 4),
+        }
     if not a.no_decode:
         dspec = W.DECODE
         dr = run_decode(ss, torch, hip, dspec, a.decode_steps)
@@ -355,12 +396,13 @@ def main():
             "ms_per_token_step_graph": round(dr["graph_s"] / a.decode_steps * 1e3, 4),
             "roofline": {"kernel": "k_step", "bound": "hbm", "achieved": round(dbytes / ks / 1e9, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dbytes / ks / 1e9 / PEAK_HBM_GBS, 4),
-                         "traffic": measured_traffic("k_step"), "kernel_us": round(dr["kernel_ms"] * 1e3, 3),
+                         "traffic": measured_traffic("k_step", digest), "kernel_us": round(dr["kernel_ms"] * 1e3, 3),
                          "bytes_per_launch": dbytes},
             "hbm_gbps_end_to_end_graph": round(dbytes * dspec.layers * a.decode_steps / dr["graph_s"] / 1e9, 1),
         }
-    if not a.no_cpu and r["sample"] is not None:
-        out["cpu_baseline"] = cpu_baseline(r["sample"], spec)
+    del g
+    if not a.no_cpu and sample is not None:
+        out["cpu_baseline"] = cpu_baseline(sample, spec)
     print(json.dumps(out), flush=True)
 
 

@@ -9,11 +9,18 @@
  *                                                               history from conv_state or zeros
  *   u_t   = SiLU(c_t) = c_t / (1 + exp(-c_t))
  *   Dt_t  = softplus(delta_t + delta_bias[d])
- *   h_t   = exp(Dt_t * A[d,n]) * h_{t-1} + Dt_t * B_t[n] * u_t
+ *   h_t   = exp(Dt_t * A[d,n]) * h_{t-1} + W_t[d,n] * B_t[n] * u_t
  *   y_t   = (sum_n C_t[n] * h_t[n] + Dskip[d] * u_t) * SiLU(z_t)
  *
+ * with the write coefficient W chosen by dims.discretization:
+ *   SS_EULER  W = Dt_t
+ *   SS_ZOH    W = (exp(Dt_t * A[d,n]) - 1) / A[d,n]   (Dt_t where A[d,n] = 0, its limit)
+ *
  * Sources: ai360xpert.com "Mamba", section "The selection mechanism" (step size
- * as softplus of an affine map of the input; A_bar = exp(Delta A); B_bar ~ Delta B);
+ * as softplus of an affine map of the input; A_bar = exp(Delta A); B_bar ~ Delta B;
+ * its code section writes the zero-order-hold term (1 - A_bar)/(-A) B);
+ * inferensys.com "Mamba" (the discretization bullet: a zero-order hold rule with
+ * a learnable step size);
  * ozercemkelahmet.com "Mamba", "A minimal selective scan in PyTorch" (state per
  * (batch, channel, state index), zero initial state, h = dA*h + dB*x, output read
  * from the updated state), "Deployment notes" (long prompts processed in chunks
@@ -40,7 +47,7 @@
  * Errors: every call returns an ss_status. Arguments are validated on the host
  * before anything is enqueued, so a rejected call writes nothing. Rejected:
  * NULL required pointers, non-positive sizes, unsupported d_state / d_conv /
- * dtype, pointers not 4-byte aligned (ssm_state: 16 bytes; workspace: 256
+ * dtype or discretization, pointers not 4-byte aligned (ssm_state: 16 bytes; workspace: 256
  * bytes), a too-small workspace, y or a state overlapping an input. Launch failures return SS_ERR_HIP; ss_last_error() gives the detail
  * (per calling thread). Faults inside a kernel surface at the caller's next
  * synchronisation. NaN/Inf inputs propagate and are not checked. Results are
@@ -56,9 +63,11 @@
 extern "C" {
 #endif
 
-#define SS_VERSION 1
+#define SS_VERSION 2
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
+
+typedef enum { SS_EULER = 0, SS_ZOH = 1 } ss_discretization;
 
 typedef enum {
     SS_OK = 0,
@@ -75,7 +84,7 @@ typedef struct {
     int32_t  d_state;   /* N in {4, 8, 16, 32, 64}                                         */
     int32_t  d_conv;    /* K; 4 is the only width built                                    */
     int32_t  io_dtype;  /* ss_dtype of x, delta, z, B, C, y                                */
-    int32_t  reserved;  /* must be 0                                                       */
+    int32_t  discretization; /* ss_discretization of the write term (0 = SS_EULER)         */
 } ss_dims;
 
 typedef struct {

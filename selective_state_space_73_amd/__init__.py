@@ -21,13 +21,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libselscan.so")
 
 SS_F32, SS_BF16 = 0, 1
+SS_EULER, SS_ZOH = 0, 1
 STATUS = {0: "SS_OK", 1: "SS_ERR_INVALID_ARG", 2: "SS_ERR_UNSUPPORTED", 3: "SS_ERR_WORKSPACE", 4: "SS_ERR_HIP"}
 
 
 class ss_dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("d_inner", ctypes.c_int64),
                 ("d_state", ctypes.c_int32), ("d_conv", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("discretization", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -105,8 +106,9 @@ def _ptr(t: Optional[torch.Tensor], shape=None, dtype=None, name="") -> Optional
     return t.data_ptr()
 
 
-def make_dims(batch: int, seqlen: int, d_inner: int, d_state: int, io_dtype: int, d_conv: int = 4) -> ss_dims:
-    return ss_dims(batch, seqlen, d_inner, d_state, d_conv, io_dtype, 0)
+def make_dims(batch: int, seqlen: int, d_inner: int, d_state: int, io_dtype: int, d_conv: int = 4,
+              discretization: int = SS_EULER) -> ss_dims:
+    return ss_dims(batch, seqlen, d_inner, d_state, d_conv, io_dtype, discretization)
 
 
 def ss_workspace_bytes(dims: ss_dims) -> int:
@@ -138,15 +140,17 @@ def ss_conv_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: t
                      delta_bias: Optional[torch.Tensor] = None, D: Optional[torch.Tensor] = None,
                      z: Optional[torch.Tensor] = None, ssm_state: Optional[torch.Tensor] = None,
                      conv_state: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                     workspace: Optional[torch.Tensor] = None, zoh: bool = False, stream=None) -> torch.Tensor:
     """Full-sequence forward. x/delta/z: [B,L,D]; B/C: [B,L,N] (float32 or bfloat16, one dtype);
     A [D,N], conv_w [D,4], conv_b/delta_bias/D [D] float32; ssm_state [B,D,N] and conv_state [B,D,3]
-    float32, updated in place when given. Returns y [B,L,D] in the I/O dtype. Asynchronous on the
-    current stream."""
+    float32, updated in place when given. zoh=True selects the zero-order-hold write term
+    (exp(Delta A) - 1) / A instead of Euler's Delta. Returns y [B,L,D] in the I/O dtype.
+    Asynchronous on the current stream."""
     if x.dim() != 3:
         raise ValueError("x must be [batch, seqlen, d_inner]")
     Bsz, L, Dn = x.shape
-    dims = make_dims(Bsz, L, Dn, A.shape[1] if A.dim() == 2 else 0, _io_dtype(x))
+    dims = make_dims(Bsz, L, Dn, A.shape[1] if A.dim() == 2 else 0, _io_dtype(x),
+                     discretization=SS_ZOH if zoh else SS_EULER)
     if y is None:
         y = torch.empty_like(x)
     args = _build_args(x, delta, A, B, C, conv_w, conv_b, delta_bias, D, z, y, ssm_state, conv_state,
@@ -165,13 +169,15 @@ def ss_step(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tens
             ssm_state: torch.Tensor, *, conv_state: Optional[torch.Tensor] = None,
             conv_w: Optional[torch.Tensor] = None, conv_b: Optional[torch.Tensor] = None,
             delta_bias: Optional[torch.Tensor] = None, D: Optional[torch.Tensor] = None,
-            z: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+            z: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None, zoh: bool = False,
+            stream=None) -> torch.Tensor:
     """One decode step. x/delta/z: [S,D]; B/C: [S,N]; ssm_state [S,D,N] and conv_state [S,D,3]
-    float32, updated in place. Returns y [S,D]."""
+    float32, updated in place. zoh as for ss_conv_scan_fwd. Returns y [S,D]."""
     if x.dim() != 2:
         raise ValueError("x must be [streams, d_inner]")
     S, Dn = x.shape
-    dims = make_dims(S, 1, Dn, A.shape[1] if A.dim() == 2 else 0, _io_dtype(x))
+    dims = make_dims(S, 1, Dn, A.shape[1] if A.dim() == 2 else 0, _io_dtype(x),
+                     discretization=SS_ZOH if zoh else SS_EULER)
     if y is None:
         y = torch.empty_like(x)
     args = _build_args(x, delta, A, B, C, conv_w, conv_b, delta_bias, D, z, y, ssm_state, conv_state, (S,), dims)
@@ -180,4 +186,4 @@ def ss_step(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tens
 
 
 __all__ = ["ss_conv_scan_fwd", "ss_step", "ss_workspace_bytes", "ss_version", "ss_time_next_call", "make_dims", "ss_dims", "ss_args",
-           "SelscanError", "SS_F32", "SS_BF16", "LIB_PATH", "lib"]
+           "SelscanError", "SS_F32", "SS_BF16", "SS_EULER", "SS_ZOH", "LIB_PATH", "lib"]

@@ -1,17 +1,23 @@
 """Build libselscan.so in-tree with hipcc for gfx950 (device code) and the host C ABI."""
 from __future__ import annotations
 
+import glob
+import hashlib
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libselscan.so")
-SOURCES = [os.path.join(CSRC, "selscan_kernels.hip"), os.path.join(CSRC, "selscan_api.cpp")]
-HEADERS = [os.path.join(CSRC, "selscan_internal.h"), os.path.join(INCLUDE, "selscan.h")]
+# one instantiation unit per I/O dtype and write rule (compiled in parallel) + the C ABI layer
+KERNEL_UNITS = sorted(glob.glob(os.path.join(CSRC, "selscan_*_*.hip")))
+SOURCES = KERNEL_UNITS + [os.path.join(CSRC, "selscan_api.cpp")]
+HEADERS = [os.path.join(CSRC, "selscan_device.h"), os.path.join(CSRC, "selscan_internal.h"),
+           os.path.join(INCLUDE, "selscan.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -29,11 +35,23 @@ def _run(cmd):
     return r
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libselscan.so next to this file. Always rebuilds."""
+def kernel_digest() -> str:
+    """sha256 over the sources that decide what a launch does (the kernels' code,
+    launch constants and the chunking rule of the C ABI layer), so that measurements
+    taken on one build can be matched to it later."""
+    h = hashlib.sha256()
+    for path in sorted(SOURCES + HEADERS[:2]):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every source (in parallel) and link libselscan.so next to this file.
+    Always rebuilds."""
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
+    cmds, objs = [], []
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
@@ -41,8 +59,12 @@ def build(verbose: bool = False) -> str:
             cmd = [HIPCC, *COMMON, "-x", "hip", *DEVICE_FLAGS, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd))
-        _run(cmd)
+        cmds.append(cmd)
         objs.append(obj)
+    jobs = jobs or min(len(cmds), os.cpu_count() or 1, 16)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        for _ in ex.map(_run, cmds):
+            pass
     tmp = LIB + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs])
     os.replace(tmp, LIB)

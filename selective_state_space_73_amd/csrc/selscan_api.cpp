@@ -101,7 +101,8 @@ Layout layout(const ss_dims& d) {
 
 ss_status check_dims(const ss_dims* d, bool step) {
     if (!d) return fail(SS_ERR_INVALID_ARG, "dims is NULL");
-    if (d->reserved != 0) return fail(SS_ERR_INVALID_ARG, "dims.reserved must be 0");
+    if (d->discretization != SS_EULER && d->discretization != SS_ZOH)
+        return fail(SS_ERR_INVALID_ARG, "dims.discretization %d unknown", d->discretization);
     if (d->batch < 1 || d->batch > kMaxGridYZ)
         return fail(SS_ERR_INVALID_ARG, "batch %lld outside [1, %lld]", (long long)d->batch, (long long)kMaxGridYZ);
     if (!step && d->seqlen < 1) return fail(SS_ERR_INVALID_ARG, "seqlen %lld < 1", (long long)d->seqlen);
@@ -173,11 +174,17 @@ ss_status check_args(const ss_dims& d, const ss_args* a, bool step) {
 selscan::LaunchScan make_launch(const ss_dims& d, const ss_args& a, void* stream) {
     selscan::LaunchScan p{};
     p.batch = d.batch; p.L = d.seqlen; p.D = d.d_inner; p.N = d.d_state; p.bf16 = d.io_dtype == SS_BF16;
+    p.zoh = d.discretization == SS_ZOH;
     p.x = a.x; p.conv_w = a.conv_w; p.conv_b = a.conv_b; p.delta = a.delta; p.delta_bias = a.delta_bias;
     p.A = a.A; p.B = a.B; p.C = a.C; p.Dskip = a.Dskip; p.z = a.z; p.y = a.y;
     p.ssm_state = a.ssm_state; p.conv_state = a.conv_state;
     p.stream = stream;
     return p;
+}
+
+hipError_t launch(const selscan::LaunchScan& p, bool step) {
+    if (p.bf16) return p.zoh ? selscan::launch_bf16_zoh(p, step) : selscan::launch_bf16_euler(p, step);
+    return p.zoh ? selscan::launch_f32_zoh(p, step) : selscan::launch_f32_euler(p, step);
 }
 
 }  // namespace
@@ -220,7 +227,7 @@ ss_status ss_conv_scan_fwd(const ss_dims* dims, const ss_args* args, void* works
         p.ws_h0 = reinterpret_cast<float*>(ws + l.off_h0);
         p.ws_c0 = reinterpret_cast<float*>(ws + l.off_c0);
     }
-    const hipError_t e = selscan::launch_scan(p);
+    const hipError_t e = launch(p, false);
     if (e != hipSuccess) return fail(SS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return SS_OK;
 }
@@ -233,7 +240,7 @@ ss_status ss_step(const ss_dims* dims, const ss_args* args, void* stream) {
     one.seqlen = 1;
     selscan::LaunchScan p = make_launch(one, *args, stream);
     take_events(p);
-    const hipError_t e = selscan::launch_step(p);
+    const hipError_t e = launch(p, true);
     if (e != hipSuccess) return fail(SS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return SS_OK;
 }

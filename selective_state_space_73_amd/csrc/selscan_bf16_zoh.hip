@@ -1,0 +1,8 @@
+// Kernel instantiations of libselscan: bfloat16 I/O, zero-order-hold write term.
+#include "selscan_device.h"
+
+namespace selscan {
+
+hipError_t launch_bf16_zoh(const LaunchScan& p, bool step) { return dispatch_n<uint16_t, true>(p, step); }
+
+}  // namespace selscan

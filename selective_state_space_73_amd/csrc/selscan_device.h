@@ -1,10 +1,15 @@
-// HIP kernels of libselscan for gfx950 (CDNA4, wave64).
+// Device code of libselscan for gfx950 (CDNA4, wave64): the kernel templates and
+// their launchers. Included by the instantiation units selscan_<io>_<rule>.hip,
+// one per I/O dtype and discretisation rule, which compile in parallel.
 //
 // The selective scan (S6) forward path: causal depthwise conv1d + SiLU,
-// softplus step size, exp(Delta A) decay, Euler write term Delta B u, readout
-// C.h + D u, SiLU(z) gate (ai360xpert.com "Mamba", "The selection mechanism";
-// ozercemkelahmet.com "Mamba", "A minimal selective scan in PyTorch"; bembew.net
-// "Overview of Mamba (SSM) Model", "How the Mamba Block Works").
+// softplus step size, exp(Delta A) decay, write term, readout C.h + D u, SiLU(z)
+// gate (ai360xpert.com "Mamba", "The selection mechanism"; ozercemkelahmet.com
+// "Mamba", "A minimal selective scan in PyTorch"; bembew.net "Overview of Mamba
+// (SSM) Model", "How the Mamba Block Works"). The write term is either the Euler
+// form Delta B u or the zero-order-hold form (exp(Delta A) - 1) / A * B u
+// (inferensys.com "Mamba", the discretization bullet; ai360xpert.com "Mamba",
+// the simplified ZOH line of its code section), selected by the ZOH template flag.
 //
 // Mapping: one lane owns one (batch row, channel) pair and keeps its N state
 // values in VGPRs for a run of consecutive tokens (a chunk). Loads of x, delta,
@@ -20,6 +25,7 @@
 // step size, so that the chunk's total decay is exp(A * sum Delta); the main pass
 // folds these aggregates of all earlier chunks into its carry-in and then runs
 // the chunk with the exact initial state.
+#pragma once
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -30,6 +36,14 @@ namespace selscan {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Zero-order hold: states with |A| below this take the coefficient's A -> 0 limit
+// Delta (exact to fp32 there, and it keeps 1/A finite)
+constexpr float kZohZeroA = 0x1p-100f;
+// (exp(x) - 1) / x = 1 + x/2 + x^2/6 + x^3/24 + O(x^4), written in t = x log2(e)
+constexpr float kPhi1 = 0.34657359027997264f;     // ln2 / 2
+constexpr float kPhi2 = 0.08007550231970024f;     // ln2^2 / 6
+constexpr float kPhi3 = 0.013876027166205393f;    // ln2^3 / 24
+constexpr float kZohSeriesT = 0.14426950408889634f;   // |t| below this (|x| < 0.1): series
 
 // ---------------------------------------------------------------------------
 // elementwise pieces (fp32)
@@ -51,6 +65,21 @@ __device__ __forceinline__ float softplus(float v) {
     const float corr = e - (s - 1.0f);
     const float lp = __builtin_fmaf(log2_fast(s), kLn2, corr);
     return __builtin_fmaxf(v, 0.0f) + lp;
+}
+
+// (exp(x) - 1) / x for x = t ln2: the series below |x| = 0.1 (truncation < 1e-6),
+// otherwise (a - 1) / x with a = 2^t. Computing a - 1 from an fp32 a loses about
+// 6e-8 / |x| relative near x = 0, which the series avoids; at x = 0 it is 1.
+__device__ __forceinline__ float phi_series(float t) {
+    return __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, kPhi3, kPhi2), kPhi1), 1.0f);
+}
+
+// Zero-order-hold write coefficient (exp(Delta A) - 1) / A from the decay a = 2^t,
+// t = Delta A log2(e), and iA = 1/A (0 for the A = 0 states, which take the series).
+__device__ __forceinline__ float zoh_coef(float a, float t, float dt, float iA) {
+    const float big = __builtin_fmaf(a, iA, -iA);
+    const float small = dt * phi_series(t);
+    return __builtin_fabsf(t) < kZohSeriesT ? small : big;
 }
 
 template <typename T> struct IO;
@@ -103,9 +132,9 @@ template <> struct Buf<float> {
 };
 
 // ---------------------------------------------------------------------------
-// The chunk pass. MAIN = true: full forward over the chunk with outputs.
-// MAIN = false: aggregate pass (end state from the chunk's initial state, and the
-// summed step size), no outputs.
+// The main pass: full forward over one chunk with outputs, from the chunk's exact
+// initial state (the caller's state for chunk 0, else the carry folded from the
+// aggregates of the earlier chunks).
 
 struct ScanArgs {
     int64_t L;            // sequence length
@@ -118,21 +147,27 @@ struct ScanArgs {
 // N <= 16, measured faster than the compiler's own choice (two waves at ~240
 // VGPRs) because more resident waves hide the long per-token dependency chains;
 // larger N needs the registers for the state and keeps one-wave-per-SIMD limits.
-// (Without the conv the compiler's schedule under that cap spills, so it is left free.)
-template <int N, bool CONV> constexpr int scan_waves_per_eu() { return (N <= 16 && CONV) ? 3 : 1; }
+// (Without the conv the schedule under that cap spills, so it is left free; the
+// zero-order hold's longer per-state chain with N more registers of 1/A is held to
+// two waves.)
+template <int N, bool CONV, bool ZOH> constexpr int scan_waves_per_eu() {
+    return N > 16 ? 1 : ZOH ? 2 : CONV ? 3 : 1;
+}
 
-template <typename T, int N, bool CONV, bool GATE, bool MAIN>
-__global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<N, CONV>())))
+// Zero-order hold: the write coefficient (exp(Delta A) - 1) / A comes from the decay
+// already computed (zoh_coef: one fma, or a short series where Delta A is small).
+template <typename T, int N, bool CONV, bool GATE, bool ZOH>
+__global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<N, CONV, ZOH>())))
 k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
        const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
        const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
        const T* __restrict__ z, T* __restrict__ y,
-       float* __restrict__ ssm_state,        // MAIN: IN (nchunks==1) and OUT (last chunk); AGG: IN
-       float* __restrict__ conv_state,       // MAIN: IN (nchunks==1) and OUT (last chunk); AGG: IN
-       float* __restrict__ ws_S,             // [B, nchunks-1, D, N] chunk end states (chunk 0 includes h0)
-       float* __restrict__ ws_sdt,           // [B, nchunks-1, D] summed step sizes
-       float* __restrict__ ws_h0,            // [B, D, N] copy of the initial state (nchunks > 1)
-       float* __restrict__ ws_c0,            // [B, D, K-1] copy of the initial conv history (nchunks > 1)
+       float* __restrict__ ssm_state,        // IN (nchunks == 1) and OUT (last chunk)
+       float* __restrict__ conv_state,       // IN (nchunks == 1) and OUT (last chunk)
+       const float* __restrict__ ws_S,       // [B, nchunks-1, D, N] chunk end states (chunk 0 includes h0)
+       const float* __restrict__ ws_sdt,     // [B, nchunks-1, D] summed step sizes
+       const float* __restrict__ ws_h0,      // [B, D, N] copy of the initial state (nchunks > 1)
+       const float* __restrict__ ws_c0,      // [B, D, K-1] copy of the initial conv history (nchunks > 1)
        ScanArgs sa) {
     const int D = sa.D;
     const int d_raw = blockIdx.x * kScanThreads + threadIdx.x;
@@ -149,8 +184,17 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 
     // per-channel parameters
     float A2[N];
+    float iA[ZOH ? N : 1];                        // ZOH: 1/A (0 for the A = 0 states)
 #pragma unroll
-    for (int n = 0; n < N; ++n) A2[n] = A[(int64_t)d * N + n] * kLog2e;
+    for (int n = 0; n < N; ++n) {
+        const float av = A[(int64_t)d * N + n];
+        A2[n] = av * kLog2e;
+        if (ZOH) {
+            const bool zero = __builtin_fabsf(av) < kZohZeroA;
+            iA[n] = zero ? 0.0f : 1.0f / av;
+            if (zero) A2[n] = 0.0f;                   // an A = 0 state decays by exactly 1
+        }
+    }
     const float dbias = delta_bias ? delta_bias[d] : 0.0f;
     const float dsk = Dskip ? Dskip[d] : 0.0f;
     float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 1.f, cb = 0.f;
@@ -163,21 +207,16 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     float h[N];
     const int64_t bd = (int64_t)b * D + d;
     if (c == 0) {
-        // with several chunks the main pass reads the copy the aggregate pass made,
-        // because the last chunk overwrites ssm_state
-        const float* src = (ssm_state && MAIN && multi) ? ws_h0 : ssm_state;
+        // with several chunks, read the copy the aggregate pass made, because the
+        // last chunk overwrites ssm_state
+        const float* src = (ssm_state && multi) ? ws_h0 : ssm_state;
 #pragma unroll
         for (int n = 0; n < N; ++n) h[n] = src ? src[bd * N + n] : 0.0f;
-        if (!MAIN && multi && ssm_state) {
-#pragma unroll
-            for (int n = 0; n < N; ++n) ws_h0[bd * N + n] = h[n];
-        }
     } else {
-        // aggregate pass: chunks after the first start from zero. Main pass: fold
-        // the aggregates of chunks 0..c-1 into the carry-in.
+        // fold the aggregates of chunks 0..c-1 into the carry-in
 #pragma unroll
         for (int n = 0; n < N; ++n) h[n] = 0.0f;
-        for (int cc = 0; MAIN && cc < c; ++cc) {
+        for (int cc = 0; cc < c; ++cc) {
             const int64_t ai = ((int64_t)b * nagg + cc) * D + d;
             const float sdt = ws_sdt[ai];
 #pragma unroll
@@ -187,11 +226,11 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     }
 
     // conv history x_{t0-3}, x_{t0-2}, x_{t0-1}: from x where t0-k >= 0, else from
-    // the initial history (the main pass of a multi-chunk call reads the copy the
-    // aggregate pass made, because the last chunk overwrites conv_state)
+    // the initial history (a multi-chunk call reads the copy the aggregate pass
+    // made, because the last chunk overwrites conv_state)
     float x3 = 0.f, x2 = 0.f, x1 = 0.f;
     if (CONV) {
-        const float* hsrc = conv_state ? ((MAIN && multi) ? ws_c0 : conv_state) : nullptr;
+        const float* hsrc = conv_state ? (multi ? ws_c0 : conv_state) : nullptr;
         float xh[3];
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
@@ -200,11 +239,6 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
                             : (hsrc ? hsrc[bd * 3 + (3 + tt)] : 0.0f);
         }
         x3 = xh[0]; x2 = xh[1]; x1 = xh[2];
-        if (!MAIN && multi && c == 0 && conv_state) {
-            ws_c0[bd * 3 + 0] = conv_state[bd * 3 + 0];
-            ws_c0[bd * 3 + 1] = conv_state[bd * 3 + 1];
-            ws_c0[bd * 3 + 2] = conv_state[bd * 3 + 2];
-        }
     }
 
     // Token loop. B_t/C_t are staged through LDS in tiles of R tokens (double
@@ -215,7 +249,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     constexpr int U = 4;
     constexpr int R = kScanTile;
     static_assert(R % (2 * U) == 0, "a tile holds whole pairs of groups");
-    constexpr int NB = MAIN ? 2 * N : N;                // staged values per token
+    constexpr int NB = 2 * N;                           // staged values per token (B row, C row)
     __shared__ float sbc[2][R][NB];
     const int tid = threadIdx.x;
     const int nrows = (int)(t1 - t0);
@@ -224,10 +258,10 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     const int64_t rowbase = (int64_t)b * sa.L + t0;     // global row of the chunk's first token
     const T* xb = x + rowbase * D;
     const T* db = delta + rowbase * D;
-    const T* zb = (MAIN && GATE) ? z + rowbase * D : nullptr;
-    T* yb = MAIN ? y + rowbase * D : nullptr;
+    const T* zb = GATE ? z + rowbase * D : nullptr;
+    T* yb = y + rowbase * D;
     const T* Bb = Bm + rowbase * N;
-    const T* Cb = MAIN ? Cm + rowbase * N : nullptr;
+    const T* Cb = Cm + rowbase * N;
 
     // cooperative tile load: element e of the tile is (row e / N, state e % N)
     constexpr int TILE_ELEMS = R * N;
@@ -237,7 +271,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         // the tile's rows are contiguous in B and C: one uniform base, a 32-bit offset per element
         const int rlast = nrows - 1 - r0;
         const T* Bt = Bb + (int64_t)r0 * N;
-        const T* Ct = MAIN ? Cb + (int64_t)r0 * N : nullptr;
+        const T* Ct = Cb + (int64_t)r0 * N;
 #pragma unroll
         for (int k = 0; k < PER_THREAD; ++k) {
             const int e0 = tid + k * kScanThreads;
@@ -245,7 +279,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
             const int r = e / N < rlast ? e / N : rlast;
             const int off = r * N + e % N;
             tb[k] = Bt[off];
-            if (MAIN) tc[k] = Ct[off];
+            tc[k] = Ct[off];
         }
     };
     auto tile_store = [&](int buf) {
@@ -254,12 +288,11 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
             const int e = tid + k * kScanThreads;
             if (e < TILE_ELEMS) {
                 sbc[buf][e / N][e % N] = IO<T>::cvt(tb[k]);
-                if (MAIN) sbc[buf][e / N][N + e % N] = IO<T>::cvt(tc[k]);
+                sbc[buf][e / N][N + e % N] = IO<T>::cvt(tc[k]);
             }
         }
     };
 
-    float sdt = 0.0f;
     // Per-token work in two phases. prologue(): the conv, SiLU, softplus and gate of
     // one token (a long dependent chain, run for a whole group of tokens first so the
     // chains of different tokens overlap). update(): the N-wide state update and
@@ -277,34 +310,37 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         }
         p.dt = softplus(IO<T>::cvt(draw) + dbias);
         p.wv = p.dt * p.u;
-        p.g = (MAIN && GATE) ? silu(IO<T>::cvt(zraw)) : 1.0f;
+        p.g = GATE ? silu(IO<T>::cvt(zraw)) : 1.0f;
         return p;
     };
     auto update = [&](const Pro& p, const float* bct, int r) {
-        float bv[N], cv[N], a[N];
+        float bv[N], cv[N], a[N], t[N];
 #pragma unroll
         for (int n = 0; n < N; ++n) bv[n] = bct[n];
-        if (MAIN) {
 #pragma unroll
-            for (int n = 0; n < N; ++n) cv[n] = bct[N + n];
+        for (int n = 0; n < N; ++n) cv[n] = bct[N + n];
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            t[n] = p.dt * A2[n];
+            a[n] = exp2_fast(t[n]);
         }
+        if constexpr (ZOH) {
 #pragma unroll
-        for (int n = 0; n < N; ++n) a[n] = exp2_fast(p.dt * A2[n]);
-#pragma unroll
-        for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(a[n], h[n], p.wv * bv[n]);
-        if (MAIN) {
-            float ya = dsk * p.u, yc = 0.0f;
-#pragma unroll
-            for (int n = 0; n < N; n += 2) {
-                ya = __builtin_fmaf(cv[n], h[n], ya);
-                yc = __builtin_fmaf(cv[n + 1], h[n + 1], yc);
-            }
-            const float yv = (ya + yc) * p.g;
-            // lanes past the last channel were clamped to it and store the same value
-            Buf<T>(yb + (int64_t)r * D).st(IO<T>::bits(yv), voff, 0u);
+            for (int n = 0; n < N; ++n)
+                h[n] = __builtin_fmaf(a[n], h[n], zoh_coef(a[n], t[n], p.dt, iA[n]) * (p.u * bv[n]));
         } else {
-            sdt += p.dt;
+#pragma unroll
+            for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(a[n], h[n], p.wv * bv[n]);
         }
+        float ya = dsk * p.u, yc = 0.0f;
+#pragma unroll
+        for (int n = 0; n < N; n += 2) {
+            ya = __builtin_fmaf(cv[n], h[n], ya);
+            yc = __builtin_fmaf(cv[n + 1], h[n + 1], yc);
+        }
+        const float yv = (ya + yc) * p.g;
+        // lanes past the last channel were clamped to it and store the same value
+        Buf<T>(yb + (int64_t)r * D).st(IO<T>::bits(yv), voff, 0u);
     };
     auto token = [&](T xraw, T draw, T zraw, const float* bct, int r) {
         const Pro p = prologue(xraw, draw, zraw);
@@ -329,7 +365,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
             const unsigned so = (unsigned)(r - rb) * rowb;
             gx[i] = bx.ld(voff, so);
             gd[i] = bdl.ld(voff, so);
-            if (MAIN && GATE) gz[i] = Buf<T>(zb + off).ld(voff, so);
+            if (GATE) gz[i] = Buf<T>(zb + off).ld(voff, so);
         }
     };
 
@@ -354,7 +390,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         } else {
             for (int r = tt; r < nrows; ++r) {
                 const int64_t off = (int64_t)r * D;
-                token((xb + off)[du], (db + off)[du], (MAIN && GATE) ? (zb + off)[du] : T(0), tile + (r - tt) * NB, r);
+                token((xb + off)[du], (db + off)[du], GATE ? (zb + off)[du] : T(0), tile + (r - tt) * NB, r);
             }
         }
         if (more) tile_store(buf ^ 1);
@@ -362,21 +398,14 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         buf ^= 1;
     }
 
-    if (MAIN) {
-        if (c == sa.nchunks - 1) {
-            if (ssm_state) {
+    if (c == sa.nchunks - 1) {
+        if (ssm_state) {
 #pragma unroll
-                for (int n = 0; n < N; ++n) ssm_state[bd * N + n] = h[n];
-            }
-            if (CONV && conv_state) {
-                conv_state[bd * 3 + 0] = x3; conv_state[bd * 3 + 1] = x2; conv_state[bd * 3 + 2] = x1;
-            }
+            for (int n = 0; n < N; ++n) ssm_state[bd * N + n] = h[n];
         }
-    } else {
-        const int64_t ai = ((int64_t)b * nagg + c) * D + d;
-        ws_sdt[ai] = sdt;
-#pragma unroll
-        for (int n = 0; n < N; ++n) ws_S[ai * N + n] = h[n];
+        if (CONV && conv_state) {
+            conv_state[bd * 3 + 0] = x3; conv_state[bd * 3 + 1] = x2; conv_state[bd * 3 + 2] = x1;
+        }
     }
 }
 
@@ -385,11 +414,17 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 // initial state: zero, or the caller's state for chunk 0) and its summed step
 // size. Written in the backward (Horner) form
 //     S_n = sum_t exp(A_n * R_t) * Delta_t * u_t * B_t[n],   R_t = sum_{k>t} Delta_k,
-// which is the unrolled recurrence. The sweep runs backward from the chunk end;
-// a state index n is dropped (wave-uniformly) once exp(A_n * R) < 2^-kAggCutLog2
-// for every lane, because R only grows from there. Rows after every n is dropped
-// only add Delta to the chunk's sum (needed exactly for its decay exp(A*sum))
-// and to a bound M on everything dropped:
+// which is the unrolled recurrence. Under zero-order hold the write coefficient
+// (exp(A_n Delta_t) - 1) / A_n times the decay exp(A_n R_t) telescopes to
+// (E_t - E'_t) / A_n with E_t = exp(A_n (R_t + Delta_t)) and E'_t = exp(A_n R_t),
+// and E'_t is the E of the token after t: one exponential per token and state, as
+// for Euler. Where A_n Delta_t is small that difference cancels, and the term is
+// taken as E'_t Delta_t phi(A_n Delta_t) with the series for phi instead.
+// The sweep runs backward from the chunk end; a state index n is dropped
+// (wave-uniformly) once exp(A_n * R) < 2^-kAggCutLog2 for every lane, because R
+// only grows from there. Rows after every n is dropped only add Delta to the
+// chunk's sum (needed exactly for its decay exp(A*sum)) and to a bound M on
+// everything dropped (both write coefficients are at most Delta for A <= 0):
 //     |dropped part of S_n| <= 2^-kAggCutLog2 * sum_t |Delta_t u_t| * max_n |B_t[n]|.
 // If 2^-kAggCutLog2 * M exceeds 2^-24 * max_n |S_n| (one unit roundoff of the
 // aggregate) for any lane, the wave recomputes S exactly with the forward
@@ -397,7 +432,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 
 constexpr int kAggCutLog2 = 40;
 
-template <typename T, int N, bool CONV>
+template <typename T, int N, bool CONV, bool ZOH>
 __global__ void __launch_bounds__(kScanThreads)
 k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
       const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
@@ -417,8 +452,14 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     const int64_t bd = (int64_t)b * D + d;
 
     float A2[N];
+    float iA[ZOH ? N : 1];                        // ZOH: 1/A (0 for the A = 0 states)
 #pragma unroll
-    for (int n = 0; n < N; ++n) A2[n] = A[(int64_t)d * N + n] * kLog2e;
+    for (int n = 0; n < N; ++n) {
+        const float av = A[(int64_t)d * N + n];
+        const bool zero = ZOH && __builtin_fabsf(av) < kZohZeroA;
+        A2[n] = zero ? 0.0f : av * kLog2e;            // ZOH: an A = 0 state decays by exactly 1
+        if (ZOH) iA[n] = zero ? 0.0f : 1.0f / av;
+    }
     const float dbias = delta_bias ? delta_bias[d] : 0.0f;
     float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 1.f, cb = 0.f;
     if (CONV) {
@@ -476,8 +517,11 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     };
 
     float S[N];
+    float Ep[ZOH ? N : 1];                        // ZOH: exp(A_n R) at the previous (later) token
 #pragma unroll
     for (int n = 0; n < N; ++n) S[n] = 0.0f;
+#pragma unroll
+    for (int n = 0; n < (ZOH ? N : 1); ++n) Ep[n] = 1.0f;
     double Rsum = 0.0;                            // sum of Delta over the tokens swept so far
     float M = 0.0f;                               // sum |Delta u| max|B| over swept rows (full mode)
     float Mh = 0.0f;                              // sum Delta max|B| over rows swept after every n was dropped
@@ -544,7 +588,7 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
             for (int i = 0; i < U; ++i) { xd[i] = IO<T>::cvt(cx[i]); pad[i] = false; }
         }
         if (act) {
-            float dt[U], wv[U];
+            float dt[U], wv[U], uu[U];
 #pragma unroll
             for (int i = 0; i < U; ++i) {
                 float u;
@@ -557,12 +601,14 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                 xa = xb; xb = xc; xc = xd[i];
                 dt[i] = pad[i] ? 0.0f : softplus(IO<T>::cvt(cd[i]) + dbias);
                 wv[i] = dt[i] * u;
+                uu[i] = u;
             }
-            // suffix sums: fp64 running total, fp32 within the group
+            // suffix sums: fp64 running total, fp32 within the group. Rf excludes the
+            // row's own Delta (Euler decay), Ri includes it (ZOH telescoping)
             const float rbase = (float)Rsum;
-            float Rf[U], part = 0.0f;
+            float Rf[U], Ri[U], part = 0.0f;
 #pragma unroll
-            for (int i = 0; i < U; ++i) { Rf[i] = rbase + part; part += dt[i]; }
+            for (int i = 0; i < U; ++i) { Rf[i] = rbase + part; part += dt[i]; Ri[i] = rbase + part; }
             Rsum += (double)part;
 #pragma unroll
             for (int i = 0; i < U; ++i) M = __builtin_fmaf(__builtin_fabsf(wv[i]), rowp[-i * NB + N], M);
@@ -574,7 +620,17 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const int n = 4 * j + q;
-                            S[n] = __builtin_fmaf(exp2_fast(A2[n] * Rf[i]), wv[i] * rowp[-i * NB + n], S[n]);
+                            if constexpr (ZOH) {
+                                const float e = exp2_fast(A2[n] * Ri[i]);
+                                const float ts = dt[i] * A2[n];
+                                const float big = (e - Ep[n]) * iA[n];                 // (E - E') / A
+                                const float small = Ep[n] * (dt[i] * phi_series(ts));   // E' Delta phi
+                                const float cf = __builtin_fabsf(ts) < kZohSeriesT ? small : big;
+                                S[n] = __builtin_fmaf(cf, uu[i] * rowp[-i * NB + n], S[n]);
+                                Ep[n] = e;
+                            } else {
+                                S[n] = __builtin_fmaf(exp2_fast(A2[n] * Rf[i]), wv[i] * rowp[-i * NB + n], S[n]);
+                            }
                         }
                     }
                     // weights only shrink further back: drop the block once every lane is below the cut
@@ -656,8 +712,15 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
             const float w = dtv * u;
             const T* Bt = Bm + (row0 + t) * N;
 #pragma unroll
-            for (int n = 0; n < N; ++n)
-                h[n] = __builtin_fmaf(exp2_fast(dtv * A2[n]), h[n], w * IO<T>::cvt(Bt[n]));
+            for (int n = 0; n < N; ++n) {
+                const float tn = dtv * A2[n];
+                const float a = exp2_fast(tn);
+                if constexpr (ZOH) {
+                    h[n] = __builtin_fmaf(a, h[n], zoh_coef(a, tn, dtv, iA[n]) * (u * IO<T>::cvt(Bt[n])));
+                } else {
+                    h[n] = __builtin_fmaf(a, h[n], w * IO<T>::cvt(Bt[n]));
+                }
+            }
         }
 #pragma unroll
         for (int n = 0; n < N; ++n) S[n] = h[n];
@@ -719,7 +782,7 @@ __device__ __forceinline__ void st_nt(float* p, const float* v) {
     }
 }
 
-template <typename T, int N, bool CONV, bool GATE>
+template <typename T, int N, bool CONV, bool GATE, bool ZOH>
 __global__ void __launch_bounds__(kStepThreads)
 k_step(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
        const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
@@ -734,9 +797,14 @@ k_step(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     if (d >= D) return;                       // whole quads leave together
 
     // channel parameters, shared by the SPT streams
-    float aq[NQ];
+    float aq[NQ], iaq[ZOH ? NQ : 1];
 #pragma unroll
-    for (int k = 0; k < NQ; ++k) aq[k] = A[(int64_t)d * N + q * NQ + k] * kLog2e;
+    for (int k = 0; k < NQ; ++k) {
+        const float av = A[(int64_t)d * N + q * NQ + k];
+        const bool zero = ZOH && __builtin_fabsf(av) < kZohZeroA;
+        aq[k] = zero ? 0.0f : av * kLog2e;
+        if (ZOH) iaq[k] = zero ? 0.0f : 1.0f / av;
+    }
     const float wq = CONV ? conv_w[d * 4 + q] : 0.0f;
     const float cb = (CONV && conv_b) ? conv_b[d] : 0.0f;
     const float dbias = delta_bias ? delta_bias[d] : 0.0f;
@@ -782,8 +850,13 @@ k_step(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         float yp = 0.0f;
 #pragma unroll
         for (int k = 0; k < NQ; ++k) {
-            const float a = exp2_fast(dt * aq[k]);
-            hq[j][k] = __builtin_fmaf(a, hq[j][k], wv * IO<T>::cvt(braw[j][k]));
+            const float tk = dt * aq[k];
+            const float a = exp2_fast(tk);
+            if constexpr (ZOH) {
+                hq[j][k] = __builtin_fmaf(a, hq[j][k], zoh_coef(a, tk, dt, iaq[k]) * (u * IO<T>::cvt(braw[j][k])));
+            } else {
+                hq[j][k] = __builtin_fmaf(a, hq[j][k], wv * IO<T>::cvt(braw[j][k]));
+            }
             yp = __builtin_fmaf(IO<T>::cvt(craw[j][k]), hq[j][k], yp);
         }
         st_nt<NQ>(ssm_state + sd * N + q * NQ, hq[j]);
@@ -794,9 +867,9 @@ k_step(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 }
 
 // ---------------------------------------------------------------------------
-// launchers
+// launchers (templates; each instantiation unit calls dispatch_n for its dtype and rule)
 
-template <typename T, int N, bool CONV, bool GATE>
+template <typename T, int N, bool CONV, bool GATE, bool ZOH>
 static hipError_t launch_scan_t(const LaunchScan& p) {
     const T* x = static_cast<const T*>(p.x);
     const T* dl = static_cast<const T*>(p.delta);
@@ -806,66 +879,60 @@ static hipError_t launch_scan_t(const LaunchScan& p) {
     ScanArgs sa{p.L, p.chunk_len, (int)p.D, p.nchunks};
     const unsigned gx = (unsigned)((p.D + kScanThreads - 1) / kScanThreads);
     if (p.nchunks > 1) {
-        hipExtLaunchKernelGGL((k_agg<T, N, CONV>), dim3(gx, p.nchunks - 1, (unsigned)p.batch),
+        hipExtLaunchKernelGGL((k_agg<T, N, CONV, ZOH>), dim3(gx, p.nchunks - 1, (unsigned)p.batch),
                               dim3(kScanThreads), 0, st, static_cast<hipEvent_t>(p.ev_agg[0]),
                               static_cast<hipEvent_t>(p.ev_agg[1]), 0, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
                               static_cast<const T*>(p.B), p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0,
                               p.ws_c0, sa);
     }
-    hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, true>), dim3(gx, p.nchunks, (unsigned)p.batch),
+    hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, ZOH>), dim3(gx, p.nchunks, (unsigned)p.batch),
                           dim3(kScanThreads), 0, st, static_cast<hipEvent_t>(p.ev_main[0]),
                           static_cast<hipEvent_t>(p.ev_main[1]), 0, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
-                       static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip, z, y, p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, sa);
+                          static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip, z, y, p.ssm_state,
+                          p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, sa);
     return hipGetLastError();
 }
 
-template <typename T, int N, bool CONV, bool GATE>
+template <typename T, int N, bool CONV, bool GATE, bool ZOH>
 static hipError_t launch_step_t(const LaunchScan& p) {
     hipStream_t st = static_cast<hipStream_t>(p.stream);
     constexpr int per_block = kStepThreads / 4;   // channels per workgroup (a quad each)
     const unsigned gx = (unsigned)((p.D + per_block - 1) / per_block);
     const unsigned gy = (unsigned)((p.batch + kStepStreams - 1) / kStepStreams);
-    hipExtLaunchKernelGGL((k_step<T, N, CONV, GATE>), dim3(gx, gy), dim3(kStepThreads), 0, st,
+    hipExtLaunchKernelGGL((k_step<T, N, CONV, GATE, ZOH>), dim3(gx, gy), dim3(kStepThreads), 0, st,
                           static_cast<hipEvent_t>(p.ev_main[0]), static_cast<hipEvent_t>(p.ev_main[1]), 0,
-                       static_cast<const T*>(p.x), p.conv_w, p.conv_b, static_cast<const T*>(p.delta),
-                       p.delta_bias, p.A, static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip,
-                       static_cast<const T*>(p.z), static_cast<T*>(p.y), p.ssm_state, p.conv_state, (int)p.D, (int)p.batch);
+                          static_cast<const T*>(p.x), p.conv_w, p.conv_b, static_cast<const T*>(p.delta),
+                          p.delta_bias, p.A, static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip,
+                          static_cast<const T*>(p.z), static_cast<T*>(p.y), p.ssm_state, p.conv_state, (int)p.D,
+                          (int)p.batch);
     return hipGetLastError();
 }
 
-template <typename T, int N>
+template <typename T, int N, bool ZOH>
 static hipError_t dispatch_flags(const LaunchScan& p, bool step) {
     const bool conv = p.conv_w != nullptr, gate = p.z != nullptr;
     if (step) {
-        if (conv && gate) return launch_step_t<T, N, true, true>(p);
-        if (conv) return launch_step_t<T, N, true, false>(p);
-        if (gate) return launch_step_t<T, N, false, true>(p);
-        return launch_step_t<T, N, false, false>(p);
+        if (conv && gate) return launch_step_t<T, N, true, true, ZOH>(p);
+        if (conv) return launch_step_t<T, N, true, false, ZOH>(p);
+        if (gate) return launch_step_t<T, N, false, true, ZOH>(p);
+        return launch_step_t<T, N, false, false, ZOH>(p);
     }
-    if (conv && gate) return launch_scan_t<T, N, true, true>(p);
-    if (conv) return launch_scan_t<T, N, true, false>(p);
-    if (gate) return launch_scan_t<T, N, false, true>(p);
-    return launch_scan_t<T, N, false, false>(p);
+    if (conv && gate) return launch_scan_t<T, N, true, true, ZOH>(p);
+    if (conv) return launch_scan_t<T, N, true, false, ZOH>(p);
+    if (gate) return launch_scan_t<T, N, false, true, ZOH>(p);
+    return launch_scan_t<T, N, false, false, ZOH>(p);
 }
 
-template <typename T>
+template <typename T, bool ZOH>
 static hipError_t dispatch_n(const LaunchScan& p, bool step) {
     switch (p.N) {
-        case 4: return dispatch_flags<T, 4>(p, step);
-        case 8: return dispatch_flags<T, 8>(p, step);
-        case 16: return dispatch_flags<T, 16>(p, step);
-        case 32: return dispatch_flags<T, 32>(p, step);
-        case 64: return dispatch_flags<T, 64>(p, step);
+        case 4: return dispatch_flags<T, 4, ZOH>(p, step);
+        case 8: return dispatch_flags<T, 8, ZOH>(p, step);
+        case 16: return dispatch_flags<T, 16, ZOH>(p, step);
+        case 32: return dispatch_flags<T, 32, ZOH>(p, step);
+        case 64: return dispatch_flags<T, 64, ZOH>(p, step);
         default: return hipErrorInvalidValue;
     }
-}
-
-hipError_t launch_scan(const LaunchScan& p) {
-    return p.bf16 ? dispatch_n<uint16_t>(p, false) : dispatch_n<float>(p, false);
-}
-
-hipError_t launch_step(const LaunchScan& p) {
-    return p.bf16 ? dispatch_n<uint16_t>(p, true) : dispatch_n<float>(p, true);
 }
 
 }  // namespace selscan

@@ -21,6 +21,7 @@ struct LaunchScan {
     int64_t batch, L, D;
     int N;
     bool bf16;
+    bool zoh;       // zero-order-hold write term instead of Euler
     const void* x; const float* conv_w; const float* conv_b; const void* delta; const float* delta_bias;
     const float* A; const void* B; const void* C; const float* Dskip; const void* z; void* y;
     float* ssm_state; float* conv_state;
@@ -35,7 +36,11 @@ struct LaunchScan {
     void* ev_main[2];  // optional hipEvent_t pair recorded around the main kernel
 };
 
-hipError_t launch_scan(const LaunchScan& p);
-hipError_t launch_step(const LaunchScan& p);
+// One entry per instantiation unit (I/O dtype x write rule); step selects the
+// decode-step kernel instead of the full-sequence scan.
+hipError_t launch_f32_euler(const LaunchScan& p, bool step);
+hipError_t launch_f32_zoh(const LaunchScan& p, bool step);
+hipError_t launch_bf16_euler(const LaunchScan& p, bool step);
+hipError_t launch_bf16_zoh(const LaunchScan& p, bool step);
 
 }  // namespace selscan

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ss.ss_version() == 1
+    assert ss.ss_version() == 2
     assert ss.lib.ss_status_str(0) == b"ok"
     assert b"workspace" in ss.lib.ss_status_str(3)
 
@@ -83,10 +83,21 @@ def test_bad_dims_rejected(kw, status):
     assert _call(_dims(**kw), _fake_args()) == status
 
 
-def test_reserved_must_be_zero():
+@pytest.mark.parametrize("disc", [-1, 2, 7])
+def test_unknown_discretization_rejected(disc):
     d = _dims()
-    d.reserved = 1
+    d.discretization = disc
     assert _call(d, _fake_args()) == 1
+    assert "discretization" in ss.lib.ss_last_error().decode()
+
+
+def test_discretization_field_layout():
+    """The field sits where the header puts it, after io_dtype, and both rules are
+    accepted by the size query (ZOH needs the same workspace as Euler)."""
+    assert ss.ss_dims.discretization.offset == 36 and ctypes.sizeof(ss.ss_dims) == 40
+    e = ss.make_dims(1, 8192, 64, 16, ss.SS_F32)
+    z = ss.make_dims(1, 8192, 64, 16, ss.SS_F32, discretization=ss.SS_ZOH)
+    assert ss.ss_workspace_bytes(e) == ss.ss_workspace_bytes(z) > 0
 
 
 def test_misaligned_pointer_rejected():

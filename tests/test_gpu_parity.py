@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_util import TOL, gpu_fwd, host, maxrel, oracle_fwd, to_dev
+from gpu_util import TOL, check_fwd, check_inputs, gpu_fwd, host, maxrel, oracle_fwd, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -20,32 +20,8 @@ def ss():
     return mod
 
 
-def _check_fwd(ss, spec, *, seed=None, shape=None, states=False, flags=None, dsel=None, label=""):
-    shape = shape or {}
-    inp = W.gen_scan_inputs(spec, seed=seed, **shape)
-    Bsz, L, Dn = inp["x"].shape
-    N = inp["A"].shape[1]
-    st = W.gen_states(Bsz, Dn, N) if states else None
-    g = to_dev(inp, spec.io_dtype)
-    hs = torch.from_numpy(st["ssm_state"]).cuda() if states else None
-    cs = torch.from_numpy(st["conv_state"]).cuda() if states else None
-    y = gpu_fwd(ss, g, hs, cs, flags)
-    torch.cuda.synchronize()
-    yr, hr, cr = oracle_fwd(inp, st["ssm_state"] if states else None, st["conv_state"] if states else None,
-                            flags, dsel)
-    yg = host(y) if dsel is None else host(y[:, :, torch.as_tensor(dsel, device=y.device)])
-    tol = TOL[spec.io_dtype]
-    e = maxrel(yg, yr)
-    print(f"{label} y maxrel {e:.3e}", flush=True)
-    assert e <= tol, (label, e)
-    if states:
-        hg = host(hs) if dsel is None else host(hs)[:, dsel]
-        eh = maxrel(hg, hr)
-        assert eh <= tol, (label, "ssm_state", eh)
-        if (flags or {}).get("conv", True):
-            cg = host(cs) if dsel is None else host(cs)[:, dsel]
-            assert np.array_equal(cg.astype(np.float64), cr), (label, "conv_state")
-    return e
+def _check_fwd(ss, spec, **kw):
+    return check_fwd(ss, spec, **kw)
 
 
 # ----------------------------------------------------------------------------- workloads
@@ -277,24 +253,9 @@ def test_step_without_conv_or_gate(ss, S, Dn, N):
 
 def _long_chunk_case(ss, inp, io, dsel, label, states=True):
     Bsz, L, Dn = inp["x"].shape
-    N = inp["A"].shape[1]
-    dims = ss.make_dims(Bsz, L, Dn, N, 0 if io == "f32" else 1)
+    dims = ss.make_dims(Bsz, L, Dn, inp["A"].shape[1], 0 if io == "f32" else 1)
     assert ss.ss_workspace_bytes(dims) > 0, "shape does not select the chunked path"
-    st = W.gen_states(Bsz, Dn, N) if states else None
-    g = to_dev(inp, io)
-    hs = torch.from_numpy(st["ssm_state"]).cuda() if states else None
-    cs = torch.from_numpy(st["conv_state"]).cuda() if states else None
-    y = gpu_fwd(ss, g, hs, cs)
-    torch.cuda.synchronize()
-    yr, hr, cr = oracle_fwd(inp, st["ssm_state"] if states else None, st["conv_state"] if states else None,
-                            dsel=dsel)
-    yg = host(y[:, :, torch.as_tensor(dsel, device=y.device)])
-    e = maxrel(yg, yr)
-    print(f"{label} y maxrel {e:.3e}", flush=True)
-    assert e <= TOL[io], (label, e)
-    if states:
-        eh = maxrel(host(hs)[:, dsel], hr)
-        assert eh <= TOL["f32"], (label, "ssm_state", eh)
+    check_inputs(ss, inp, io, states=states, dsel=dsel, label=label, state_tol=TOL["f32"])
 
 
 def test_long_chunks_fp32_truncated_aggregates(ss):
