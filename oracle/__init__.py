@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the selective-scan (S6) forward path and its decode step.
+"""fp64 CPU oracle for the selective-scan (S6) forward path, its decode step and
+its backward (gradients of every input).
 
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package; the HIP library
@@ -62,6 +63,8 @@ class Oracle:
         lib.oracle_conv_scan_fwd.restype = ctypes.c_int
         lib.oracle_step.argtypes = [ctypes.c_int64] * 4 + [_dp] * 13 + [ctypes.c_int, ctypes.c_int]
         lib.oracle_step.restype = ctypes.c_int
+        lib.oracle_conv_scan_bwd.argtypes = [ctypes.c_int64] * 5 + [_dp] * 27 + [ctypes.c_int, ctypes.c_int]
+        lib.oracle_conv_scan_bwd.restype = ctypes.c_int
         self._lib = lib
 
     @staticmethod
@@ -119,6 +122,60 @@ class Oracle:
         return y[:, 0, :], hs, cs
 
 
+    def conv_scan_bwd(self, x, delta, A, B, C, dy, *, conv_w=None, conv_b=None, delta_bias=None, D=None,
+                      z=None, ssm_state=None, conv_state=None, dstate_final=None, dconv_final=None,
+                      zoh: bool = False, nthreads: int = 0):
+        """Gradients through conv_scan_fwd of sum(dy * out) + sum(dstate_final * h_final)
+        + sum(dconv_final * conv_history_final). ssm_state / conv_state are the INITIAL
+        states (None = zero). Returns a dict: dx, ddelta, dB, dC, dA, and where the
+        corresponding input exists dz, dD, dconv_w, dconv_b, ddelta_bias, dstate_init,
+        dconv_init (float64)."""
+        x = np.asarray(x)
+        Bsz, L, Dn = x.shape
+        N = np.asarray(A).shape[1]
+        K = np.asarray(conv_w).shape[1] if conv_w is not None else 4
+        keep = []
+
+        def p(a, shape=None):
+            arr, ptr = self._in(a, shape)
+            keep.append(arr)
+            return ptr
+
+        def out(shape, cond=True):
+            if not cond:
+                return None, None
+            arr = np.zeros(shape, dtype=np.float64)
+            return arr, arr.ctypes.data_as(_dp)
+
+        conv = conv_w is not None
+        g = {}
+        names = [("dx", (Bsz, L, Dn), True), ("ddelta", (Bsz, L, Dn), True), ("dz", (Bsz, L, Dn), z is not None),
+                 ("dB", (Bsz, L, N), True), ("dC", (Bsz, L, N), True), ("dA", (Dn, N), True),
+                 ("dD", (Dn,), D is not None), ("dconv_w", (Dn, K), conv), ("dconv_b", (Dn,), conv and conv_b is not None),
+                 ("ddelta_bias", (Dn,), delta_bias is not None), ("dstate_init", (Bsz, Dn, N), True),
+                 ("dconv_init", (Bsz, Dn, K - 1), conv)]
+        ptrs = {}
+        for name, shape, cond in names:
+            arr, ptr = out(shape, cond)
+            if arr is not None:
+                g[name] = arr
+            ptrs[name] = ptr
+        rc = self._lib.oracle_conv_scan_bwd(
+            Bsz, L, Dn, N, K,
+            p(x), p(conv_w, (Dn, K) if conv else None), p(conv_b, (Dn,) if conv_b is not None else None),
+            p(delta, (Bsz, L, Dn)), p(delta_bias, (Dn,) if delta_bias is not None else None), p(A, (Dn, N)),
+            p(B, (Bsz, L, N)), p(C, (Bsz, L, N)), p(D, (Dn,) if D is not None else None),
+            p(z, (Bsz, L, Dn) if z is not None else None),
+            p(ssm_state, (Bsz, Dn, N) if ssm_state is not None else None),
+            p(conv_state, (Bsz, Dn, K - 1) if conv_state is not None else None),
+            p(dy, (Bsz, L, Dn)), p(dstate_final, (Bsz, Dn, N) if dstate_final is not None else None),
+            p(dconv_final, (Bsz, Dn, K - 1) if dconv_final is not None else None),
+            *[ptrs[n] for n, _, _ in names], int(bool(zoh)), int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments")
+        return g
+
+
 _default: Optional[Oracle] = None
 
 
@@ -135,3 +192,7 @@ def conv_scan_fwd(*args, **kwargs):
 
 def step(*args, **kwargs):
     return default().step(*args, **kwargs)
+
+
+def conv_scan_bwd(*args, **kwargs):
+    return default().conv_scan_bwd(*args, **kwargs)

@@ -430,3 +430,122 @@ ALL_PINS = [
     pin_gate_and_skip, pin_softplus_sum, pin_state_handoff, pin_step_matches_scan,
     pin_zoh_van_loan, pin_zoh_equilibrium, pin_zoh_composition,
 ]
+
+
+# ---------------------------------------------------------------------------
+# backward (gradients through the forward): the hand-derived adjoint sweep of the
+# oracle against (1) central finite differences of the forward oracle and (2)
+# torch float64 autograd through an independently written forward.
+
+GRAD_INPUTS = ("x", "delta", "z", "B", "C", "A", "D", "conv_w", "conv_b", "delta_bias", "ssm_state", "conv_state")
+GRAD_NAME = {"x": "dx", "delta": "ddelta", "z": "dz", "B": "dB", "C": "dC", "A": "dA", "D": "dD",
+             "conv_w": "dconv_w", "conv_b": "dconv_b", "delta_bias": "ddelta_bias",
+             "ssm_state": "dstate_init", "conv_state": "dconv_init"}
+
+
+def bwd_case(seed, shape=(2, 7, 3, 4), zoh=False):
+    rng = np.random.default_rng(seed)
+    c = rand_case(rng, *shape, states=True)
+    Bsz, L, D, N = shape
+    cot = dict(dy=rng.standard_normal((Bsz, L, D)), dstate_final=rng.standard_normal((Bsz, D, N)),
+               dconv_final=rng.standard_normal((Bsz, D, 3)))
+    return c, cot
+
+
+def loss_of(orc, c, cot, zoh):
+    y, h, cs = orc.conv_scan_fwd(**c, zoh=zoh)
+    return float(np.sum(cot["dy"] * y) + np.sum(cot["dstate_final"] * h) + np.sum(cot["dconv_final"] * cs))
+
+
+def _pin_bwd_fd(orc, zoh, seed, eps=1e-6):
+    c, cot = bwd_case(seed, zoh=zoh)
+    g = orc.conv_scan_bwd(**c, **cot, zoh=zoh)
+    rng = np.random.default_rng(seed + 1000)
+    for name in GRAD_INPUTS:
+        v = rng.standard_normal(np.shape(c[name]))
+        cp, cm = dict(c), dict(c)
+        cp[name] = c[name] + eps * v
+        cm[name] = c[name] - eps * v
+        fd = (loss_of(orc, cp, cot, zoh) - loss_of(orc, cm, cot, zoh)) / (2 * eps)
+        an = float(np.sum(g[GRAD_NAME[name]] * v))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def pin_bwd_finite_differences(orc, seed=21):
+    """Directional derivative of the loss along a random direction, for every input
+    tensor: central difference of the forward oracle vs the backward's gradient."""
+    _pin_bwd_fd(orc, False, seed)
+
+
+def pin_bwd_finite_differences_zoh(orc, seed=22):
+    _pin_bwd_fd(orc, True, seed)
+
+
+def torch_forward(c, zoh):
+    """The forward written with torch ops (float64), for autograd: conv over the
+    history-padded input, SiLU, softplus as logaddexp(v, 0), the recurrence over t
+    with the Euler or zero-order-hold write term, readout, skip and SiLU gate."""
+    x, delta, A, B, C = c["x"], c["delta"], c["A"], c["B"], c["C"]
+    Bsz, L, D = x.shape
+    xp = torch.cat([c["conv_state"].transpose(1, 2), x], dim=1)               # [B, L+3, D]
+    pre = c["conv_b"] + sum(c["conv_w"][:, k] * xp[:, k:k + L, :] for k in range(4))
+    u = pre * torch.sigmoid(pre)
+    dt = torch.logaddexp(delta + c["delta_bias"], torch.zeros((), dtype=torch.float64))
+    h = c["ssm_state"]
+    ys = []
+    for t in range(L):
+        at = dt[:, t, :, None] * A                                             # [B, D, N]
+        w = torch.expm1(at) / A if zoh else dt[:, t, :, None]
+        h = torch.exp(at) * h + w * B[:, t, None, :] * u[:, t, :, None]
+        ys.append((h * C[:, t, None, :]).sum(-1) + c["D"] * u[:, t])
+    y = torch.stack(ys, 1) * (c["z"] * torch.sigmoid(c["z"]))
+    return y, h, xp[:, L:L + 3, :].transpose(1, 2)
+
+
+def _pin_bwd_autograd(orc, zoh, seed):
+    c, cot = bwd_case(seed, shape=(2, 6, 3, 5), zoh=zoh)
+    g = orc.conv_scan_bwd(**c, **cot, zoh=zoh)
+    tc = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in c.items()}
+    y, h, cs = torch_forward(tc, zoh)
+    loss = ((y * torch.from_numpy(cot["dy"])).sum() + (h * torch.from_numpy(cot["dstate_final"])).sum()
+            + (cs * torch.from_numpy(cot["dconv_final"])).sum())
+    names = list(GRAD_INPUTS)
+    grads = torch.autograd.grad(loss, [tc[n] for n in names])
+    for n, tg in zip(names, grads):
+        ref = tg.numpy()
+        assert relerr(g[GRAD_NAME[n]], ref) < 1e-10, (n, relerr(g[GRAD_NAME[n]], ref))
+
+
+def pin_bwd_autograd(orc, seed=23):
+    """Every gradient element against torch autograd through torch_forward."""
+    _pin_bwd_autograd(orc, False, seed)
+
+
+def pin_bwd_autograd_zoh(orc, seed=24):
+    _pin_bwd_autograd(orc, True, seed)
+
+
+def pin_bwd_without_optional_pieces(orc, seed=25):
+    """No conv, gate, skip, bias or initial states: the gradients that remain still
+    match autograd (u = x, ungated output, zero initial state)."""
+    rng = np.random.default_rng(seed)
+    c = rand_case(rng, 1, 5, 2, 3, conv=False, gate=False, skip=False, bias=False)
+    dy = rng.standard_normal((1, 5, 2))
+    g = orc.conv_scan_bwd(**c, dy=dy)
+    assert set(g) == {"dx", "ddelta", "dB", "dC", "dA", "dstate_init"}
+    tc = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in c.items()}
+    dt = torch.logaddexp(tc["delta"], torch.zeros((), dtype=torch.float64))
+    h = torch.zeros(1, 2, 3, dtype=torch.float64)
+    ys = []
+    for t in range(5):
+        h = torch.exp(dt[:, t, :, None] * tc["A"]) * h + dt[:, t, :, None] * tc["B"][:, t, None, :] * tc["x"][:, t, :, None]
+        ys.append((h * tc["C"][:, t, None, :]).sum(-1))
+    loss = (torch.stack(ys, 1) * torch.from_numpy(dy)).sum()
+    for n, tg in zip(("x", "delta", "B", "C", "A"), torch.autograd.grad(loss, [tc[k] for k in ("x", "delta", "B", "C", "A")])):
+        assert relerr(g[GRAD_NAME[n]], tg.numpy()) < 1e-10, n
+    assert np.all(g["dstate_init"] != 0.0)
+
+
+BWD_PINS = [pin_bwd_finite_differences, pin_bwd_finite_differences_zoh, pin_bwd_autograd, pin_bwd_autograd_zoh,
+            pin_bwd_without_optional_pieces]
+ALL_PINS = ALL_PINS + BWD_PINS

@@ -52,6 +52,28 @@ MUTANTS = {
     "initial_state_ignored": [("h[n] = ssm_state ? ssm_state[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;")],
     "conv_history_ignored": [("win[k] = conv_state ? conv_state[(b * D + d) * (K - 1) + k] : 0.0;",
                               "win[k] = 0.0;")],
+    # backward
+    "bwd_adjoint_not_decayed": [("g_next[n] = ab * g;", "g_next[n] = g;")],
+    "bwd_dA_missing_delta": [("dA_loc[n] += g * (dt[t] * ab * hp", "dA_loc[n] += g * (ab * hp")],
+    "bwd_ddelta_missing_write_term": [("dDelta += g * (an * ab * hp + dw_ddt * Bn * u[t]);",
+                                       "dDelta += g * (an * ab * hp);")],
+    "bwd_dC_uses_previous_state": [("dCacc[bc + n] += dyg * h[(t + 1) * N + n];",
+                                    "dCacc[bc + n] += dyg * h[t * N + n];")],
+    "bwd_dB_missing_u": [("dBacc[bc + n] += g * w * u[t];", "dBacc[bc + n] += g * w;")],
+    "bwd_dz_with_gated_output": [("a->dz[row] = a->dy[row] * yt * dsilu(zt);",
+                                  "a->dz[row] = a->dy[row] * yt * silu(zt) * dsilu(zt);")],
+    "bwd_softplus_derivative_flipped": [("const double ddel = dDelta * sigmoid(v[t]);",
+                                         "const double ddel = dDelta * sigmoid(-v[t]);")],
+    "bwd_conv_taps_reversed": [("dxa[t + k] += a->conv_w[d * K + k] * dc;",
+                                "dxa[t + k] += a->conv_w[d * K + (K - 1 - k)] * dc;")],
+    "bwd_dsilu_is_dsigmoid": [("return s * (1.0 + v * (1.0 - s));", "return s * (1.0 - s);")],
+    "bwd_skip_gradient_dropped": [("double du = dsk * dyg, dDelta = 0.0;", "double du = 0.0 * dyg, dDelta = 0.0;")],
+    "bwd_zoh_dwdA_sign": [("dw_dA = (dt[t] * ab - w) / an;", "dw_dA = (w - dt[t] * ab) / an;")],
+    "bwd_zoh_dwddelta_euler": [("dw_ddt = ab;", "dw_ddt = 1.0;")],
+    "bwd_final_state_grad_ignored": [("g_next[n] = a->dstate_final ? a->dstate_final[(b * D + d) * N + n] : 0.0;",
+                                      "g_next[n] = 0.0;")],
+    "bwd_final_history_grad_misplaced": [("dxa[L + k] += a->dconv_final[(b * D + d) * H + k];",
+                                          "dxa[L + H - 1 - k] += a->dconv_final[(b * D + d) * H + k];")],
 }
 
 
