@@ -1,6 +1,7 @@
 /*
- * libselscan: selective-scan (S6) forward path and single-token decode step
- * for AMD Instinct MI355X (gfx950), as hand-written HIP kernels behind a C ABI.
+ * libselscan: selective-scan (S6) forward path, its backward and the single-token
+ * decode step for AMD Instinct MI355X (gfx950), as hand-written HIP kernels behind
+ * a C ABI.
  *
  * The operation (per batch row b, channel d, state index n, time t):
  *
@@ -63,7 +64,7 @@
 extern "C" {
 #endif
 
-#define SS_VERSION 2
+#define SS_VERSION 3
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
@@ -124,12 +125,56 @@ ss_status ss_conv_scan_fwd(const ss_dims* dims, const ss_args* args,
  * ssm_state [B,D,N] and conv_state [B,D,K-1] in place. dims->seqlen is ignored. */
 ss_status ss_step(const ss_dims* dims, const ss_args* args, void* stream);
 
+/* Gradients for ss_conv_scan_bwd. The loss being differentiated is
+ *     sum(dy * y) + sum(dstate_final * ssm_state_out) + sum(dconv_final * conv_state_out)
+ * where y, ssm_state_out and conv_state_out are what ss_conv_scan_fwd returns for
+ * the same inputs and initial states. All pointers are DEVICE pointers; outputs are
+ * overwritten (not accumulated). The io dtype is the forward's. */
+typedef struct {
+    const void*  dy;           /* [B,L,D] io, gradient of the output y (required)               */
+    const float* dstate_final; /* [B,D,N] or NULL (zero): gradient of the returned ssm_state     */
+    const float* dconv_final;  /* [B,D,K-1] or NULL (zero): gradient of the returned conv history;
+                                  only with conv_w                                               */
+    void*  dx;                 /* [B,L,D] io OUT (required)                                      */
+    void*  ddelta;             /* [B,L,D] io OUT (required)                                      */
+    void*  dz;                 /* [B,L,D] io OUT; required when z is given, else NULL            */
+    float* dB;                 /* [B,L,N] OUT (required), summed over channels                   */
+    float* dC;                 /* [B,L,N] OUT (required), summed over channels                   */
+    float* dA;                 /* [D,N] OUT (required), summed over batch and time               */
+    float* dDskip;             /* [D] OUT or NULL                                                */
+    float* dconv_w;            /* [D,K] OUT or NULL; only with conv_w                            */
+    float* dconv_b;            /* [D] OUT or NULL; only with conv_w                              */
+    float* ddelta_bias;        /* [D] OUT or NULL                                                */
+    float* dstate_init;        /* [B,D,N] OUT or NULL: gradient of the initial ssm_state         */
+    float* dconv_init;         /* [B,D,K-1] OUT or NULL: gradient of the initial conv history;
+                                  only with conv_w                                               */
+} ss_grads;
+
+/* Bytes of device workspace ss_conv_scan_bwd needs (0 for invalid dims). It holds
+ * the forward's state after every 4th token (B * (L/4) * D * N fp32), the chunk
+ * aggregates of both directions and per-workgroup partial sums. */
+size_t ss_bwd_workspace_bytes(const ss_dims* dims);
+
+/* Backward of ss_conv_scan_fwd: every gradient of the loss above, for the inputs
+ * in `args` (x, conv_w, conv_b, delta, delta_bias, A, B, C, Dskip, z as given to the
+ * forward; args->ssm_state / conv_state are the forward's INITIAL states, read only,
+ * NULL = zero; args->y is ignored). The chain rule through the forward's steps in
+ * reverse order: the state adjoint runs backward in time (g_t = C_t dy_t SiLU(z_t) +
+ * exp(Delta_{t+1} A) g_{t+1}), the states it needs are recomputed from checkpoints
+ * rather than stored by the forward. dims->discretization must be SS_EULER
+ * (SS_ERR_UNSUPPORTED otherwise). Gradients of per-channel parameters are summed over
+ * batch and time, dB / dC over channels, in a fixed order (deterministic). Outputs
+ * must not overlap any input, each other or the workspace. Asynchronous on `stream`. */
+ss_status ss_conv_scan_bwd(const ss_dims* dims, const ss_args* args, const ss_grads* grads,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Profiling support for benchmarks: events (hipEvent_t handles created by the
- * caller) that the NEXT ss_conv_scan_fwd or ss_step call made on this thread
- * records around its kernels, at the kernels' own start and end on the call's
- * stream: agg_start/agg_stop around the chunk-aggregate kernel (left unrecorded
- * when the call launches none), main_start/main_stop around the main scan or
- * decode-step kernel. Any pointer may be NULL. The setting is consumed by that
+ * caller) that the NEXT ss_conv_scan_fwd, ss_conv_scan_bwd or ss_step call made on
+ * this thread records around its kernels, at the kernels' own start and end on the
+ * call's stream: agg_start/agg_stop around the forward's chunk-aggregate kernel
+ * (left unrecorded when the call launches none, and by the backward),
+ * main_start/main_stop around the main scan, backward-sweep or decode-step kernel.
+ * Any pointer may be NULL. The setting is consumed by that
  * next call, also when it fails. Always returns SS_OK. */
 ss_status ss_time_next_call(void* agg_start, void* agg_stop, void* main_start, void* main_stop);
 

@@ -6,8 +6,8 @@ the C ABI declared in include/selscan.h, and every step of the computation
 runs in the library's HIP kernels. There is no CPU fallback: importing the
 package without a built ``libselscan.so`` raises.
 
-Names follow the C ABI: ``ss_conv_scan_fwd``, ``ss_step``,
-``ss_workspace_bytes``, ``ss_version``.
+Names follow the C ABI: ``ss_conv_scan_fwd``, ``ss_conv_scan_bwd``, ``ss_step``,
+``ss_workspace_bytes``, ``ss_bwd_workspace_bytes``, ``ss_version``.
 """
 from __future__ import annotations
 
@@ -39,6 +39,11 @@ class ss_args(ctypes.Structure):
                                    "z", "y", "ssm_state", "conv_state")]
 
 
+class ss_grads(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("dy", "dstate_final", "dconv_final", "dx", "ddelta", "dz", "dB", "dC", "dA",
+                                   "dDskip", "dconv_w", "dconv_b", "ddelta_bias", "dstate_init", "dconv_init")]
+
+
 class SelscanError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"{STATUS.get(status, status)}: {detail}")
@@ -63,6 +68,11 @@ def _load() -> ctypes.CDLL:
     lib.ss_version.restype = ctypes.c_int
     lib.ss_time_next_call.argtypes = [_vp, _vp, _vp, _vp]
     lib.ss_time_next_call.restype = ctypes.c_int
+    lib.ss_bwd_workspace_bytes.argtypes = [ctypes.POINTER(ss_dims)]
+    lib.ss_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ss_conv_scan_bwd.argtypes = [ctypes.POINTER(ss_dims), ctypes.POINTER(ss_args), ctypes.POINTER(ss_grads), _vp,
+                                     ctypes.c_size_t, _vp]
+    lib.ss_conv_scan_bwd.restype = ctypes.c_int
     return lib
 
 
@@ -185,5 +195,63 @@ def ss_step(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tens
     return y
 
 
-__all__ = ["ss_conv_scan_fwd", "ss_step", "ss_workspace_bytes", "ss_version", "ss_time_next_call", "make_dims", "ss_dims", "ss_args",
+def ss_bwd_workspace_bytes(dims: ss_dims) -> int:
+    return int(lib.ss_bwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def ss_conv_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                     dy: torch.Tensor, *, conv_w: Optional[torch.Tensor] = None, conv_b: Optional[torch.Tensor] = None,
+                     delta_bias: Optional[torch.Tensor] = None, D: Optional[torch.Tensor] = None,
+                     z: Optional[torch.Tensor] = None, ssm_state: Optional[torch.Tensor] = None,
+                     conv_state: Optional[torch.Tensor] = None, dstate_final: Optional[torch.Tensor] = None,
+                     dconv_final: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     zoh: bool = False, stream=None) -> dict:
+    """Backward of ss_conv_scan_fwd for the same inputs; ssm_state / conv_state are the
+    forward's INITIAL states (read only). dy [B,L,D] in the I/O dtype; dstate_final
+    [B,D,N] and dconv_final [B,D,3] float32 are the gradients of the returned states.
+    Returns a dict of new tensors: dx, ddelta (I/O dtype), dB, dC, dA (float32), and
+    where the input exists dz, dD, dconv_w, dconv_b, ddelta_bias (float32); always
+    dstate_init and, with the conv, dconv_init (float32). Asynchronous on the stream."""
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, d_inner]")
+    Bsz, L, Dn = x.shape
+    N = A.shape[1] if A.dim() == 2 else 0
+    dims = make_dims(Bsz, L, Dn, N, _io_dtype(x), discretization=SS_ZOH if zoh else SS_EULER)
+    args = _build_args(x, delta, A, B, C, conv_w, conv_b, delta_bias, D, z, None, ssm_state, conv_state,
+                       (Bsz, L), dims)
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(x), "dB": torch.empty(Bsz, L, N, **f32),
+           "dC": torch.empty(Bsz, L, N, **f32), "dA": torch.empty(Dn, N, **f32),
+           "dstate_init": torch.empty(Bsz, Dn, N, **f32)}
+    if z is not None:
+        out["dz"] = torch.empty_like(x)
+    if D is not None:
+        out["dD"] = torch.empty(Dn, **f32)
+    if delta_bias is not None:
+        out["ddelta_bias"] = torch.empty(Dn, **f32)
+    if conv_w is not None:
+        out["dconv_w"] = torch.empty(Dn, 4, **f32)
+        out["dconv_init"] = torch.empty(Bsz, Dn, 3, **f32)
+        if conv_b is not None:
+            out["dconv_b"] = torch.empty(Dn, **f32)
+    K = dims.d_conv
+    g = ss_grads(dy=_ptr(dy, (Bsz, L, Dn), x.dtype, "dy"),
+                 dstate_final=_ptr(dstate_final, (Bsz, Dn, N), torch.float32, "dstate_final"),
+                 dconv_final=_ptr(dconv_final, (Bsz, Dn, K - 1), torch.float32, "dconv_final"),
+                 **{k: (out[k].data_ptr() if k in out else None) for k in
+                    ("dx", "ddelta", "dz", "dB", "dC", "dA", "dconv_w", "dconv_b", "ddelta_bias", "dstate_init",
+                     "dconv_init")},
+                 dDskip=out["dD"].data_ptr() if "dD" in out else None)
+    need = ss_bwd_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
+    _check(lib.ss_conv_scan_bwd(ctypes.byref(dims), ctypes.byref(args), ctypes.byref(g), workspace.data_ptr(),
+                                workspace.numel(), _stream_handle(stream)))
+    return out
+
+
+__all__ = ["ss_conv_scan_fwd", "ss_conv_scan_bwd", "ss_bwd_workspace_bytes", "ss_grads", "ss_step", "ss_workspace_bytes", "ss_version", "ss_time_next_call", "make_dims", "ss_dims", "ss_args",
            "SelscanError", "SS_F32", "SS_BF16", "SS_EULER", "SS_ZOH", "LIB_PATH", "lib"]

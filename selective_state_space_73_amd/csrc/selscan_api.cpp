@@ -47,6 +47,11 @@ bool supported_n(int n) { return n == 4 || n == 8 || n == 16 || n == 32 || n == 
 
 size_t io_size(int dt) { return dt == SS_BF16 ? 2 : 4; }
 
+int64_t chunk_len_for(int64_t L, int64_t nc) {
+    const int64_t len = (L + nc - 1) / nc;
+    return nc > 1 ? (len + selscan::kScanTile - 1) / selscan::kScanTile * selscan::kScanTile : len;
+}
+
 // Chunk count for the full-sequence scan. One chunk when batch x channel
 // workgroups already fill the GPU; otherwise enough chunks (each at least
 // kMinChunk tokens) to reach about kTargetGroups workgroups.
@@ -69,8 +74,10 @@ int choose_chunks(const ss_dims& d) {
     if (nc > d.seqlen) nc = d.seqlen;
     if (nc > kMaxGridYZ) nc = kMaxGridYZ;
     if (nc < 1) nc = 1;
-    // equalise: every chunk has ceil(L / nc) tokens except the last
-    const int64_t len = (d.seqlen + nc - 1) / nc;
+    // equalise: every chunk has ceil(L / nc) tokens, rounded up to whole B/C tiles,
+    // except the last (chunk starts are multiples of the tile, hence of the
+    // backward's checkpoint spacing)
+    const int64_t len = chunk_len_for(d.seqlen, nc);
     return (int)((d.seqlen + len - 1) / len);
 }
 
@@ -85,7 +92,7 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 Layout layout(const ss_dims& d) {
     Layout l;
     l.nchunks = choose_chunks(d);
-    l.chunk_len = (d.seqlen + l.nchunks - 1) / l.nchunks;
+    l.chunk_len = chunk_len_for(d.seqlen, l.nchunks);
     const size_t B = (size_t)d.batch, D = (size_t)d.d_inner, N = (size_t)d.d_state;
     size_t off = 0;
     if (l.nchunks > 1) {
@@ -95,6 +102,34 @@ Layout layout(const ss_dims& d) {
         l.off_h0 = off;  off = align256(off + B * D * N * sizeof(float));
         l.off_c0 = off;  off = align256(off + B * D * (size_t)(d.d_conv - 1) * sizeof(float));
     }
+    l.total = off;
+    return l;
+}
+
+// Backward workspace: the forward's (chunk aggregates) followed by the checkpoints,
+// the adjoint aggregates and the partial sums.
+struct BwdLayout {
+    Layout f;
+    int64_t nck = 0;
+    int nblk = 0;
+    size_t off_ckpt = 0, off_Q = 0, off_qsdt = 0, off_dbc = 0, off_par = 0, off_dxh = 0, off_dc3 = 0, total = 0;
+};
+
+BwdLayout bwd_layout(const ss_dims& d) {
+    BwdLayout l;
+    l.f = layout(d);
+    const size_t B = (size_t)d.batch, L = (size_t)d.seqlen, D = (size_t)d.d_inner, N = (size_t)d.d_state;
+    const size_t nC = (size_t)l.f.nchunks;
+    l.nck = d.seqlen / 4;
+    l.nblk = (int)((d.d_inner + selscan::kScanThreads - 1) / selscan::kScanThreads);
+    size_t off = l.f.total;
+    l.off_ckpt = off; off = align256(off + B * (size_t)l.nck * D * N * sizeof(float));
+    l.off_Q = off;    off = align256(off + B * (nC - 1) * D * N * sizeof(float));
+    l.off_qsdt = off; off = align256(off + B * (nC - 1) * D * sizeof(float));
+    l.off_dbc = off;  off = align256(off + B * L * (size_t)l.nblk * 2 * N * sizeof(float));
+    l.off_par = off;  off = align256(off + B * nC * D * (N + 8) * sizeof(float));
+    l.off_dxh = off;  off = align256(off + B * nC * D * 3 * sizeof(float));
+    l.off_dc3 = off;  off = align256(off + B * nC * D * 3 * sizeof(float));
     l.total = off;
     return l;
 }
@@ -129,7 +164,9 @@ bool overlap(const Range& a, const Range& b) {
     return a0 < b1 && b0 < a1;
 }
 
-ss_status check_args(const ss_dims& d, const ss_args* a, bool step) {
+// bwd: the arguments of the backward (the forward's inputs; y is not used there, the
+// outputs are checked by check_grads)
+ss_status check_args(const ss_dims& d, const ss_args* a, bool step, bool bwd = false) {
     if (!a) return fail(SS_ERR_INVALID_ARG, "args is NULL");
     const int64_t L = step ? 1 : d.seqlen;
     const size_t es = io_size(d.io_dtype);
@@ -139,8 +176,9 @@ ss_status check_args(const ss_dims& d, const ss_args* a, bool step) {
     const size_t BD = (size_t)d.batch * D;
     struct Req { const void* p; const char* name; };
     const Req req[] = {{a->x, "x"}, {a->delta, "delta"}, {a->A, "A"}, {a->B, "B"}, {a->C, "C"}, {a->y, "y"}};
-    for (const Req& r : req)
-        if (!r.p) return fail(SS_ERR_INVALID_ARG, "%s is NULL", r.name);
+    const int nreq = bwd ? 5 : 6;                  // the backward does not use y (the last entry)
+    for (int i = 0; i < nreq; ++i)
+        if (!req[i].p) return fail(SS_ERR_INVALID_ARG, "%s is NULL", req[i].name);
     if (step && !a->ssm_state) return fail(SS_ERR_INVALID_ARG, "ss_step needs ssm_state");
     if (step && a->conv_w && !a->conv_state) return fail(SS_ERR_INVALID_ARG, "ss_step with conv_w needs conv_state");
     if (!a->conv_w && a->conv_state) return fail(SS_ERR_INVALID_ARG, "conv_state given without conv_w");
@@ -154,10 +192,10 @@ ss_status check_args(const ss_dims& d, const ss_args* a, bool step) {
     };
     for (const Range& r : in)
         if (r.p && ((uintptr_t)r.p & 3u)) return fail(SS_ERR_INVALID_ARG, "%s not 4-byte aligned", r.name);
-    if ((uintptr_t)a->y & 3u) return fail(SS_ERR_INVALID_ARG, "y not 4-byte aligned");
+    if (!bwd && ((uintptr_t)a->y & 3u)) return fail(SS_ERR_INVALID_ARG, "y not 4-byte aligned");
     if (a->ssm_state && ((uintptr_t)a->ssm_state & 15u))
         return fail(SS_ERR_INVALID_ARG, "ssm_state not 16-byte aligned");
-    const Range yr{a->y, BLD * es, "y"};
+    const Range yr{bwd ? nullptr : a->y, BLD * es, "y"};
     for (const Range& r : in)
         if (overlap(yr, r)) return fail(SS_ERR_INVALID_ARG, "y overlaps %s", r.name);
     if (overlap(Range{a->ssm_state, BD * N * 4, "ssm_state"}, Range{a->conv_state, BD * (K - 1) * 4, "conv_state"}))
@@ -180,6 +218,47 @@ selscan::LaunchScan make_launch(const ss_dims& d, const ss_args& a, void* stream
     p.ssm_state = a.ssm_state; p.conv_state = a.conv_state;
     p.stream = stream;
     return p;
+}
+
+ss_status check_grads(const ss_dims& d, const ss_args* a, const ss_grads* g) {
+    if (!g) return fail(SS_ERR_INVALID_ARG, "grads is NULL");
+    const size_t es = io_size(d.io_dtype);
+    const size_t B = (size_t)d.batch, L = (size_t)d.seqlen, D = (size_t)d.d_inner, N = (size_t)d.d_state;
+    const size_t K = (size_t)d.d_conv;
+    const size_t BLD = B * L * D, BLN = B * L * N;
+    struct Req { const void* p; const char* name; };
+    const Req req[] = {{g->dy, "dy"}, {g->dx, "dx"}, {g->ddelta, "ddelta"}, {g->dB, "dB"}, {g->dC, "dC"}, {g->dA, "dA"}};
+    for (const Req& r : req)
+        if (!r.p) return fail(SS_ERR_INVALID_ARG, "grads.%s is NULL", r.name);
+    if (a->z && !g->dz) return fail(SS_ERR_INVALID_ARG, "grads.dz is required when z is given");
+    if (!a->z && g->dz) return fail(SS_ERR_INVALID_ARG, "grads.dz given without z");
+    if (!a->conv_w && (g->dconv_final || g->dconv_w || g->dconv_b || g->dconv_init))
+        return fail(SS_ERR_INVALID_ARG, "conv gradients given without conv_w");
+    const Range outs[] = {
+        {g->dx, BLD * es, "dx"}, {g->ddelta, BLD * es, "ddelta"}, {g->dz, BLD * es, "dz"},
+        {g->dB, BLN * 4, "dB"}, {g->dC, BLN * 4, "dC"}, {g->dA, D * N * 4, "dA"}, {g->dDskip, D * 4, "dDskip"},
+        {g->dconv_w, D * K * 4, "dconv_w"}, {g->dconv_b, D * 4, "dconv_b"}, {g->ddelta_bias, D * 4, "ddelta_bias"},
+        {g->dstate_init, B * D * N * 4, "dstate_init"}, {g->dconv_init, B * D * (K - 1) * 4, "dconv_init"},
+    };
+    const Range ins[] = {
+        {a->x, BLD * es, "x"}, {a->delta, BLD * es, "delta"}, {a->z, BLD * es, "z"}, {a->B, BLN * es, "B"},
+        {a->C, BLN * es, "C"}, {a->A, D * N * 4, "A"}, {a->conv_w, D * K * 4, "conv_w"}, {a->conv_b, D * 4, "conv_b"},
+        {a->delta_bias, D * 4, "delta_bias"}, {a->Dskip, D * 4, "Dskip"},
+        {a->ssm_state, B * D * N * 4, "ssm_state"}, {a->conv_state, B * D * (K - 1) * 4, "conv_state"},
+        {g->dy, BLD * es, "dy"}, {g->dstate_final, B * D * N * 4, "dstate_final"},
+        {g->dconv_final, B * D * (K - 1) * 4, "dconv_final"},
+    };
+    for (const Range& r : outs)
+        if (r.p && ((uintptr_t)r.p & 3u)) return fail(SS_ERR_INVALID_ARG, "%s not 4-byte aligned", r.name);
+    for (const Range& r : ins)
+        if (r.p && ((uintptr_t)r.p & 3u)) return fail(SS_ERR_INVALID_ARG, "%s not 4-byte aligned", r.name);
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return fail(SS_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, r.name);
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (overlap(outs[i], outs[j])) return fail(SS_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+    }
+    return SS_OK;
 }
 
 hipError_t launch(const selscan::LaunchScan& p, bool step) {
@@ -241,6 +320,66 @@ ss_status ss_step(const ss_dims* dims, const ss_args* args, void* stream) {
     selscan::LaunchScan p = make_launch(one, *args, stream);
     take_events(p);
     const hipError_t e = launch(p, true);
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return SS_OK;
+}
+
+size_t ss_bwd_workspace_bytes(const ss_dims* dims) {
+    if (check_dims(dims, false) != SS_OK) return 0;
+    return bwd_layout(*dims).total;
+}
+
+ss_status ss_conv_scan_bwd(const ss_dims* dims, const ss_args* args, const ss_grads* grads, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    ss_status s = check_dims(dims, false);
+    if (s == SS_OK && dims->discretization != SS_EULER)
+        s = fail(SS_ERR_UNSUPPORTED, "the backward is built for the Euler write term only");
+    if (s == SS_OK) {
+        s = check_args(*dims, args, false, true);
+    }
+    if (s == SS_OK) s = check_grads(*dims, args, grads);
+    if (s != SS_OK) { drop_events(); return s; }
+    const BwdLayout l = bwd_layout(*dims);
+    if (!workspace || workspace_bytes < l.total) {
+        drop_events();
+        return fail(SS_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, l.total);
+    }
+    if ((uintptr_t)workspace & 255u) { drop_events(); return fail(SS_ERR_INVALID_ARG, "workspace not 256-byte aligned"); }
+    const Range wr{workspace, l.total, "workspace"};
+    const Range others[] = {{args->x, 1, "x"}, {args->B, 1, "B"}, {args->C, 1, "C"}, {args->delta, 1, "delta"},
+                            {args->ssm_state, 1, "ssm_state"}, {grads->dy, 1, "dy"}, {grads->dx, 1, "dx"},
+                            {grads->ddelta, 1, "ddelta"}, {grads->dB, 1, "dB"}, {grads->dC, 1, "dC"},
+                            {grads->dA, 1, "dA"}};
+    for (const Range& r : others)
+        if (overlap(wr, r)) { drop_events(); return fail(SS_ERR_INVALID_ARG, "workspace overlaps %s", r.name); }
+
+    selscan::LaunchBwd q{};
+    q.f = make_launch(*dims, *args, stream);
+    q.f.y = nullptr;
+    take_events(q.f);
+    char* ws = static_cast<char*>(workspace);
+    q.f.nchunks = l.f.nchunks;
+    q.f.chunk_len = l.f.chunk_len;
+    if (l.f.nchunks > 1) {
+        q.f.ws_S = reinterpret_cast<float*>(ws + l.f.off_S);
+        q.f.ws_sdt = reinterpret_cast<float*>(ws + l.f.off_sdt);
+        q.f.ws_h0 = reinterpret_cast<float*>(ws + l.f.off_h0);
+        q.f.ws_c0 = reinterpret_cast<float*>(ws + l.f.off_c0);
+    }
+    q.dy = grads->dy; q.dstate_final = grads->dstate_final; q.dconv_final = grads->dconv_final;
+    q.dx = grads->dx; q.ddelta = grads->ddelta; q.dz = grads->dz;
+    q.dB = grads->dB; q.dC = grads->dC; q.dA = grads->dA; q.dD = grads->dDskip;
+    q.dconv_w = grads->dconv_w; q.dconv_b = grads->dconv_b; q.ddelta_bias = grads->ddelta_bias;
+    q.dstate_init = grads->dstate_init; q.dconv_init = grads->dconv_init;
+    q.ws_ckpt = reinterpret_cast<float*>(ws + l.off_ckpt);
+    q.ws_Q = reinterpret_cast<float*>(ws + l.off_Q);
+    q.ws_qsdt = reinterpret_cast<float*>(ws + l.off_qsdt);
+    q.ws_dbc = reinterpret_cast<float*>(ws + l.off_dbc);
+    q.ws_par = reinterpret_cast<float*>(ws + l.off_par);
+    q.ws_dxh = reinterpret_cast<float*>(ws + l.off_dxh);
+    q.ws_dc3 = reinterpret_cast<float*>(ws + l.off_dc3);
+    q.nck = l.nck;
+    const hipError_t e = q.f.bf16 ? selscan::launch_bwd_bf16_euler(q) : selscan::launch_bwd_f32_euler(q);
     if (e != hipSuccess) return fail(SS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return SS_OK;
 }

@@ -1,0 +1,608 @@
+// Backward kernels of libselscan for gfx950: gradients of every input of the
+// forward path (ss_conv_scan_bwd). Included by the instantiation units after
+// selscan_device.h.
+//
+// The gradients are the chain rule through the forward's steps in reverse order.
+// The adjoint of the state, g_t = dLoss/dh_t, runs backward in time:
+//     g_t = C_t * dyg_t + exp(Delta_{t+1} A) g_{t+1}        (dyg_t = dy_t * SiLU(z_t))
+// and every gradient is a product of g_t or dyg_t with forward quantities at the
+// same token, h_t and h_{t-1} among them (ozercemkelahmet.com "Mamba", "Step 2":
+// the recurrence; "Step 4": states are recomputed rather than stored; gunjandhanuka
+// "Mamba", linear-time training). Pipeline, per call:
+//   1. k_agg        forward chunk aggregates (as in the forward), when chunked;
+//   2. k_scan<CK>   forward recompute writing the state after every 4th token;
+//   3. k_bagg       per chunk (after the first): the adjoint arriving at its start
+//                   from its own tokens, Q_c = sum_t prod_{k<=t} a_k C_t dyg_t, and its
+//                   summed step size, so that chunk c's adjoint carry-in is the fold
+//                   gamma_c = Q_{c+1} + exp(A sum Delta_{c+1}) gamma_{c+1};
+//   4. k_bwd        per chunk, 4-token segments from the end: recompute the segment
+//                   forward from its checkpoint (states kept in registers), then sweep
+//                   it backward; channel sums of dB/dC are reduced across the lanes of
+//                   a wave and the waves of a workgroup; per-channel parameter sums
+//                   and the conv halo of dx at chunk ends go to the workspace;
+//   5. k_bwd_sum_*  fixed-order sums of the partials (deterministic results).
+#pragma once
+#include "selscan_device.h"
+
+namespace selscan {
+
+static_assert(kCkptEvery == 4, "the backward recomputes 4-token segments");
+
+struct BwdArgs {
+    int64_t L;
+    int64_t chunk_len;
+    int D;
+    int nchunks;
+    int64_t nck;          // checkpoint slots per batch row
+    int nblk;             // workgroups along d (partials of dB/dC per token)
+};
+
+// --------------------------------------------------------------------------
+// Sum of V values (V a power of two, >= 4) over the 64 lanes of a wave by
+// recursive halving: each level pairs lanes in the two halves of a block and
+// keeps half of the values, so no lane adds a value it does not need. Levels:
+// lanes 32 apart (permlane32 swap), 16 apart (permlane16 swap), then mirrored
+// lanes within 16, 8, 4 and 2 lanes (DPP). On return v[i] (i < R = max(1, V/64))
+// on lane l holds the total of value i + (l >> SH) * R, SH = max(0, 6 - log2 V).
+template <int V> struct WaveSum {
+    static constexpr int LOG = V >= 128 ? 7 : V >= 64 ? 6 : V >= 32 ? 5 : V >= 16 ? 4 : V >= 8 ? 3 : 2;
+    static constexpr int R = V >= 64 ? V / 64 : 1;
+    static constexpr int SH = LOG >= 6 ? 0 : 6 - LOG;
+};
+
+__device__ __forceinline__ unsigned fbits(float v) { return __builtin_bit_cast(unsigned, v); }
+__device__ __forceinline__ float bitsf(unsigned v) { return __builtin_bit_cast(float, v); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int kDppRowMirror = 0x140;       // lane l of a 16-lane row takes lane 15 - l
+constexpr int kDppRowHalfMirror = 0x141;   // lane l of an 8-lane half row takes lane 7 - l
+constexpr int kDppQuadMirror = 3 | (2 << 2) | (1 << 4) | (0 << 6);
+constexpr int kDppQuadSwap = 1 | (0 << 2) | (3 << 4) | (2 << 6);
+
+// one mirrored level: lanes whose bit B is clear keep x, the others keep y; each adds
+// its mirror partner's copy of the value it keeps
+template <int CTRL, int B>
+__device__ __forceinline__ float mirror_level(float x, float y, int lane) {
+    const bool lo = (lane & B) == 0;
+    const float send = lo ? y : x;
+    const float keep = lo ? x : y;
+    return keep + dpp_mov<CTRL>(send);
+}
+
+template <int C, int CTRL, int B, int V>
+__device__ __forceinline__ void mirror_step(float (&v)[V], int lane) {
+    if constexpr (C >= 2) {
+#pragma unroll
+        for (int i = 0; i < C / 2; ++i) v[i] = mirror_level<CTRL, B>(v[i], v[i + C / 2], lane);
+    } else {
+        v[0] += dpp_mov<CTRL>(v[0]);
+    }
+}
+
+template <int C> constexpr int halved() { return C >= 2 ? C / 2 : 1; }
+
+template <int V>
+__device__ __forceinline__ void wave_sum(float (&v)[V], int lane) {
+    static_assert(V >= 4 && (V & (V - 1)) == 0, "power of two");
+    // lanes 32 apart: v[i] keeps value i on lanes 0-31 and value i + V/2 on lanes 32-63
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+        const auto r = __builtin_amdgcn_permlane32_swap(fbits(v[i]), fbits(v[i + V / 2]), false, false);
+        v[i] = bitsf(r[0]) + bitsf(r[1]);
+    }
+    // lanes 16 apart
+#pragma unroll
+    for (int i = 0; i < V / 4; ++i) {
+        const auto r = __builtin_amdgcn_permlane16_swap(fbits(v[i]), fbits(v[i + V / 4]), false, false);
+        v[i] = bitsf(r[0]) + bitsf(r[1]);
+    }
+    constexpr int C0 = V / 4;
+    mirror_step<C0, kDppRowMirror, 8>(v, lane);
+    constexpr int C1 = halved<C0>();
+    mirror_step<C1, kDppRowHalfMirror, 4>(v, lane);
+    constexpr int C2 = halved<C1>();
+    mirror_step<C2, kDppQuadMirror, 2>(v, lane);
+    constexpr int C3 = halved<C2>();
+    mirror_step<C3, kDppQuadSwap, 1>(v, lane);
+}
+
+// --------------------------------------------------------------------------
+// Adjoint chunk aggregates (chunks 1 .. nchunks-1): swept backward over the chunk,
+// q <- exp(Delta_t A) (q + C_t dyg_t), so that q ends as the adjoint that the
+// chunk's own tokens send to the state before it, and the chunk's summed step
+// size (fp64 running total) for its decay exp(A sum Delta).
+template <typename T, int N, bool GATE>
+__global__ void __launch_bounds__(kScanThreads)
+k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
+       const T* __restrict__ Cm, const T* __restrict__ z, const T* __restrict__ dy,
+       float* __restrict__ ws_Q, float* __restrict__ ws_qsdt, BwdArgs ba) {
+    const int D = ba.D;
+    const int d_raw = blockIdx.x * kScanThreads + threadIdx.x;
+    const int d = d_raw < D ? d_raw : D - 1;      // clamped lanes repeat the last channel
+    const unsigned du = (unsigned)d;
+    const int c = blockIdx.y + 1;
+    const int b = blockIdx.z;
+    const int64_t t0 = (int64_t)c * ba.chunk_len;
+    const int64_t t1 = (t0 + ba.chunk_len < ba.L) ? t0 + ba.chunk_len : ba.L;
+    const int clen = (int)(t1 - t0);
+    float A2[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) A2[n] = A[(int64_t)d * N + n] * kLog2e;
+    const float dbias = delta_bias ? delta_bias[d] : 0.0f;
+
+    constexpr int R = kScanTile;
+    constexpr int U = 4;
+    __shared__ float sC[2][R][N];
+    const int tid = threadIdx.x;
+    constexpr int TILE_ELEMS = R * N;
+    constexpr int PER_THREAD = (TILE_ELEMS + kScanThreads - 1) / kScanThreads;
+    const int64_t rowbase = (int64_t)b * ba.L + t0;
+    const T* Cc = Cm + rowbase * N;
+    T tc[PER_THREAD];
+    auto tile_fetch = [&](int rlo) {          // rows [rlo, rlo + R) clamped into the chunk
+#pragma unroll
+        for (int k = 0; k < PER_THREAD; ++k) {
+            const int e0 = tid + k * kScanThreads;
+            const int e = e0 < TILE_ELEMS ? e0 : TILE_ELEMS - 1;
+            int r = rlo + e / N;
+            r = r < 0 ? 0 : (r > clen - 1 ? clen - 1 : r);
+            tc[k] = Cc[(int64_t)r * N + e % N];
+        }
+    };
+    auto tile_store = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < PER_THREAD; ++k) {
+            const int e = tid + k * kScanThreads;
+            if (e < TILE_ELEMS) sC[buf][e / N][e % N] = IO<T>::cvt(tc[k]);
+        }
+    };
+    const T* db = delta + rowbase * D;
+    const T* zb = GATE ? z + rowbase * D : nullptr;
+    const T* yb = dy + rowbase * D;
+    auto ld = [&](const T* base, int r) -> float { return IO<T>::cvt((base + (int64_t)r * D)[du]); };
+
+    float q[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) q[n] = 0.0f;
+    double sdt = 0.0;
+    const int ntiles = (clen + R - 1) / R;
+    tile_fetch((ntiles - 1) * R);
+    tile_store(0);
+    __syncthreads();
+    int buf = 0;
+    for (int k = ntiles - 1; k >= 0; --k) {
+        if (k > 0) tile_fetch((k - 1) * R);
+        const int rlo = k * R;
+        const int rhi = (rlo + R < clen) ? rlo + R : clen;
+        const float* tile = &sC[buf][0][0] - (int64_t)rlo * N;
+        float part = 0.0f;
+        for (int r = rhi - 1; r >= rlo; --r) {
+            const float dt = softplus(ld(db, r) + dbias);
+            float dyg = ld(yb, r);
+            if (GATE) dyg *= silu(ld(zb, r));
+            const float* crow = tile + (int64_t)r * N;
+#pragma unroll
+            for (int n = 0; n < N; ++n) q[n] = exp2_fast(dt * A2[n]) * __builtin_fmaf(crow[n], dyg, q[n]);
+            part += dt;
+            if (((r - rlo) & (U - 1)) == 0) { sdt += (double)part; part = 0.0f; }
+        }
+        sdt += (double)part;
+        if (k > 0) tile_store(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+    }
+    const int64_t ai = ((int64_t)b * (ba.nchunks - 1) + (c - 1)) * D + d;
+    ws_qsdt[ai] = (float)sdt;
+#pragma unroll
+    for (int n = 0; n < N; ++n) ws_Q[ai * N + n] = q[n];
+}
+
+// --------------------------------------------------------------------------
+// The backward sweep of one chunk (Euler write term). One lane owns one (b, d) as
+// in the forward. The chunk is taken in 4-token segments from its end; each segment
+// is first recomputed forward from its checkpoint (the state before it), keeping the
+// five states h_{s-1} .. h_{s+3} in registers, then swept backward. Lanes past the
+// last channel repeat it (identical stores) and are masked out of the channel sums.
+template <typename T, int N, bool CONV, bool GATE>
+__global__ void __launch_bounds__(kScanThreads)
+k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
+      const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
+      const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip, const T* __restrict__ z,
+      const float* __restrict__ ssm_state0, const float* __restrict__ conv_state0,
+      const T* __restrict__ dy, const float* __restrict__ dstate_final, const float* __restrict__ dconv_final,
+      T* __restrict__ dx, T* __restrict__ ddelta, T* __restrict__ dz,
+      const float* __restrict__ ckpt, const float* __restrict__ ws_Q, const float* __restrict__ ws_qsdt,
+      float* __restrict__ ws_dbc,        // [B, L, nblk, 2N] per-workgroup sums of dB, dC
+      float* __restrict__ ws_par,        // [B, nchunks, D, N + 8] per-chunk parameter sums
+      float* __restrict__ ws_dxh,        // [B, nchunks, D, 3] dx of a chunk's last 3 tokens without the next chunk's share
+      float* __restrict__ ws_dc3,        // [B, nchunks, D, 3] conv-input gradient of a chunk's first 3 tokens
+      float* __restrict__ dstate_init, float* __restrict__ dconv_init, BwdArgs ba) {
+    constexpr int S = kCkptEvery;
+    constexpr int V = 2 * N;                      // per token: dB partials, then dC partials
+    using WS = WaveSum<V>;
+    const int D = ba.D;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int d_raw = blockIdx.x * kScanThreads + tid;
+    const float livef = d_raw < D ? 1.0f : 0.0f;
+    const int d = d_raw < D ? d_raw : D - 1;
+    const unsigned du = (unsigned)d;
+    const int c = blockIdx.y, b = blockIdx.z;
+    const int nC = ba.nchunks;
+    const bool last = c == nC - 1;
+    const int64_t L = ba.L;
+    const int64_t t0 = (int64_t)c * ba.chunk_len;
+    const int64_t t1 = (t0 + ba.chunk_len < L) ? t0 + ba.chunk_len : L;
+    const int clen = (int)(t1 - t0);
+    const int64_t bd = (int64_t)b * D + d;
+
+    float A2[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) A2[n] = A[(int64_t)d * N + n] * kLog2e;
+    const float dbias = delta_bias ? delta_bias[d] : 0.0f;
+    const float dsk = Dskip ? Dskip[d] : 0.0f;
+    float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 1.f, cb = 0.f;
+    if (CONV) {
+        w0 = conv_w[d * 4 + 0]; w1 = conv_w[d * 4 + 1]; w2 = conv_w[d * 4 + 2]; w3 = conv_w[d * 4 + 3];
+        cb = conv_b ? conv_b[d] : 0.0f;
+    }
+
+    // adjoint arriving at the chunk's last state from later tokens (and the final state)
+    float gc[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) gc[n] = dstate_final ? dstate_final[bd * N + n] : 0.0f;
+    for (int cc = nC - 1; cc > c; --cc) {
+        const int64_t ai = ((int64_t)b * (nC - 1) + (cc - 1)) * D + d;
+        const float sdt = ws_qsdt[ai];
+#pragma unroll
+        for (int n = 0; n < N; ++n) gc[n] = __builtin_fmaf(exp2_fast(sdt * A2[n]), gc[n], ws_Q[ai * N + n]);
+    }
+
+    float dAacc[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) dAacc[n] = 0.0f;
+    float dDacc = 0.f, dcbacc = 0.f, dbacc = 0.f, dcw0 = 0.f, dcw1 = 0.f, dcw2 = 0.f, dcw3 = 0.f;
+    float dc1 = 0.f, dc2 = 0.f, dc3 = 0.f;       // conv-input gradient at t+1, t+2, t+3
+
+    constexpr int R = kScanTile;
+    static_assert(R % S == 0, "segments do not cross tiles");
+    __shared__ float sbc[2][R][V];
+    __shared__ float red[2][S][4][V];
+    constexpr int TILE_ELEMS = R * N;
+    constexpr int PER_THREAD = (TILE_ELEMS + kScanThreads - 1) / kScanThreads;
+    const int64_t rowbase = (int64_t)b * L + t0;
+    const T* Bc = Bm + rowbase * N;
+    const T* Cc = Cm + rowbase * N;
+    T tb[PER_THREAD], tc[PER_THREAD];
+    auto tile_fetch = [&](int rlo) {
+#pragma unroll
+        for (int k = 0; k < PER_THREAD; ++k) {
+            const int e0 = tid + k * kScanThreads;
+            const int e = e0 < TILE_ELEMS ? e0 : TILE_ELEMS - 1;
+            int r = rlo + e / N;
+            r = r > clen - 1 ? clen - 1 : r;
+            const int64_t off = (int64_t)r * N + e % N;
+            tb[k] = Bc[off];
+            tc[k] = Cc[off];
+        }
+    };
+    auto tile_store = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < PER_THREAD; ++k) {
+            const int e = tid + k * kScanThreads;
+            if (e < TILE_ELEMS) {
+                sbc[buf][e / N][e % N] = IO<T>::cvt(tb[k]);
+                sbc[buf][e / N][N + e % N] = IO<T>::cvt(tc[k]);
+            }
+        }
+    };
+    const int64_t rowoff = rowbase * D;            // element offset of the chunk's first token
+    auto ld = [&](const T* base, int r) -> T { return (base + rowoff + (int64_t)r * D)[du]; };
+    // x at chunk-relative row r (r >= -3): before token 0 it is the initial history
+    auto xat = [&](int r) -> float {
+        const int64_t t = t0 + r;
+        if (t >= 0) return IO<T>::cvt(ld(x, r));
+        return conv_state0 ? conv_state0[bd * 3 + (3 + t)] : 0.0f;
+    };
+
+    const int ntiles = (clen + R - 1) / R;
+    tile_fetch((ntiles - 1) * R);
+    tile_store(0);
+    __syncthreads();
+    int buf = 0, rp = 0;
+    for (int k = ntiles - 1; k >= 0; --k) {
+        if (k > 0) tile_fetch((k - 1) * R);
+        const int rlo = k * R;
+        const int rhi = (rlo + R < clen) ? rlo + R : clen;
+        const float* tile = &sbc[buf][0][0] - (int64_t)rlo * V;
+        for (int s = rlo + ((rhi - 1 - rlo) / S) * S; s >= rlo; s -= S) {
+            const int ns = (s + S < rhi) ? S : rhi - s;      // tokens in this segment (uniform)
+            const int64_t gs = t0 + s;
+            // the state before the segment
+            float hs[S + 1][N];
+            if (gs == 0) {
+#pragma unroll
+                for (int n = 0; n < N; ++n) hs[0][n] = ssm_state0 ? ssm_state0[bd * N + n] : 0.0f;
+            } else {
+                const vf4* src = reinterpret_cast<const vf4*>(ckpt + (((int64_t)b * ba.nck + gs / S - 1) * D + d) * N);
+#pragma unroll
+                for (int q = 0; q < N / 4; ++q) {
+                    const vf4 v = src[q];
+                    hs[0][4 * q] = v.x; hs[0][4 * q + 1] = v.y; hs[0][4 * q + 2] = v.z; hs[0][4 * q + 3] = v.w;
+                }
+            }
+            // inputs of the segment; xw[j] = x at row s - 3 + j
+            float xw[S + 3];
+            T draw[S], zraw[S], yraw[S];
+#pragma unroll
+            for (int j = 0; j < S + 3; ++j) xw[j] = (CONV || j >= 3) && j < ns + 3 ? xat(s - 3 + j) : 0.0f;
+#pragma unroll
+            for (int i = 0; i < S; ++i) {
+                const int r = s + (i < ns ? i : ns - 1);
+                draw[i] = ld(delta, r);
+                yraw[i] = ld(dy, r);
+                zraw[i] = GATE ? ld(z, r) : T(0);
+            }
+            // forward over the segment
+            float dtv[S], uv[S], cv[S], vv[S];
+#pragma unroll
+            for (int i = 0; i < S; ++i) {
+                if (CONV) {
+                    cv[i] = __builtin_fmaf(w3, xw[i + 3], __builtin_fmaf(w2, xw[i + 2], __builtin_fmaf(w1, xw[i + 1], __builtin_fmaf(w0, xw[i], cb))));
+                    uv[i] = silu(cv[i]);
+                } else {
+                    cv[i] = 0.0f;
+                    uv[i] = xw[i + 3];
+                }
+                vv[i] = IO<T>::cvt(draw[i]) + dbias;
+                dtv[i] = softplus(vv[i]);
+                const float* brow = tile + (int64_t)(s + i) * V;
+                const float wv = dtv[i] * uv[i];
+#pragma unroll
+                for (int n = 0; n < N; ++n)
+                    hs[i + 1][n] = __builtin_fmaf(exp2_fast(dtv[i] * A2[n]), hs[i][n], wv * brow[n]);
+            }
+            // backward over the segment
+#pragma unroll
+            for (int i = S - 1; i >= 0; --i) {
+                if (i >= ns) continue;                     // uniform: only the sequence's last segment is short
+                const int r = s + i;
+                const int64_t row = (int64_t)r * D;      // relative to the chunk's first token
+                const float* brow = tile + (int64_t)r * V;
+                const float* crow = brow + N;
+                float yv = dsk * uv[i];
+#pragma unroll
+                for (int n = 0; n < N; ++n) yv = __builtin_fmaf(crow[n], hs[i + 1][n], yv);
+                const float dyv = IO<T>::cvt(yraw[i]);
+                float dyg = dyv;
+                if (GATE) {
+                    const float zt = IO<T>::cvt(zraw[i]);
+                    const float sz = rcp_fast(1.0f + exp2_fast(-kLog2e * zt));
+                    dyg = dyv * zt * sz;
+                    const float dzv = dyv * yv * sz * __builtin_fmaf(zt, 1.0f - sz, 1.0f);
+                    Buf<T>(dz + rowoff + row).st(IO<T>::bits(dzv), du * (unsigned)sizeof(T), 0u);
+                }
+                dDacc = __builtin_fmaf(dyg, uv[i], dDacc);
+                const float dygm = dyg * livef;
+                const float dtum = dtv[i] * uv[i] * livef;
+                float vals[V];
+                float sgB = 0.0f, sA = 0.0f;
+#pragma unroll
+                for (int n = 0; n < N; ++n) {
+                    const float g = __builtin_fmaf(crow[n], dyg, gc[n]);
+                    vals[N + n] = dygm * hs[i + 1][n];
+                    vals[n] = g * dtum;
+                    sgB = __builtin_fmaf(g, brow[n], sgB);
+                    const float a = exp2_fast(dtv[i] * A2[n]);
+                    const float gq = g * (a * hs[i][n]);
+                    sA = __builtin_fmaf(A2[n], gq, sA);
+                    dAacc[n] = __builtin_fmaf(dtv[i], gq, dAacc[n]);
+                    gc[n] = a * g;
+                }
+                const float dDelta = __builtin_fmaf(sA, kLn2, uv[i] * sgB);
+                const float dU = __builtin_fmaf(dsk, dyg, dtv[i] * sgB);
+                const float ddel = dDelta * rcp_fast(1.0f + exp2_fast(-kLog2e * vv[i]));   // softplus' = sigmoid
+                Buf<T>(ddelta + rowoff + row).st(IO<T>::bits(ddel), du * (unsigned)sizeof(T), 0u);
+                dbacc += ddel;
+                float dxv;
+                if (CONV) {
+                    const float sc = rcp_fast(1.0f + exp2_fast(-kLog2e * cv[i]));
+                    const float dc = dU * sc * __builtin_fmaf(cv[i], 1.0f - sc, 1.0f);    // SiLU'
+                    dcbacc += dc;
+                    dcw0 = __builtin_fmaf(dc, xw[i], dcw0);
+                    dcw1 = __builtin_fmaf(dc, xw[i + 1], dcw1);
+                    dcw2 = __builtin_fmaf(dc, xw[i + 2], dcw2);
+                    dcw3 = __builtin_fmaf(dc, xw[i + 3], dcw3);
+                    dxv = __builtin_fmaf(w3, dc, __builtin_fmaf(w2, dc1, __builtin_fmaf(w1, dc2, w0 * dc3)));
+                    dc3 = dc2; dc2 = dc1; dc1 = dc;
+                    const int64_t t = t0 + r;
+                    if (last && dconv_final && t >= L - 3) dxv += dconv_final[bd * 3 + (t - (L - 3))];
+                } else {
+                    dxv = dU;
+                }
+                if (CONV && !last && r >= clen - 3)
+                    ws_dxh[(((int64_t)b * nC + c) * D + d) * 3 + (r - (clen - 3))] = dxv;
+                else
+                    Buf<T>(dx + rowoff + row).st(IO<T>::bits(dxv), du * (unsigned)sizeof(T), 0u);
+                // channel sums of this token's dB/dC partials
+                wave_sum<V>(vals, lane);
+                if ((lane & ((1 << WS::SH) - 1)) == 0) {
+#pragma unroll
+                    for (int q = 0; q < WS::R; ++q) red[rp][i][wave][q + (lane >> WS::SH) * WS::R] = vals[q];
+                }
+            }
+            __syncthreads();
+            for (int e = tid; e < ns * V; e += kScanThreads) {
+                const int i = e / V, j = e % V;
+                const float sum = (red[rp][i][0][j] + red[rp][i][1][j]) + (red[rp][i][2][j] + red[rp][i][3][j]);
+                ws_dbc[((rowbase + s + i) * ba.nblk + blockIdx.x) * V + j] = sum;
+            }
+            rp ^= 1;
+        }
+        if (k > 0) tile_store(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+    }
+
+    float* pp = ws_par + (((int64_t)b * nC + c) * D + d) * (N + 8);
+#pragma unroll
+    for (int n = 0; n < N; ++n) pp[n] = dAacc[n];
+    pp[N] = dDacc;
+    pp[N + 1] = dcw0; pp[N + 2] = dcw1; pp[N + 3] = dcw2; pp[N + 4] = dcw3;
+    pp[N + 5] = dcbacc;
+    pp[N + 6] = dbacc;
+    if (CONV && c > 0) {
+        float* e3 = ws_dc3 + (((int64_t)b * nC + c) * D + d) * 3;
+        e3[0] = dc1; e3[1] = dc2; e3[2] = dc3;
+    }
+    if (c == 0) {
+        if (dstate_init) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) dstate_init[bd * N + n] = gc[n];
+        }
+        if (CONV && dconv_init) {
+            // history positions -3, -2, -1: x_{-3+k'} feeds tokens 0..2 through tap k
+            float p[3] = {w0 * dc1, __builtin_fmaf(w1, dc1, w0 * dc2),
+                          __builtin_fmaf(w2, dc1, __builtin_fmaf(w1, dc2, w0 * dc3))};
+            if (last && dconv_final && L < 3) {
+#pragma unroll
+                for (int k2 = 0; k2 < 3; ++k2)
+                    if (L + k2 < 3) p[L + k2] += dconv_final[bd * 3 + k2];
+            }
+            dconv_init[bd * 3 + 0] = p[0]; dconv_init[bd * 3 + 1] = p[1]; dconv_init[bd * 3 + 2] = p[2];
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
+// Fixed-order sums of the partials.
+
+// dB, dC [B, L, N]: sum over the workgroups along d
+template <int N>
+__global__ void __launch_bounds__(256)
+k_bwd_sum_dbc(const float* __restrict__ ws_dbc, float* __restrict__ dB, float* __restrict__ dC, int64_t rows, int nblk) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;    // over rows * 2N
+    if (i >= rows * 2 * N) return;
+    const int64_t row = i / (2 * N);
+    const int j = (int)(i % (2 * N));
+    float s = 0.0f;
+    for (int k = 0; k < nblk; ++k) s += ws_dbc[(row * nblk + k) * 2 * N + j];
+    if (j < N) dB[row * N + j] = s;
+    else dC[row * N + (j - N)] = s;
+}
+
+// parameter gradients: sum over (batch row, chunk)
+template <int N>
+__global__ void __launch_bounds__(256)
+k_bwd_sum_par(const float* __restrict__ ws_par, int parts, int D, float* __restrict__ dA, float* __restrict__ dD,
+              float* __restrict__ dconv_w, float* __restrict__ dconv_b, float* __restrict__ ddelta_bias) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;    // over D * (N + 7)
+    if (i >= (int64_t)D * (N + 7)) return;
+    const int d = (int)(i / (N + 7));
+    const int k = (int)(i % (N + 7));
+    float s = 0.0f;
+    for (int p = 0; p < parts; ++p) s += ws_par[((int64_t)p * D + d) * (N + 8) + k];
+    if (k < N) dA[(int64_t)d * N + k] = s;
+    else if (k == N) { if (dD) dD[d] = s; }
+    else if (k <= N + 4) { if (dconv_w) dconv_w[d * 4 + (k - N - 1)] = s; }
+    else if (k == N + 5) { if (dconv_b) dconv_b[d] = s; }
+    else { if (ddelta_bias) ddelta_bias[d] = s; }
+}
+
+// dx of each chunk's last 3 tokens: the chunk's own share plus the next chunk's
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_bwd_dx_halo(const float* __restrict__ ws_dxh, const float* __restrict__ ws_dc3, const float* __restrict__ conv_w,
+              T* __restrict__ dx, int64_t L, int64_t chunk_len, int nC, int D, int Bsz) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;    // over B * (nC - 1) * D
+    if (i >= (int64_t)Bsz * (nC - 1) * D) return;
+    const int d = (int)(i % D);
+    const int c = (int)((i / D) % (nC - 1));
+    const int b = (int)(i / ((int64_t)D * (nC - 1)));
+    const float w0 = conv_w[d * 4 + 0], w1 = conv_w[d * 4 + 1], w2 = conv_w[d * 4 + 2];
+    const float* p = ws_dxh + (((int64_t)b * nC + c) * D + d) * 3;
+    const float* e = ws_dc3 + (((int64_t)b * nC + c + 1) * D + d) * 3;
+    const int64_t t1 = (int64_t)(c + 1) * chunk_len;
+    const float v0 = __builtin_fmaf(w0, e[0], p[0]);
+    const float v1 = __builtin_fmaf(w1, e[0], __builtin_fmaf(w0, e[1], p[1]));
+    const float v2 = __builtin_fmaf(w2, e[0], __builtin_fmaf(w1, e[1], __builtin_fmaf(w0, e[2], p[2])));
+    IO<T>::st(dx + ((int64_t)b * L + t1 - 3) * D + d, v0);
+    IO<T>::st(dx + ((int64_t)b * L + t1 - 2) * D + d, v1);
+    IO<T>::st(dx + ((int64_t)b * L + t1 - 1) * D + d, v2);
+}
+
+// --------------------------------------------------------------------------
+// launcher
+
+template <typename T, int N, bool CONV, bool GATE>
+static hipError_t launch_bwd_t(const LaunchBwd& q) {
+    const LaunchScan& p = q.f;
+    hipStream_t st = static_cast<hipStream_t>(p.stream);
+    const T* x = static_cast<const T*>(p.x);
+    const T* dl = static_cast<const T*>(p.delta);
+    const T* z = static_cast<const T*>(p.z);
+    const T* Bm = static_cast<const T*>(p.B);
+    const T* Cm = static_cast<const T*>(p.C);
+    const unsigned gx = (unsigned)((p.D + kScanThreads - 1) / kScanThreads);
+    const int nC = p.nchunks;
+    ScanArgs sa{p.L, p.chunk_len, (int)p.D, nC, q.nck};
+    BwdArgs ba{p.L, p.chunk_len, (int)p.D, nC, q.nck, (int)gx};
+    if (nC > 1) {
+        hipLaunchKernelGGL((k_agg<T, N, CONV, false>), dim3(gx, nC - 1, (unsigned)p.batch), dim3(kScanThreads), 0, st,
+                           x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A, Bm, p.ssm_state, p.conv_state, p.ws_S,
+                           p.ws_sdt, p.ws_h0, p.ws_c0, sa);
+    }
+    hipLaunchKernelGGL((k_scan<T, N, CONV, false, false, true>), dim3(gx, nC, (unsigned)p.batch), dim3(kScanThreads), 0,
+                       st, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A, Bm, Cm, p.Dskip, nullptr,
+                       static_cast<T*>(nullptr), p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0,
+                       q.ws_ckpt, sa);
+    const T* dy = static_cast<const T*>(q.dy);
+    if (nC > 1) {
+        hipLaunchKernelGGL((k_bagg<T, N, GATE>), dim3(gx, nC - 1, (unsigned)p.batch), dim3(kScanThreads), 0, st,
+                           dl, p.delta_bias, p.A, Cm, z, dy, q.ws_Q, q.ws_qsdt, ba);
+    }
+    hipExtLaunchKernelGGL((k_bwd<T, N, CONV, GATE>), dim3(gx, nC, (unsigned)p.batch), dim3(kScanThreads), 0, st,
+                          static_cast<hipEvent_t>(p.ev_main[0]), static_cast<hipEvent_t>(p.ev_main[1]), 0,
+                          x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A, Bm, Cm, p.Dskip, z, p.ssm_state, p.conv_state,
+                          dy, q.dstate_final, q.dconv_final, static_cast<T*>(q.dx), static_cast<T*>(q.ddelta),
+                          static_cast<T*>(q.dz), q.ws_ckpt, q.ws_Q, q.ws_qsdt, q.ws_dbc, q.ws_par, q.ws_dxh, q.ws_dc3,
+                          q.dstate_init, q.dconv_init, ba);
+    const int64_t rows = p.batch * p.L;
+    hipLaunchKernelGGL((k_bwd_sum_dbc<N>), dim3((unsigned)((rows * 2 * N + 255) / 256)), dim3(256), 0, st,
+                       q.ws_dbc, q.dB, q.dC, rows, (int)gx);
+    hipLaunchKernelGGL((k_bwd_sum_par<N>), dim3((unsigned)((p.D * (N + 7) + 255) / 256)), dim3(256), 0, st,
+                       q.ws_par, (int)(p.batch * nC), (int)p.D, q.dA, q.dD, q.dconv_w, q.dconv_b, q.ddelta_bias);
+    if (CONV && nC > 1) {
+        const int64_t n = p.batch * (nC - 1) * p.D;
+        hipLaunchKernelGGL((k_bwd_dx_halo<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                           q.ws_dxh, q.ws_dc3, p.conv_w, static_cast<T*>(q.dx), p.L, p.chunk_len, nC, (int)p.D,
+                           (int)p.batch);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int N>
+static hipError_t dispatch_bwd_flags(const LaunchBwd& q) {
+    const bool conv = q.f.conv_w != nullptr, gate = q.f.z != nullptr;
+    if (conv && gate) return launch_bwd_t<T, N, true, true>(q);
+    if (conv) return launch_bwd_t<T, N, true, false>(q);
+    if (gate) return launch_bwd_t<T, N, false, true>(q);
+    return launch_bwd_t<T, N, false, false>(q);
+}
+
+template <typename T>
+static hipError_t dispatch_bwd(const LaunchBwd& q) {
+    switch (q.f.N) {
+        case 4: return dispatch_bwd_flags<T, 4>(q);
+        case 8: return dispatch_bwd_flags<T, 8>(q);
+        case 16: return dispatch_bwd_flags<T, 16>(q);
+        case 32: return dispatch_bwd_flags<T, 32>(q);
+        case 64: return dispatch_bwd_flags<T, 64>(q);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace selscan

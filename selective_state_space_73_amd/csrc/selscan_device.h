@@ -82,6 +82,8 @@ __device__ __forceinline__ float zoh_coef(float a, float t, float dt, float iA) 
     return __builtin_fabsf(t) < kZohSeriesT ? small : big;
 }
 
+typedef float vf4 __attribute__((ext_vector_type(4)));
+
 template <typename T> struct IO;
 template <> struct IO<float> {
     static __device__ __forceinline__ float cvt(float v) { return v; }
@@ -134,14 +136,21 @@ template <> struct Buf<float> {
 // ---------------------------------------------------------------------------
 // The main pass: full forward over one chunk with outputs, from the chunk's exact
 // initial state (the caller's state for chunk 0, else the carry folded from the
-// aggregates of the earlier chunks).
+// aggregates of the earlier chunks). CK = true: checkpoint mode, no readout and no
+// outputs, the state written every kCkptEvery tokens instead, states left untouched.
 
 struct ScanArgs {
     int64_t L;            // sequence length
-    int64_t chunk_len;    // tokens per chunk
+    int64_t chunk_len;    // tokens per chunk (a multiple of kScanTile when nchunks > 1)
     int D;                // channels
     int nchunks;
+    int64_t nck;          // checkpoint slots per batch row (checkpoint mode): L / kCkptEvery
 };
+
+// Checkpoint mode of the main pass (used by the backward): the state after every
+// kCkptEvery-th token is written to a [B, L / kCkptEvery, D, N] buffer, slot j
+// holding the state after token kCkptEvery*j + kCkptEvery - 1.
+constexpr int kCkptEvery = 4;
 
 // Register budget of the scan kernel: three waves per SIMD (<= 168 VGPRs) for
 // N <= 16, measured faster than the compiler's own choice (two waves at ~240
@@ -150,14 +159,14 @@ struct ScanArgs {
 // (Without the conv the schedule under that cap spills, so it is left free; the
 // zero-order hold's longer per-state chain with N more registers of 1/A is held to
 // two waves.)
-template <int N, bool CONV, bool ZOH> constexpr int scan_waves_per_eu() {
-    return N > 16 ? 1 : ZOH ? 2 : CONV ? 3 : 1;
+template <int N, bool CONV, bool ZOH, bool CK> constexpr int scan_waves_per_eu() {
+    return N > 16 ? 1 : (ZOH || CK) ? 2 : CONV ? 3 : 1;
 }
 
 // Zero-order hold: the write coefficient (exp(Delta A) - 1) / A comes from the decay
 // already computed (zoh_coef: one fma, or a short series where Delta A is small).
-template <typename T, int N, bool CONV, bool GATE, bool ZOH>
-__global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<N, CONV, ZOH>())))
+template <typename T, int N, bool CONV, bool GATE, bool ZOH, bool CK = false>
+__global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<N, CONV, ZOH, CK>())))
 k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
        const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
        const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
@@ -168,7 +177,9 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
        const float* __restrict__ ws_sdt,     // [B, nchunks-1, D] summed step sizes
        const float* __restrict__ ws_h0,      // [B, D, N] copy of the initial state (nchunks > 1)
        const float* __restrict__ ws_c0,      // [B, D, K-1] copy of the initial conv history (nchunks > 1)
+       float* __restrict__ ckpt,             // CK: [B, nck, D, N] state checkpoints
        ScanArgs sa) {
+    static_assert(!(CK && GATE), "checkpoint mode has no gate");
     const int D = sa.D;
     const int d_raw = blockIdx.x * kScanThreads + threadIdx.x;
     // lanes past the last channel work on the last channel: they compute and store
@@ -249,7 +260,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     constexpr int U = 4;
     constexpr int R = kScanTile;
     static_assert(R % (2 * U) == 0, "a tile holds whole pairs of groups");
-    constexpr int NB = 2 * N;                           // staged values per token (B row, C row)
+    constexpr int NB = CK ? N : 2 * N;                  // staged values per token (B row, C row)
     __shared__ float sbc[2][R][NB];
     const int tid = threadIdx.x;
     const int nrows = (int)(t1 - t0);
@@ -259,9 +270,9 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     const T* xb = x + rowbase * D;
     const T* db = delta + rowbase * D;
     const T* zb = GATE ? z + rowbase * D : nullptr;
-    T* yb = y + rowbase * D;
+    T* yb = CK ? nullptr : y + rowbase * D;
     const T* Bb = Bm + rowbase * N;
-    const T* Cb = Cm + rowbase * N;
+    const T* Cb = CK ? nullptr : Cm + rowbase * N;
 
     // cooperative tile load: element e of the tile is (row e / N, state e % N)
     constexpr int TILE_ELEMS = R * N;
@@ -271,7 +282,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         // the tile's rows are contiguous in B and C: one uniform base, a 32-bit offset per element
         const int rlast = nrows - 1 - r0;
         const T* Bt = Bb + (int64_t)r0 * N;
-        const T* Ct = Cb + (int64_t)r0 * N;
+        const T* Ct = CK ? nullptr : Cb + (int64_t)r0 * N;
 #pragma unroll
         for (int k = 0; k < PER_THREAD; ++k) {
             const int e0 = tid + k * kScanThreads;
@@ -279,7 +290,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
             const int r = e / N < rlast ? e / N : rlast;
             const int off = r * N + e % N;
             tb[k] = Bt[off];
-            tc[k] = Ct[off];
+            if (!CK) tc[k] = Ct[off];
         }
     };
     auto tile_store = [&](int buf) {
@@ -288,7 +299,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
             const int e = tid + k * kScanThreads;
             if (e < TILE_ELEMS) {
                 sbc[buf][e / N][e % N] = IO<T>::cvt(tb[k]);
-                sbc[buf][e / N][N + e % N] = IO<T>::cvt(tc[k]);
+                if (!CK) sbc[buf][e / N][N + e % N] = IO<T>::cvt(tc[k]);
             }
         }
     };
@@ -317,8 +328,10 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         float bv[N], cv[N], a[N], t[N];
 #pragma unroll
         for (int n = 0; n < N; ++n) bv[n] = bct[n];
+        if constexpr (!CK) {
 #pragma unroll
-        for (int n = 0; n < N; ++n) cv[n] = bct[N + n];
+            for (int n = 0; n < N; ++n) cv[n] = bct[N + n];
+        }
 #pragma unroll
         for (int n = 0; n < N; ++n) {
             t[n] = p.dt * A2[n];
@@ -332,15 +345,24 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 #pragma unroll
             for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(a[n], h[n], p.wv * bv[n]);
         }
-        float ya = dsk * p.u, yc = 0.0f;
+        if constexpr (!CK) {
+            float ya = dsk * p.u, yc = 0.0f;
 #pragma unroll
-        for (int n = 0; n < N; n += 2) {
-            ya = __builtin_fmaf(cv[n], h[n], ya);
-            yc = __builtin_fmaf(cv[n + 1], h[n + 1], yc);
+            for (int n = 0; n < N; n += 2) {
+                ya = __builtin_fmaf(cv[n], h[n], ya);
+                yc = __builtin_fmaf(cv[n + 1], h[n + 1], yc);
+            }
+            const float yv = (ya + yc) * p.g;
+            // lanes past the last channel were clamped to it and store the same value
+            Buf<T>(yb + (int64_t)r * D).st(IO<T>::bits(yv), voff, 0u);
         }
-        const float yv = (ya + yc) * p.g;
-        // lanes past the last channel were clamped to it and store the same value
-        Buf<T>(yb + (int64_t)r * D).st(IO<T>::bits(yv), voff, 0u);
+    };
+    // checkpoint after chunk-relative row r (CK; the caller checks the spacing)
+    auto store_ckpt = [&](int r) {
+        const int64_t slot = (t0 + r + 1) / kCkptEvery - 1;
+        vf4* dst = reinterpret_cast<vf4*>(ckpt + (((int64_t)b * sa.nck + slot) * D + d) * N);
+#pragma unroll
+        for (int k = 0; k < N / 4; ++k) dst[k] = vf4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
     };
     auto token = [&](T xraw, T draw, T zraw, const float* bct, int r) {
         const Pro p = prologue(xraw, draw, zraw);
@@ -352,6 +374,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         for (int i = 0; i < U; ++i) p[i] = prologue(gx[i], gd[i], gz[i]);
 #pragma unroll
         for (int i = 0; i < U; ++i) update(p[i], tile_rows + i * NB, r0 + i);
+        if constexpr (CK) store_ckpt(r0 + U - 1);      // r0 + U is a multiple of kCkptEvery
     };
     T gx0[U], gd0[U], gz0[U], gx1[U], gd1[U], gz1[U];
     auto load_group = [&](int r0, T* gx, T* gd, T* gz) {
@@ -391,6 +414,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
             for (int r = tt; r < nrows; ++r) {
                 const int64_t off = (int64_t)r * D;
                 token((xb + off)[du], (db + off)[du], GATE ? (zb + off)[du] : T(0), tile + (r - tt) * NB, r);
+                if (CK && ((t0 + r + 1) % kCkptEvery) == 0) store_ckpt(r);
             }
         }
         if (more) tile_store(buf ^ 1);
@@ -398,7 +422,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         buf ^= 1;
     }
 
-    if (c == sa.nchunks - 1) {
+    if (!CK && c == sa.nchunks - 1) {
         if (ssm_state) {
 #pragma unroll
             for (int n = 0; n < N; ++n) ssm_state[bd * N + n] = h[n];
@@ -739,8 +763,6 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
 // summed across the quad with DPP; lane q < 3 holds conv history entry q and
 // lane 3 the new input, so the shifted history is one quad rotation away.
 
-typedef float vf4 __attribute__((ext_vector_type(4)));
-
 // DPP quad permutations: xor-1, xor-2 and "take lane q+1" (lane 3 keeps its own)
 constexpr int kQuadXor1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);
 constexpr int kQuadXor2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);
@@ -876,7 +898,7 @@ static hipError_t launch_scan_t(const LaunchScan& p) {
     const T* z = static_cast<const T*>(p.z);
     T* y = static_cast<T*>(p.y);
     hipStream_t st = static_cast<hipStream_t>(p.stream);
-    ScanArgs sa{p.L, p.chunk_len, (int)p.D, p.nchunks};
+    ScanArgs sa{p.L, p.chunk_len, (int)p.D, p.nchunks, 0};
     const unsigned gx = (unsigned)((p.D + kScanThreads - 1) / kScanThreads);
     if (p.nchunks > 1) {
         hipExtLaunchKernelGGL((k_agg<T, N, CONV, ZOH>), dim3(gx, p.nchunks - 1, (unsigned)p.batch),
@@ -889,7 +911,7 @@ static hipError_t launch_scan_t(const LaunchScan& p) {
                           dim3(kScanThreads), 0, st, static_cast<hipEvent_t>(p.ev_main[0]),
                           static_cast<hipEvent_t>(p.ev_main[1]), 0, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
                           static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip, z, y, p.ssm_state,
-                          p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, sa);
+                          p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, nullptr, sa);
     return hipGetLastError();
 }
 

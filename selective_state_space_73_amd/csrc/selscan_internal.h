@@ -36,11 +36,31 @@ struct LaunchScan {
     void* ev_main[2];  // optional hipEvent_t pair recorded around the main kernel
 };
 
+// The backward: the forward's launch description (its ssm_state / conv_state are
+// the initial states, read only) plus the gradients and the backward workspace.
+struct LaunchBwd {
+    LaunchScan f;
+    const void* dy; const float* dstate_final; const float* dconv_final;
+    void* dx; void* ddelta; void* dz;
+    float* dB; float* dC; float* dA; float* dD; float* dconv_w; float* dconv_b; float* ddelta_bias;
+    float* dstate_init; float* dconv_init;
+    float* ws_ckpt;   // [B, nck, D, N] state after every 4th token
+    float* ws_Q;      // [B, nchunks-1, D, N] adjoint aggregates of chunks 1..nchunks-1
+    float* ws_qsdt;   // [B, nchunks-1, D] their summed step sizes
+    float* ws_dbc;    // [B, L, nblk, 2N] per-workgroup sums of dB, dC
+    float* ws_par;    // [B, nchunks, D, N + 8] per-chunk parameter sums
+    float* ws_dxh;    // [B, nchunks, D, 3] partial dx of each chunk's last 3 tokens
+    float* ws_dc3;    // [B, nchunks, D, 3] conv-input gradient of each chunk's first 3 tokens
+    int64_t nck;      // checkpoint slots per batch row
+};
+
 // One entry per instantiation unit (I/O dtype x write rule); step selects the
 // decode-step kernel instead of the full-sequence scan.
 hipError_t launch_f32_euler(const LaunchScan& p, bool step);
 hipError_t launch_f32_zoh(const LaunchScan& p, bool step);
 hipError_t launch_bf16_euler(const LaunchScan& p, bool step);
 hipError_t launch_bf16_zoh(const LaunchScan& p, bool step);
+hipError_t launch_bwd_f32_euler(const LaunchBwd& p);
+hipError_t launch_bwd_bf16_euler(const LaunchBwd& p);
 
 }  // namespace selscan

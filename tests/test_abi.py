@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["ss_workspace_bytes", "ss_conv_scan_fwd", "ss_step", "ss_status_str",
-                                           "ss_last_error", "ss_version", "ss_time_next_call"])
+                                           "ss_last_error", "ss_version", "ss_time_next_call",
+                                           "ss_bwd_workspace_bytes", "ss_conv_scan_bwd"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -35,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ss.ss_version() == 2
+    assert ss.ss_version() == 3
     assert ss.lib.ss_status_str(0) == b"ok"
     assert b"workspace" in ss.lib.ss_status_str(3)
 
@@ -43,6 +44,7 @@ def test_version_and_status_strings():
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(ss.ss_dims) == 40
     assert ctypes.sizeof(ss.ss_args) == 13 * ctypes.sizeof(ctypes.c_void_p)
+    assert ctypes.sizeof(ss.ss_grads) == 15 * ctypes.sizeof(ctypes.c_void_p)
 
 
 def _dims(**kw):
@@ -146,3 +148,51 @@ def test_workspace_alignment_and_overlap_checked():
     assert _call(d, _fake_args(), (1 << 45) + 4, need) == 1
     a = _fake_args()
     assert _call(d, a, a.x, need) == 1
+
+
+# ----------------------------------------------------------------------------- backward
+
+def _fake_grads(**kw):
+    base = 1 << 44
+    g = {}
+    for i, name in enumerate(["dy", "dstate_final", "dconv_final", "dx", "ddelta", "dz", "dB", "dC", "dA", "dDskip",
+                              "dconv_w", "dconv_b", "ddelta_bias", "dstate_init", "dconv_init"]):
+        g[name] = base + i * (1 << 32)
+    g.update(kw)
+    return ss.ss_grads(**g)
+
+
+def _bwd(dims, args, grads, ws=(1 << 47), ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = ss.ss_bwd_workspace_bytes(dims)
+    return ss.lib.ss_conv_scan_bwd(ctypes.byref(dims), ctypes.byref(args), ctypes.byref(grads), ws, ws_bytes, None)
+
+
+def test_bwd_workspace_covers_checkpoints():
+    d = _dims(batch=2, seqlen=4096, d_inner=64, d_state=16)
+    # at least the state after every 4th token
+    assert ss.ss_bwd_workspace_bytes(d) >= 2 * (4096 // 4) * 64 * 16 * 4
+    assert ss.ss_bwd_workspace_bytes(_dims(batch=0)) == 0
+
+
+@pytest.mark.parametrize("field", ["dy", "dx", "ddelta", "dB", "dC", "dA"])
+def test_bwd_null_required_gradient_rejected(field):
+    assert _bwd(_dims(), _fake_args(), _fake_grads(**{field: None})) == 1
+    assert field in ss.lib.ss_last_error().decode()
+
+
+def test_bwd_rejects_zoh_and_inconsistent_optional_pieces():
+    z = ss.make_dims(2, 16, 64, 16, ss.SS_F32, discretization=ss.SS_ZOH)
+    assert _bwd(z, _fake_args(), _fake_grads()) == 2
+    assert _bwd(_dims(), _fake_args(), _fake_grads(dz=None)) == 1                 # z given, dz missing
+    assert _bwd(_dims(), _fake_args(z=None), _fake_grads()) == 1                  # dz given, no z
+    assert _bwd(_dims(), _fake_args(conv_w=None, conv_state=None), _fake_grads()) == 1   # conv grads, no conv
+
+
+def test_bwd_rejects_overlaps_and_small_workspace():
+    a, g = _fake_args(), _fake_grads()
+    assert _bwd(_dims(), a, _fake_grads(dx=a.x + 4)) == 1
+    assert "overlaps" in ss.lib.ss_last_error().decode()
+    assert _bwd(_dims(), a, _fake_grads(dB=g.dC + 4)) == 1
+    assert _bwd(_dims(), a, g, ws_bytes=ss.ss_bwd_workspace_bytes(_dims()) - 1) == 3
+    assert _bwd(_dims(), a, g, ws=(1 << 47) + 8) == 1                               # misaligned workspace
