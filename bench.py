@@ -2,7 +2,7 @@
 """Benchmark of the selective-scan (S6) forward path and decode step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|train|block]
-                    [--no-decode] [--no-cpu] [--zoh-steps K]
+                    [--no-decode] [--no-cpu] [--zoh-steps K] [--bwd-steps K]
 
 A step is one ss_conv_scan_fwd call over the whole workload (conv1d + SiLU,
 softplus step, discretisation, scan, C.h + D.u readout, SiLU(z) gate), with
@@ -18,6 +18,8 @@ parameters. Prints one JSON line:
   view (algorithmic bytes / duration vs 8 TB/s) is given as hbm_view.
 * zoh: the same workload and inputs with the zero-order-hold write term, its
   step rate and main-kernel roofline on the same model.
+* bwd: the backward (ss_conv_scan_bwd) on the same inputs with a seeded output
+  gradient: whole-call time and the backward-sweep kernel's roofline.
 * decode: 64 streams x 32 layers x 256 token steps (d_inner 8192, d_state 16),
   one ss_step per layer and token, timed end to end eagerly and replayed from
   HIP graphs (one graph per token step over the 32 layers); its roofline is
@@ -80,6 +82,18 @@ def instr_per_row(N: int, zoh: bool = False) -> int:
 
 def trans_per_row(N: int) -> int:
     return 6 + N
+
+
+def bwd_instr_per_row(N: int) -> int:
+    """Algorithmic fp32 VALU instructions per row of the backward sweep (k_bwd), given
+    checkpointed states: the segment's forward recompute 17 + 4N (conv 4, SiLU 5,
+    softplus 7, Delta*u 1; per state Delta*A, exp, Delta*u*B, fma); the reverse per
+    state 9 (adjoint fma, dC and dB partial products, sum g*B, a*h, g*(a*h), the
+    A-weighted and Delta-weighted accumulations, the decayed adjoint) and the readout
+    fma; per row 30 (gate: sigmoid 3, dyg 2, dz 4; dD 1; softplus' 4 and its product;
+    dU and dDelta 3; conv: SiLU' 6, dconv_w 4, dconv_b 1, dx 4); and the channel sums
+    of dB and dC, one add per value: 2N. Total 47 + 16N."""
+    return 47 + 16 * N
 
 
 class Hip:
@@ -191,6 +205,42 @@ def run_scan(ss, torch, hip, spec, g, steps, warmup, zoh=False):
             hip.destroy(x)
     return dict(wall_s=wall, main_ms=float(np.mean(main_ms)), agg_ms=float(np.mean(agg_ms)),
                 main_ms_min=float(np.min(main_ms)))
+
+
+def run_bwd(ss, torch, hip, spec, g, steps, warmup):
+    """Time `steps` whole backward calls on the workload's resident inputs with a
+    seeded bf16/fp32 output gradient, and the backward-sweep kernel by events."""
+    dev = g["x"].device
+    rng = np.random.default_rng(spec.seed + 500)
+    dy = torch.from_numpy(rng.standard_normal(tuple(g["x"].shape), dtype=np.float32)).to(dev).to(g["x"].dtype)
+    Bz, L, D, N = spec.batch, spec.seqlen, spec.d_inner, spec.d_state
+    dims = ss.make_dims(Bz, L, D, N, ss.SS_BF16 if spec.io_dtype == "bf16" else ss.SS_F32)
+    ws = torch.empty(ss.ss_bwd_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+
+    def call():
+        return ss.ss_conv_scan_bwd(g["x"], g["delta"], g["A"], g["B"], g["C"], dy, conv_w=g["conv_w"],
+                                   conv_b=g["conv_b"], delta_bias=g["delta_bias"], D=g["D"], z=g["z"], workspace=ws)
+
+    for _ in range(warmup):
+        out = call()
+    del out
+    torch.cuda.synchronize()
+    ev = [[hip.event(), hip.event()] for _ in range(steps)]
+    outs = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(steps):
+        ss.ss_time_next_call(None, None, ev[i][0], ev[i][1])
+        outs.append(call())
+        if len(outs) > 1:
+            outs.pop(0)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    kms = [hip.elapsed_ms(a, b) for a, b in ev]
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    return dict(wall_s=wall, kernel_ms=float(np.mean(kms)), workspace_bytes=int(ws.numel()))
 
 
 def run_decode(ss, torch, hip, spec: W.DecodeSpec, token_steps: int):
@@ -314,6 +364,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--zoh-steps", type=int, default=10,
                     help="timed calls of the zero-order-hold variant on the same inputs (0: skip)")
+    ap.add_argument("--bwd-steps", type=int, default=5,
+                    help="timed backward calls on the same inputs (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known-size reference for "
                          "hardware traffic counters)")
@@ -399,6 +451,22 @@ def main():
                          "traffic": measured_traffic("k_step", digest), "kernel_us": round(dr["kernel_ms"] * 1e3, 3),
                          "bytes_per_launch": dbytes},
             "hbm_gbps_end_to_end_graph": round(dbytes * dspec.layers * a.decode_steps / dr["graph_s"] / 1e9, 1),
+        }
+    if a.bwd_steps > 0:
+        rb = run_bwd(ss, torch, hip, spec, g, a.bwd_steps, 1)
+        bms = rb["wall_s"] / a.bwd_steps * 1e3
+        binstr = rows * bwd_instr_per_row(N)
+        out["bwd"] = {
+            "workload": "same inputs, gradients of every input for a seeded output gradient",
+            "value": round(rows * N / (bms / 1e3) / 1e9, 2), "unit": "Gelem/s", "ms_per_call": round(bms, 4),
+            "ratio_to_forward": round(bms / ms_step, 3),
+            "roofline": {"kernel": "k_bwd backward sweep", "bound": "alu",
+                         "achieved": round(binstr / (rb["kernel_ms"] / 1e3) / 1e12, 3),
+                         "peak": round(VALU_INSTR_PER_S / 1e12, 3), "unit": "T fp32 VALU instr/s",
+                         "frac": round(binstr / (rb["kernel_ms"] / 1e3) / VALU_INSTR_PER_S, 4),
+                         "kernel_ms": round(rb["kernel_ms"], 4), "valu_instr_per_row": bwd_instr_per_row(N),
+                         "rows_per_launch": rows},
+            "workspace_bytes": rb["workspace_bytes"],
         }
     del g
     if not a.no_cpu and sample is not None:

@@ -163,15 +163,31 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
     const T* db = delta + rowbase * D;
     const T* zb = GATE ? z + rowbase * D : nullptr;
     const T* yb = dy + rowbase * D;
-    auto ld = [&](const T* base, int r) -> float { return IO<T>::cvt((base + (int64_t)r * D)[du]); };
+    auto ld = [&](const T* base, int r) -> T { return (base + (int64_t)r * D)[du]; };
 
+    // rows go in groups of U aligned to the chunk start (so a group never crosses a
+    // tile), from the last group down; each group's loads are issued one group ahead
+    static_assert(R % U == 0, "groups do not cross tiles");
+    T cd[U], cz[U], cy[U], nd[U], nz[U], ny[U];
+    auto load_group = [&](int j, T* pd, T* pz, T* py) {
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            int r = U * j + U - 1 - i;                // rows of the group, last first
+            r = r < clen ? r : clen - 1;
+            pd[i] = ld(db, r);
+            pz[i] = GATE ? ld(zb, r) : T(0);
+            py[i] = ld(yb, r);
+        }
+    };
     float q[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) q[n] = 0.0f;
     double sdt = 0.0;
     const int ntiles = (clen + R - 1) / R;
+    const int ngroups = (clen + U - 1) / U;
     tile_fetch((ntiles - 1) * R);
     tile_store(0);
+    load_group(ngroups - 1, cd, cz, cy);
     __syncthreads();
     int buf = 0;
     for (int k = ntiles - 1; k >= 0; --k) {
@@ -179,18 +195,25 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
         const int rlo = k * R;
         const int rhi = (rlo + R < clen) ? rlo + R : clen;
         const float* tile = &sC[buf][0][0] - (int64_t)rlo * N;
-        float part = 0.0f;
-        for (int r = rhi - 1; r >= rlo; --r) {
-            const float dt = softplus(ld(db, r) + dbias);
-            float dyg = ld(yb, r);
-            if (GATE) dyg *= silu(ld(zb, r));
-            const float* crow = tile + (int64_t)r * N;
+        for (int j = (rhi - 1) / U; j >= rlo / U; --j) {
+            if (j > 0) load_group(j - 1, nd, nz, ny);
+            float part = 0.0f;
 #pragma unroll
-            for (int n = 0; n < N; ++n) q[n] = exp2_fast(dt * A2[n]) * __builtin_fmaf(crow[n], dyg, q[n]);
-            part += dt;
-            if (((r - rlo) & (U - 1)) == 0) { sdt += (double)part; part = 0.0f; }
+            for (int i = 0; i < U; ++i) {
+                const int r = U * j + U - 1 - i;
+                const bool valid = r < clen;           // only the chunk's last group can be short
+                const float dt = valid ? softplus(IO<T>::cvt(cd[i]) + dbias) : 0.0f;
+                float dyg = valid ? IO<T>::cvt(cy[i]) : 0.0f;
+                if (GATE) dyg *= silu(IO<T>::cvt(cz[i]));
+                const float* crow = tile + (int64_t)(valid ? r : rhi - 1) * N;
+#pragma unroll
+                for (int n = 0; n < N; ++n) q[n] = exp2_fast(dt * A2[n]) * __builtin_fmaf(crow[n], dyg, q[n]);
+                part += dt;
+            }
+            sdt += (double)part;
+#pragma unroll
+            for (int i = 0; i < U; ++i) { cd[i] = nd[i]; cz[i] = nz[i]; cy[i] = ny[i]; }
         }
-        sdt += (double)part;
         if (k > 0) tile_store(buf ^ 1);
         __syncthreads();
         buf ^= 1;
@@ -203,12 +226,17 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
 
 // --------------------------------------------------------------------------
 // The backward sweep of one chunk (Euler write term). One lane owns one (b, d) as
-// in the forward. The chunk is taken in 4-token segments from its end; each segment
-// is first recomputed forward from its checkpoint (the state before it), keeping the
-// five states h_{s-1} .. h_{s+3} in registers, then swept backward. Lanes past the
-// last channel repeat it (identical stores) and are masked out of the channel sums.
+// in the forward. The chunk is taken in 4-token segments from its end. Within a
+// segment the states go in blocks of 8: each block is recomputed forward from the
+// checkpoint (the state before the segment), keeping its five states h_{s-1} ..
+// h_{s+3} and four decays in registers, then swept backward; the per-token sums over
+// states (readout, sum g*B, sum A g a h) collect over the blocks, and the gradients
+// that need them follow. Lanes past the last channel repeat it (identical stores)
+// and are masked out of the channel sums.
+// two waves per SIMD: the long per-token dependency chains (recompute, adjoint,
+// lane reductions) need a second wave to overlap
 template <typename T, int N, bool CONV, bool GATE>
-__global__ void __launch_bounds__(kScanThreads)
+__global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(N <= 16 ? 2 : 1)))
 k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
       const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
       const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip, const T* __restrict__ z,
@@ -223,7 +251,7 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
       float* __restrict__ dstate_init, float* __restrict__ dconv_init, BwdArgs ba) {
     constexpr int S = kCkptEvery;
     constexpr int V = 2 * N;                      // per token: dB partials, then dC partials
-    using WS = WaveSum<V>;
+    constexpr int NBK = N < 4 ? N : 4;            // states recomputed and swept together
     const int D = ba.D;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d_raw = blockIdx.x * kScanThreads + tid;
@@ -321,19 +349,6 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
         for (int s = rlo + ((rhi - 1 - rlo) / S) * S; s >= rlo; s -= S) {
             const int ns = (s + S < rhi) ? S : rhi - s;      // tokens in this segment (uniform)
             const int64_t gs = t0 + s;
-            // the state before the segment
-            float hs[S + 1][N];
-            if (gs == 0) {
-#pragma unroll
-                for (int n = 0; n < N; ++n) hs[0][n] = ssm_state0 ? ssm_state0[bd * N + n] : 0.0f;
-            } else {
-                const vf4* src = reinterpret_cast<const vf4*>(ckpt + (((int64_t)b * ba.nck + gs / S - 1) * D + d) * N);
-#pragma unroll
-                for (int q = 0; q < N / 4; ++q) {
-                    const vf4 v = src[q];
-                    hs[0][4 * q] = v.x; hs[0][4 * q + 1] = v.y; hs[0][4 * q + 2] = v.z; hs[0][4 * q + 3] = v.w;
-                }
-            }
             // inputs of the segment; xw[j] = x at row s - 3 + j
             float xw[S + 3];
             T draw[S], zraw[S], yraw[S];
@@ -346,8 +361,8 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                 yraw[i] = ld(dy, r);
                 zraw[i] = GATE ? ld(z, r) : T(0);
             }
-            // forward over the segment
-            float dtv[S], uv[S], cv[S], vv[S];
+            // per-token forward quantities and the gradient of the pre-gate output
+            float dtv[S], uv[S], cv[S], vv[S], dyg[S], szv[S];
 #pragma unroll
             for (int i = 0; i < S; ++i) {
                 if (CONV) {
@@ -359,51 +374,100 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                 }
                 vv[i] = IO<T>::cvt(draw[i]) + dbias;
                 dtv[i] = softplus(vv[i]);
-                const float* brow = tile + (int64_t)(s + i) * V;
-                const float wv = dtv[i] * uv[i];
-#pragma unroll
-                for (int n = 0; n < N; ++n)
-                    hs[i + 1][n] = __builtin_fmaf(exp2_fast(dtv[i] * A2[n]), hs[i][n], wv * brow[n]);
-            }
-            // backward over the segment
-#pragma unroll
-            for (int i = S - 1; i >= 0; --i) {
-                if (i >= ns) continue;                     // uniform: only the sequence's last segment is short
-                const int r = s + i;
-                const int64_t row = (int64_t)r * D;      // relative to the chunk's first token
-                const float* brow = tile + (int64_t)r * V;
-                const float* crow = brow + N;
-                float yv = dsk * uv[i];
-#pragma unroll
-                for (int n = 0; n < N; ++n) yv = __builtin_fmaf(crow[n], hs[i + 1][n], yv);
                 const float dyv = IO<T>::cvt(yraw[i]);
-                float dyg = dyv;
                 if (GATE) {
                     const float zt = IO<T>::cvt(zraw[i]);
-                    const float sz = rcp_fast(1.0f + exp2_fast(-kLog2e * zt));
-                    dyg = dyv * zt * sz;
-                    const float dzv = dyv * yv * sz * __builtin_fmaf(zt, 1.0f - sz, 1.0f);
+                    szv[i] = rcp_fast(1.0f + exp2_fast(-kLog2e * zt));
+                    dyg[i] = dyv * zt * szv[i];
+                } else {
+                    szv[i] = 1.0f;
+                    dyg[i] = dyv;
+                }
+            }
+            // per token, summed over the state blocks: readout, sum g*B, sum A g a h
+            float yacc[S], sgB[S], sA[S];
+#pragma unroll
+            for (int i = 0; i < S; ++i) { yacc[i] = dsk * uv[i]; sgB[i] = 0.0f; sA[i] = 0.0f; }
+            const float* ck = ckpt + (((int64_t)b * ba.nck + (gs > 0 ? gs / S - 1 : 0)) * D + d) * N;
+            // states in blocks of NBK: recompute the block over the segment from the
+            // state before it, then sweep the block backward
+#pragma unroll
+            for (int j0 = 0; j0 < N; j0 += NBK) {
+                float hs[S + 1][NBK];
+                if (gs == 0) {
+#pragma unroll
+                    for (int n = 0; n < NBK; ++n) hs[0][n] = ssm_state0 ? ssm_state0[bd * N + j0 + n] : 0.0f;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < NBK / 4; ++q) {
+                        const vf4 v = reinterpret_cast<const vf4*>(ck + j0)[q];
+                        hs[0][4 * q] = v.x; hs[0][4 * q + 1] = v.y; hs[0][4 * q + 2] = v.z; hs[0][4 * q + 3] = v.w;
+                    }
+                }
+                float av[S][NBK];
+#pragma unroll
+                for (int i = 0; i < S; ++i) {
+                    const float* brow = tile + (int64_t)(s + i) * V + j0;
+                    const float wv = dtv[i] * uv[i];
+#pragma unroll
+                    for (int n = 0; n < NBK; ++n) {
+                        av[i][n] = exp2_fast(dtv[i] * A2[j0 + n]);
+                        hs[i + 1][n] = __builtin_fmaf(av[i][n], hs[i][n], wv * brow[n]);
+                    }
+                }
+#pragma unroll
+                for (int i = S - 1; i >= 0; --i) {
+                    if (i >= ns) continue;                 // uniform: only the sequence's last segment is short
+                    const int r = s + i;
+                    const float* brow = tile + (int64_t)r * V + j0;
+                    const float* crow = tile + (int64_t)r * V + N + j0;
+                    const float dygm = dyg[i] * livef;
+                    const float dtum = dtv[i] * uv[i] * livef;
+                    float vals[2 * NBK];
+                    float ya = 0.0f, gb = 0.0f, sa = 0.0f;
+#pragma unroll
+                    for (int n = 0; n < NBK; ++n) {
+                        const int m = j0 + n;
+                        ya = __builtin_fmaf(crow[n], hs[i + 1][n], ya);
+                        const float g = __builtin_fmaf(crow[n], dyg[i], gc[m]);
+                        vals[NBK + n] = dygm * hs[i + 1][n];
+                        vals[n] = g * dtum;
+                        gb = __builtin_fmaf(g, brow[n], gb);
+                        const float gq = g * (av[i][n] * hs[i][n]);
+                        sa = __builtin_fmaf(A2[m], gq, sa);
+                        dAacc[m] = __builtin_fmaf(dtv[i], gq, dAacc[m]);
+                        gc[m] = av[i][n] * g;
+                    }
+                    yacc[i] += ya;
+                    sgB[i] += gb;
+                    sA[i] += sa;
+                    // channel sums of this token's dB/dC partials of the block
+                    wave_sum<2 * NBK>(vals, lane);
+                    using WB = WaveSum<2 * NBK>;
+                    if ((lane & ((1 << WB::SH) - 1)) == 0) {
+#pragma unroll
+                        for (int q = 0; q < WB::R; ++q) {
+                            const int jv = q + (lane >> WB::SH) * WB::R;      // 0 .. 2*NBK-1
+                            const int col = jv < NBK ? j0 + jv : N + j0 + (jv - NBK);
+                            red[rp][i][wave][col] = vals[q];
+                        }
+                    }
+                }
+            }
+            // per-token gradients that need every state
+#pragma unroll
+            for (int i = S - 1; i >= 0; --i) {
+                if (i >= ns) continue;
+                const int r = s + i;
+                const int64_t row = (int64_t)r * D;
+                if (GATE) {
+                    const float zt = IO<T>::cvt(zraw[i]);
+                    const float dzv = IO<T>::cvt(yraw[i]) * yacc[i] * szv[i] * __builtin_fmaf(zt, 1.0f - szv[i], 1.0f);
                     Buf<T>(dz + rowoff + row).st(IO<T>::bits(dzv), du * (unsigned)sizeof(T), 0u);
                 }
-                dDacc = __builtin_fmaf(dyg, uv[i], dDacc);
-                const float dygm = dyg * livef;
-                const float dtum = dtv[i] * uv[i] * livef;
-                float vals[V];
-                float sgB = 0.0f, sA = 0.0f;
-#pragma unroll
-                for (int n = 0; n < N; ++n) {
-                    const float g = __builtin_fmaf(crow[n], dyg, gc[n]);
-                    vals[N + n] = dygm * hs[i + 1][n];
-                    vals[n] = g * dtum;
-                    sgB = __builtin_fmaf(g, brow[n], sgB);
-                    const float a = exp2_fast(dtv[i] * A2[n]);
-                    const float gq = g * (a * hs[i][n]);
-                    sA = __builtin_fmaf(A2[n], gq, sA);
-                    dAacc[n] = __builtin_fmaf(dtv[i], gq, dAacc[n]);
-                    gc[n] = a * g;
-                }
-                const float dDelta = __builtin_fmaf(sA, kLn2, uv[i] * sgB);
-                const float dU = __builtin_fmaf(dsk, dyg, dtv[i] * sgB);
+                dDacc = __builtin_fmaf(dyg[i], uv[i], dDacc);
+                const float dDelta = __builtin_fmaf(sA[i], kLn2, uv[i] * sgB[i]);
+                const float dU = __builtin_fmaf(dsk, dyg[i], dtv[i] * sgB[i]);
                 const float ddel = dDelta * rcp_fast(1.0f + exp2_fast(-kLog2e * vv[i]));   // softplus' = sigmoid
                 Buf<T>(ddelta + rowoff + row).st(IO<T>::bits(ddel), du * (unsigned)sizeof(T), 0u);
                 dbacc += ddel;
@@ -427,12 +491,6 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                     ws_dxh[(((int64_t)b * nC + c) * D + d) * 3 + (r - (clen - 3))] = dxv;
                 else
                     Buf<T>(dx + rowoff + row).st(IO<T>::bits(dxv), du * (unsigned)sizeof(T), 0u);
-                // channel sums of this token's dB/dC partials
-                wave_sum<V>(vals, lane);
-                if ((lane & ((1 << WS::SH) - 1)) == 0) {
-#pragma unroll
-                    for (int q = 0; q < WS::R; ++q) red[rp][i][wave][q + (lane >> WS::SH) * WS::R] = vals[q];
-                }
             }
             __syncthreads();
             for (int e = tid; e < ns * V; e += kScanThreads) {
