@@ -388,7 +388,8 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
             float yacc[S], sgB[S], sA[S];
 #pragma unroll
             for (int i = 0; i < S; ++i) { yacc[i] = dsk * uv[i]; sgB[i] = 0.0f; sA[i] = 0.0f; }
-            const float* ck = ckpt + (((int64_t)b * ba.nck + (gs > 0 ? gs / S - 1 : 0)) * D + d) * N;
+            // checkpoint slot of the state before the segment: [.., N/4, D, 4]
+            const vf4* ck = reinterpret_cast<const vf4*>(ckpt) + ((int64_t)b * ba.nck + (gs > 0 ? gs / S - 1 : 0)) * (N / 4) * D + d;
             // states in blocks of NBK: recompute the block over the segment from the
             // state before it, then sweep the block backward
 #pragma unroll
@@ -400,7 +401,7 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                 } else {
 #pragma unroll
                     for (int q = 0; q < NBK / 4; ++q) {
-                        const vf4 v = reinterpret_cast<const vf4*>(ck + j0)[q];
+                        const vf4 v = ck[(int64_t)(j0 / 4 + q) * D];
                         hs[0][4 * q] = v.x; hs[0][4 * q + 1] = v.y; hs[0][4 * q + 2] = v.z; hs[0][4 * q + 3] = v.w;
                     }
                 }

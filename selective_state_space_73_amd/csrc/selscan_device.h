@@ -148,8 +148,10 @@ struct ScanArgs {
 };
 
 // Checkpoint mode of the main pass (used by the backward): the state after every
-// kCkptEvery-th token is written to a [B, L / kCkptEvery, D, N] buffer, slot j
-// holding the state after token kCkptEvery*j + kCkptEvery - 1.
+// kCkptEvery-th token is written to a [B, L / kCkptEvery, N/4, D, 4] buffer (four
+// consecutive state entries per channel, channels consecutive, so each 16-byte
+// store of a wave is contiguous), slot j holding the state after token
+// kCkptEvery*j + kCkptEvery - 1.
 constexpr int kCkptEvery = 4;
 
 // Register budget of the scan kernel: three waves per SIMD (<= 168 VGPRs) for
@@ -177,7 +179,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
        const float* __restrict__ ws_sdt,     // [B, nchunks-1, D] summed step sizes
        const float* __restrict__ ws_h0,      // [B, D, N] copy of the initial state (nchunks > 1)
        const float* __restrict__ ws_c0,      // [B, D, K-1] copy of the initial conv history (nchunks > 1)
-       float* __restrict__ ckpt,             // CK: [B, nck, D, N] state checkpoints
+       float* __restrict__ ckpt,             // CK: [B, nck, N/4, D, 4] state checkpoints
        ScanArgs sa) {
     static_assert(!(CK && GATE), "checkpoint mode has no gate");
     const int D = sa.D;
@@ -360,9 +362,9 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     // checkpoint after chunk-relative row r (CK; the caller checks the spacing)
     auto store_ckpt = [&](int r) {
         const int64_t slot = (t0 + r + 1) / kCkptEvery - 1;
-        vf4* dst = reinterpret_cast<vf4*>(ckpt + (((int64_t)b * sa.nck + slot) * D + d) * N);
+        vf4* dst = reinterpret_cast<vf4*>(ckpt) + ((int64_t)b * sa.nck + slot) * (N / 4) * D + d;
 #pragma unroll
-        for (int k = 0; k < N / 4; ++k) dst[k] = vf4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
+        for (int k = 0; k < N / 4; ++k) dst[(int64_t)k * D] = vf4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
     };
     auto token = [&](T xraw, T draw, T zraw, const float* bct, int r) {
         const Pro p = prologue(xraw, draw, zraw);

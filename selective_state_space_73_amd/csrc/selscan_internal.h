@@ -44,7 +44,7 @@ struct LaunchBwd {
     void* dx; void* ddelta; void* dz;
     float* dB; float* dC; float* dA; float* dD; float* dconv_w; float* dconv_b; float* ddelta_bias;
     float* dstate_init; float* dconv_init;
-    float* ws_ckpt;   // [B, nck, D, N] state after every 4th token
+    float* ws_ckpt;   // [B, nck, N/4, D, 4] state after every 4th token
     float* ws_Q;      // [B, nchunks-1, D, N] adjoint aggregates of chunks 1..nchunks-1
     float* ws_qsdt;   // [B, nchunks-1, D] their summed step sizes
     float* ws_dbc;    // [B, L, nblk, 2N] per-workgroup sums of dB, dC
