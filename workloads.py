@@ -42,7 +42,7 @@ import numpy as np
 __all__ = [
     "ScanSpec", "WORKLOADS", "bf16_round", "bf16_bits", "gen_scan_inputs",
     "gen_states", "gen_decode_layer_params", "gen_decode_step_inputs",
-    "DecodeSpec", "DECODE",
+    "DecodeSpec", "DECODE", "BlockSpec", "BLOCKS", "gen_block_weights", "gen_block_input",
 ]
 
 SEED_BASE = 73000
@@ -188,3 +188,72 @@ def gen_decode_step_inputs(spec: DecodeSpec, layer: int, slot: int,
         B=_to_io(_normal(rng, (S, N)), spec.io_dtype),
         C=_to_io(_normal(rng, (S, N)), spec.io_dtype),
     )
+
+
+# ---------------------------------------------------------------------------
+# The Mamba block around the scan: seeded random weights of the block's shape
+# (the Mamba(d_model=512, d_state=16, d_conv=4, expand=2) example on the bembew.net
+# page, "Code Example") and its input. Draws only; the block's arithmetic lives in
+# the oracle and in the library.
+
+@dataclasses.dataclass(frozen=True)
+class BlockSpec:
+    name: str
+    batch: int
+    seqlen: int
+    d_model: int
+    expand: int = 2
+    d_state: int = 16
+    d_conv: int = 4
+    dt_rank: int = 0               # 0: ceil(d_model / 16)
+    io_dtype: str = "f32"
+    seed: int = SEED_BASE + 10
+
+    @property
+    def d_inner(self) -> int:
+        return self.expand * self.d_model
+
+    @property
+    def rank(self) -> int:
+        return self.dt_rank or -(-self.d_model // 16)
+
+
+BLOCKS: Dict[str, BlockSpec] = {
+    "block_f32": BlockSpec("block_f32", 2, 1024, 512, io_dtype="f32", seed=SEED_BASE + 10),
+    "block_bf16": BlockSpec("block_bf16", 2, 1024, 512, io_dtype="bf16", seed=SEED_BASE + 11),
+    # training-shaped block: d_inner 5120 as the train workload
+    "block_train": BlockSpec("block_train", 8, 2048, 2560, io_dtype="bf16", seed=SEED_BASE + 12),
+}
+
+
+def gen_block_weights(spec: BlockSpec, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Random-init weights (float32 arrays; GEMM weights rounded to the I/O dtype):
+    norm_w ~ 1 + 0.1 N(0,1); W_in [2 d_inner, d_model] ~ N(0, 1/d_model);
+    conv_w ~ U(-0.5, 0.5), conv_b ~ U(-0.1, 0.1); W_x [R + 2N, d_inner] ~ N(0, 1/d_inner);
+    W_dt [d_inner, R] ~ N(0, 1/R) / 2; dt_bias = inverse-softplus of a log-uniform draw
+    in [1e-3, 1e-1]; A = -(n+1); D = 1; W_out [d_model, d_inner] ~ N(0, 1/d_inner)."""
+    rng = np.random.default_rng([spec.seed if seed is None else seed, 7])
+    dm, di, N, R = spec.d_model, spec.d_inner, spec.d_state, spec.rank
+    io = spec.io_dtype
+    W = dict(
+        norm_w=(1.0 + 0.1 * _normal(rng, dm)).astype(np.float32),
+        W_in=_to_io(_normal(rng, (2 * di, dm)) / np.float32(np.sqrt(dm)), io),
+        conv_w=rng.uniform(-0.5, 0.5, size=(di, spec.d_conv)).astype(np.float32),
+        conv_b=rng.uniform(-0.1, 0.1, size=di).astype(np.float32),
+        W_x=_to_io(_normal(rng, (R + 2 * N, di)) / np.float32(np.sqrt(di)), io),
+        W_dt=_to_io(_normal(rng, (di, R)) / np.float32(2.0 * np.sqrt(R)), io),
+        dt_bias=_inv_softplus(_log_uniform(rng, di)).astype(np.float32),
+        A=-np.broadcast_to(np.arange(1, N + 1, dtype=np.float32), (di, N)).copy(),
+        D=np.ones(di, dtype=np.float32),
+        W_out=_to_io(_normal(rng, (dm, di)) / np.float32(np.sqrt(di)), io),
+    )
+    return W
+
+
+def gen_block_input(spec: BlockSpec, seed: Optional[int] = None, batch: Optional[int] = None,
+                    seqlen: Optional[int] = None) -> np.ndarray:
+    """x [B, L, d_model] ~ N(0,1) in the I/O dtype (float32 array)."""
+    rng = np.random.default_rng([spec.seed if seed is None else seed, 8])
+    Bsz = spec.batch if batch is None else batch
+    L = spec.seqlen if seqlen is None else seqlen
+    return _to_io(_normal(rng, (Bsz, L, spec.d_model)), spec.io_dtype)
