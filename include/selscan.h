@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define SS_VERSION 3
+#define SS_VERSION 4
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
@@ -167,6 +167,66 @@ size_t ss_bwd_workspace_bytes(const ss_dims* dims);
  * must not overlap any input, each other or the workspace. Asynchronous on `stream`. */
 ss_status ss_conv_scan_bwd(const ss_dims* dims, const ss_args* args, const ss_grads* grads,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * The Mamba block around the scan (bembew.net "Overview of Mamba (SSM) Model",
+ * "How the Mamba Block Works"; ozercemkelahmet.com "Mamba", "The block"), pre-norm
+ * and residual:
+ *   xn  = RMSNorm(x) * norm_w                     (eps = norm_eps)
+ *   xi  = xn W_in[0:Di]^T,  z = xn W_in[Di:2Di]^T  (main branch and gate)
+ *   u   = SiLU(causal conv(xi))                    (conv_w, conv_b, history conv_state)
+ *   dr  = u W_x[0:R]^T,  B = u W_x[R:R+N]^T,  C = u W_x[R+N:R+2N]^T
+ *   delta = dr W_dt^T                              (dt_bias goes inside the softplus)
+ *   y   = scan(u, delta, A, B, C, Dskip, z)        (ss_conv_scan_fwd / ss_step, conv off)
+ *   out = x + y W_out^T
+ * Activations x, out [B,L,d_model] and the GEMM weights have the I/O dtype; the
+ * GEMMs (hipBLASLt, matrix cores) accumulate in fp32. Readings (the pages name a
+ * normalisation, small projections for the step size, B and C, and residual
+ * stacking): pre-norm RMSNorm, a rank-R step-size projection with its bias inside
+ * the softplus, unbiased projections. */
+typedef struct {
+    int64_t  batch;          /* B (streams for ss_block_step)                      */
+    int64_t  seqlen;         /* L (ignored by ss_block_step)                        */
+    int64_t  d_model;        /* model width                                         */
+    int64_t  d_inner;        /* Di, the scan's channels (expand * d_model)          */
+    int32_t  d_state;        /* N in {4, 8, 16, 32, 64}                             */
+    int32_t  d_conv;         /* 4                                                   */
+    int32_t  dt_rank;        /* R >= 1                                              */
+    int32_t  io_dtype;       /* ss_dtype of activations and GEMM weights            */
+    int32_t  discretization; /* ss_discretization of the scan's write term          */
+    float    norm_eps;       /* > 0                                                 */
+} ss_block_dims;
+
+typedef struct {             /* DEVICE pointers, row-major, y = v W^T convention    */
+    const float* norm_w;     /* [d_model]                                           */
+    const void*  W_in;       /* [2 Di, d_model] io: rows 0..Di-1 main branch, rest gate */
+    const float* conv_w;     /* [Di, 4]                                             */
+    const float* conv_b;     /* [Di] or NULL                                        */
+    const void*  W_x;        /* [R + 2N, Di] io: step-size, B, C rows               */
+    const void*  W_dt;       /* [Di, R] io                                          */
+    const float* dt_bias;    /* [Di] or NULL                                        */
+    const float* A;          /* [Di, N]                                             */
+    const float* Dskip;      /* [Di] or NULL                                        */
+    const void*  W_out;      /* [d_model, Di] io                                    */
+} ss_block_weights;
+
+/* Bytes of device workspace for ss_block_fwd (step = 0) or ss_block_step (step != 0):
+ * the block's intermediate activations, the scan's workspace and 32 MiB of GEMM
+ * scratch. 0 for invalid sizes. */
+size_t ss_block_workspace_bytes(const ss_block_dims* dims, int step);
+
+/* Block forward over a sequence: out [B,L,d_model] from x [B,L,d_model]. ssm_state
+ * [B,Di,N] and conv_state [B,Di,3] (fp32) are the initial states when given and are
+ * overwritten with the final ones (NULL: zero, not returned). out may equal x
+ * (in place) but not partly overlap it. Activations and GEMM weights must be 16-byte
+ * aligned. Everything is validated before anything is enqueued. The GEMM plans are
+ * created on first use per device and shape (hipBLASLt handle kept for the process). */
+ss_status ss_block_fwd(const ss_block_dims* dims, const ss_block_weights* weights, const void* x, void* out,
+                       float* ssm_state, float* conv_state, void* workspace, size_t workspace_bytes, void* stream);
+
+/* One decode token per stream: x, out [B,d_model]; both states required and updated. */
+ss_status ss_block_step(const ss_block_dims* dims, const ss_block_weights* weights, const void* x, void* out,
+                        float* ssm_state, float* conv_state, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Profiling support for benchmarks: events (hipEvent_t handles created by the
  * caller) that the NEXT ss_conv_scan_fwd, ss_conv_scan_bwd or ss_step call made on

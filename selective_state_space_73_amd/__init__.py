@@ -44,6 +44,18 @@ class ss_grads(ctypes.Structure):
                                    "dDskip", "dconv_w", "dconv_b", "ddelta_bias", "dstate_init", "dconv_init")]
 
 
+class ss_block_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("d_model", ctypes.c_int64),
+                ("d_inner", ctypes.c_int64), ("d_state", ctypes.c_int32), ("d_conv", ctypes.c_int32),
+                ("dt_rank", ctypes.c_int32), ("io_dtype", ctypes.c_int32), ("discretization", ctypes.c_int32),
+                ("norm_eps", ctypes.c_float)]
+
+
+class ss_block_weights(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("norm_w", "W_in", "conv_w", "conv_b", "W_x", "W_dt", "dt_bias", "A", "Dskip",
+                                   "W_out")]
+
+
 class SelscanError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"{STATUS.get(status, status)}: {detail}")
@@ -73,6 +85,13 @@ def _load() -> ctypes.CDLL:
     lib.ss_conv_scan_bwd.argtypes = [ctypes.POINTER(ss_dims), ctypes.POINTER(ss_args), ctypes.POINTER(ss_grads), _vp,
                                      ctypes.c_size_t, _vp]
     lib.ss_conv_scan_bwd.restype = ctypes.c_int
+    lib.ss_block_workspace_bytes.argtypes = [ctypes.POINTER(ss_block_dims), ctypes.c_int]
+    lib.ss_block_workspace_bytes.restype = ctypes.c_size_t
+    for name in ("ss_block_fwd", "ss_block_step"):
+        fn = getattr(lib, name)
+        fn.argtypes = [ctypes.POINTER(ss_block_dims), ctypes.POINTER(ss_block_weights), _vp, _vp, _vp, _vp, _vp,
+                       ctypes.c_size_t, _vp]
+        fn.restype = ctypes.c_int
     return lib
 
 
@@ -253,5 +272,73 @@ def ss_conv_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: t
     return out
 
 
-__all__ = ["ss_conv_scan_fwd", "ss_conv_scan_bwd", "ss_bwd_workspace_bytes", "ss_grads", "ss_step", "ss_workspace_bytes", "ss_version", "ss_time_next_call", "make_dims", "ss_dims", "ss_args",
+BLOCK_WEIGHTS = ("norm_w", "W_in", "conv_w", "conv_b", "W_x", "W_dt", "dt_bias", "A", "D", "W_out")
+
+
+def block_dims(batch: int, seqlen: int, d_model: int, d_inner: int, d_state: int, dt_rank: int, io_dtype: int,
+               norm_eps: float = 1e-5, discretization: int = SS_EULER, d_conv: int = 4) -> ss_block_dims:
+    return ss_block_dims(batch, seqlen, d_model, d_inner, d_state, d_conv, dt_rank, io_dtype, discretization,
+                         norm_eps)
+
+
+def ss_block_workspace_bytes(dims: ss_block_dims, step: bool = False) -> int:
+    return int(lib.ss_block_workspace_bytes(ctypes.byref(dims), int(bool(step))))
+
+
+def _block_call(step, x, W, dt_rank, ssm_state, conv_state, out, workspace, norm_eps, zoh, stream):
+    io = x.dtype
+    if step:
+        if x.dim() != 2:
+            raise ValueError("x must be [streams, d_model]")
+        Bsz, dm = x.shape
+        L = 1
+    else:
+        if x.dim() != 3:
+            raise ValueError("x must be [batch, seqlen, d_model]")
+        Bsz, L, dm = x.shape
+    di = W["W_in"].shape[0] // 2
+    N = W["A"].shape[1]
+    dims = block_dims(Bsz, L, dm, di, N, dt_rank, _io_dtype(x), norm_eps, SS_ZOH if zoh else SS_EULER)
+    f32 = torch.float32
+    w = ss_block_weights(
+        norm_w=_ptr(W["norm_w"], (dm,), f32, "norm_w"), W_in=_ptr(W["W_in"], (2 * di, dm), io, "W_in"),
+        conv_w=_ptr(W["conv_w"], (di, 4), f32, "conv_w"), conv_b=_ptr(W.get("conv_b"), (di,), f32, "conv_b"),
+        W_x=_ptr(W["W_x"], (dt_rank + 2 * N, di), io, "W_x"), W_dt=_ptr(W["W_dt"], (di, dt_rank), io, "W_dt"),
+        dt_bias=_ptr(W.get("dt_bias"), (di,), f32, "dt_bias"), A=_ptr(W["A"], (di, N), f32, "A"),
+        Dskip=_ptr(W.get("D"), (di,), f32, "D"), W_out=_ptr(W["W_out"], (dm, di), io, "W_out"))
+    if out is None:
+        out = torch.empty_like(x)
+    need = ss_block_workspace_bytes(dims, step)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
+    fn = lib.ss_block_step if step else lib.ss_block_fwd
+    _check(fn(ctypes.byref(dims), ctypes.byref(w), _ptr(x, None, io, "x"), _ptr(out, tuple(x.shape), io, "out"),
+              _ptr(ssm_state, (Bsz, di, N), f32, "ssm_state"), _ptr(conv_state, (Bsz, di, 3), f32, "conv_state"),
+              workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
+    return out
+
+
+def ss_block_fwd(x: torch.Tensor, W: dict, dt_rank: int, *, ssm_state: Optional[torch.Tensor] = None,
+                 conv_state: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, norm_eps: float = 1e-5, zoh: bool = False,
+                 stream=None) -> torch.Tensor:
+    """Mamba block forward: x [B,L,d_model] (float32 or bfloat16) -> out, same shape.
+    W: device tensors named as BLOCK_WEIGHTS (GEMM weights in the I/O dtype, the rest
+    float32; conv_b, dt_bias and D optional). ssm_state [B,Di,N] / conv_state [B,Di,3]
+    float32 are read and updated when given."""
+    return _block_call(False, x, W, dt_rank, ssm_state, conv_state, out, workspace, norm_eps, zoh, stream)
+
+
+def ss_block_step(x: torch.Tensor, W: dict, dt_rank: int, ssm_state: torch.Tensor, conv_state: torch.Tensor, *,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  norm_eps: float = 1e-5, zoh: bool = False, stream=None) -> torch.Tensor:
+    """One decode token per stream through the block: x [S,d_model] -> out [S,d_model];
+    both states required and updated in place."""
+    return _block_call(True, x, W, dt_rank, ssm_state, conv_state, out, workspace, norm_eps, zoh, stream)
+
+
+__all__ = ["ss_block_fwd", "ss_block_step", "ss_block_workspace_bytes", "block_dims", "ss_block_dims",
+           "ss_block_weights", "BLOCK_WEIGHTS", "ss_conv_scan_fwd", "ss_conv_scan_bwd", "ss_bwd_workspace_bytes", "ss_grads", "ss_step", "ss_workspace_bytes", "ss_version", "ss_time_next_call", "make_dims", "ss_dims", "ss_args",
            "SelscanError", "SS_F32", "SS_BF16", "SS_EULER", "SS_ZOH", "LIB_PATH", "lib"]

@@ -13,11 +13,14 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libselscan.so")
-# one instantiation unit per I/O dtype and write rule (compiled in parallel) + the C ABI layer
-KERNEL_UNITS = sorted(glob.glob(os.path.join(CSRC, "selscan_*_*.hip")))
-SOURCES = KERNEL_UNITS + [os.path.join(CSRC, "selscan_api.cpp")]
-HEADERS = [os.path.join(CSRC, "selscan_device.h"), os.path.join(CSRC, "selscan_internal.h"),
+# kernel units (one per I/O dtype and write rule, plus the block's elementwise kernels;
+# compiled in parallel) + the C ABI layer and the block pipeline (host code, hipBLASLt)
+KERNEL_UNITS = sorted(glob.glob(os.path.join(CSRC, "selscan_*.hip")))
+SOURCES = KERNEL_UNITS + [os.path.join(CSRC, "selscan_api.cpp"), os.path.join(CSRC, "selscan_block.cpp")]
+HEADERS = [os.path.join(CSRC, "selscan_device.h"), os.path.join(CSRC, "selscan_bwd.h"),
+           os.path.join(CSRC, "selscan_block.h"), os.path.join(CSRC, "selscan_internal.h"),
            os.path.join(INCLUDE, "selscan.h")]
+LIBS = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -40,7 +43,7 @@ def kernel_digest() -> str:
     launch constants and the chunking rule of the C ABI layer), so that measurements
     taken on one build can be matched to it later."""
     h = hashlib.sha256()
-    for path in sorted(SOURCES + HEADERS[:2]):
+    for path in sorted(SOURCES + HEADERS[:4]):
         with open(path, "rb") as f:
             h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -66,7 +69,7 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
         for _ in ex.map(_run, cmds):
             pass
     tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs])
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs, *LIBS])
     os.replace(tmp, LIB)
     return LIB
 

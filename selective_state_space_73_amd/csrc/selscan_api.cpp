@@ -268,6 +268,14 @@ hipError_t launch(const selscan::LaunchScan& p, bool step) {
 
 }  // namespace
 
+namespace selscan {
+ss_status set_error(ss_status s, const char* msg) {
+    g_last_error = msg;
+    return s;
+}
+ss_status validate_dims(const ss_dims* d, bool step) { return check_dims(d, step); }
+}  // namespace selscan
+
 extern "C" {
 
 size_t ss_workspace_bytes(const ss_dims* dims) {

@@ -1,0 +1,270 @@
+// Host pipeline of the Mamba block around the scan (ss_block_fwd / ss_block_step).
+//
+// The block (bembew.net "Overview of Mamba (SSM) Model", "How the Mamba Block Works";
+// ozercemkelahmet.com "Mamba", "The block"; inferensys.com "Mamba", block list):
+// RMSNorm, a widening projection into the main branch and the gate, causal conv +
+// SiLU on the main branch, step size / B / C as small projections of that branch
+// (ai360xpert.com "Mamba", "The selection mechanism"), the selective scan with its
+// D skip and SiLU gate, the projection back to the model width and the residual.
+// The projections are dense GEMMs on the matrix cores through hipBLASLt (row-major
+// activations times transposed row-major weights, fp32 accumulation); everything
+// else runs in this library's kernels; the residual is fused into the output GEMM
+// as its C operand. Plans (descriptors, layouts and the chosen algorithm) are made
+// once per device and shape and kept for the life of the process.
+#include <hip/hip_runtime.h>
+#include <hipblaslt/hipblaslt.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "selscan.h"
+#include "selscan_internal.h"
+
+namespace {
+
+ss_status failf(ss_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    return selscan::set_error(s, buf);
+}
+
+constexpr size_t kBlasWorkspace = size_t(32) << 20;   // hipBLASLt scratch inside the block workspace
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Plan {
+    hipblasLtMatmulDesc_t desc = nullptr;
+    hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
+    hipblasLtMatmulAlgo_t algo{};
+    bool ok = false;
+};
+
+// (device, bf16, m, n, k)
+using PlanKey = std::tuple<int, bool, int64_t, int64_t, int64_t>;
+
+std::mutex g_mu;
+std::map<int, hipblasLtHandle_t> g_handles;
+std::map<PlanKey, Plan> g_plans;
+
+// Y[M, Nout] (+)= X[M, K] * W[Nout, K]^T, all row-major; Cres (if not null) is added
+// (beta = 1) and may equal Y.
+ss_status gemm(bool bf16, int64_t M, int64_t Nout, int64_t K, const void* W, const void* X, const void* Cres,
+               void* Y, void* ws, hipStream_t st) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return failf(SS_ERR_HIP, "hipGetDevice failed");
+    const hipDataType dt = bf16 ? HIP_R_16BF : HIP_R_32F;
+    Plan plan;
+    hipblasLtHandle_t h = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto hi = g_handles.find(dev);
+        if (hi == g_handles.end()) {
+            if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS) return failf(SS_ERR_HIP, "hipblasLtCreate failed");
+            g_handles[dev] = h;
+        } else {
+            h = hi->second;
+        }
+        const PlanKey key{dev, bf16, M, Nout, K};
+        auto pi = g_plans.find(key);
+        if (pi == g_plans.end()) {
+            // column-major view: Y^T [Nout, M] = op(W^T [K, Nout]) * X^T [K, M] with op = transpose
+            Plan p;
+            const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+            bool good = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
+                        hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) == HIPBLAS_STATUS_SUCCESS &&
+                        hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) == HIPBLAS_STATUS_SUCCESS &&
+                        hipblasLtMatrixLayoutCreate(&p.a, dt, K, Nout, K) == HIPBLAS_STATUS_SUCCESS &&
+                        hipblasLtMatrixLayoutCreate(&p.b, dt, K, M, K) == HIPBLAS_STATUS_SUCCESS &&
+                        hipblasLtMatrixLayoutCreate(&p.c, dt, Nout, M, Nout) == HIPBLAS_STATUS_SUCCESS;
+            if (good) {
+                hipblasLtMatmulPreference_t pref = nullptr;
+                const uint64_t wsb = kBlasWorkspace;
+                hipblasLtMatmulHeuristicResult_t res[1];
+                int n = 0;
+                good = hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
+                       hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb,
+                                                             sizeof(wsb)) == HIPBLAS_STATUS_SUCCESS &&
+                       hipblasLtMatmulAlgoGetHeuristic(h, p.desc, p.a, p.b, p.c, p.c, pref, 1, res, &n) ==
+                           HIPBLAS_STATUS_SUCCESS &&
+                       n > 0;
+                if (good) p.algo = res[0].algo;
+                if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+            }
+            p.ok = good;
+            pi = g_plans.emplace(key, p).first;
+        }
+        plan = pi->second;
+    }
+    if (!plan.ok)
+        return failf(SS_ERR_UNSUPPORTED, "no hipBLASLt algorithm for a %lld x %lld x %lld GEMM", (long long)M,
+                     (long long)Nout, (long long)K);
+    const float alpha = 1.0f, beta = Cres ? 1.0f : 0.0f;
+    const hipblasStatus_t s = hipblasLtMatmul(h, plan.desc, &alpha, W, plan.a, X, plan.b, &beta, Cres ? Cres : Y,
+                                              plan.c, Y, plan.c, &plan.algo, ws, kBlasWorkspace, st);
+    if (s != HIPBLAS_STATUS_SUCCESS) return failf(SS_ERR_HIP, "hipblasLtMatmul failed (%d)", (int)s);
+    return SS_OK;
+}
+
+struct BlockLayout {
+    size_t xn, xi, z, u, dr, bm, cm, delta, y, scan, blas, total;
+};
+
+ss_dims scan_dims(const ss_block_dims& d, bool step) {
+    ss_dims s{};
+    s.batch = d.batch;
+    s.seqlen = step ? 1 : d.seqlen;
+    s.d_inner = d.d_inner;
+    s.d_state = d.d_state;
+    s.d_conv = d.d_conv;
+    s.io_dtype = d.io_dtype;
+    s.discretization = d.discretization;
+    return s;
+}
+
+BlockLayout block_layout(const ss_block_dims& d, bool step) {
+    BlockLayout l{};
+    const size_t es = d.io_dtype == SS_BF16 ? 2 : 4;
+    const size_t M = (size_t)d.batch * (size_t)(step ? 1 : d.seqlen);
+    const size_t dm = (size_t)d.d_model, di = (size_t)d.d_inner, N = (size_t)d.d_state, R = (size_t)d.dt_rank;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
+    l.xn = take(M * dm * es);
+    l.xi = take(M * di * es);
+    l.z = take(M * di * es);
+    l.u = take(M * di * es);
+    l.dr = take(M * R * es);
+    l.bm = take(M * N * es);
+    l.cm = take(M * N * es);
+    l.delta = take(M * di * es);
+    l.y = take(M * di * es);
+    const ss_dims sd = scan_dims(d, step);
+    l.scan = take(step ? 0 : ss_workspace_bytes(&sd));
+    l.blas = take(kBlasWorkspace);
+    l.total = off;
+    return l;
+}
+
+ss_status check_block(const ss_block_dims* d, const ss_block_weights* w, const void* x, const void* out,
+                      const float* ssm_state, const float* conv_state, bool step) {
+    if (!d || !w) return failf(SS_ERR_INVALID_ARG, "dims or weights is NULL");
+    if (d->batch < 1 || (!step && d->seqlen < 1) || d->d_model < 1 || d->d_inner < 1 || d->dt_rank < 1)
+        return failf(SS_ERR_INVALID_ARG, "block sizes must be positive");
+    if (d->d_model > (int64_t(1) << 20) || d->dt_rank > 4096)
+        return failf(SS_ERR_INVALID_ARG, "d_model or dt_rank out of range");
+    if (!(d->norm_eps > 0.0f)) return failf(SS_ERR_INVALID_ARG, "norm_eps must be positive");
+    if (!x || !out) return failf(SS_ERR_INVALID_ARG, "x or out is NULL");
+    const void* req[] = {w->norm_w, w->W_in, w->conv_w, w->W_x, w->W_dt, w->A, w->W_out};
+    const char* names[] = {"norm_w", "W_in", "conv_w", "W_x", "W_dt", "A", "W_out"};
+    for (int i = 0; i < 7; ++i)
+        if (!req[i]) return failf(SS_ERR_INVALID_ARG, "weights.%s is NULL", names[i]);
+    if (step && (!ssm_state || !conv_state)) return failf(SS_ERR_INVALID_ARG, "ss_block_step needs both states");
+    const size_t es = d->io_dtype == SS_BF16 ? 2 : 4;
+    const size_t xbytes = (size_t)d->batch * (size_t)(step ? 1 : d->seqlen) * (size_t)d->d_model * es;
+    const uintptr_t x0 = (uintptr_t)x, o0 = (uintptr_t)out;
+    if (x0 != o0 && x0 < o0 + xbytes && o0 < x0 + xbytes)
+        return failf(SS_ERR_INVALID_ARG, "out overlaps x (only out == x is allowed)");
+    const void* aligned[] = {x, out, w->W_in, w->W_x, w->W_dt, w->W_out};
+    for (const void* p : aligned)
+        if ((uintptr_t)p & 15u) return failf(SS_ERR_INVALID_ARG, "activations and GEMM weights must be 16-byte aligned");
+    const void* f4[] = {w->norm_w, w->conv_w, w->conv_b, w->dt_bias, w->A, w->Dskip, ssm_state, conv_state};
+    for (const void* p : f4)
+        if ((uintptr_t)p & 3u) return failf(SS_ERR_INVALID_ARG, "parameters and states must be 4-byte aligned");
+    if (ssm_state && ((uintptr_t)ssm_state & 15u)) return failf(SS_ERR_INVALID_ARG, "ssm_state not 16-byte aligned");
+    if (d->d_conv != 4) return failf(SS_ERR_UNSUPPORTED, "d_conv %d: only 4 is built", d->d_conv);
+    // the scan's own checks (sizes, d_state, dtype, discretization) before anything is enqueued
+    const ss_dims sd = scan_dims(*d, step);
+    return selscan::validate_dims(&sd, step);
+}
+
+ss_status run_block(const ss_block_dims* d, const ss_block_weights* w, const void* x, void* out, float* ssm_state,
+                    float* conv_state, void* workspace, size_t workspace_bytes, void* stream, bool step) {
+    ss_status s = check_block(d, w, x, out, ssm_state, conv_state, step);
+    if (s != SS_OK) return s;
+    const ss_dims sd = scan_dims(*d, step);
+    const BlockLayout l = block_layout(*d, step);
+    if (!workspace || workspace_bytes < l.total)
+        return failf(SS_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, l.total);
+    if ((uintptr_t)workspace & 255u) return failf(SS_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+    const bool bf16 = d->io_dtype == SS_BF16;
+    const size_t es = bf16 ? 2 : 4;
+    char* ws = static_cast<char*>(workspace);
+    void* xn = ws + l.xn; void* xi = ws + l.xi; void* z = ws + l.z; void* u = ws + l.u; void* dr = ws + l.dr;
+    void* bm = ws + l.bm; void* cm = ws + l.cm; void* delta = ws + l.delta; void* y = ws + l.y;
+    void* blas = ws + l.blas;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t L = step ? 1 : d->seqlen;
+    const int64_t M = d->batch * L;
+    const int64_t dm = d->d_model, di = d->d_inner, N = d->d_state, R = d->dt_rank;
+
+    selscan::LaunchBlockOps op{};
+    op.bf16 = bf16;
+    op.stream = stream;
+    op.op = selscan::LaunchBlockOps::kRmsNorm;
+    op.in = x; op.out = xn; op.w = w->norm_w; op.eps = d->norm_eps; op.rows = M; op.cols = (int)dm;
+    if (selscan::launch_block_op(op) != hipSuccess) return failf(SS_ERR_HIP, "RMSNorm launch failed");
+
+    const char* W_in = static_cast<const char*>(w->W_in);
+    if ((s = gemm(bf16, M, di, dm, W_in, xn, nullptr, xi, blas, st)) != SS_OK) return s;
+    if ((s = gemm(bf16, M, di, dm, W_in + (size_t)di * dm * es, xn, nullptr, z, blas, st)) != SS_OK) return s;
+
+    op = selscan::LaunchBlockOps{};
+    op.bf16 = bf16;
+    op.stream = stream;
+    op.in = xi; op.out = u; op.conv_w = w->conv_w; op.conv_b = w->conv_b; op.hist = conv_state;
+    op.cols = (int)di; op.L = L; op.batch = d->batch;
+    if (step) {
+        op.op = selscan::LaunchBlockOps::kConvStep;
+        if (selscan::launch_block_op(op) != hipSuccess) return failf(SS_ERR_HIP, "conv step launch failed");
+    } else {
+        op.op = selscan::LaunchBlockOps::kConvSilu;
+        if (selscan::launch_block_op(op) != hipSuccess) return failf(SS_ERR_HIP, "conv launch failed");
+        if (conv_state) {
+            op.op = selscan::LaunchBlockOps::kConvHistory;
+            if (selscan::launch_block_op(op) != hipSuccess) return failf(SS_ERR_HIP, "conv history launch failed");
+        }
+    }
+
+    const char* W_x = static_cast<const char*>(w->W_x);
+    if ((s = gemm(bf16, M, R, di, W_x, u, nullptr, dr, blas, st)) != SS_OK) return s;
+    if ((s = gemm(bf16, M, N, di, W_x + (size_t)R * di * es, u, nullptr, bm, blas, st)) != SS_OK) return s;
+    if ((s = gemm(bf16, M, N, di, W_x + (size_t)(R + N) * di * es, u, nullptr, cm, blas, st)) != SS_OK) return s;
+    if ((s = gemm(bf16, M, di, R, w->W_dt, dr, nullptr, delta, blas, st)) != SS_OK) return s;
+
+    ss_args a{};
+    a.x = u; a.delta = delta; a.delta_bias = w->dt_bias; a.A = w->A; a.B = bm; a.C = cm; a.Dskip = w->Dskip;
+    a.z = z; a.y = y; a.ssm_state = ssm_state;
+    s = step ? ss_step(&sd, &a, stream) : ss_conv_scan_fwd(&sd, &a, ws + l.scan, ss_workspace_bytes(&sd), stream);
+    if (s != SS_OK) return s;
+
+    return gemm(bf16, M, dm, di, w->W_out, y, x, out, blas, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ss_block_workspace_bytes(const ss_block_dims* dims, int step) {
+    if (!dims || dims->batch < 1 || dims->d_model < 1 || dims->d_inner < 1 || dims->dt_rank < 1 ||
+        (!step && dims->seqlen < 1))
+        return 0;
+    return block_layout(*dims, step != 0).total;
+}
+
+ss_status ss_block_fwd(const ss_block_dims* dims, const ss_block_weights* weights, const void* x, void* out,
+                       float* ssm_state, float* conv_state, void* workspace, size_t workspace_bytes, void* stream) {
+    return run_block(dims, weights, x, out, ssm_state, conv_state, workspace, workspace_bytes, stream, false);
+}
+
+ss_status ss_block_step(const ss_block_dims* dims, const ss_block_weights* weights, const void* x, void* out,
+                        float* ssm_state, float* conv_state, void* workspace, size_t workspace_bytes, void* stream) {
+    return run_block(dims, weights, x, out, ssm_state, conv_state, workspace, workspace_bytes, stream, true);
+}
+
+}  // extern "C"

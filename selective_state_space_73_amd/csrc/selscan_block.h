@@ -1,0 +1,128 @@
+// Device kernels of the Mamba block around the scan (ss_block_fwd / ss_block_step):
+// the RMSNorm in front of the block and the block's causal conv + SiLU, which is
+// materialised here (as u) because the step-size, B and C projections read it
+// (bembew.net "Overview of Mamba (SSM) Model", "How the Mamba Block Works";
+// ozercemkelahmet.com "Mamba", "The block"). The projections are hipBLASLt GEMMs and
+// the scan is the library's own kernel, both launched from selscan_block.cpp.
+#pragma once
+#include "selscan_device.h"
+
+namespace selscan {
+
+// RMSNorm: out = x / sqrt(mean(x^2) + eps) * w, one wave per row of d_model values.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_rmsnorm(const T* __restrict__ x, const float* __restrict__ w, T* __restrict__ out, int64_t rows, int dm,
+          float eps) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;                      // whole waves leave together
+    const T* xr = x + row * dm;
+    float ss = 0.0f;
+    for (int i = lane; i < dm; i += 64) {
+        const float v = IO<T>::ld(xr + i);
+        ss = __builtin_fmaf(v, v, ss);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float r = __builtin_amdgcn_rsqf(ss / (float)dm + eps);
+    T* orow = out + row * dm;
+    for (int i = lane; i < dm; i += 64) IO<T>::st(orow + i, IO<T>::ld(xr + i) * r * w[i]);
+}
+
+// Causal depthwise conv (width 4, tap 3 on the current token) + SiLU over a run of
+// kBlockConvRun tokens per lane: u[b,t,d] = SiLU(cb + sum_k w_k xi[b,t-3+k,d]), with
+// the initial history (oldest first) before token 0, or zeros. Reads the history
+// only; k_conv_history writes the new one afterwards.
+constexpr int kBlockConvRun = 64;
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_conv_silu(const T* __restrict__ xi, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
+            const float* __restrict__ hist, T* __restrict__ u, int64_t L, int D) {
+    const int d = blockIdx.x * 256 + threadIdx.x;
+    if (d >= D) return;
+    const int b = blockIdx.z;
+    const int64_t t0 = (int64_t)blockIdx.y * kBlockConvRun;
+    const int64_t t1 = (t0 + kBlockConvRun < L) ? t0 + kBlockConvRun : L;
+    const float w0 = conv_w[d * 4 + 0], w1 = conv_w[d * 4 + 1], w2 = conv_w[d * 4 + 2], w3 = conv_w[d * 4 + 3];
+    const float cb = conv_b ? conv_b[d] : 0.0f;
+    const int64_t bd = (int64_t)b * D + d;
+    auto xat = [&](int64_t t) -> float {
+        if (t >= 0) return IO<T>::ld(xi + ((int64_t)b * L + t) * D + d);
+        return hist ? hist[bd * 3 + (3 + t)] : 0.0f;
+    };
+    float x3 = xat(t0 - 3), x2 = xat(t0 - 2), x1 = xat(t0 - 1);
+    for (int64_t t = t0; t < t1; ++t) {
+        const float xt = IO<T>::ld(xi + ((int64_t)b * L + t) * D + d);
+        const float c = __builtin_fmaf(w3, xt, __builtin_fmaf(w2, x1, __builtin_fmaf(w1, x2, __builtin_fmaf(w0, x3, cb))));
+        IO<T>::st(u + ((int64_t)b * L + t) * D + d, silu(c));
+        x3 = x2; x2 = x1; x1 = xt;
+    }
+}
+
+// New conv history [B,D,3] = the last three of (history, xi) for every (b, d).
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_conv_history(const T* __restrict__ xi, float* __restrict__ hist, int64_t L, int D, int Bsz) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)Bsz * D) return;
+    const int d = (int)(i % D);
+    const int64_t b = i / D;
+    float h[3] = {hist[i * 3 + 0], hist[i * 3 + 1], hist[i * 3 + 2]};
+    float n[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int64_t t = L - 3 + k;                 // sequence position of new entry k
+        n[k] = t >= 0 ? IO<T>::ld(xi + (b * L + t) * D + d) : h[3 + t];
+    }
+    hist[i * 3 + 0] = n[0]; hist[i * 3 + 1] = n[1]; hist[i * 3 + 2] = n[2];
+}
+
+// Decode: one token per stream; u = SiLU(conv over (history, x)), history shifted in place.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_conv_step(const T* __restrict__ xi, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
+            float* __restrict__ hist, T* __restrict__ u, int D, int S) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)S * D) return;
+    const int d = (int)(i % D);
+    const float xt = IO<T>::ld(xi + i);
+    const float h0 = hist[i * 3 + 0], h1 = hist[i * 3 + 1], h2 = hist[i * 3 + 2];
+    const float cb = conv_b ? conv_b[d] : 0.0f;
+    const float c = __builtin_fmaf(conv_w[d * 4 + 3], xt, __builtin_fmaf(conv_w[d * 4 + 2], h2,
+                    __builtin_fmaf(conv_w[d * 4 + 1], h1, __builtin_fmaf(conv_w[d * 4 + 0], h0, cb))));
+    IO<T>::st(u + i, silu(c));
+    hist[i * 3 + 0] = h1; hist[i * 3 + 1] = h2; hist[i * 3 + 2] = xt;
+}
+
+template <typename T>
+static hipError_t launch_block_kernels_t(const LaunchBlockOps& p) {
+    hipStream_t st = static_cast<hipStream_t>(p.stream);
+    switch (p.op) {
+        case LaunchBlockOps::kRmsNorm:
+            hipLaunchKernelGGL((k_rmsnorm<T>), dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, st,
+                               static_cast<const T*>(p.in), p.w, static_cast<T*>(p.out), p.rows, p.cols, p.eps);
+            break;
+        case LaunchBlockOps::kConvSilu:
+            hipLaunchKernelGGL((k_conv_silu<T>), dim3((unsigned)((p.cols + 255) / 256),
+                               (unsigned)((p.L + kBlockConvRun - 1) / kBlockConvRun), (unsigned)p.batch), dim3(256), 0,
+                               st, static_cast<const T*>(p.in), p.conv_w, p.conv_b, p.hist, static_cast<T*>(p.out), p.L,
+                               p.cols);
+            break;
+        case LaunchBlockOps::kConvHistory:
+            hipLaunchKernelGGL((k_conv_history<T>), dim3((unsigned)((p.batch * p.cols + 255) / 256)), dim3(256), 0, st,
+                               static_cast<const T*>(p.in), p.hist, p.L, p.cols, (int)p.batch);
+            break;
+        case LaunchBlockOps::kConvStep:
+            hipLaunchKernelGGL((k_conv_step<T>), dim3((unsigned)((p.batch * p.cols + 255) / 256)), dim3(256), 0, st,
+                               static_cast<const T*>(p.in), p.conv_w, p.conv_b, p.hist, static_cast<T*>(p.out), p.cols,
+                               (int)p.batch);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace selscan

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "selscan.h"
+
 namespace selscan {
 
 constexpr int kScanThreads = 256;   // channels per workgroup of the scan kernels (4 waves)
@@ -53,6 +55,24 @@ struct LaunchBwd {
     float* ws_dc3;    // [B, nchunks, D, 3] conv-input gradient of each chunk's first 3 tokens
     int64_t nck;      // checkpoint slots per batch row
 };
+
+// Elementwise kernels of the block (selscan_block.h): one launch description for all.
+struct LaunchBlockOps {
+    enum Op { kRmsNorm, kConvSilu, kConvHistory, kConvStep } op;
+    bool bf16;
+    const void* in; void* out;
+    const float* w; float eps;                 // RMSNorm scale and epsilon
+    const float* conv_w; const float* conv_b; float* hist;
+    int64_t rows; int cols;                    // rows of the norm; channels (d_model or d_inner)
+    int64_t L; int64_t batch;                  // sequence length and batch (streams for the step)
+    void* stream;
+};
+hipError_t launch_block_op(const LaunchBlockOps& p);
+
+// Records the calling thread's error detail (ss_last_error) and returns s.
+ss_status set_error(ss_status s, const char* msg);
+// The scan's own dims check (ss_conv_scan_fwd / ss_step), for callers that validate first.
+ss_status validate_dims(const ss_dims* d, bool step);
 
 // One entry per instantiation unit (I/O dtype x write rule); step selects the
 // decode-step kernel instead of the full-sequence scan.

@@ -24,7 +24,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["ss_workspace_bytes", "ss_conv_scan_fwd", "ss_step", "ss_status_str",
                                            "ss_last_error", "ss_version", "ss_time_next_call",
-                                           "ss_bwd_workspace_bytes", "ss_conv_scan_bwd"])
+                                           "ss_bwd_workspace_bytes", "ss_conv_scan_bwd",
+                                           "ss_block_workspace_bytes", "ss_block_fwd", "ss_block_step"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ss.ss_version() == 3
+    assert ss.ss_version() == 4
     assert ss.lib.ss_status_str(0) == b"ok"
     assert b"workspace" in ss.lib.ss_status_str(3)
 
@@ -45,6 +46,8 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(ss.ss_dims) == 40
     assert ctypes.sizeof(ss.ss_args) == 13 * ctypes.sizeof(ctypes.c_void_p)
     assert ctypes.sizeof(ss.ss_grads) == 15 * ctypes.sizeof(ctypes.c_void_p)
+    assert ctypes.sizeof(ss.ss_block_dims) == 56
+    assert ctypes.sizeof(ss.ss_block_weights) == 10 * ctypes.sizeof(ctypes.c_void_p)
 
 
 def _dims(**kw):
@@ -196,3 +199,48 @@ def test_bwd_rejects_overlaps_and_small_workspace():
     assert _bwd(_dims(), a, _fake_grads(dB=g.dC + 4)) == 1
     assert _bwd(_dims(), a, g, ws_bytes=ss.ss_bwd_workspace_bytes(_dims()) - 1) == 3
     assert _bwd(_dims(), a, g, ws=(1 << 47) + 8) == 1                               # misaligned workspace
+
+
+# ----------------------------------------------------------------------------- block
+
+def _bdims(**kw):
+    d = dict(batch=2, seqlen=16, d_model=64, d_inner=128, d_state=16, dt_rank=4, io_dtype=ss.SS_F32, norm_eps=1e-5)
+    d.update(kw)
+    return ss.block_dims(d["batch"], d["seqlen"], d["d_model"], d["d_inner"], d["d_state"], d["dt_rank"],
+                         d["io_dtype"], d["norm_eps"], d_conv=d.get("d_conv", 4))
+
+
+def _bweights(**kw):
+    base = 1 << 45
+    w = {n: base + i * (1 << 32) for i, n in enumerate(["norm_w", "W_in", "conv_w", "conv_b", "W_x", "W_dt",
+                                                         "dt_bias", "A", "Dskip", "W_out"])}
+    w.update(kw)
+    return ss.ss_block_weights(**w)
+
+
+def _block(dims, w, x=(1 << 46), out=(1 << 46) + (1 << 40), h=None, c=None, step=False, ws=(1 << 47), ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = ss.ss_block_workspace_bytes(dims, step)
+    fn = ss.lib.ss_block_step if step else ss.lib.ss_block_fwd
+    return fn(ctypes.byref(dims), ctypes.byref(w), x, out, h, c, ws, ws_bytes, None)
+
+
+def test_block_workspace_size():
+    assert ss.ss_block_workspace_bytes(_bdims(), False) > 32 << 20
+    assert ss.ss_block_workspace_bytes(_bdims(batch=0), False) == 0
+
+
+@pytest.mark.parametrize("field", ["norm_w", "W_in", "conv_w", "W_x", "W_dt", "A", "W_out"])
+def test_block_null_weight_rejected(field):
+    assert _block(_bdims(), _bweights(**{field: None})) == 1
+    assert field in ss.lib.ss_last_error().decode()
+
+
+def test_block_rejects_bad_arguments():
+    assert _block(_bdims(norm_eps=0.0), _bweights()) == 1
+    assert _block(_bdims(d_state=12), _bweights()) == 2                      # the scan's own check
+    assert _block(_bdims(d_conv=3), _bweights()) == 2
+    assert _block(_bdims(), _bweights(W_in=(1 << 45) + 8)) == 1               # GEMM weight not 16-byte aligned
+    assert _block(_bdims(), _bweights(), out=(1 << 46) + 64) == 1              # out partly overlaps x
+    assert _block(_bdims(), _bweights(), step=True) == 1                       # the step needs both states
+    assert _block(_bdims(), _bweights(), ws_bytes=ss.ss_block_workspace_bytes(_bdims(), False) - 1) == 3

@@ -1,0 +1,115 @@
+"""GPU parity of the Mamba block (ss_block_fwd / ss_block_step: RMSNorm, hipBLASLt
+projections, conv + SiLU, the scan, gate and residual) against the fp64 block oracle
+on the same seeded weights and inputs. The block shape is the Mamba(d_model=512,
+d_state=16, d_conv=4, expand=2) example of the bembew.net page ("Code Example").
+Tolerances as for the scan: max relative error (rms floor) 1e-4 with fp32 I/O; with
+bf16 I/O the library rounds every intermediate activation (GEMM outputs, u, y) to
+bf16 while the oracle keeps them in fp64, so 2e-2."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.block as ob
+import workloads as W
+from gpu_util import TOL, host, maxrel
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ss():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_73_amd as mod
+    return mod
+
+
+def dev_weights(w, io):
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    out = {}
+    for k, v in w.items():
+        t = torch.from_numpy(np.ascontiguousarray(v, np.float32)).cuda()
+        out[k] = t.to(tdt) if k in ("W_in", "W_x", "W_dt", "W_out") else t
+    return out
+
+
+def run_case(ss, spec, *, states, L=None, Bsz=None, inplace=False, label=""):
+    w = W.gen_block_weights(spec)
+    x = W.gen_block_input(spec, batch=Bsz, seqlen=L)
+    Bn, Ln, _ = x.shape
+    st = W.gen_states(Bn, spec.d_inner, spec.d_state, seed=spec.seed + 3) if states else None
+    g = dev_weights(w, spec.io_dtype)
+    tdt = torch.bfloat16 if spec.io_dtype == "bf16" else torch.float32
+    xd = torch.from_numpy(x).cuda().to(tdt)
+    hs = torch.from_numpy(st["ssm_state"]).cuda() if states else None
+    cs = torch.from_numpy(st["conv_state"]).cuda() if states else None
+    out = ss.ss_block_fwd(xd, g, spec.rank, ssm_state=hs, conv_state=cs, out=xd if inplace else None)
+    torch.cuda.synchronize()
+    ro, rh, rc = ob.block_forward(x, w, spec.rank, st["ssm_state"] if states else None,
+                                  st["conv_state"] if states else None)
+    e = maxrel(host(out), ro)
+    print(f"{label} out maxrel {e:.3e}", flush=True)
+    tol = TOL[spec.io_dtype]
+    assert e <= tol, (label, e)
+    if states:
+        assert maxrel(host(hs), rh) <= tol and maxrel(host(cs), rc) <= tol
+    return e
+
+
+@pytest.mark.parametrize("states", [False, True])
+def test_block_fwd_f32(ss, states):
+    run_case(ss, W.BLOCKS["block_f32"], states=states, label="block f32")
+
+
+@pytest.mark.parametrize("states", [False, True])
+def test_block_fwd_bf16(ss, states):
+    run_case(ss, W.BLOCKS["block_bf16"], states=states, label="block bf16")
+
+
+def test_block_fwd_in_place(ss):
+    run_case(ss, W.BLOCKS["block_f32"], states=True, L=200, inplace=True, label="block in place")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_block_fwd_ragged(ss, io):
+    """Small and ragged: d_model 48, d_inner 96, N 8, rank 3, L 67 (chunk and tile edges)."""
+    spec = W.BlockSpec("ragged", 3, 67, 48, expand=2, d_state=8, dt_rank=3, io_dtype=io, seed=777)
+    run_case(ss, spec, states=True, label=f"block ragged {io}")
+
+
+def test_block_fwd_chunked_long(ss):
+    """A long sequence with few channels takes the scan's chunked path inside the block."""
+    spec = W.BlockSpec("longblock", 1, 8192, 64, expand=2, d_state=16, io_dtype="f32", seed=778)
+    run_case(ss, spec, states=True, label="block chunked")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_block_steps(ss, io):
+    """Decode: ss_block_step from carried states against the oracle's step, and the
+    steps against the forward over the same tokens."""
+    spec = W.BLOCKS["block_f32" if io == "f32" else "block_bf16"]
+    w = W.gen_block_weights(spec)
+    S, steps = 8, 6
+    x = W.gen_block_input(spec, batch=S, seqlen=steps)
+    st = W.gen_states(S, spec.d_inner, spec.d_state, seed=spec.seed + 5)
+    g = dev_weights(w, io)
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    xd = torch.from_numpy(x).cuda().to(tdt)
+    hs = torch.from_numpy(st["ssm_state"]).cuda()
+    cs = torch.from_numpy(st["conv_state"]).cuda()
+    hr, cr = st["ssm_state"].astype(np.float64), st["conv_state"].astype(np.float64)
+    outs = []
+    for t in range(steps):
+        o = ss.ss_block_step(xd[:, t].contiguous(), g, spec.rank, hs, cs)
+        ro, hr, cr = ob.block_step(x[:, t], w, spec.rank, hr, cr)
+        e = maxrel(host(o), ro)
+        assert e <= TOL[io], (t, e)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert maxrel(host(hs), hr) <= TOL[io] and maxrel(host(cs), cr) <= TOL[io]
+    # the same tokens through the forward from the same initial states
+    hs2 = torch.from_numpy(st["ssm_state"]).cuda()
+    cs2 = torch.from_numpy(st["conv_state"]).cuda()
+    fw = ss.ss_block_fwd(xd, g, spec.rank, ssm_state=hs2, conv_state=cs2)
+    torch.cuda.synchronize()
+    assert maxrel(host(torch.stack(outs, 1)), host(fw)) <= TOL[io]
