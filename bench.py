@@ -2,7 +2,7 @@
 """Benchmark of the selective-scan (S6) forward path and decode step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|train|block]
-                    [--no-decode] [--no-cpu] [--zoh-steps K] [--bwd-steps K]
+                    [--no-decode] [--no-cpu] [--zoh-steps K] [--bwd-steps K] [--block-steps K]
 
 A step is one ss_conv_scan_fwd call over the whole workload (conv1d + SiLU,
 softplus step, discretisation, scan, C.h + D.u readout, SiLU(z) gate), with
@@ -20,6 +20,9 @@ parameters. Prints one JSON line:
   step rate and main-kernel roofline on the same model.
 * bwd: the backward (ss_conv_scan_bwd) on the same inputs with a seeded output
   gradient: whole-call time and the backward-sweep kernel's roofline.
+* block: the Mamba block (ss_block_fwd, hipBLASLt projections around the scan) at
+  d_model 512 and at the training shape (d_model 2560, d_inner 5120), random
+  weights, with its decode step for 64 streams.
 * decode: 64 streams x 32 layers x 256 token steps (d_inner 8192, d_state 16),
   one ss_step per layer and token, timed end to end eagerly and replayed from
   HIP graphs (one graph per token step over the 32 layers); its roofline is
@@ -53,6 +56,11 @@ METRIC = "selective-scan fwd Gelem(B·L·D·N)/s + achieved HBM GB/s vs peak; de
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def progress(msg):
+    """A flushed line on stdout naming the leg about to run (the JSON line stays last)."""
+    print(f"[bench] {msg}", flush=True)
 
 
 def measured_traffic(key: str, digest: str):
@@ -243,6 +251,64 @@ def run_bwd(ss, torch, hip, spec, g, steps, warmup):
     return dict(wall_s=wall, kernel_ms=float(np.mean(kms)), workspace_bytes=int(ws.numel()))
 
 
+def block_gemm_flops(spec, M):
+    """Flops of the block's projections per call: in_proj, x_proj, dt_proj, out_proj."""
+    dm, di, N, R = spec.d_model, spec.d_inner, spec.d_state, spec.rank
+    return 2 * M * (dm * 2 * di + di * (R + 2 * N) + R * di + di * dm)
+
+
+def run_block(ss, torch, hip, spec, steps, warmup, decode_steps):
+    """Block forward over the spec's batch and sequence (inputs resident), timed whole
+    and with the inner scan's kernels by events; then decode steps for 64 streams."""
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if spec.io_dtype == "bf16" else torch.float32
+    w = {}
+    for k, v in W.gen_block_weights(spec).items():
+        t = torch.from_numpy(v).to(dev)
+        w[k] = t.to(tdt) if k in ("W_in", "W_x", "W_dt", "W_out") else t
+    x = torch.from_numpy(W.gen_block_input(spec)).to(dev).to(tdt)
+    out = torch.empty_like(x)
+    dims = ss.block_dims(spec.batch, spec.seqlen, spec.d_model, spec.d_inner, spec.d_state, spec.rank,
+                         ss.SS_BF16 if spec.io_dtype == "bf16" else ss.SS_F32)
+    ws = torch.empty(ss.ss_block_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+
+    def call():
+        ss.ss_block_fwd(x, w, spec.rank, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [[hip.event() for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ss.ss_time_next_call(*ev[i])
+        call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    scan_ms = float(np.mean([hip.elapsed_ms(e[2], e[3]) for e in ev]))
+    for e in ev:
+        for q in e:
+            hip.destroy(q)
+    # decode: 64 streams, one token per step
+    S = 64
+    xs = torch.from_numpy(W.gen_block_input(spec, batch=S, seqlen=1)[:, 0]).to(dev).to(tdt).contiguous()
+    hs = torch.zeros(S, spec.d_inner, spec.d_state, device=dev)
+    cs = torch.zeros(S, spec.d_inner, 3, device=dev)
+    sd = ss.block_dims(S, 1, spec.d_model, spec.d_inner, spec.d_state, spec.rank,
+                       ss.SS_BF16 if spec.io_dtype == "bf16" else ss.SS_F32)
+    sws = torch.empty(ss.ss_block_workspace_bytes(sd, True), dtype=torch.uint8, device=dev)
+    so = torch.empty_like(xs)
+    for _ in range(3):
+        ss.ss_block_step(xs, w, spec.rank, hs, cs, out=so, workspace=sws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(decode_steps):
+        ss.ss_block_step(xs, w, spec.rank, hs, cs, out=so, workspace=sws)
+    torch.cuda.synchronize()
+    dwall = time.perf_counter() - t0
+    return dict(ms=wall / steps * 1e3, scan_ms=scan_ms, decode_ms=dwall / decode_steps * 1e3, streams=S)
+
+
 def run_decode(ss, torch, hip, spec: W.DecodeSpec, token_steps: int):
     dev = torch.device("cuda:0")
     S, D, N, Lyr = spec.streams, spec.d_inner, spec.d_state, spec.layers
@@ -366,6 +432,9 @@ def main():
                     help="timed calls of the zero-order-hold variant on the same inputs (0: skip)")
     ap.add_argument("--bwd-steps", type=int, default=5,
                     help="timed backward calls on the same inputs (0: skip)")
+    ap.add_argument("--block-steps", type=int, default=0,
+                    help="timed calls of the Mamba block (d_model 512 and the training-shaped d_model 2560; "
+                         "0: skip, the default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known-size reference for "
                          "hardware traffic counters)")
@@ -392,6 +461,7 @@ def main():
     spec = W.WORKLOADS[a.workload]
     log(f"[bench] workload {spec}")
     g, sample = prepare_scan(torch, spec, not a.no_cpu)
+    progress(f"scan {spec.name}: {a.steps} steps")
     r = run_scan(ss, torch, hip, spec, g, a.steps, a.warmup)
     Bz, L, D, N = spec.batch, spec.seqlen, spec.d_inner, spec.d_state
     rows = Bz * L * D
@@ -419,6 +489,7 @@ def main():
         "aggregate_kernel_ms": round(r["agg_ms"], 4),
     }
     if a.zoh_steps > 0:
+        progress(f"scan {spec.name} zero-order hold: {a.zoh_steps} steps")
         rz = run_scan(ss, torch, hip, spec, g, a.zoh_steps, a.warmup, zoh=True)
         zms = rz["wall_s"] / a.zoh_steps * 1e3
         zinstr = rows * instr_per_row(N, zoh=True)
@@ -436,6 +507,7 @@ def main():
         }
     if not a.no_decode:
         dspec = W.DECODE
+        progress(f"decode: {dspec.streams} streams x {dspec.layers} layers x {a.decode_steps} steps")
         dr = run_decode(ss, torch, hip, dspec, a.decode_steps)
         tokens = dspec.streams * a.decode_steps
         dbytes = decode_bytes(dspec)
@@ -453,6 +525,7 @@ def main():
             "hbm_gbps_end_to_end_graph": round(dbytes * dspec.layers * a.decode_steps / dr["graph_s"] / 1e9, 1),
         }
     if a.bwd_steps > 0:
+        progress(f"backward {spec.name}: {a.bwd_steps} calls")
         rb = run_bwd(ss, torch, hip, spec, g, a.bwd_steps, 1)
         bms = rb["wall_s"] / a.bwd_steps * 1e3
         binstr = rows * bwd_instr_per_row(N)
@@ -469,6 +542,29 @@ def main():
             "workspace_bytes": rb["workspace_bytes"],
         }
     del g
+    if a.block_steps > 0:
+        torch.cuda.empty_cache()
+        blocks = {}
+        for name in ("block_bf16", "block_train"):
+            bs = W.BLOCKS[name]
+            progress(f"block {name}: B{bs.batch} L{bs.seqlen} d_model {bs.d_model} rank {bs.rank}")
+            rb = run_block(ss, torch, hip, bs, a.block_steps, 2, 64)
+            M = bs.batch * bs.seqlen
+            fl = block_gemm_flops(bs, M)
+            rest_ms = rb["ms"] - rb["scan_ms"]
+            blocks[name] = {
+                "workload": f"Mamba block: batch {bs.batch}, L={bs.seqlen}, d_model {bs.d_model}, d_inner {bs.d_inner}, "
+                            f"d_state {bs.d_state}, dt_rank {bs.rank}, {bs.io_dtype}, random weights",
+                "tokens_per_s": round(M / (rb["ms"] / 1e3), 1), "ms_per_step": round(rb["ms"], 4),
+                "scan_kernel_ms": round(rb["scan_ms"], 4),
+                "gemm_gflop_per_step": round(fl / 1e9, 2),
+                # upper bound on the projections' time: everything but the scan's main kernel
+                "gemm_tflops_lower_bound": round(fl / (rest_ms / 1e3) / 1e12, 1) if rest_ms > 0 else None,
+                "mfma_peak_tflops": 2500.0,
+                "decode": {"streams": rb["streams"], "ms_per_token_step": round(rb["decode_ms"], 4),
+                           "tokens_per_s": round(rb["streams"] / (rb["decode_ms"] / 1e3), 1)},
+            }
+        out["block"] = blocks
     if not a.no_cpu and sample is not None:
         out["cpu_baseline"] = cpu_baseline(sample, spec)
     print(json.dumps(out), flush=True)

@@ -93,7 +93,7 @@ ss_status gemm(bool bf16, int64_t M, int64_t Nout, int64_t K, const void* W, con
                                                              sizeof(wsb)) == HIPBLAS_STATUS_SUCCESS &&
                        hipblasLtMatmulAlgoGetHeuristic(h, p.desc, p.a, p.b, p.c, p.c, pref, 1, res, &n) ==
                            HIPBLAS_STATUS_SUCCESS &&
-                       n > 0;
+                       n > 0 && res[0].state == HIPBLAS_STATUS_SUCCESS && res[0].workspaceSize <= kBlasWorkspace;
                 if (good) p.algo = res[0].algo;
                 if (pref) hipblasLtMatmulPreferenceDestroy(pref);
             }

@@ -227,7 +227,7 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
 // --------------------------------------------------------------------------
 // The backward sweep of one chunk (Euler write term). One lane owns one (b, d) as
 // in the forward. The chunk is taken in 4-token segments from its end. Within a
-// segment the states go in blocks of 8: each block is recomputed forward from the
+// segment the states go in blocks of 4: each block is recomputed forward from the
 // checkpoint (the state before the segment), keeping its five states h_{s-1} ..
 // h_{s+3} and four decays in registers, then swept backward; the per-token sums over
 // states (readout, sum g*B, sum A g a h) collect over the blocks, and the gradients
