@@ -1,5 +1,5 @@
-"""fp64 CPU oracle for the selective-scan (S6) forward path, its decode step and
-its backward (gradients of every input).
+"""fp64 CPU oracle for the selective-scan (S6) forward path, its decode step, its
+backward (gradients of every input) and the bidirectional scan.
 
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package; the HIP library
@@ -12,7 +12,9 @@ builds that file with gcc, widens arrays to float64 and marshals pointers.
 Pinned by ``tests/test_oracle_pins.py`` (closed form, LTI convolution,
 worked example, limits, conv impulse / library conv, gate and skip,
 softplus through a cumulative sum; for the zero-order-hold variant: Van Loan
-``expm``, equilibrium, composition of steps) and ``tests/test_oracle_mutants.py``.
+``expm``, equilibrium, composition of steps; for the bidirectional scan: the
+unrolled two-sided closed form, a two-sided LTI convolution by ``numpy.fft`` and
+the mirror symmetry) and ``tests/test_oracle_mutants.py``.
 """
 from __future__ import annotations
 
@@ -65,6 +67,8 @@ class Oracle:
         lib.oracle_step.restype = ctypes.c_int
         lib.oracle_conv_scan_bwd.argtypes = [ctypes.c_int64] * 5 + [_dp] * 27 + [ctypes.c_int, ctypes.c_int]
         lib.oracle_conv_scan_bwd.restype = ctypes.c_int
+        lib.oracle_conv_scan_bidir.argtypes = [ctypes.c_int64] * 5 + [_dp] * 19 + [ctypes.c_int, ctypes.c_int]
+        lib.oracle_conv_scan_bidir.restype = ctypes.c_int
         self._lib = lib
 
     @staticmethod
@@ -176,6 +180,48 @@ class Oracle:
         return g
 
 
+    BIDIR_KEYS = ("conv_w", "conv_b", "delta", "delta_bias", "A", "B", "C", "D")
+
+    def conv_scan_bidir(self, x, delta, A, B, C, *, conv_w=None, conv_b=None, delta_bias=None, D=None,
+                        z=None, rev: Optional[dict] = None, zoh: bool = False, nthreads: int = 0):
+        """Bidirectional scan: the forward scan plus the same layer over the
+        time-reversed sequence, pre-gate outputs summed, then the SiLU(z) gate.
+        The arguments are the forward direction's; rev holds the backward
+        direction's own parameters (keys BIDIR_KEYS; delta, A, B and C required, the
+        others absent = not used), or None to share the forward's. Zero initial
+        states. Returns y [B,L,D] float64."""
+        x = np.asarray(x)
+        Bsz, L, Dn = x.shape
+        N = np.asarray(A).shape[1]
+        fwd = dict(conv_w=conv_w, conv_b=conv_b, delta=delta, delta_bias=delta_bias, A=A, B=B, C=C, D=D)
+        if rev is None:
+            rev = fwd
+        elif set(rev) - set(self.BIDIR_KEYS):
+            raise ValueError(f"unknown keys in rev: {sorted(set(rev) - set(self.BIDIR_KEYS))}")
+        cw = [q["conv_w"] for q in (fwd, rev) if q.get("conv_w") is not None]
+        K = np.asarray(cw[0]).shape[1] if cw else 4
+        keep = []
+
+        def p(a, shape=None):
+            arr, ptr = self._in(a, shape)
+            keep.append(arr)
+            return ptr
+
+        def params(q):
+            opt = lambda k, shape: p(q.get(k), shape if q.get(k) is not None else None)  # noqa: E731
+            return [opt("conv_w", (Dn, K)), opt("conv_b", (Dn,)), p(q["delta"], (Bsz, L, Dn)),
+                    opt("delta_bias", (Dn,)), p(q["A"], (Dn, N)), p(q["B"], (Bsz, L, N)), p(q["C"], (Bsz, L, N)),
+                    opt("D", (Dn,))]
+
+        y = np.zeros((Bsz, L, Dn), dtype=np.float64)
+        rc = self._lib.oracle_conv_scan_bidir(
+            Bsz, L, Dn, N, K, p(x), p(z, (Bsz, L, Dn) if z is not None else None), y.ctypes.data_as(_dp),
+            *params(fwd), *params(rev), int(bool(zoh)), int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments")
+        return y
+
+
 _default: Optional[Oracle] = None
 
 
@@ -196,3 +242,7 @@ def step(*args, **kwargs):
 
 def conv_scan_bwd(*args, **kwargs):
     return default().conv_scan_bwd(*args, **kwargs)
+
+
+def conv_scan_bidir(*args, **kwargs):
+    return default().conv_scan_bidir(*args, **kwargs)

@@ -368,4 +368,105 @@ int oracle_conv_scan_bwd(int64_t Bsz, int64_t L, int64_t D, int64_t N, int64_t K
     return fail ? -1 : 0;
 }
 
-int oracle_version(void) { return 3; }
+/* ---------------------------------------------------------------------------
+ * Bidirectional scan (ozercemkelahmet.com "Mamba", "Variants and extensions": for
+ * data with no natural order one scan runs forward, one runs backward, and their
+ * results are merged; the same page's "Order is a problem to manage" for tables).
+ *
+ * Readings where the page is silent:
+ *  - the backward scan is the same layer run over the time-reversed sequence: its
+ *    causal conv sees the current and LATER positions (zeros past the end), and its
+ *    state is carried from position t+1 to position t;
+ *  - each direction has its own conv, step-size, A, B, C and skip parameters (pass
+ *    the same arrays to share them); the input x and the gate z are shared;
+ *  - the merge is the sum of the two directions' pre-gate outputs, gated once;
+ *  - both directions start from zero state and return none.
+ * Per batch row b and channel d:
+ *   forward : h_t  = exp(D_t A) h_{t-1} + W_t B_t u_t,        t = 0 .. L-1
+ *   backward: g_t  = exp(D'_t A') g_{t+1} + W'_t B'_t u'_t,   t = L-1 .. 0
+ *             u'_t = SiLU(conv_b' + sum_k conv_w'[k] x_{t+(K-1)-k})
+ *   out_t   = (C_t.h_t + Dskip u_t + C'_t.g_t + Dskip' u'_t) * SiLU(z_t)
+ * with W the Euler or zero-order-hold write coefficient as in the forward above.
+ */
+typedef struct {
+    const double *conv_w, *conv_b, *delta, *delta_bias, *A, *Bm, *Cm, *Dskip;
+} DirParams;
+
+/* One direction over channel (b,d): positions taken in scan order (ascending, or
+ * descending when reverse), its pre-gate output added into acc[t]. */
+static void direction_channel(int64_t L, int64_t D, int64_t N, int64_t K, const double* x,
+                              const DirParams* p, int reverse, int zoh, int64_t b, int64_t d,
+                              double* st, double* acc) {
+    double prev[ORACLE_MAX_K];           /* the K-1 inputs before the current one in scan order, oldest first */
+    for (int64_t k = 0; k < K - 1; ++k) prev[k] = 0.0;
+    for (int64_t n = 0; n < N; ++n) st[n] = 0.0;
+    const double skip = p->Dskip ? p->Dskip[d] : 0.0;
+    const double bias = p->delta_bias ? p->delta_bias[d] : 0.0;
+    for (int64_t i = 0; i < L; ++i) {
+        const int64_t t = reverse ? L - 1 - i : i;       /* the i-th position in scan order */
+        const int64_t at = (b * L + t) * D + d;
+        const int64_t bn = (b * L + t) * N;
+        const double xin = x[at];
+        double uv = xin;
+        if (p->conv_w) {
+            double cv = p->conv_b ? p->conv_b[d] : 0.0;
+            for (int64_t k = 0; k < K - 1; ++k) cv += p->conv_w[d * K + k] * prev[k];
+            cv += p->conv_w[d * K + K - 1] * xin;
+            uv = silu(cv);
+            for (int64_t k = 0; k + 1 < K - 1; ++k) prev[k] = prev[k + 1];
+            if (K > 1) prev[K - 2] = xin;
+        }
+        const double step = softplus(p->delta[at] + bias);
+        double out = skip * uv;
+        for (int64_t n = 0; n < N; ++n) {
+            const double an = p->A[d * N + n];
+            const double wn = (zoh && an != 0.0) ? expm1(step * an) / an : step;
+            st[n] = exp(step * an) * st[n] + wn * p->Bm[bn + n] * uv;
+            out += p->Cm[bn + n] * st[n];
+        }
+        acc[t] += out;
+    }
+}
+
+/* Returns 0 on success, -1 on bad arguments. f_* are the forward direction's
+ * parameters, r_* the backward direction's (the same arrays to share them). */
+int oracle_conv_scan_bidir(int64_t Bsz, int64_t L, int64_t D, int64_t N, int64_t K,
+                           const double* x, const double* z, double* y,
+                           const double* f_conv_w, const double* f_conv_b, const double* f_delta,
+                           const double* f_delta_bias, const double* f_A, const double* f_B,
+                           const double* f_C, const double* f_Dskip,
+                           const double* r_conv_w, const double* r_conv_b, const double* r_delta,
+                           const double* r_delta_bias, const double* r_A, const double* r_B,
+                           const double* r_C, const double* r_Dskip, int zoh, int nthreads) {
+    if (Bsz < 0 || L < 0 || D < 0 || N < 1 || N > 1024 || K < 1 || K > ORACLE_MAX_K) return -1;
+    if (!x || !y || !f_delta || !f_A || !f_B || !f_C || !r_delta || !r_A || !r_B || !r_C) return -1;
+    const DirParams fw = {f_conv_w, f_conv_b, f_delta, f_delta_bias, f_A, f_B, f_C, f_Dskip};
+    const DirParams bw = {r_conv_w, r_conv_b, r_delta, r_delta_bias, r_A, r_B, r_C, r_Dskip};
+    const int64_t channels = Bsz * D;
+    int fail = 0;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : omp_get_max_threads())
+    {
+        double st[1024];
+        double* acc = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        if (!acc) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < channels; ++i) {
+            if (!acc) continue;
+            const int64_t b = i / D, d = i % D;
+            for (int64_t t = 0; t < L; ++t) acc[t] = 0.0;
+            direction_channel(L, D, N, K, x, &fw, 0, zoh, b, d, st, acc);
+            direction_channel(L, D, N, K, x, &bw, 1, zoh, b, d, st, acc);
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t at = (b * L + t) * D + d;
+                y[at] = z ? acc[t] * silu(z[at]) : acc[t];
+            }
+        }
+        free(acc);
+    }
+    return fail ? -1 : 0;
+}
+
+int oracle_version(void) { return 4; }

@@ -549,3 +549,132 @@ def pin_bwd_without_optional_pieces(orc, seed=25):
 BWD_PINS = [pin_bwd_finite_differences, pin_bwd_finite_differences_zoh, pin_bwd_autograd, pin_bwd_autograd_zoh,
             pin_bwd_without_optional_pieces]
 ALL_PINS = ALL_PINS + BWD_PINS
+
+
+# ---------------------------------------------------------------------------
+# bidirectional scan (ozercemkelahmet.com "Mamba", "Variants and extensions")
+
+def lib_anticausal_conv_silu(x, conv_w, conv_b):
+    """u' = SiLU(conv_b + sum_k conv_w[k] x_{t+(K-1)-k}), zeros past the end, through
+    torch.nn.functional.conv1d (a cross-correlation) on the right-padded input with the
+    taps in reverse order."""
+    Bsz, L, D = x.shape
+    K = conv_w.shape[1]
+    xt = torch.from_numpy(np.ascontiguousarray(np.transpose(x, (0, 2, 1)))).double()
+    full = torch.cat([xt, torch.zeros(Bsz, D, K - 1, dtype=torch.float64)], dim=2)
+    w = torch.from_numpy(np.ascontiguousarray(np.asarray(conv_w, np.float64)[:, ::-1])).unsqueeze(1)
+    b = None if conv_b is None else torch.from_numpy(np.asarray(conv_b, np.float64))
+    c = torch.nn.functional.conv1d(full, w, b, groups=D)
+    return np.transpose(torch.nn.functional.silu(c).numpy(), (0, 2, 1))
+
+
+def brute_bidir(x, fwd, rev, z=None, zoh=False):
+    """Both directions unrolled by brute force, O(L^2 D N):
+    forward  h_t = sum_{s<=t} exp(A sum_{s<k<=t} Delta_k) W_s B_s u_s,
+    backward g_t = sum_{s>=t} exp(A' sum_{t<=k<s} Delta'_k) W'_s B'_s u'_s,
+    y_t = (C_t.h_t + D u_t + C'_t.g_t + D' u'_t) SiLU(z_t); W = Delta (Euler) or
+    expm1(Delta A)/A (zero-order hold)."""
+    x = np.asarray(x, np.float64)
+    Bsz, L, Dn = x.shape
+    out = np.zeros((Bsz, L, Dn))
+    for q, backward in ((fwd, False), (rev, True)):
+        A = np.asarray(q["A"], np.float64)
+        if q.get("conv_w") is None:
+            u = x
+        elif backward:
+            u = lib_anticausal_conv_silu(x, q["conv_w"], q.get("conv_b"))
+        else:
+            u, _ = lib_conv_silu(x, q["conv_w"], q.get("conv_b"), None)
+        v = np.asarray(q["delta"], np.float64) + (0.0 if q.get("delta_bias") is None else q["delta_bias"])
+        dt = lib_softplus(v)
+        for b in range(Bsz):
+            for t in range(L):
+                hv = np.zeros(A.shape)
+                srange = range(t, L) if backward else range(t + 1)
+                for s in srange:
+                    span = dt[b, t:s].sum(0) if backward else dt[b, s + 1:t + 1].sum(0)   # [D]
+                    decay = np.exp(A * span[:, None])
+                    w = (np.expm1(dt[b, s][:, None] * A) / A) if zoh else dt[b, s][:, None]
+                    hv = hv + decay * w * u[b, s][:, None] * np.asarray(q["B"], np.float64)[b, s][None, :]
+                out[b, t] += (hv * np.asarray(q["C"], np.float64)[b, t][None, :]).sum(1)
+        if q.get("D") is not None:
+            out += np.asarray(q["D"], np.float64)[None, None, :] * u
+    if z is not None:
+        out *= lib_silu(np.asarray(z, np.float64))
+    return out
+
+
+def bidir_case(seed, shape=(2, 9, 3, 4), separate=True, conv=True):
+    rng = np.random.default_rng(seed)
+    c = rand_case(rng, *shape, conv=conv, states=False)
+    keys = ("conv_w", "conv_b", "delta", "delta_bias", "A", "B", "C", "D")
+    fwd = {k: c[k] for k in keys if k in c}
+    if separate:
+        r = rand_case(rng, *shape, conv=conv, states=False)
+        rev = {k: r[k] for k in keys if k in r}
+    else:
+        rev = dict(fwd)
+    return c["x"], c.get("z"), fwd, rev
+
+
+def _bidir_call(orc, x, z, fwd, rev, zoh=False, shared=False):
+    return orc.conv_scan_bidir(x, fwd["delta"], fwd["A"], fwd["B"], fwd["C"], conv_w=fwd.get("conv_w"),
+                               conv_b=fwd.get("conv_b"), delta_bias=fwd.get("delta_bias"), D=fwd.get("D"), z=z,
+                               rev=None if shared else rev, zoh=zoh)
+
+
+def pin_bidir_closed_form(orc, seed=31):
+    """Both directions against their unrolled closed forms, separate and shared
+    parameters (the anti-causal conv through torch conv1d)."""
+    for i, separate in enumerate((True, False)):
+        x, z, fwd, rev = bidir_case(seed + i, separate=separate)
+        y = _bidir_call(orc, x, z, fwd, rev, shared=not separate)
+        ref = brute_bidir(x, fwd, rev, z)
+        assert relerr(y, ref) < 1e-12, relerr(y, ref)
+
+
+def pin_bidir_closed_form_zoh(orc, seed=33):
+    x, z, fwd, rev = bidir_case(seed, shape=(1, 8, 3, 4))
+    y = _bidir_call(orc, x, z, fwd, rev, zoh=True)
+    ref = brute_bidir(x, fwd, rev, z, zoh=True)
+    assert relerr(y, ref) < 1e-12, relerr(y, ref)
+
+
+def pin_bidir_lti_fft(orc, seed=34, Bsz=2, L=48, D=3, N=5):
+    """Delta, B, C fixed over time, shared parameters, no conv: the output is a
+    two-sided convolution y_t = sum_{s<=t} K_{t-s} u_s + sum_{s>=t} K_{s-t} u_s + 2 D u_t
+    with the LTI kernel K_j = sum_n C[n] exp(Delta A[n])^j Delta B[n], by numpy.fft."""
+    rng = np.random.default_rng(seed)
+    A = -rng.uniform(0.05, 1.0, (D, N))
+    Bv, Cv = rng.standard_normal(N), rng.standard_normal(N)
+    dpre = rng.uniform(-3.0, 0.0, D)
+    x = rng.standard_normal((Bsz, L, D))
+    Dsk = rng.standard_normal(D)
+    delta = np.broadcast_to(dpre, (Bsz, L, D)).copy()
+    Bm = np.broadcast_to(Bv, (Bsz, L, N)).copy()
+    Cm = np.broadcast_to(Cv, (Bsz, L, N)).copy()
+    y = orc.conv_scan_bidir(x, delta, A, Bm, Cm, D=Dsk)
+    dt = lib_softplus(dpre)
+    j = np.arange(L)
+    Kj = ((Cv * Bv)[None, None, :] * np.exp(dt[:, None] * A)[None] ** j[:, None, None]).sum(-1) * dt[None, :]
+    nfft = 2 * L
+    Kf = np.fft.rfft(Kj, n=nfft, axis=0)
+    for b in range(Bsz):
+        causal = np.fft.irfft(np.fft.rfft(x[b], n=nfft, axis=0) * Kf, n=nfft, axis=0)[:L]
+        anti = np.fft.irfft(np.fft.rfft(x[b][::-1], n=nfft, axis=0) * Kf, n=nfft, axis=0)[:L][::-1]
+        ref = causal + anti + 2.0 * Dsk[None, :] * x[b]
+        assert relerr(y[b], ref) < 1e-12, relerr(y[b], ref)
+
+
+def pin_bidir_mirror(orc, seed=35):
+    """Reversing the sequence and exchanging the two directions' parameters reverses
+    the output."""
+    x, z, fwd, rev = bidir_case(seed, shape=(2, 11, 3, 4))
+    y = _bidir_call(orc, x, z, fwd, rev)
+    flip = lambda q: {k: (v[:, ::-1].copy() if k in ("delta", "B", "C") else v) for k, v in q.items()}  # noqa: E731
+    ym = _bidir_call(orc, x[:, ::-1].copy(), z[:, ::-1].copy(), flip(rev), flip(fwd))
+    assert relerr(ym[:, ::-1], y) < 1e-13, relerr(ym[:, ::-1], y)
+
+
+BIDIR_PINS = [pin_bidir_closed_form, pin_bidir_closed_form_zoh, pin_bidir_lti_fft, pin_bidir_mirror]
+ALL_PINS = ALL_PINS + BIDIR_PINS

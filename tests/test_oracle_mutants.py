@@ -74,6 +74,21 @@ MUTANTS = {
                                       "g_next[n] = 0.0;")],
     "bwd_final_history_grad_misplaced": [("dxa[L + k] += a->dconv_final[(b * D + d) * H + k];",
                                           "dxa[L + H - 1 - k] += a->dconv_final[(b * D + d) * H + k];")],
+    # bidirectional
+    "bidir_backward_runs_forward": [("const int64_t t = reverse ? L - 1 - i : i;", "const int64_t t = i;")],
+    "bidir_backward_output_not_reversed": [("        acc[t] += out;", "        acc[i] += out;")],
+    "bidir_backward_uses_forward_params": [("direction_channel(L, D, N, K, x, &bw, 1,", "direction_channel(L, D, N, K, x, &fw, 1,")],
+    "bidir_merge_averaged": [("y[at] = z ? acc[t] * silu(z[at]) : acc[t];",
+                              "y[at] = z ? 0.5 * acc[t] * silu(z[at]) : 0.5 * acc[t];")],
+    "bidir_gate_dropped": [("y[at] = z ? acc[t] * silu(z[at]) : acc[t];", "y[at] = acc[t];")],
+    "bidir_skip_dropped": [("double out = skip * uv;", "double out = 0.0 * uv;")],
+    "bidir_decay_from_next_step": [("st[n] = exp(step * an) * st[n] + wn * p->Bm[bn + n] * uv;",
+                                    "st[n] = exp(prevstep * an) * st[n] + wn * p->Bm[bn + n] * uv;"),
+                                   ("        const double step = softplus(p->delta[at] + bias);",
+                                    "        const double step = softplus(p->delta[at] + bias);\n"
+                                    "        const double prevstep = i > 0 ? softplus(p->delta[(b * L + (reverse ? t + 1 : t - 1)) * D + d] + bias) : step;")],
+    "bidir_zoh_ignored": [("const double wn = (zoh && an != 0.0) ?", "const double wn = (0 && an != 0.0) ?")],
+    "bidir_conv_taps_reversed": [("cv += p->conv_w[d * K + k] * prev[k];", "cv += p->conv_w[d * K + (K - 2 - k)] * prev[k];")],
 }
 
 
