@@ -2,7 +2,8 @@
 """Benchmark of the selective-scan (S6) forward path and decode step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|train|block]
-                    [--no-decode] [--no-cpu] [--zoh-steps K] [--bwd-steps K] [--block-steps K]
+                    [--no-decode] [--no-cpu] [--zoh-steps K] [--bidir-steps K] [--bwd-steps K]
+                    [--block-steps K]
 
 A step is one ss_conv_scan_fwd call over the whole workload (conv1d + SiLU,
 softplus step, discretisation, scan, C.h + D.u readout, SiLU(z) gate), with
@@ -18,11 +19,15 @@ parameters. Prints one JSON line:
   view (algorithmic bytes / duration vs 8 TB/s) is given as hbm_view.
 * zoh: the same workload and inputs with the zero-order-hold write term, its
   step rate and main-kernel roofline on the same model.
+* bidir: the bidirectional scan (ss_conv_scan_bidir_fwd) on the same inputs, both
+  directions sharing the parameters: whole-call time and the reversed main pass's
+  roofline on the same model.
 * bwd: the backward (ss_conv_scan_bwd) on the same inputs with a seeded output
   gradient: whole-call time and the backward-sweep kernel's roofline.
-* block: the Mamba block (ss_block_fwd, hipBLASLt projections around the scan) at
-  d_model 512 and at the training shape (d_model 2560, d_inner 5120), random
-  weights, with its decode step for 64 streams.
+* block (only with --block-steps > 0; off by default): the Mamba block
+  (ss_block_fwd, hipBLASLt projections around the scan) at d_model 512 and at the
+  training shape (d_model 2560, d_inner 5120), random weights, with its decode step
+  for 64 streams.
 * decode: 64 streams x 32 layers x 256 token steps (d_inner 8192, d_state 16),
   one ss_step per layer and token, timed end to end eagerly and replayed from
   HIP graphs (one graph per token step over the 32 layers); its roofline is
@@ -176,9 +181,11 @@ def prepare_scan(torch, spec, want_sample):
     return g, sample
 
 
-def run_scan(ss, torch, hip, spec, g, steps, warmup, zoh=False):
+def run_scan(ss, torch, hip, spec, g, steps, warmup, zoh=False, bidir=False):
     """Time `steps` whole forward calls (wall clock between synchronisations) and,
-    with events recorded at the kernels' own start and end, each kernel."""
+    with events recorded at the kernels' own start and end, each kernel. bidir: the
+    bidirectional scan with both directions sharing the parameters (the events then
+    cover the reversed pass's kernels)."""
     tdt = g["x"].dtype
     dev = g["x"].device
     Bz, L, D, N = spec.batch, spec.seqlen, spec.d_inner, spec.d_state
@@ -187,9 +194,15 @@ def run_scan(ss, torch, hip, spec, g, steps, warmup, zoh=False):
     y = torch.empty(Bz, L, D, dtype=tdt, device=dev)
     dims = ss.make_dims(Bz, L, D, N, ss.SS_BF16 if spec.io_dtype == "bf16" else ss.SS_F32,
                         discretization=ss.SS_ZOH if zoh else ss.SS_EULER)
-    ws = torch.empty(max(ss.ss_workspace_bytes(dims), 1), dtype=torch.uint8, device=dev)
+    wsb = ss.ss_bidir_workspace_bytes(dims) if bidir else ss.ss_workspace_bytes(dims)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
     def call():
+        if bidir:
+            ss.ss_conv_scan_bidir_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], conv_w=g["conv_w"],
+                                      conv_b=g["conv_b"], delta_bias=g["delta_bias"], D=g["D"], z=g["z"], y=y,
+                                      workspace=ws, zoh=zoh)
+            return
         ss.ss_conv_scan_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], conv_w=g["conv_w"], conv_b=g["conv_b"],
                             delta_bias=g["delta_bias"], D=g["D"], z=g["z"], ssm_state=h, conv_state=cs, y=y,
                             workspace=ws, zoh=zoh)
@@ -430,6 +443,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--zoh-steps", type=int, default=10,
                     help="timed calls of the zero-order-hold variant on the same inputs (0: skip)")
+    ap.add_argument("--bidir-steps", type=int, default=5,
+                    help="timed bidirectional calls on the same inputs, parameters shared (0: skip)")
     ap.add_argument("--bwd-steps", type=int, default=5,
                     help="timed backward calls on the same inputs (0: skip)")
     ap.add_argument("--block-steps", type=int, default=0,
@@ -504,6 +519,22 @@ def main():
                          "kernel_ms": round(rz["main_ms"], 4), "valu_instr_per_row": instr_per_row(N, zoh=True),
                          "of_which_transcendental": trans_per_row(N), "rows_per_launch": rows},
             "aggregate_kernel_ms": round(rz["agg_ms"], 4),
+        }
+    if a.bidir_steps > 0:
+        progress(f"scan {spec.name} bidirectional: {a.bidir_steps} steps")
+        rbd = run_scan(ss, torch, hip, spec, g, a.bidir_steps, a.warmup, bidir=True)
+        bdms = rbd["wall_s"] / a.bidir_steps * 1e3
+        out["bidir"] = {
+            "workload": "same inputs, forward scan plus the reversed scan sharing the parameters, outputs summed",
+            "value": round(rows * N / (bdms / 1e3) / 1e9, 2), "unit": "Gelem/s", "ms_per_call": round(bdms, 4),
+            "ratio_to_forward": round(bdms / ms_step, 3),
+            "roofline": {"kernel": "k_scan main pass, reversed order", "bound": "alu",
+                         "achieved": round(instrs / (rbd["main_ms"] / 1e3) / 1e12, 3),
+                         "peak": round(VALU_INSTR_PER_S / 1e12, 3), "unit": "T fp32 VALU instr/s",
+                         "frac": round(instrs / (rbd["main_ms"] / 1e3) / VALU_INSTR_PER_S, 4),
+                         "kernel_ms": round(rbd["main_ms"], 4), "valu_instr_per_row": instr_per_row(N),
+                         "rows_per_launch": rows},
+            "aggregate_kernel_ms": round(rbd["agg_ms"], 4),
         }
     if not a.no_decode:
         dspec = W.DECODE

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define SS_VERSION 4
+#define SS_VERSION 5
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
@@ -124,6 +124,36 @@ ss_status ss_conv_scan_fwd(const ss_dims* dims, const ss_args* args,
  * (x, delta, z, y: [B,D]; B, C: [B,N]) from the carried state, updating
  * ssm_state [B,D,N] and conv_state [B,D,K-1] in place. dims->seqlen is ignored. */
 ss_status ss_step(const ss_dims* dims, const ss_args* args, void* stream);
+
+/* The backward direction's own parameters for ss_conv_scan_bidir_fwd. Shapes,
+ * dtypes, alignment and NULL rules are those of the ss_args fields of the same names. */
+typedef struct {
+    const float* conv_w;      /* [D,K] or NULL (no conv in this direction)             */
+    const float* conv_b;      /* [D] or NULL                                            */
+    const void*  delta;       /* [B,L,D] io (required)                                  */
+    const float* delta_bias;  /* [D] or NULL                                            */
+    const float* A;           /* [D,N] (required)                                       */
+    const void*  B;           /* [B,L,N] io (required)                                  */
+    const void*  C;           /* [B,L,N] io (required)                                  */
+    const float* Dskip;       /* [D] or NULL                                            */
+} ss_dir_args;
+
+/* Bidirectional scan (ozercemkelahmet.com "Mamba", "Variants and extensions": one scan
+ * forward, one backward, results merged): the forward scan of `args` plus the same
+ * layer run over the time-reversed sequence, whose conv sees the current and later
+ * positions (zeros past the end) and whose state runs from position t+1 to t. With
+ * yf and yb the two directions' pre-gate outputs (C.h + Dskip u),
+ *     y = (yf + yb) * SiLU(z)      (y = yf + yb without z).
+ * x and z are shared; `rev` holds the backward direction's parameters, or NULL to use
+ * the forward's. Both directions start from zero state: args->ssm_state and
+ * args->conv_state must be NULL (SS_ERR_INVALID_ARG otherwise). `workspace` is device
+ * memory of at least ss_bidir_workspace_bytes(dims) bytes, 256-byte aligned, contents
+ * irrelevant. Two passes on `stream`: the forward pass writes its gated output in fp32
+ * to the workspace, the reversed pass adds its own and writes y (one rounding to the
+ * I/O dtype). */
+size_t ss_bidir_workspace_bytes(const ss_dims* dims);   /* 0 for invalid dims */
+ss_status ss_conv_scan_bidir_fwd(const ss_dims* dims, const ss_args* args, const ss_dir_args* rev,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Gradients for ss_conv_scan_bwd. The loss being differentiated is
  *     sum(dy * y) + sum(dstate_final * ssm_state_out) + sum(dconv_final * conv_state_out)
@@ -229,11 +259,12 @@ ss_status ss_block_step(const ss_block_dims* dims, const ss_block_weights* weigh
                         float* ssm_state, float* conv_state, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Profiling support for benchmarks: events (hipEvent_t handles created by the
- * caller) that the NEXT ss_conv_scan_fwd, ss_conv_scan_bwd or ss_step call made on
- * this thread records around its kernels, at the kernels' own start and end on the
- * call's stream: agg_start/agg_stop around the forward's chunk-aggregate kernel
- * (left unrecorded when the call launches none, and by the backward),
- * main_start/main_stop around the main scan, backward-sweep or decode-step kernel.
+ * caller) that the NEXT ss_conv_scan_fwd, ss_conv_scan_bidir_fwd, ss_conv_scan_bwd or
+ * ss_step call made on this thread records around its kernels, at the kernels' own
+ * start and end on the call's stream: agg_start/agg_stop around the forward's
+ * chunk-aggregate kernel (left unrecorded when the call launches none, and by the
+ * backward), main_start/main_stop around the main scan, backward-sweep or decode-step
+ * kernel. For ss_conv_scan_bidir_fwd both pairs cover the reversed pass's kernels.
  * Any pointer may be NULL. The setting is consumed by that
  * next call, also when it fails. Always returns SS_OK. */
 ss_status ss_time_next_call(void* agg_start, void* agg_stop, void* main_start, void* main_stop);

@@ -39,6 +39,10 @@ class ss_args(ctypes.Structure):
                                    "z", "y", "ssm_state", "conv_state")]
 
 
+class ss_dir_args(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("conv_w", "conv_b", "delta", "delta_bias", "A", "B", "C", "Dskip")]
+
+
 class ss_grads(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("dy", "dstate_final", "dconv_final", "dx", "ddelta", "dz", "dB", "dC", "dA",
                                    "dDskip", "dconv_w", "dconv_b", "ddelta_bias", "dstate_init", "dconv_init")]
@@ -70,6 +74,11 @@ def _load() -> ctypes.CDLL:
     lib.ss_workspace_bytes.restype = ctypes.c_size_t
     lib.ss_conv_scan_fwd.argtypes = [ctypes.POINTER(ss_dims), ctypes.POINTER(ss_args), _vp, ctypes.c_size_t, _vp]
     lib.ss_conv_scan_fwd.restype = ctypes.c_int
+    lib.ss_conv_scan_bidir_fwd.argtypes = [ctypes.POINTER(ss_dims), ctypes.POINTER(ss_args),
+                                           ctypes.POINTER(ss_dir_args), _vp, ctypes.c_size_t, _vp]
+    lib.ss_conv_scan_bidir_fwd.restype = ctypes.c_int
+    lib.ss_bidir_workspace_bytes.argtypes = [ctypes.POINTER(ss_dims)]
+    lib.ss_bidir_workspace_bytes.restype = ctypes.c_size_t
     lib.ss_step.argtypes = [ctypes.POINTER(ss_dims), ctypes.POINTER(ss_args), _vp]
     lib.ss_step.restype = ctypes.c_int
     lib.ss_status_str.argtypes = [ctypes.c_int]
@@ -104,7 +113,8 @@ def ss_version() -> int:
 
 def ss_time_next_call(agg_start=None, agg_stop=None, main_start=None, main_stop=None) -> None:
     """Arm hipEvent_t handles (ints) to be recorded around the kernels of the next
-    ss_conv_scan_fwd / ss_step call on this thread (profiling)."""
+    ss_conv_scan_fwd / ss_conv_scan_bidir_fwd / ss_conv_scan_bwd / ss_step call on this
+    thread (profiling)."""
     lib.ss_time_next_call(agg_start, agg_stop, main_start, main_stop)
 
 
@@ -191,6 +201,55 @@ def ss_conv_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: t
         raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
     _check(lib.ss_conv_scan_fwd(ctypes.byref(dims), ctypes.byref(args), workspace.data_ptr() if need else None,
                                 workspace.numel(), _stream_handle(stream)))
+    return y
+
+
+DIR_KEYS = ("conv_w", "conv_b", "delta", "delta_bias", "A", "B", "C", "D")
+
+
+def ss_bidir_workspace_bytes(dims: ss_dims) -> int:
+    return int(lib.ss_bidir_workspace_bytes(ctypes.byref(dims)))
+
+
+def ss_conv_scan_bidir_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                           C: torch.Tensor, *, conv_w: Optional[torch.Tensor] = None,
+                           conv_b: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                           D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                           rev: Optional[dict] = None, y: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, zoh: bool = False, stream=None) -> torch.Tensor:
+    """Bidirectional scan: the forward scan plus the same layer over the time-reversed
+    sequence, y = (y_fwd + y_bwd) * SiLU(z). Arguments as for ss_conv_scan_fwd (no
+    states); rev: the backward direction's own tensors keyed by DIR_KEYS (delta, A, B,
+    C required, the others absent = not used), or None to share the forward's."""
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, d_inner]")
+    Bsz, L, Dn = x.shape
+    dims = make_dims(Bsz, L, Dn, A.shape[1] if A.dim() == 2 else 0, _io_dtype(x),
+                     discretization=SS_ZOH if zoh else SS_EULER)
+    if y is None:
+        y = torch.empty_like(x)
+    args = _build_args(x, delta, A, B, C, conv_w, conv_b, delta_bias, D, z, y, None, None, (Bsz, L), dims)
+    rargs = None
+    if rev is not None:
+        unknown = set(rev) - set(DIR_KEYS)
+        if unknown:
+            raise ValueError(f"unknown keys in rev: {sorted(unknown)}")
+        for k in ("delta", "A", "B", "C"):
+            if rev.get(k) is None:
+                raise ValueError(f"rev[{k!r}] is required")
+        r = _build_args(x, rev["delta"], rev["A"], rev["B"], rev["C"], rev.get("conv_w"), rev.get("conv_b"),
+                        rev.get("delta_bias"), rev.get("D"), None, y, None, None, (Bsz, L), dims)
+        rargs = ss_dir_args(conv_w=r.conv_w, conv_b=r.conv_b, delta=r.delta, delta_bias=r.delta_bias, A=r.A,
+                            B=r.B, C=r.C, Dskip=r.Dskip)
+    need = ss_bidir_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
+    _check(lib.ss_conv_scan_bidir_fwd(ctypes.byref(dims), ctypes.byref(args),
+                                      ctypes.byref(rargs) if rargs is not None else None,
+                                      workspace.data_ptr() if need else None, workspace.numel(),
+                                      _stream_handle(stream)))
     return y
 
 
@@ -339,6 +398,6 @@ def ss_block_step(x: torch.Tensor, W: dict, dt_rank: int, ssm_state: torch.Tenso
     return _block_call(True, x, W, dt_rank, ssm_state, conv_state, out, workspace, norm_eps, zoh, stream)
 
 
-__all__ = ["ss_block_fwd", "ss_block_step", "ss_block_workspace_bytes", "block_dims", "ss_block_dims",
+__all__ = ["ss_conv_scan_bidir_fwd", "ss_bidir_workspace_bytes", "ss_dir_args", "DIR_KEYS", "ss_block_fwd", "ss_block_step", "ss_block_workspace_bytes", "block_dims", "ss_block_dims",
            "ss_block_weights", "BLOCK_WEIGHTS", "ss_conv_scan_fwd", "ss_conv_scan_bwd", "ss_bwd_workspace_bytes", "ss_grads", "ss_step", "ss_workspace_bytes", "ss_version", "ss_time_next_call", "make_dims", "ss_dims", "ss_args",
            "SelscanError", "SS_F32", "SS_BF16", "SS_EULER", "SS_ZOH", "LIB_PATH", "lib"]

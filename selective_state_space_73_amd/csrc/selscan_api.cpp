@@ -266,6 +266,41 @@ hipError_t launch(const selscan::LaunchScan& p, bool step) {
     return p.zoh ? selscan::launch_f32_zoh(p, step) : selscan::launch_f32_euler(p, step);
 }
 
+// Bidirectional workspace: the scan's (used by each pass in turn), then the forward
+// pass's fp32 output [B, L, D].
+Layout bidir_layout(const ss_dims& d, size_t* off_part = nullptr) {
+    Layout l = layout(d);
+    const size_t off = align256(l.total);
+    if (off_part) *off_part = off;
+    l.total = off + (size_t)d.batch * (size_t)d.seqlen * (size_t)d.d_inner * sizeof(float);
+    return l;
+}
+
+// The workspace of a full-sequence call: size, alignment, no overlap with the arguments.
+ss_status check_workspace(const Layout& l, const ss_args& a, const void* workspace, size_t workspace_bytes) {
+    if (l.total > 0 && (!workspace || workspace_bytes < l.total))
+        return fail(SS_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, l.total);
+    if (workspace && ((uintptr_t)workspace & 255u)) return fail(SS_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+    const Range wr{workspace, l.total, "workspace"};
+    const Range others[] = {{a.x, 1, "x"}, {a.y, 1, "y"}, {a.B, 1, "B"}, {a.C, 1, "C"},
+                            {a.delta, 1, "delta"}, {a.ssm_state, 1, "ssm_state"}};
+    for (const Range& r : others)
+        if (overlap(wr, r)) return fail(SS_ERR_INVALID_ARG, "workspace overlaps %s", r.name);
+    return SS_OK;
+}
+
+void attach_workspace(selscan::LaunchScan& p, const Layout& l, void* workspace) {
+    char* ws = static_cast<char*>(workspace);
+    p.nchunks = l.nchunks;
+    p.chunk_len = l.chunk_len;
+    if (l.nchunks > 1) {
+        p.ws_S = reinterpret_cast<float*>(ws + l.off_S);
+        p.ws_sdt = reinterpret_cast<float*>(ws + l.off_sdt);
+        p.ws_h0 = reinterpret_cast<float*>(ws + l.off_h0);
+        p.ws_c0 = reinterpret_cast<float*>(ws + l.off_c0);
+    }
+}
+
 }  // namespace
 
 namespace selscan {
@@ -283,38 +318,63 @@ size_t ss_workspace_bytes(const ss_dims* dims) {
     return layout(*dims).total;
 }
 
+size_t ss_bidir_workspace_bytes(const ss_dims* dims) {
+    if (check_dims(dims, false) != SS_OK) return 0;
+    return bidir_layout(*dims).total;
+}
+
 ss_status ss_conv_scan_fwd(const ss_dims* dims, const ss_args* args, void* workspace,
                            size_t workspace_bytes, void* stream) {
     ss_status s = check_dims(dims, false);
     if (s == SS_OK) s = check_args(*dims, args, false);
+    const Layout l = s == SS_OK ? layout(*dims) : Layout{};
+    if (s == SS_OK) s = check_workspace(l, *args, workspace, workspace_bytes);
     if (s != SS_OK) { drop_events(); return s; }
-    const Layout l = layout(*dims);
-    if (l.total > 0 && (!workspace || workspace_bytes < l.total)) {
-        drop_events();
-        return fail(SS_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, l.total);
-    }
-    if (workspace && ((uintptr_t)workspace & 255u)) {
-        drop_events();
-        return fail(SS_ERR_INVALID_ARG, "workspace not 256-byte aligned");
-    }
-    const Range wr{workspace, l.total, "workspace"};
-    const Range others[] = {{args->x, 1, "x"}, {args->y, 1, "y"}, {args->B, 1, "B"}, {args->C, 1, "C"},
-                            {args->delta, 1, "delta"}, {args->ssm_state, 1, "ssm_state"}};
-    for (const Range& r : others)
-        if (overlap(wr, r)) { drop_events(); return fail(SS_ERR_INVALID_ARG, "workspace overlaps %s", r.name); }
 
     selscan::LaunchScan p = make_launch(*dims, *args, stream);
     take_events(p);
-    char* ws = static_cast<char*>(workspace);
-    p.nchunks = l.nchunks;
-    p.chunk_len = l.chunk_len;
-    if (l.nchunks > 1) {
-        p.ws_S = reinterpret_cast<float*>(ws + l.off_S);
-        p.ws_sdt = reinterpret_cast<float*>(ws + l.off_sdt);
-        p.ws_h0 = reinterpret_cast<float*>(ws + l.off_h0);
-        p.ws_c0 = reinterpret_cast<float*>(ws + l.off_c0);
-    }
+    attach_workspace(p, l, workspace);
     const hipError_t e = launch(p, false);
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return SS_OK;
+}
+
+ss_status ss_conv_scan_bidir_fwd(const ss_dims* dims, const ss_args* args, const ss_dir_args* rev,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    ss_status s = check_dims(dims, false);
+    if (s == SS_OK) s = check_args(*dims, args, false);
+    if (s == SS_OK && (args->ssm_state || args->conv_state))
+        s = fail(SS_ERR_INVALID_ARG, "a bidirectional scan takes no states (ssm_state and conv_state must be NULL)");
+    // the backward direction: the forward's arguments with its own parameters
+    ss_args ra{};
+    if (s == SS_OK) {
+        ra = *args;
+        if (rev) {
+            ra.conv_w = rev->conv_w; ra.conv_b = rev->conv_b; ra.delta = rev->delta; ra.delta_bias = rev->delta_bias;
+            ra.A = rev->A; ra.B = rev->B; ra.C = rev->C; ra.Dskip = rev->Dskip;
+        }
+        s = check_args(*dims, &ra, false);
+        if (s != SS_OK) s = fail(s, "backward direction: %s", std::string(g_last_error).c_str());
+    }
+    size_t off_part = 0;
+    const Layout l = s == SS_OK ? bidir_layout(*dims, &off_part) : Layout{};
+    if (s == SS_OK) s = check_workspace(l, *args, workspace, workspace_bytes);
+    if (s == SS_OK) s = check_workspace(l, ra, workspace, workspace_bytes);
+    if (s != SS_OK) { drop_events(); return s; }
+
+    // forward pass (its gated output to the fp32 buffer), then the reversed pass (adds
+    // its own and writes y); the scan's part of the workspace is reused in stream order
+    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_part);
+    selscan::LaunchScan pf = make_launch(*dims, *args, stream);
+    attach_workspace(pf, l, workspace);
+    pf.ypart = part;
+    selscan::LaunchScan pr = make_launch(*dims, ra, stream);
+    pr.reverse = true;
+    pr.ypart = part;
+    take_events(pr);
+    attach_workspace(pr, l, workspace);
+    hipError_t e = launch(pf, false);
+    if (e == hipSuccess) e = launch(pr, false);
     if (e != hipSuccess) return fail(SS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return SS_OK;
 }

@@ -617,7 +617,7 @@ static hipError_t launch_bwd_t(const LaunchBwd& q) {
     hipLaunchKernelGGL((k_scan<T, N, CONV, false, false, true>), dim3(gx, nC, (unsigned)p.batch), dim3(kScanThreads), 0,
                        st, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A, Bm, Cm, p.Dskip, nullptr,
                        static_cast<T*>(nullptr), p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0,
-                       q.ws_ckpt, sa);
+                       q.ws_ckpt, nullptr, sa);
     const T* dy = static_cast<const T*>(q.dy);
     if (nC > 1) {
         hipLaunchKernelGGL((k_bagg<T, N, GATE>), dim3(gx, nC - 1, (unsigned)p.batch), dim3(kScanThreads), 0, st,

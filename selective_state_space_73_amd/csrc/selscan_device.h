@@ -159,16 +159,21 @@ constexpr int kCkptEvery = 4;
 // VGPRs) because more resident waves hide the long per-token dependency chains;
 // larger N needs the registers for the state and keeps one-wave-per-SIMD limits.
 // (Without the conv the schedule under that cap spills, so it is left free; the
-// zero-order hold's longer per-state chain with N more registers of 1/A is held to
-// two waves.)
-template <int N, bool CONV, bool ZOH, bool CK> constexpr int scan_waves_per_eu() {
-    return N > 16 ? 1 : (ZOH || CK) ? 2 : CONV ? 3 : 1;
+// zero-order hold's longer per-state chain with N more registers of 1/A, and the
+// reversed pass's extra prefetched y, are held to two waves.)
+template <int N, bool CONV, bool ZOH, bool CK, bool REV> constexpr int scan_waves_per_eu() {
+    return N > 16 ? 1 : (ZOH || CK || REV) ? 2 : CONV ? 3 : 1;
 }
 
 // Zero-order hold: the write coefficient (exp(Delta A) - 1) / A comes from the decay
 // already computed (zoh_coef: one fma, or a short series where Delta A is small).
-template <typename T, int N, bool CONV, bool GATE, bool ZOH, bool CK = false>
-__global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<N, CONV, ZOH, CK>())))
+// A bidirectional scan (ozercemkelahmet.com "Mamba", "Variants and extensions") runs
+// two passes, neither with states in or out. PART: the forward pass, writing its
+// gated output as fp32 to ypart [B, L, D] instead of y. REV: the same layer over the
+// time-reversed sequence, so chunk-relative token r of chunk c is position
+// L-1-(c*chunk_len + r); it adds its gated output to ypart's and writes the sum to y.
+template <typename T, int N, bool CONV, bool GATE, bool ZOH, bool CK = false, bool REV = false, bool PART = false>
+__global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<N, CONV, ZOH, CK, REV>())))
 k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
        const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
        const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
@@ -180,8 +185,10 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
        const float* __restrict__ ws_h0,      // [B, D, N] copy of the initial state (nchunks > 1)
        const float* __restrict__ ws_c0,      // [B, D, K-1] copy of the initial conv history (nchunks > 1)
        float* __restrict__ ckpt,             // CK: [B, nck, N/4, D, 4] state checkpoints
+       float* __restrict__ ypart,            // PART (written) / REV (read): [B, L, D] fp32 forward output
        ScanArgs sa) {
     static_assert(!(CK && GATE), "checkpoint mode has no gate");
+    static_assert(!(CK && (REV || PART)) && !(REV && PART), "one mode per pass");
     const int D = sa.D;
     const int d_raw = blockIdx.x * kScanThreads + threadIdx.x;
     // lanes past the last channel work on the last channel: they compute and store
@@ -194,6 +201,11 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     const int64_t t1 = (t0 + sa.chunk_len < sa.L) ? t0 + sa.chunk_len : sa.L;
     const int nagg = sa.nchunks - 1;
     const bool multi = sa.nchunks > 1;
+    // token v of the scan order sits at row prow(v) of [B, L, *]; consecutive tokens
+    // are sD elements apart in [B, L, D] and sN in [B, L, N]
+    auto prow = [&](int64_t v) -> int64_t { return (int64_t)b * sa.L + (REV ? sa.L - 1 - v : v); };
+    const int64_t sD = REV ? -(int64_t)D : (int64_t)D;
+    constexpr int sN = REV ? -N : N;
 
     // per-channel parameters
     float A2[N];
@@ -222,7 +234,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     if (c == 0) {
         // with several chunks, read the copy the aggregate pass made, because the
         // last chunk overwrites ssm_state
-        const float* src = (ssm_state && multi) ? ws_h0 : ssm_state;
+        const float* src = REV ? nullptr : (ssm_state && multi) ? ws_h0 : ssm_state;
 #pragma unroll
         for (int n = 0; n < N; ++n) h[n] = src ? src[bd * N + n] : 0.0f;
     } else {
@@ -243,12 +255,12 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     // made, because the last chunk overwrites conv_state)
     float x3 = 0.f, x2 = 0.f, x1 = 0.f;
     if (CONV) {
-        const float* hsrc = conv_state ? (multi ? ws_c0 : conv_state) : nullptr;
+        const float* hsrc = (conv_state && !REV) ? (multi ? ws_c0 : conv_state) : nullptr;
         float xh[3];
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
             const int64_t tt = t0 - 3 + j;
-            xh[j] = tt >= 0 ? IO<T>::ld(x + ((int64_t)b * sa.L + tt) * D + d)
+            xh[j] = tt >= 0 ? IO<T>::ld(x + prow(tt) * D + d)
                             : (hsrc ? hsrc[bd * 3 + (3 + tt)] : 0.0f);
         }
         x3 = xh[0]; x2 = xh[1]; x1 = xh[2];
@@ -268,11 +280,14 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     const int nrows = (int)(t1 - t0);
     const unsigned voff = du * (unsigned)sizeof(T);               // lane byte offset within a token row
     const unsigned rowb = (unsigned)D * (unsigned)sizeof(T);      // bytes per token row
-    const int64_t rowbase = (int64_t)b * sa.L + t0;     // global row of the chunk's first token
+    const int64_t rowbase = prow(t0);                   // global row of the chunk's first token
     const T* xb = x + rowbase * D;
     const T* db = delta + rowbase * D;
     const T* zb = GATE ? z + rowbase * D : nullptr;
-    T* yb = CK ? nullptr : y + rowbase * D;
+    T* yb = (CK || PART) ? nullptr : y + rowbase * D;
+    float* ypb = (PART || REV) ? ypart + rowbase * D : nullptr;   // fp32 forward output of the chunk's first token
+    const unsigned voff4 = du * 4u;                      // lane byte offset within an fp32 row
+    const unsigned rowb4 = (unsigned)D * 4u;
     const T* Bb = Bm + rowbase * N;
     const T* Cb = CK ? nullptr : Cm + rowbase * N;
 
@@ -283,14 +298,14 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     auto tile_fetch = [&](int r0) {
         // the tile's rows are contiguous in B and C: one uniform base, a 32-bit offset per element
         const int rlast = nrows - 1 - r0;
-        const T* Bt = Bb + (int64_t)r0 * N;
-        const T* Ct = CK ? nullptr : Cb + (int64_t)r0 * N;
+        const T* Bt = Bb + (int64_t)r0 * sN;
+        const T* Ct = CK ? nullptr : Cb + (int64_t)r0 * sN;
 #pragma unroll
         for (int k = 0; k < PER_THREAD; ++k) {
             const int e0 = tid + k * kScanThreads;
             const int e = e0 < TILE_ELEMS ? e0 : TILE_ELEMS - 1;
             const int r = e / N < rlast ? e / N : rlast;
-            const int off = r * N + e % N;
+            const int off = r * sN + e % N;
             tb[k] = Bt[off];
             if (!CK) tc[k] = Ct[off];
         }
@@ -310,8 +325,8 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     // one token (a long dependent chain, run for a whole group of tokens first so the
     // chains of different tokens overlap). update(): the N-wide state update and
     // readout of one token, with its B/C row read from LDS up front.
-    struct Pro { float u, dt, wv, g; };
-    auto prologue = [&](T xraw, T draw, T zraw) -> Pro {
+    struct Pro { float u, dt, wv, g, yo; };
+    auto prologue = [&](T xraw, T draw, T zraw, float yprev) -> Pro {
         Pro p;
         const float xt = IO<T>::cvt(xraw);
         if (CONV) {
@@ -324,6 +339,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         p.dt = softplus(IO<T>::cvt(draw) + dbias);
         p.wv = p.dt * p.u;
         p.g = GATE ? silu(IO<T>::cvt(zraw)) : 1.0f;
+        p.yo = REV ? yprev : 0.0f;                     // the forward pass's output at this position
         return p;
     };
     auto update = [&](const Pro& p, const float* bct, int r) {
@@ -354,9 +370,10 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
                 ya = __builtin_fmaf(cv[n], h[n], ya);
                 yc = __builtin_fmaf(cv[n + 1], h[n + 1], yc);
             }
-            const float yv = (ya + yc) * p.g;
+            const float yv = REV ? __builtin_fmaf(ya + yc, p.g, p.yo) : (ya + yc) * p.g;
             // lanes past the last channel were clamped to it and store the same value
-            Buf<T>(yb + (int64_t)r * D).st(IO<T>::bits(yv), voff, 0u);
+            if constexpr (PART) Buf<float>(ypb + (int64_t)r * sD).st(yv, voff4, 0u);
+            else Buf<T>(yb + (int64_t)r * sD).st(IO<T>::bits(yv), voff, 0u);
         }
     };
     // checkpoint after chunk-relative row r (CK; the caller checks the spacing)
@@ -366,31 +383,36 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 #pragma unroll
         for (int k = 0; k < N / 4; ++k) dst[(int64_t)k * D] = vf4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
     };
-    auto token = [&](T xraw, T draw, T zraw, const float* bct, int r) {
-        const Pro p = prologue(xraw, draw, zraw);
+    auto token = [&](T xraw, T draw, T zraw, float yprev, const float* bct, int r) {
+        const Pro p = prologue(xraw, draw, zraw, yprev);
         update(p, bct, r);
     };
-    auto group = [&](const T* gx, const T* gd, const T* gz, const float* tile_rows, int r0) {
+    auto group = [&](const T* gx, const T* gd, const T* gz, const float* gy, const float* tile_rows, int r0) {
         Pro p[U];
 #pragma unroll
-        for (int i = 0; i < U; ++i) p[i] = prologue(gx[i], gd[i], gz[i]);
+        for (int i = 0; i < U; ++i) p[i] = prologue(gx[i], gd[i], gz[i], gy[i]);
 #pragma unroll
         for (int i = 0; i < U; ++i) update(p[i], tile_rows + i * NB, r0 + i);
         if constexpr (CK) store_ckpt(r0 + U - 1);      // r0 + U is a multiple of kCkptEvery
     };
     T gx0[U], gd0[U], gz0[U], gx1[U], gd1[U], gz1[U];
-    auto load_group = [&](int r0, T* gx, T* gd, T* gz) {
-        // rows r0 .. r0+U-1 relative to one base per group (clamped to the chunk's last row)
-        const int rb = r0 < nrows ? r0 : nrows - 1;
-        const int64_t off = (int64_t)rb * D;
+    float gy0[U], gy1[U];
+    auto load_group = [&](int r0, T* gx, T* gd, T* gz, float* gy) {
+        // rows r0 .. r0+U-1 (clamped to the chunk's last row) at non-negative byte
+        // offsets from the group's lowest-address row: the first row, or the last one
+        // when the tokens run backward through memory (REV)
+        const int rl = (r0 + U - 1 < nrows) ? r0 + U - 1 : nrows - 1;
+        const int rb = REV ? rl : (r0 < nrows ? r0 : nrows - 1);
+        const int64_t off = (int64_t)rb * sD;
         const Buf<T> bx(xb + off), bdl(db + off);
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const int r = (r0 + i < nrows) ? r0 + i : nrows - 1;
-            const unsigned so = (unsigned)(r - rb) * rowb;
+            const unsigned so = (unsigned)(REV ? rb - r : r - rb) * rowb;
             gx[i] = bx.ld(voff, so);
             gd[i] = bdl.ld(voff, so);
             if (GATE) gz[i] = Buf<T>(zb + off).ld(voff, so);
+            if (REV) gy[i] = Buf<float>(ypb + off).ld(voff4, (unsigned)(rb - r) * rowb4);
         }
     };
 
@@ -398,7 +420,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     if (nrows > 0) {
         tile_fetch(0);
         tile_store(0);
-        load_group(0, gx0, gd0, gz0);
+        load_group(0, gx0, gd0, gz0, gy0);
     }
     __syncthreads();
     for (int tt = 0; tt < nrows; tt += R) {
@@ -407,15 +429,16 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         const float* tile = &sbc[buf][0][0];
         if (tt + R <= nrows) {
             for (int g = 0; g < R; g += 2 * U) {
-                load_group(tt + g + U, gx1, gd1, gz1);
-                group(gx0, gd0, gz0, tile + g * NB, tt + g);
-                load_group(tt + g + 2 * U, gx0, gd0, gz0);
-                group(gx1, gd1, gz1, tile + (g + U) * NB, tt + g + U);
+                load_group(tt + g + U, gx1, gd1, gz1, gy1);
+                group(gx0, gd0, gz0, gy0, tile + g * NB, tt + g);
+                load_group(tt + g + 2 * U, gx0, gd0, gz0, gy0);
+                group(gx1, gd1, gz1, gy1, tile + (g + U) * NB, tt + g + U);
             }
         } else {
             for (int r = tt; r < nrows; ++r) {
-                const int64_t off = (int64_t)r * D;
-                token((xb + off)[du], (db + off)[du], GATE ? (zb + off)[du] : T(0), tile + (r - tt) * NB, r);
+                const int64_t off = (int64_t)r * sD;
+                token((xb + off)[du], (db + off)[du], GATE ? (zb + off)[du] : T(0), REV ? (ypb + off)[du] : 0.0f,
+                      tile + (r - tt) * NB, r);
                 if (CK && ((t0 + r + 1) % kCkptEvery) == 0) store_ckpt(r);
             }
         }
@@ -424,7 +447,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         buf ^= 1;
     }
 
-    if (!CK && c == sa.nchunks - 1) {
+    if (!CK && !REV && !PART && c == sa.nchunks - 1) {
         if (ssm_state) {
 #pragma unroll
             for (int n = 0; n < N; ++n) ssm_state[bd * N + n] = h[n];
@@ -458,7 +481,8 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 
 constexpr int kAggCutLog2 = 40;
 
-template <typename T, int N, bool CONV, bool ZOH>
+// REV: the aggregates of the reversed scan order (see k_scan), no initial states.
+template <typename T, int N, bool CONV, bool ZOH, bool REV = false>
 __global__ void __launch_bounds__(kScanThreads)
 k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
       const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
@@ -476,6 +500,12 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     const int nagg = sa.nchunks - 1;
     const int64_t row0 = (int64_t)b * sa.L;
     const int64_t bd = (int64_t)b * D + d;
+    // token v of the scan order sits at row prow(v); consecutive tokens are sD / sN
+    // elements apart (negative for the reversed order)
+    auto prow = [&](int64_t v) -> int64_t { return row0 + (REV ? sa.L - 1 - v : v); };
+    const int64_t sD = REV ? -(int64_t)D : (int64_t)D;
+    constexpr int sN = REV ? -N : N;
+    if (REV) { ssm_state = nullptr; conv_state = nullptr; }
 
     float A2[N];
     float iA[ZOH ? N : 1];                        // ZOH: 1/A (0 for the A = 0 states)
@@ -517,14 +547,14 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     T tb[PER_THREAD];
     // tile with chunk-relative rows [rlo, rlo + R); rows before the chunk start are
     // clamped to it (they are zero-weight padding)
-    const T* Bc = Bm + (row0 + t0) * N;                   // uniform: B of the chunk's first token
+    const T* Bc = Bm + prow(t0) * N;                      // uniform: B of the chunk's first token
     auto tile_fetch = [&](int rlo) {
 #pragma unroll
         for (int k = 0; k < PER_THREAD; ++k) {
             const int e0 = tid + k * kScanThreads;
             const int e = e0 < TILE_ELEMS ? e0 : TILE_ELEMS - 1;
             const int r = rlo + e / N;
-            tb[k] = Bc[(r < 0 ? 0 : r) * N + e % N];
+            tb[k] = Bc[(r < 0 ? 0 : r) * sN + e % N];
         }
     };
     auto tile_store = [&](int buf) {
@@ -572,10 +602,10 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     // lowest chunk-relative row of x this sweep reads from memory: rows down to -(3+U)
     // are touched (x_{r-3} of the padding rows); below global token 0 nothing exists
     const int minrel = t0 >= 3 + U ? -(3 + U) : (int)-t0;
-    const T* xrow0 = x + (row0 + t0) * D;                 // uniform: token t0 of this batch row
-    const T* drow0 = delta + (row0 + t0) * D;
+    const T* xrow0 = x + prow(t0) * D;                    // uniform: token t0 of this batch row
+    const T* drow0 = delta + prow(t0) * D;
     auto xrel = [&](int r) -> float {                     // x at chunk-relative row r (may be < 0)
-        if (r >= minrel) return IO<T>::cvt(xrow0[(int64_t)r * D + d]);
+        if (r >= minrel) return IO<T>::cvt(xrow0[(int64_t)r * sD + d]);
         const int64_t tt = t0 + r;                       // < 0 here
         return tt == -1 ? hist2 : (tt == -2 ? hist1 : (tt == -3 ? hist0 : 0.0f));
     };
@@ -590,8 +620,8 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
             const int r = gr - 1 - i;
             const int rd = r < 0 ? 0 : r;
             const int rx = (r - 3) < minrel ? minrel : r - 3;
-            pd[i] = (drow0 + (int64_t)rd * D)[du];
-            px[i] = (xrow0 + (int64_t)rx * D)[du];
+            pd[i] = (drow0 + (int64_t)rd * sD)[du];
+            px[i] = (xrow0 + (int64_t)rx * sD)[du];
         }
     };
     bool cut_seen = false;                                // the window at the switch enters xmax once
@@ -726,17 +756,17 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
         float x3 = xrel(-3), x2 = xrel(-2), x1 = xrel(-1);
         double sd = 0.0;
         for (int64_t t = t0; t < t1; ++t) {
-            const float xt = IO<T>::ld(x + (row0 + t) * D + d);
+            const float xt = IO<T>::ld(x + prow(t) * D + d);
             float u = xt;
             if (CONV) {
                 const float cv = __builtin_fmaf(w3, xt, __builtin_fmaf(w2, x1, __builtin_fmaf(w1, x2, __builtin_fmaf(w0, x3, cb))));
                 x3 = x2; x2 = x1; x1 = xt;
                 u = silu(cv);
             }
-            const float dtv = softplus(IO<T>::ld(delta + (row0 + t) * D + d) + dbias);
+            const float dtv = softplus(IO<T>::ld(delta + prow(t) * D + d) + dbias);
             sd += (double)dtv;
             const float w = dtv * u;
-            const T* Bt = Bm + (row0 + t) * N;
+            const T* Bt = Bm + prow(t) * N;
 #pragma unroll
             for (int n = 0; n < N; ++n) {
                 const float tn = dtv * A2[n];
@@ -893,7 +923,7 @@ k_step(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 // ---------------------------------------------------------------------------
 // launchers (templates; each instantiation unit calls dispatch_n for its dtype and rule)
 
-template <typename T, int N, bool CONV, bool GATE, bool ZOH>
+template <typename T, int N, bool CONV, bool GATE, bool ZOH, bool REV = false, bool PART = false>
 static hipError_t launch_scan_t(const LaunchScan& p) {
     const T* x = static_cast<const T*>(p.x);
     const T* dl = static_cast<const T*>(p.delta);
@@ -903,17 +933,17 @@ static hipError_t launch_scan_t(const LaunchScan& p) {
     ScanArgs sa{p.L, p.chunk_len, (int)p.D, p.nchunks, 0};
     const unsigned gx = (unsigned)((p.D + kScanThreads - 1) / kScanThreads);
     if (p.nchunks > 1) {
-        hipExtLaunchKernelGGL((k_agg<T, N, CONV, ZOH>), dim3(gx, p.nchunks - 1, (unsigned)p.batch),
+        hipExtLaunchKernelGGL((k_agg<T, N, CONV, ZOH, REV>), dim3(gx, p.nchunks - 1, (unsigned)p.batch),
                               dim3(kScanThreads), 0, st, static_cast<hipEvent_t>(p.ev_agg[0]),
                               static_cast<hipEvent_t>(p.ev_agg[1]), 0, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
                               static_cast<const T*>(p.B), p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0,
                               p.ws_c0, sa);
     }
-    hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, ZOH>), dim3(gx, p.nchunks, (unsigned)p.batch),
+    hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, ZOH, false, REV, PART>), dim3(gx, p.nchunks, (unsigned)p.batch),
                           dim3(kScanThreads), 0, st, static_cast<hipEvent_t>(p.ev_main[0]),
                           static_cast<hipEvent_t>(p.ev_main[1]), 0, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
                           static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip, z, y, p.ssm_state,
-                          p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, nullptr, sa);
+                          p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, nullptr, p.ypart, sa);
     return hipGetLastError();
 }
 
@@ -940,6 +970,18 @@ static hipError_t dispatch_flags(const LaunchScan& p, bool step) {
         if (conv) return launch_step_t<T, N, true, false, ZOH>(p);
         if (gate) return launch_step_t<T, N, false, true, ZOH>(p);
         return launch_step_t<T, N, false, false, ZOH>(p);
+    }
+    if (p.reverse) {
+        if (conv && gate) return launch_scan_t<T, N, true, true, ZOH, true>(p);
+        if (conv) return launch_scan_t<T, N, true, false, ZOH, true>(p);
+        if (gate) return launch_scan_t<T, N, false, true, ZOH, true>(p);
+        return launch_scan_t<T, N, false, false, ZOH, true>(p);
+    }
+    if (p.ypart) {
+        if (conv && gate) return launch_scan_t<T, N, true, true, ZOH, false, true>(p);
+        if (conv) return launch_scan_t<T, N, true, false, ZOH, false, true>(p);
+        if (gate) return launch_scan_t<T, N, false, true, ZOH, false, true>(p);
+        return launch_scan_t<T, N, false, false, ZOH, false, true>(p);
     }
     if (conv && gate) return launch_scan_t<T, N, true, true, ZOH>(p);
     if (conv) return launch_scan_t<T, N, true, false, ZOH>(p);

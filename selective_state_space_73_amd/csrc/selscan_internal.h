@@ -24,6 +24,9 @@ struct LaunchScan {
     int N;
     bool bf16;
     bool zoh;       // zero-order-hold write term instead of Euler
+    bool reverse;   // the reversed pass of a bidirectional scan: reads ypart, adds its output, writes y
+    float* ypart;   // [B, L, D] fp32 forward output of a bidirectional scan (written by the
+                    // forward pass when reverse is false, read by the reversed pass)
     const void* x; const float* conv_w; const float* conv_b; const void* delta; const float* delta_bias;
     const float* A; const void* B; const void* C; const float* Dskip; const void* z; void* y;
     float* ssm_state; float* conv_state;

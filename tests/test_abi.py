@@ -24,7 +24,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["ss_workspace_bytes", "ss_conv_scan_fwd", "ss_step", "ss_status_str",
                                            "ss_last_error", "ss_version", "ss_time_next_call",
-                                           "ss_bwd_workspace_bytes", "ss_conv_scan_bwd",
+                                           "ss_bwd_workspace_bytes", "ss_conv_scan_bwd", "ss_conv_scan_bidir_fwd",
+                                           "ss_bidir_workspace_bytes",
                                            "ss_block_workspace_bytes", "ss_block_fwd", "ss_block_step"])
 
 
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ss.ss_version() == 4
+    assert ss.ss_version() == 5
     assert ss.lib.ss_status_str(0) == b"ok"
     assert b"workspace" in ss.lib.ss_status_str(3)
 
@@ -48,6 +49,7 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(ss.ss_grads) == 15 * ctypes.sizeof(ctypes.c_void_p)
     assert ctypes.sizeof(ss.ss_block_dims) == 56
     assert ctypes.sizeof(ss.ss_block_weights) == 10 * ctypes.sizeof(ctypes.c_void_p)
+    assert ctypes.sizeof(ss.ss_dir_args) == 8 * ctypes.sizeof(ctypes.c_void_p)
 
 
 def _dims(**kw):
@@ -151,6 +153,62 @@ def test_workspace_alignment_and_overlap_checked():
     assert _call(d, _fake_args(), (1 << 45) + 4, need) == 1
     a = _fake_args()
     assert _call(d, a, a.x, need) == 1
+
+
+# ----------------------------------------------------------------------------- bidirectional
+
+def _fake_dir(**kw):
+    base = 1 << 46
+    r = {}
+    for i, name in enumerate(["conv_w", "conv_b", "delta", "delta_bias", "A", "B", "C", "Dskip"]):
+        r[name] = base + i * (1 << 32)
+    r.update(kw)
+    return ss.ss_dir_args(**r)
+
+
+def _bidir(dims, args, rev, ws=None, ws_bytes=0):
+    return ss.lib.ss_conv_scan_bidir_fwd(ctypes.byref(dims), ctypes.byref(args),
+                                         ctypes.byref(rev) if rev is not None else None, ws, ws_bytes, None)
+
+
+def test_bidir_rejects_states():
+    assert _bidir(_dims(), _fake_args(conv_state=None), None) == 1
+    assert "no states" in ss.lib.ss_last_error().decode()
+    assert _bidir(_dims(), _fake_args(ssm_state=None), None) == 1
+
+
+@pytest.mark.parametrize("field", ["delta", "A", "B", "C"])
+def test_bidir_null_required_backward_parameter_rejected(field):
+    a = _fake_args(ssm_state=None, conv_state=None)
+    assert _bidir(_dims(), a, _fake_dir(**{field: None})) == 1
+    err = ss.lib.ss_last_error().decode()
+    assert "backward direction" in err and field in err
+
+
+def test_bidir_backward_parameters_checked():
+    a = _fake_args(ssm_state=None, conv_state=None)
+    assert _bidir(_dims(), a, _fake_dir(A=(1 << 46) + 4 * (1 << 32) + 2)) == 1
+    assert "aligned" in ss.lib.ss_last_error().decode()
+    assert _bidir(_dims(), a, _fake_dir(B=a.y + 64)) == 1
+    assert "overlaps" in ss.lib.ss_last_error().decode()
+    # shared parameters, or separate ones, pass validation up to the workspace check
+    d = _dims(batch=1, seqlen=1 << 14, d_inner=64)
+    assert _bidir(d, a, None) == 3
+    assert _bidir(d, a, _fake_dir()) == 3
+    need = ss.ss_bidir_workspace_bytes(d)
+    # the scan's workspace plus the forward pass's fp32 output
+    assert need >= ss.ss_workspace_bytes(d) + 1 * (1 << 14) * 64 * 4
+    assert _bidir(d, a, _fake_dir(), 1 << 45, need - 1) == 3
+    assert _bidir(d, a, _fake_dir(), (1 << 45) + 4, need) == 1
+    # an unchunked shape still needs the fp32 buffer
+    assert ss.ss_bidir_workspace_bytes(_dims()) == 2 * 16 * 64 * 4 and ss.ss_workspace_bytes(_dims()) == 0
+    assert ss.ss_bidir_workspace_bytes(_dims(batch=0)) == 0
+
+
+def test_bidir_events_consumed_by_a_failing_call():
+    assert ss.lib.ss_time_next_call(1, 2, 3, 4) == 0
+    assert _bidir(_dims(), _fake_args(), None) == 1
+    assert ss.lib.ss_time_next_call(None, None, None, None) == 0
 
 
 # ----------------------------------------------------------------------------- backward
