@@ -25,9 +25,8 @@ parameters. Prints one JSON line:
 * bwd: the backward (ss_conv_scan_bwd) on the same inputs with a seeded output
   gradient: whole-call time and the backward-sweep kernel's roofline.
 * block (only with --block-steps > 0; off by default): the Mamba block
-  (ss_block_fwd, hipBLASLt projections around the scan) at d_model 512 and at the
-  training shape (d_model 2560, d_inner 5120), random weights, with its decode step
-  for 64 streams.
+  (ss_block_fwd, the library's MFMA projections around the scan) at d_model 512
+  (B2 L1024), random weights, with its decode step (ss_block_step) for 8 streams.
 * decode: 64 streams x 32 layers x 256 token steps (d_inner 8192, d_state 16),
   one ss_step per layer and token, timed end to end eagerly and replayed from
   HIP graphs (one graph per token step over the 32 layers); its roofline is
@@ -56,6 +55,7 @@ PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E
 # (a wave64 instruction holds a SIMD16 for 4 cycles; no packed fp32). Transcendentals
 # issue in one slot too; measured interleaved with fmas they cost 1.3-1.9 slots.
 VALU_INSTR_PER_S = 256 * 4 * 16 * 2.4e9
+BLOCK_DECODE_STREAMS = 8                    # streams of the block's decode leg
 METRIC = "selective-scan fwd Gelem(B·L·D·N)/s + achieved HBM GB/s vs peak; decode tokens/s"
 
 
@@ -270,9 +270,9 @@ def block_gemm_flops(spec, M):
     return 2 * M * (dm * 2 * di + di * (R + 2 * N) + R * di + di * dm)
 
 
-def run_block(ss, torch, hip, spec, steps, warmup, decode_steps):
+def run_block(ss, torch, hip, spec, steps, warmup, decode_steps, streams):
     """Block forward over the spec's batch and sequence (inputs resident), timed whole
-    and with the inner scan's kernels by events; then decode steps for 64 streams."""
+    and with the inner scan's kernels by events; then decode steps for `streams` streams."""
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if spec.io_dtype == "bf16" else torch.float32
     w = {}
@@ -303,7 +303,7 @@ def run_block(ss, torch, hip, spec, steps, warmup, decode_steps):
         for q in e:
             hip.destroy(q)
     # decode: 64 streams, one token per step
-    S = 64
+    S = streams
     xs = torch.from_numpy(W.gen_block_input(spec, batch=S, seqlen=1)[:, 0]).to(dev).to(tdt).contiguous()
     hs = torch.zeros(S, spec.d_inner, spec.d_state, device=dev)
     cs = torch.zeros(S, spec.d_inner, 3, device=dev)
@@ -576,10 +576,11 @@ def main():
     if a.block_steps > 0:
         torch.cuda.empty_cache()
         blocks = {}
-        for name in ("block_bf16", "block_train"):
+        for name in ("block_bf16",):
             bs = W.BLOCKS[name]
-            progress(f"block {name}: B{bs.batch} L{bs.seqlen} d_model {bs.d_model} rank {bs.rank}")
-            rb = run_block(ss, torch, hip, bs, a.block_steps, 2, 64)
+            progress(f"block {name}: B{bs.batch} L{bs.seqlen} d_model {bs.d_model} rank {bs.rank}, "
+                     f"decode {BLOCK_DECODE_STREAMS} streams")
+            rb = run_block(ss, torch, hip, bs, a.block_steps, 2, 64, BLOCK_DECODE_STREAMS)
             M = bs.batch * bs.seqlen
             fl = block_gemm_flops(bs, M)
             rest_ms = rb["ms"] - rb["scan_ms"]

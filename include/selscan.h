@@ -210,7 +210,7 @@ ss_status ss_conv_scan_bwd(const ss_dims* dims, const ss_args* args, const ss_gr
  *   y   = scan(u, delta, A, B, C, Dskip, z)        (ss_conv_scan_fwd / ss_step, conv off)
  *   out = x + y W_out^T
  * Activations x, out [B,L,d_model] and the GEMM weights have the I/O dtype; the
- * GEMMs (hipBLASLt, matrix cores) accumulate in fp32. Readings (the pages name a
+ * GEMMs (this library's, on the matrix cores) accumulate in fp32. Readings (the pages name a
  * normalisation, small projections for the step size, B and C, and residual
  * stacking): pre-norm RMSNorm, a rank-R step-size projection with its bias inside
  * the softplus, unbiased projections. */
@@ -241,16 +241,15 @@ typedef struct {             /* DEVICE pointers, row-major, y = v W^T convention
 } ss_block_weights;
 
 /* Bytes of device workspace for ss_block_fwd (step = 0) or ss_block_step (step != 0):
- * the block's intermediate activations, the scan's workspace and 32 MiB of GEMM
- * scratch. 0 for invalid sizes. */
+ * the block's intermediate activations and the scan's workspace. 0 for invalid sizes. */
 size_t ss_block_workspace_bytes(const ss_block_dims* dims, int step);
 
 /* Block forward over a sequence: out [B,L,d_model] from x [B,L,d_model]. ssm_state
  * [B,Di,N] and conv_state [B,Di,3] (fp32) are the initial states when given and are
  * overwritten with the final ones (NULL: zero, not returned). out may equal x
  * (in place) but not partly overlap it. Activations and GEMM weights must be 16-byte
- * aligned. Everything is validated before anything is enqueued. The GEMM plans are
- * created on first use per device and shape (hipBLASLt handle kept for the process). */
+ * aligned. Everything is validated before anything is enqueued; the call allocates
+ * nothing and keeps no state between calls. */
 ss_status ss_block_fwd(const ss_block_dims* dims, const ss_block_weights* weights, const void* x, void* out,
                        float* ssm_state, float* conv_state, void* workspace, size_t workspace_bytes, void* stream);
 

@@ -6,20 +6,14 @@
 // SiLU on the main branch, step size / B / C as small projections of that branch
 // (ai360xpert.com "Mamba", "The selection mechanism"), the selective scan with its
 // D skip and SiLU gate, the projection back to the model width and the residual.
-// The projections are dense GEMMs on the matrix cores through hipBLASLt (row-major
-// activations times transposed row-major weights, fp32 accumulation); everything
-// else runs in this library's kernels; the residual is fused into the output GEMM
-// as its C operand. Plans (descriptors, layouts and the chosen algorithm) are made
-// once per device and shape and kept for the life of the process.
+// Every step runs in this library's kernels: the projections are its MFMA GEMM
+// (row-major activations times transposed row-major weights, fp32 accumulation), with
+// the residual fused into the output projection's epilogue.
 #include <hip/hip_runtime.h>
-#include <hipblaslt/hipblaslt.h>
 
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
-#include <map>
-#include <mutex>
-#include <tuple>
 
 #include "selscan.h"
 #include "selscan_internal.h"
@@ -35,85 +29,26 @@ ss_status failf(ss_status s, const char* fmt, ...) {
     return selscan::set_error(s, buf);
 }
 
-constexpr size_t kBlasWorkspace = size_t(32) << 20;   // hipBLASLt scratch inside the block workspace
-
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-struct Plan {
-    hipblasLtMatmulDesc_t desc = nullptr;
-    hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
-    hipblasLtMatmulAlgo_t algo{};
-    bool ok = false;
-};
-
-// (device, bf16, m, n, k)
-using PlanKey = std::tuple<int, bool, int64_t, int64_t, int64_t>;
-
-std::mutex g_mu;
-std::map<int, hipblasLtHandle_t> g_handles;
-std::map<PlanKey, Plan> g_plans;
-
 // Y[M, Nout] (+)= X[M, K] * W[Nout, K]^T, all row-major; Cres (if not null) is added
-// (beta = 1) and may equal Y.
+// and may equal Y.
 ss_status gemm(bool bf16, int64_t M, int64_t Nout, int64_t K, const void* W, const void* X, const void* Cres,
-               void* Y, void* ws, hipStream_t st) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return failf(SS_ERR_HIP, "hipGetDevice failed");
-    const hipDataType dt = bf16 ? HIP_R_16BF : HIP_R_32F;
-    Plan plan;
-    hipblasLtHandle_t h = nullptr;
-    {
-        std::lock_guard<std::mutex> lk(g_mu);
-        auto hi = g_handles.find(dev);
-        if (hi == g_handles.end()) {
-            if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS) return failf(SS_ERR_HIP, "hipblasLtCreate failed");
-            g_handles[dev] = h;
-        } else {
-            h = hi->second;
-        }
-        const PlanKey key{dev, bf16, M, Nout, K};
-        auto pi = g_plans.find(key);
-        if (pi == g_plans.end()) {
-            // column-major view: Y^T [Nout, M] = op(W^T [K, Nout]) * X^T [K, M] with op = transpose
-            Plan p;
-            const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
-            bool good = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
-                        hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) == HIPBLAS_STATUS_SUCCESS &&
-                        hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) == HIPBLAS_STATUS_SUCCESS &&
-                        hipblasLtMatrixLayoutCreate(&p.a, dt, K, Nout, K) == HIPBLAS_STATUS_SUCCESS &&
-                        hipblasLtMatrixLayoutCreate(&p.b, dt, K, M, K) == HIPBLAS_STATUS_SUCCESS &&
-                        hipblasLtMatrixLayoutCreate(&p.c, dt, Nout, M, Nout) == HIPBLAS_STATUS_SUCCESS;
-            if (good) {
-                hipblasLtMatmulPreference_t pref = nullptr;
-                const uint64_t wsb = kBlasWorkspace;
-                hipblasLtMatmulHeuristicResult_t res[1];
-                int n = 0;
-                good = hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
-                       hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb,
-                                                             sizeof(wsb)) == HIPBLAS_STATUS_SUCCESS &&
-                       hipblasLtMatmulAlgoGetHeuristic(h, p.desc, p.a, p.b, p.c, p.c, pref, 1, res, &n) ==
-                           HIPBLAS_STATUS_SUCCESS &&
-                       n > 0 && res[0].state == HIPBLAS_STATUS_SUCCESS && res[0].workspaceSize <= kBlasWorkspace;
-                if (good) p.algo = res[0].algo;
-                if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-            }
-            p.ok = good;
-            pi = g_plans.emplace(key, p).first;
-        }
-        plan = pi->second;
-    }
-    if (!plan.ok)
-        return failf(SS_ERR_UNSUPPORTED, "no hipBLASLt algorithm for a %lld x %lld x %lld GEMM", (long long)M,
-                     (long long)Nout, (long long)K);
-    const float alpha = 1.0f, beta = Cres ? 1.0f : 0.0f;
-    const hipblasStatus_t s = hipblasLtMatmul(h, plan.desc, &alpha, W, plan.a, X, plan.b, &beta, Cres ? Cres : Y,
-                                              plan.c, Y, plan.c, &plan.algo, ws, kBlasWorkspace, st);
-    if (s != HIPBLAS_STATUS_SUCCESS) return failf(SS_ERR_HIP, "hipblasLtMatmul failed (%d)", (int)s);
+               void* Y, hipStream_t st) {
+    selscan::LaunchGemm g{};
+    g.bf16 = bf16;
+    g.X = X; g.W = W; g.R = Cres; g.Y = Y;
+    g.M = M; g.N = Nout; g.K = K;
+    g.stream = st;
+    const hipError_t e = selscan::launch_gemm(g);
+    if (e != hipSuccess)
+        return failf(SS_ERR_HIP, "GEMM %lld x %lld x %lld launch failed: %s", (long long)M, (long long)Nout,
+                     (long long)K, hipGetErrorString(e));
     return SS_OK;
 }
 
 struct BlockLayout {
-    size_t xn, xi, z, u, dr, bm, cm, delta, y, scan, blas, total;
+    size_t xn, xi, z, u, dr, bm, cm, delta, y, scan, total;
 };
 
 ss_dims scan_dims(const ss_block_dims& d, bool step) {
@@ -146,7 +81,6 @@ BlockLayout block_layout(const ss_block_dims& d, bool step) {
     l.y = take(M * di * es);
     const ss_dims sd = scan_dims(d, step);
     l.scan = take(step ? 0 : ss_workspace_bytes(&sd));
-    l.blas = take(kBlasWorkspace);
     l.total = off;
     return l;
 }
@@ -197,7 +131,6 @@ ss_status run_block(const ss_block_dims* d, const ss_block_weights* w, const voi
     char* ws = static_cast<char*>(workspace);
     void* xn = ws + l.xn; void* xi = ws + l.xi; void* z = ws + l.z; void* u = ws + l.u; void* dr = ws + l.dr;
     void* bm = ws + l.bm; void* cm = ws + l.cm; void* delta = ws + l.delta; void* y = ws + l.y;
-    void* blas = ws + l.blas;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t L = step ? 1 : d->seqlen;
     const int64_t M = d->batch * L;
@@ -211,8 +144,8 @@ ss_status run_block(const ss_block_dims* d, const ss_block_weights* w, const voi
     if (selscan::launch_block_op(op) != hipSuccess) return failf(SS_ERR_HIP, "RMSNorm launch failed");
 
     const char* W_in = static_cast<const char*>(w->W_in);
-    if ((s = gemm(bf16, M, di, dm, W_in, xn, nullptr, xi, blas, st)) != SS_OK) return s;
-    if ((s = gemm(bf16, M, di, dm, W_in + (size_t)di * dm * es, xn, nullptr, z, blas, st)) != SS_OK) return s;
+    if ((s = gemm(bf16, M, di, dm, W_in, xn, nullptr, xi, st)) != SS_OK) return s;
+    if ((s = gemm(bf16, M, di, dm, W_in + (size_t)di * dm * es, xn, nullptr, z, st)) != SS_OK) return s;
 
     op = selscan::LaunchBlockOps{};
     op.bf16 = bf16;
@@ -232,10 +165,10 @@ ss_status run_block(const ss_block_dims* d, const ss_block_weights* w, const voi
     }
 
     const char* W_x = static_cast<const char*>(w->W_x);
-    if ((s = gemm(bf16, M, R, di, W_x, u, nullptr, dr, blas, st)) != SS_OK) return s;
-    if ((s = gemm(bf16, M, N, di, W_x + (size_t)R * di * es, u, nullptr, bm, blas, st)) != SS_OK) return s;
-    if ((s = gemm(bf16, M, N, di, W_x + (size_t)(R + N) * di * es, u, nullptr, cm, blas, st)) != SS_OK) return s;
-    if ((s = gemm(bf16, M, di, R, w->W_dt, dr, nullptr, delta, blas, st)) != SS_OK) return s;
+    if ((s = gemm(bf16, M, R, di, W_x, u, nullptr, dr, st)) != SS_OK) return s;
+    if ((s = gemm(bf16, M, N, di, W_x + (size_t)R * di * es, u, nullptr, bm, st)) != SS_OK) return s;
+    if ((s = gemm(bf16, M, N, di, W_x + (size_t)(R + N) * di * es, u, nullptr, cm, st)) != SS_OK) return s;
+    if ((s = gemm(bf16, M, di, R, w->W_dt, dr, nullptr, delta, st)) != SS_OK) return s;
 
     ss_args a{};
     a.x = u; a.delta = delta; a.delta_bias = w->dt_bias; a.A = w->A; a.B = bm; a.C = cm; a.Dskip = w->Dskip;
@@ -243,7 +176,7 @@ ss_status run_block(const ss_block_dims* d, const ss_block_weights* w, const voi
     s = step ? ss_step(&sd, &a, stream) : ss_conv_scan_fwd(&sd, &a, ws + l.scan, ss_workspace_bytes(&sd), stream);
     if (s != SS_OK) return s;
 
-    return gemm(bf16, M, dm, di, w->W_out, y, x, out, blas, st);
+    return gemm(bf16, M, dm, di, w->W_out, y, x, out, st);
 }
 
 }  // namespace

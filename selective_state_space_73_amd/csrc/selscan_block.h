@@ -2,7 +2,7 @@
 // the RMSNorm in front of the block and the block's causal conv + SiLU, which is
 // materialised here (as u) because the step-size, B and C projections read it
 // (bembew.net "Overview of Mamba (SSM) Model", "How the Mamba Block Works";
-// ozercemkelahmet.com "Mamba", "The block"). The projections are hipBLASLt GEMMs and
+// ozercemkelahmet.com "Mamba", "The block"). The projections are the GEMM of selscan_gemm.h and
 // the scan is the library's own kernel, both launched from selscan_block.cpp.
 #pragma once
 #include "selscan_device.h"

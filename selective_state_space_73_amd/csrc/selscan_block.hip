@@ -1,10 +1,16 @@
-// Instantiations of the block's elementwise kernels (RMSNorm, conv + SiLU, conv history, conv step).
+// Instantiations of the block's kernels: RMSNorm, conv + SiLU, conv history, conv step
+// and the projections' GEMM.
 #include "selscan_block.h"
+#include "selscan_gemm.h"
 
 namespace selscan {
 
 hipError_t launch_block_op(const LaunchBlockOps& p) {
     return p.bf16 ? launch_block_kernels_t<uint16_t>(p) : launch_block_kernels_t<float>(p);
+}
+
+hipError_t launch_gemm(const LaunchGemm& p) {
+    return p.bf16 ? launch_gemm_t<uint16_t>(p) : launch_gemm_t<float>(p);
 }
 
 }  // namespace selscan

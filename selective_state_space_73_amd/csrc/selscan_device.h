@@ -481,9 +481,25 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 
 constexpr int kAggCutLog2 = 40;
 
+// Tuning knobs of the aggregate pass: rows per prefetched group for N <= 16 and the
+// minimum resident waves per SIMD the register allocation must allow (0: the
+// compiler's own). Larger N keeps groups of 4: with 8 the per-state arrays of the
+// zero-order-hold form at N = 64 no longer fit in registers and go to scratch memory.
+#ifndef SELSCAN_AGG_U
+#define SELSCAN_AGG_U 8
+#endif
+#ifndef SELSCAN_AGG_WAVES
+#define SELSCAN_AGG_WAVES 0
+#endif
+#if SELSCAN_AGG_WAVES > 0
+#define SELSCAN_AGG_ATTR __attribute__((amdgpu_waves_per_eu(SELSCAN_AGG_WAVES)))
+#else
+#define SELSCAN_AGG_ATTR
+#endif
+
 // REV: the aggregates of the reversed scan order (see k_scan), no initial states.
 template <typename T, int N, bool CONV, bool ZOH, bool REV = false>
-__global__ void __launch_bounds__(kScanThreads)
+__global__ void __launch_bounds__(kScanThreads) SELSCAN_AGG_ATTR
 k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
       const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
       const T* __restrict__ Bm, const float* __restrict__ ssm_state, const float* __restrict__ conv_state,
@@ -535,7 +551,7 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
             ws_c0[bd * 3 + 2] = conv_state[bd * 3 + 2];
         }
     }
-    constexpr int U = 4;
+    constexpr int U = N <= 16 ? SELSCAN_AGG_U : 4;
     constexpr int R = kScanTile;
     static_assert(R % (2 * U) == 0, "tiles hold whole pairs of groups");
     constexpr int NB = N + 1;                     // B values and max_n |B| per token

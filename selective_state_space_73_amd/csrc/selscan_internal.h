@@ -72,6 +72,16 @@ struct LaunchBlockOps {
 };
 hipError_t launch_block_op(const LaunchBlockOps& p);
 
+// Y[M, N] = X[M, K] W[N, K]^T (+ R[M, N]), row-major, in the I/O dtype, fp32 accumulation
+// (selscan_gemm.h). R may equal Y.
+struct LaunchGemm {
+    bool bf16;
+    const void* X; const void* W; const void* R; void* Y;
+    int64_t M, N, K;
+    void* stream;
+};
+hipError_t launch_gemm(const LaunchGemm& p);
+
 // Records the calling thread's error detail (ss_last_error) and returns s.
 ss_status set_error(ss_status s, const char* msg);
 // The scan's own dims check (ss_conv_scan_fwd / ss_step), for callers that validate first.

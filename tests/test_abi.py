@@ -284,7 +284,17 @@ def _block(dims, w, x=(1 << 46), out=(1 << 46) + (1 << 40), h=None, c=None, step
 
 
 def test_block_workspace_size():
-    assert ss.ss_block_workspace_bytes(_bdims(), False) > 32 << 20
+    """The block's activations (xn, xi, z, u, dr, B, C, delta, y; 256-byte aligned) plus
+    the scan's workspace: M = 32 rows, d_model 64, d_inner 128, R 4, N 16, fp32."""
+    a = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    M, dm, di, R, N, es = 32, 64, 128, 4, 16, 4
+    acts = a(M * dm * es) + 5 * a(M * di * es) + a(M * R * es) + 2 * a(M * N * es)
+    assert ss.ss_workspace_bytes(ss.make_dims(2, 16, 128, 16, ss.SS_F32)) == 0
+    assert ss.ss_block_workspace_bytes(_bdims(), False) == acts
+    # a long sequence adds the chunked scan's workspace
+    long = _bdims(batch=1, seqlen=1 << 14)
+    scan = ss.ss_workspace_bytes(ss.make_dims(1, 1 << 14, 128, 16, ss.SS_F32))
+    assert scan > 0 and ss.ss_block_workspace_bytes(long, False) >= scan + (1 << 14) * 128 * 4 * 5
     assert ss.ss_block_workspace_bytes(_bdims(batch=0), False) == 0
 
 

@@ -1,4 +1,4 @@
-"""GPU parity of the Mamba block (ss_block_fwd / ss_block_step: RMSNorm, hipBLASLt
+"""GPU parity of the Mamba block (ss_block_fwd / ss_block_step: RMSNorm, MFMA
 projections, conv + SiLU, the scan, gate and residual) against the fp64 block oracle
 on the same seeded weights and inputs. The block shape is the Mamba(d_model=512,
 d_state=16, d_conv=4, expand=2) example of the bembew.net page ("Code Example").

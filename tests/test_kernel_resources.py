@@ -1,0 +1,50 @@
+"""The compiler's resource report of the last build (kept by build.py): no kernel
+holds a private array in scratch memory (scratch without register spills: an array
+indexed at run time), and the chunk-aggregate kernels use no scratch at all. A
+zero-order-hold aggregate kernel at d_state 64 with 8-row groups once put its
+per-state arrays there and faulted on the GPU; this keeps such a build from
+shipping. CPU only: reads the report, runs nothing."""
+import os
+import subprocess
+
+import pytest
+
+from selective_state_space_73_amd import build as B
+
+
+@pytest.fixture(scope="module")
+def report():
+    if not os.path.exists(B.RESOURCES):
+        pytest.skip("no build report (build() has not run in this tree)")
+    r = B.kernel_resources()
+    assert r, "empty resource report"
+    return r
+
+
+def demangle(name):
+    return subprocess.run(["c++filt"], input=name, capture_output=True, text=True).stdout.strip()
+
+
+def test_report_covers_the_kernels(report):
+    names = " ".join(report)
+    for k in ("k_scan", "k_agg", "k_step", "k_bwd", "k_bagg", "k_gemm", "k_rmsnorm"):
+        assert k in names, k
+
+
+def test_no_private_arrays_in_scratch(report):
+    bad = [demangle(n) for n, v in report.items() if v.get("scratch", 0) > 0 and v.get("vgpr_spill", 0) == 0]
+    assert not bad, bad
+
+
+def test_aggregate_kernels_use_no_scratch(report):
+    bad = [demangle(n) for n, v in report.items() if "k_agg" in n and v.get("scratch", 0) > 0]
+    assert not bad, bad
+
+
+def test_benchmarked_kernels_do_not_spill(report):
+    """The kernels of the bf16, d_state 16 workloads (forward, zero-order hold,
+    bidirectional, backward) keep everything in registers."""
+    for n, v in report.items():
+        d = demangle(n)
+        if "unsigned short, 16," in d and any(k in d for k in ("k_scan<", "k_agg<", "k_bwd<", "k_bagg<")):
+            assert v.get("scratch", 0) == 0, d
