@@ -24,7 +24,7 @@ parameters. Prints one JSON line:
   roofline on the same model.
 * bwd: the backward (ss_conv_scan_bwd) on the same inputs with a seeded output
   gradient: whole-call time and the backward-sweep kernel's roofline.
-* block (only with --block-steps > 0; off by default): the Mamba block
+* block: the Mamba block
   (ss_block_fwd, the library's MFMA projections around the scan) at d_model 512
   (B2 L1024), random weights, with its decode step (ss_block_step) for 8 streams.
 * decode: 64 streams x 32 layers x 256 token steps (d_inner 8192, d_state 16),
@@ -447,9 +447,8 @@ def main():
                     help="timed bidirectional calls on the same inputs, parameters shared (0: skip)")
     ap.add_argument("--bwd-steps", type=int, default=5,
                     help="timed backward calls on the same inputs (0: skip)")
-    ap.add_argument("--block-steps", type=int, default=0,
-                    help="timed calls of the Mamba block (d_model 512 and the training-shaped d_model 2560; "
-                         "0: skip, the default)")
+    ap.add_argument("--block-steps", type=int, default=10,
+                    help="timed calls of the Mamba block at d_model 512 (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known-size reference for "
                          "hardware traffic counters)")
@@ -532,6 +531,7 @@ def main():
                          "achieved": round(instrs / (rbd["main_ms"] / 1e3) / 1e12, 3),
                          "peak": round(VALU_INSTR_PER_S / 1e12, 3), "unit": "T fp32 VALU instr/s",
                          "frac": round(instrs / (rbd["main_ms"] / 1e3) / VALU_INSTR_PER_S, 4),
+                         "traffic": measured_traffic("k_scan_main_reversed", digest) if a.workload == "long" else None,
                          "kernel_ms": round(rbd["main_ms"], 4), "valu_instr_per_row": instr_per_row(N),
                          "rows_per_launch": rows},
             "aggregate_kernel_ms": round(rbd["agg_ms"], 4),
@@ -568,6 +568,7 @@ def main():
                          "achieved": round(binstr / (rb["kernel_ms"] / 1e3) / 1e12, 3),
                          "peak": round(VALU_INSTR_PER_S / 1e12, 3), "unit": "T fp32 VALU instr/s",
                          "frac": round(binstr / (rb["kernel_ms"] / 1e3) / VALU_INSTR_PER_S, 4),
+                         "traffic": measured_traffic("k_bwd", digest) if a.workload == "long" else None,
                          "kernel_ms": round(rb["kernel_ms"], 4), "valu_instr_per_row": bwd_instr_per_row(N),
                          "rows_per_launch": rows},
             "workspace_bytes": rb["workspace_bytes"],
