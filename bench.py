@@ -23,7 +23,8 @@ parameters. Prints one JSON line:
   directions sharing the parameters: whole-call time and the reversed main pass's
   roofline on the same model.
 * bwd: the backward (ss_conv_scan_bwd) on the same inputs with a seeded output
-  gradient: whole-call time and the backward-sweep kernel's roofline.
+  gradient: whole-call time and the backward-sweep kernel's roofline; the same for
+  the zero-order hold (whole-call and sweep-kernel time).
 * block: the Mamba block
   (ss_block_fwd, the library's MFMA projections around the scan) at d_model 512
   (B2 L1024), random weights, with its decode step (ss_block_step) for 8 streams.
@@ -228,19 +229,21 @@ def run_scan(ss, torch, hip, spec, g, steps, warmup, zoh=False, bidir=False):
                 main_ms_min=float(np.min(main_ms)))
 
 
-def run_bwd(ss, torch, hip, spec, g, steps, warmup):
+def run_bwd(ss, torch, hip, spec, g, steps, warmup, zoh=False):
     """Time `steps` whole backward calls on the workload's resident inputs with a
     seeded bf16/fp32 output gradient, and the backward-sweep kernel by events."""
     dev = g["x"].device
     rng = np.random.default_rng(spec.seed + 500)
     dy = torch.from_numpy(rng.standard_normal(tuple(g["x"].shape), dtype=np.float32)).to(dev).to(g["x"].dtype)
     Bz, L, D, N = spec.batch, spec.seqlen, spec.d_inner, spec.d_state
-    dims = ss.make_dims(Bz, L, D, N, ss.SS_BF16 if spec.io_dtype == "bf16" else ss.SS_F32)
+    dims = ss.make_dims(Bz, L, D, N, ss.SS_BF16 if spec.io_dtype == "bf16" else ss.SS_F32,
+                        discretization=ss.SS_ZOH if zoh else ss.SS_EULER)
     ws = torch.empty(ss.ss_bwd_workspace_bytes(dims), dtype=torch.uint8, device=dev)
 
     def call():
         return ss.ss_conv_scan_bwd(g["x"], g["delta"], g["A"], g["B"], g["C"], dy, conv_w=g["conv_w"],
-                                   conv_b=g["conv_b"], delta_bias=g["delta_bias"], D=g["D"], z=g["z"], workspace=ws)
+                                   conv_b=g["conv_b"], delta_bias=g["delta_bias"], D=g["D"], z=g["z"], workspace=ws,
+                                   zoh=zoh)
 
     for _ in range(warmup):
         out = call()
@@ -573,6 +576,12 @@ def main():
                          "rows_per_launch": rows},
             "workspace_bytes": rb["workspace_bytes"],
         }
+        progress(f"backward {spec.name} zero-order hold: {a.bwd_steps} calls")
+        rbz = run_bwd(ss, torch, hip, spec, g, a.bwd_steps, 1, zoh=True)
+        bzms = rbz["wall_s"] / a.bwd_steps * 1e3
+        out["bwd"]["zoh"] = {"ms_per_call": round(bzms, 4), "value": round(rows * N / (bzms / 1e3) / 1e9, 2),
+                             "unit": "Gelem/s", "sweep_kernel_ms": round(rbz["kernel_ms"], 4),
+                             "ratio_to_zoh_forward": round(bzms / out["zoh"]["ms_per_step"], 3) if "zoh" in out else None}
     del g
     if a.block_steps > 0:
         torch.cuda.empty_cache()

@@ -191,8 +191,9 @@ size_t ss_bwd_workspace_bytes(const ss_dims* dims);
  * NULL = zero; args->y is ignored). The chain rule through the forward's steps in
  * reverse order: the state adjoint runs backward in time (g_t = C_t dy_t SiLU(z_t) +
  * exp(Delta_{t+1} A) g_{t+1}), the states it needs are recomputed from checkpoints
- * rather than stored by the forward. dims->discretization must be SS_EULER
- * (SS_ERR_UNSUPPORTED otherwise). Gradients of per-channel parameters are summed over
+ * rather than stored by the forward. Both write terms (dims->discretization): for the
+ * zero-order hold W = (exp(Delta A) - 1) / A, dW/dDelta = exp(Delta A) and dW/dA =
+ * (Delta exp(Delta A) - W) / A (its series near Delta A = 0). Gradients of per-channel parameters are summed over
  * batch and time, dB / dC over channels, in a fixed order (deterministic). Outputs
  * must not overlap any input, each other or the workspace. Asynchronous on `stream`. */
 ss_status ss_conv_scan_bwd(const ss_dims* dims, const ss_args* args, const ss_grads* grads,

@@ -24,8 +24,11 @@ LIBS = []
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-# packed fp32 instructions are disabled for all device code
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# packed fp32 instructions are disabled for all device code. Fully unrolled loops
+# (#pragma unroll) may be large: the zero-order-hold backward at d_state 64 exceeds
+# the compiler's default size limit for them, and a loop left rolled indexes its
+# per-state arrays at run time and moves them to scratch memory.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-pragma-unroll-threshold=200000"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-command-line-argument"]
 

@@ -400,11 +400,7 @@ size_t ss_bwd_workspace_bytes(const ss_dims* dims) {
 ss_status ss_conv_scan_bwd(const ss_dims* dims, const ss_args* args, const ss_grads* grads, void* workspace,
                            size_t workspace_bytes, void* stream) {
     ss_status s = check_dims(dims, false);
-    if (s == SS_OK && dims->discretization != SS_EULER)
-        s = fail(SS_ERR_UNSUPPORTED, "the backward is built for the Euler write term only");
-    if (s == SS_OK) {
-        s = check_args(*dims, args, false, true);
-    }
+    if (s == SS_OK) s = check_args(*dims, args, false, true);
     if (s == SS_OK) s = check_grads(*dims, args, grads);
     if (s != SS_OK) { drop_events(); return s; }
     const BwdLayout l = bwd_layout(*dims);
@@ -447,7 +443,8 @@ ss_status ss_conv_scan_bwd(const ss_dims* dims, const ss_args* args, const ss_gr
     q.ws_dxh = reinterpret_cast<float*>(ws + l.off_dxh);
     q.ws_dc3 = reinterpret_cast<float*>(ws + l.off_dc3);
     q.nck = l.nck;
-    const hipError_t e = q.f.bf16 ? selscan::launch_bwd_bf16_euler(q) : selscan::launch_bwd_f32_euler(q);
+    const hipError_t e = q.f.bf16 ? (q.f.zoh ? selscan::launch_bwd_bf16_zoh(q) : selscan::launch_bwd_bf16_euler(q))
+                                  : (q.f.zoh ? selscan::launch_bwd_f32_zoh(q) : selscan::launch_bwd_f32_euler(q));
     if (e != hipSuccess) return fail(SS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return SS_OK;
 }

@@ -28,6 +28,12 @@ namespace selscan {
 
 static_assert(kCkptEvery == 4, "the backward recomputes 4-token segments");
 
+// dW/dA of the zero-order hold near Delta A = 0: Delta^2 (1/2 + x/3 + x^2/8 + x^3/30) with
+// x = t ln2 (t = Delta A log2(e), the kernels' exponent)
+constexpr float kPsi1 = 0.23104906018664842f;     // ln2 / 3
+constexpr float kPsi2 = 0.060056626739775174f;    // ln2^2 / 8
+constexpr float kPsi3 = 0.011100821732964315f;    // ln2^3 / 30
+
 struct BwdArgs {
     int64_t L;
     int64_t chunk_len;
@@ -233,10 +239,18 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
 // states (readout, sum g*B, sum A g a h) collect over the blocks, and the gradients
 // that need them follow. Lanes past the last channel repeat it (identical stores)
 // and are masked out of the channel sums.
-// two waves per SIMD: the long per-token dependency chains (recompute, adjoint,
-// lane reductions) need a second wave to overlap
-template <typename T, int N, bool CONV, bool GATE>
-__global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(N <= 16 ? 2 : 1)))
+// two waves per SIMD for the Euler form: the long per-token dependency chains
+// (recompute, adjoint, lane reductions) need a second wave to overlap; the
+// zero-order hold's extra per-state terms (1/A, the coefficient and its A-derivative)
+// would spill under that cap, so it runs with the full register file.
+//
+// ZOH: the zero-order-hold write coefficient W = (exp(Delta A) - 1) / A (Delta where
+// A = 0) in place of Delta. Its derivatives: dW/dDelta = exp(Delta A) and
+// dW/dA = (Delta exp(Delta A) - W) / A, which cancels for small Delta A and is taken
+// there as Delta^2 (1/2 + x/3 + x^2/8 + x^3/30), x = Delta A (the series of
+// (x e^x - e^x + 1) / x^2; truncation below 2e-6 for |x| < 0.1).
+template <typename T, int N, bool CONV, bool GATE, bool ZOH = false>
+__global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(N <= 16 && !ZOH ? 2 : 1)))
 k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
       const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
       const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip, const T* __restrict__ z,
@@ -268,8 +282,14 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     const int64_t bd = (int64_t)b * D + d;
 
     float A2[N];
+    float iA[ZOH ? N : 1];                        // ZOH: 1/A (0 for the A = 0 states)
 #pragma unroll
-    for (int n = 0; n < N; ++n) A2[n] = A[(int64_t)d * N + n] * kLog2e;
+    for (int n = 0; n < N; ++n) {
+        const float av = A[(int64_t)d * N + n];
+        const bool zero = ZOH && __builtin_fabsf(av) < kZohZeroA;
+        A2[n] = zero ? 0.0f : av * kLog2e;
+        if (ZOH) iA[n] = zero ? 0.0f : 1.0f / av;
+    }
     const float dbias = delta_bias ? delta_bias[d] : 0.0f;
     const float dsk = Dskip ? Dskip[d] : 0.0f;
     float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 1.f, cb = 0.f;
@@ -384,10 +404,13 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                     dyg[i] = dyv;
                 }
             }
-            // per token, summed over the state blocks: readout, sum g*B, sum A g a h
-            float yacc[S], sgB[S], sA[S];
+            // per token, summed over the state blocks: readout, sum g*B (ZOH: sum g*W*B),
+            // sum A g a h, and for ZOH sum g*a*B
+            float yacc[S], sgB[S], sA[S], sgaB[ZOH ? S : 1];
 #pragma unroll
             for (int i = 0; i < S; ++i) { yacc[i] = dsk * uv[i]; sgB[i] = 0.0f; sA[i] = 0.0f; }
+#pragma unroll
+            for (int i = 0; i < (ZOH ? S : 1); ++i) sgaB[i] = 0.0f;
             // checkpoint slot of the state before the segment: [.., N/4, D, 4]
             const vf4* ck = reinterpret_cast<const vf4*>(ckpt) + ((int64_t)b * ba.nck + (gs > 0 ? gs / S - 1 : 0)) * (N / 4) * D + d;
             // states in blocks of NBK: recompute the block over the segment from the
@@ -412,8 +435,16 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                     const float wv = dtv[i] * uv[i];
 #pragma unroll
                     for (int n = 0; n < NBK; ++n) {
-                        av[i][n] = exp2_fast(dtv[i] * A2[j0 + n]);
-                        hs[i + 1][n] = __builtin_fmaf(av[i][n], hs[i][n], wv * brow[n]);
+                        const float tn = dtv[i] * A2[j0 + n];
+                        av[i][n] = exp2_fast(tn);
+                        if constexpr (ZOH) {
+                            // the write coefficient is recomputed in the sweep below rather
+                            // than kept (registers)
+                            const float w = zoh_coef(av[i][n], tn, dtv[i], iA[j0 + n]);
+                            hs[i + 1][n] = __builtin_fmaf(av[i][n], hs[i][n], w * (uv[i] * brow[n]));
+                        } else {
+                            hs[i + 1][n] = __builtin_fmaf(av[i][n], hs[i][n], wv * brow[n]);
+                        }
                     }
                 }
 #pragma unroll
@@ -424,24 +455,40 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                     const float* crow = tile + (int64_t)r * V + N + j0;
                     const float dygm = dyg[i] * livef;
                     const float dtum = dtv[i] * uv[i] * livef;
+                    const float um = uv[i] * livef;
                     float vals[2 * NBK];
-                    float ya = 0.0f, gb = 0.0f, sa = 0.0f;
+                    float ya = 0.0f, gb = 0.0f, sa = 0.0f, gab = 0.0f;
 #pragma unroll
                     for (int n = 0; n < NBK; ++n) {
                         const int m = j0 + n;
                         ya = __builtin_fmaf(crow[n], hs[i + 1][n], ya);
                         const float g = __builtin_fmaf(crow[n], dyg[i], gc[m]);
                         vals[NBK + n] = dygm * hs[i + 1][n];
-                        vals[n] = g * dtum;
-                        gb = __builtin_fmaf(g, brow[n], gb);
                         const float gq = g * (av[i][n] * hs[i][n]);
                         sa = __builtin_fmaf(A2[m], gq, sa);
-                        dAacc[m] = __builtin_fmaf(dtv[i], gq, dAacc[m]);
+                        if constexpr (ZOH) {
+                            const float tn = dtv[i] * A2[m];
+                            const float w = zoh_coef(av[i][n], tn, dtv[i], iA[m]);
+                            const float gB = g * brow[n];
+                            vals[n] = g * w * um;
+                            gb = __builtin_fmaf(gB, w, gb);
+                            gab = __builtin_fmaf(gB, av[i][n], gab);
+                            const float dt2 = dtv[i] * dtv[i];
+                            const float ser = dt2 * __builtin_fmaf(tn, __builtin_fmaf(tn, __builtin_fmaf(tn, kPsi3, kPsi2), kPsi1), 0.5f);
+                            const float dir = __builtin_fmaf(dtv[i], av[i][n], -w) * iA[m];
+                            const float dwda = __builtin_fabsf(tn) < kZohSeriesT ? ser : dir;
+                            dAacc[m] = __builtin_fmaf(dtv[i], gq, __builtin_fmaf(dwda, gB * uv[i], dAacc[m]));
+                        } else {
+                            vals[n] = g * dtum;
+                            gb = __builtin_fmaf(g, brow[n], gb);
+                            dAacc[m] = __builtin_fmaf(dtv[i], gq, dAacc[m]);
+                        }
                         gc[m] = av[i][n] * g;
                     }
                     yacc[i] += ya;
                     sgB[i] += gb;
                     sA[i] += sa;
+                    if constexpr (ZOH) sgaB[ZOH ? i : 0] += gab;
                     // channel sums of this token's dB/dC partials of the block
                     wave_sum<2 * NBK>(vals, lane);
                     using WB = WaveSum<2 * NBK>;
@@ -467,8 +514,10 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                     Buf<T>(dz + rowoff + row).st(IO<T>::bits(dzv), du * (unsigned)sizeof(T), 0u);
                 }
                 dDacc = __builtin_fmaf(dyg[i], uv[i], dDacc);
-                const float dDelta = __builtin_fmaf(sA[i], kLn2, uv[i] * sgB[i]);
-                const float dU = __builtin_fmaf(dsk, dyg[i], dtv[i] * sgB[i]);
+                // Euler: dW/dDelta = 1 and du gets Delta sum g B; ZOH: dW/dDelta = a and
+                // du gets sum g W B directly
+                const float dDelta = __builtin_fmaf(sA[i], kLn2, uv[i] * (ZOH ? sgaB[ZOH ? i : 0] : sgB[i]));
+                const float dU = __builtin_fmaf(dsk, dyg[i], ZOH ? sgB[i] : dtv[i] * sgB[i]);
                 const float ddel = dDelta * rcp_fast(1.0f + exp2_fast(-kLog2e * vv[i]));   // softplus' = sigmoid
                 Buf<T>(ddelta + rowoff + row).st(IO<T>::bits(ddel), du * (unsigned)sizeof(T), 0u);
                 dbacc += ddel;
@@ -596,7 +645,7 @@ k_bwd_dx_halo(const float* __restrict__ ws_dxh, const float* __restrict__ ws_dc3
 // --------------------------------------------------------------------------
 // launcher
 
-template <typename T, int N, bool CONV, bool GATE>
+template <typename T, int N, bool CONV, bool GATE, bool ZOH>
 static hipError_t launch_bwd_t(const LaunchBwd& q) {
     const LaunchScan& p = q.f;
     hipStream_t st = static_cast<hipStream_t>(p.stream);
@@ -610,11 +659,11 @@ static hipError_t launch_bwd_t(const LaunchBwd& q) {
     ScanArgs sa{p.L, p.chunk_len, (int)p.D, nC, q.nck};
     BwdArgs ba{p.L, p.chunk_len, (int)p.D, nC, q.nck, (int)gx};
     if (nC > 1) {
-        hipLaunchKernelGGL((k_agg<T, N, CONV, false>), dim3(gx, nC - 1, (unsigned)p.batch), dim3(kScanThreads), 0, st,
+        hipLaunchKernelGGL((k_agg<T, N, CONV, ZOH>), dim3(gx, nC - 1, (unsigned)p.batch), dim3(kScanThreads), 0, st,
                            x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A, Bm, p.ssm_state, p.conv_state, p.ws_S,
                            p.ws_sdt, p.ws_h0, p.ws_c0, sa);
     }
-    hipLaunchKernelGGL((k_scan<T, N, CONV, false, false, true>), dim3(gx, nC, (unsigned)p.batch), dim3(kScanThreads), 0,
+    hipLaunchKernelGGL((k_scan<T, N, CONV, false, ZOH, true>), dim3(gx, nC, (unsigned)p.batch), dim3(kScanThreads), 0,
                        st, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A, Bm, Cm, p.Dskip, nullptr,
                        static_cast<T*>(nullptr), p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0,
                        q.ws_ckpt, nullptr, sa);
@@ -623,7 +672,7 @@ static hipError_t launch_bwd_t(const LaunchBwd& q) {
         hipLaunchKernelGGL((k_bagg<T, N, GATE>), dim3(gx, nC - 1, (unsigned)p.batch), dim3(kScanThreads), 0, st,
                            dl, p.delta_bias, p.A, Cm, z, dy, q.ws_Q, q.ws_qsdt, ba);
     }
-    hipExtLaunchKernelGGL((k_bwd<T, N, CONV, GATE>), dim3(gx, nC, (unsigned)p.batch), dim3(kScanThreads), 0, st,
+    hipExtLaunchKernelGGL((k_bwd<T, N, CONV, GATE, ZOH>), dim3(gx, nC, (unsigned)p.batch), dim3(kScanThreads), 0, st,
                           static_cast<hipEvent_t>(p.ev_main[0]), static_cast<hipEvent_t>(p.ev_main[1]), 0,
                           x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A, Bm, Cm, p.Dskip, z, p.ssm_state, p.conv_state,
                           dy, q.dstate_final, q.dconv_final, static_cast<T*>(q.dx), static_cast<T*>(q.ddelta),
@@ -643,23 +692,23 @@ static hipError_t launch_bwd_t(const LaunchBwd& q) {
     return hipGetLastError();
 }
 
-template <typename T, int N>
+template <typename T, int N, bool ZOH>
 static hipError_t dispatch_bwd_flags(const LaunchBwd& q) {
     const bool conv = q.f.conv_w != nullptr, gate = q.f.z != nullptr;
-    if (conv && gate) return launch_bwd_t<T, N, true, true>(q);
-    if (conv) return launch_bwd_t<T, N, true, false>(q);
-    if (gate) return launch_bwd_t<T, N, false, true>(q);
-    return launch_bwd_t<T, N, false, false>(q);
+    if (conv && gate) return launch_bwd_t<T, N, true, true, ZOH>(q);
+    if (conv) return launch_bwd_t<T, N, true, false, ZOH>(q);
+    if (gate) return launch_bwd_t<T, N, false, true, ZOH>(q);
+    return launch_bwd_t<T, N, false, false, ZOH>(q);
 }
 
-template <typename T>
+template <typename T, bool ZOH>
 static hipError_t dispatch_bwd(const LaunchBwd& q) {
     switch (q.f.N) {
-        case 4: return dispatch_bwd_flags<T, 4>(q);
-        case 8: return dispatch_bwd_flags<T, 8>(q);
-        case 16: return dispatch_bwd_flags<T, 16>(q);
-        case 32: return dispatch_bwd_flags<T, 32>(q);
-        case 64: return dispatch_bwd_flags<T, 64>(q);
+        case 4: return dispatch_bwd_flags<T, 4, ZOH>(q);
+        case 8: return dispatch_bwd_flags<T, 8, ZOH>(q);
+        case 16: return dispatch_bwd_flags<T, 16, ZOH>(q);
+        case 32: return dispatch_bwd_flags<T, 32, ZOH>(q);
+        case 64: return dispatch_bwd_flags<T, 64, ZOH>(q);
         default: return hipErrorInvalidValue;
     }
 }

@@ -95,5 +95,7 @@ hipError_t launch_bf16_euler(const LaunchScan& p, bool step);
 hipError_t launch_bf16_zoh(const LaunchScan& p, bool step);
 hipError_t launch_bwd_f32_euler(const LaunchBwd& p);
 hipError_t launch_bwd_bf16_euler(const LaunchBwd& p);
+hipError_t launch_bwd_f32_zoh(const LaunchBwd& p);
+hipError_t launch_bwd_bf16_zoh(const LaunchBwd& p);
 
 }  // namespace selscan

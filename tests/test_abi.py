@@ -242,9 +242,11 @@ def test_bwd_null_required_gradient_rejected(field):
     assert field in ss.lib.ss_last_error().decode()
 
 
-def test_bwd_rejects_zoh_and_inconsistent_optional_pieces():
+def test_bwd_validates_zoh_like_euler_and_rejects_inconsistent_optional_pieces():
     z = ss.make_dims(2, 16, 64, 16, ss.SS_F32, discretization=ss.SS_ZOH)
-    assert _bwd(z, _fake_args(), _fake_grads()) == 2
+    assert ss.ss_bwd_workspace_bytes(z) == ss.ss_bwd_workspace_bytes(_dims())
+    assert _bwd(z, _fake_args(), _fake_grads(dz=None)) == 1
+    assert _bwd(z, _fake_args(), _fake_grads(), ws_bytes=ss.ss_bwd_workspace_bytes(z) - 1) == 3
     assert _bwd(_dims(), _fake_args(), _fake_grads(dz=None)) == 1                 # z given, dz missing
     assert _bwd(_dims(), _fake_args(z=None), _fake_grads()) == 1                  # dz given, no z
     assert _bwd(_dims(), _fake_args(conv_w=None, conv_state=None), _fake_grads()) == 1   # conv grads, no conv

@@ -2,7 +2,8 @@
 on the same seeded inputs and cotangents: every gradient, with the initial and
 final-state gradients, on small and chunked shapes, ragged lengths and channel
 counts, every d_state, without the optional pieces, and the bench workloads at
-full size. Tolerances by output dtype, max relative error with an rms floor: the
+full size; for the Euler and the zero-order-hold write terms (the latter with
+A = 0 and small-|A| states, which take the series of its A-derivative). Tolerances by output dtype, max relative error with an rms floor: the
 I/O-dtype outputs (dx, ddelta, dz) 1e-4 with fp32 I/O and 2e-2 with bf16 I/O, as
 for the forward; the fp32 outputs (dB, dC, dA, the parameter gradients and the
 initial-state gradients) 1e-4 with either I/O dtype, since both sides compute from
@@ -38,7 +39,7 @@ def _cotangents(Bsz, L, Dn, N, seed, io):
                 dconv_final=rng.standard_normal((Bsz, Dn, 3)).astype(np.float32))
 
 
-def check_bwd(ss, inp, io, *, states=True, finals=True, flags=None, label="", seed=900, full_sums=True):
+def check_bwd(ss, inp, io, *, states=True, finals=True, flags=None, label="", seed=900, full_sums=True, zoh=False):
     f = dict(conv=True, gate=True, skip=True, bias=True)
     f.update(flags or {})
     Bsz, L, Dn = inp["x"].shape
@@ -55,7 +56,7 @@ def check_bwd(ss, inp, io, *, states=True, finals=True, flags=None, label="", se
     dsf = torch.from_numpy(cot["dstate_final"]).cuda() if finals else None
     dcf = torch.from_numpy(cot["dconv_final"]).cuda() if (finals and f["conv"]) else None
     out = ss.ss_conv_scan_bwd(g["x"], g["delta"], g["A"], g["B"], g["C"], torch.from_numpy(cot["dy"]).cuda().to(tdt),
-                              ssm_state=hs, conv_state=cs, dstate_final=dsf, dconv_final=dcf, **kw)
+                              ssm_state=hs, conv_state=cs, dstate_final=dsf, dconv_final=dcf, zoh=zoh, **kw)
     torch.cuda.synchronize()
     ref = oracle.conv_scan_bwd(
         inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], cot["dy"],
@@ -64,7 +65,7 @@ def check_bwd(ss, inp, io, *, states=True, finals=True, flags=None, label="", se
         z=inp["z"] if f["gate"] else None, ssm_state=st["ssm_state"] if states else None,
         conv_state=st["conv_state"] if (states and f["conv"]) else None,
         dstate_final=cot["dstate_final"] if finals else None,
-        dconv_final=cot["dconv_final"] if (finals and f["conv"]) else None)
+        dconv_final=cot["dconv_final"] if (finals and f["conv"]) else None, zoh=zoh)
     assert set(ref) == set(out), (sorted(ref), sorted(out))
     errs = {}
     for k in sorted(ref):
@@ -143,3 +144,54 @@ def test_bwd_train_full_size(ss):
 
 def test_bwd_long_full_size(ss):
     check_bwd(ss, W.gen_scan_inputs(W.WORKLOADS["long"]), "bf16", label="bwd long")
+
+
+# ----------------------------------------------------------------------------- zero-order hold
+
+@pytest.mark.parametrize("states", [False, True])
+def test_bwd_zoh_tiny(ss, states):
+    check_bwd(ss, W.gen_scan_inputs(W.WORKLOADS["tiny"]), "f32", states=states, finals=states, zoh=True,
+              label="bwd zoh tiny")
+
+
+def test_bwd_zoh_block(ss):
+    check_bwd(ss, W.gen_scan_inputs(W.WORKLOADS["block"]), "f32", zoh=True, label="bwd zoh block")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{batch}L{seqlen}D{d_inner}N{d_state}".format(**s))
+def test_bwd_zoh_shapes(ss, io, shape):
+    spec = W.ScanSpec("bwdz", 1, 1, 1, 4, io_dtype=io, delta_mode="bias", seed=5153)
+    check_bwd(ss, W.gen_scan_inputs(spec, **shape), io, zoh=True, label=f"bwd zoh {shape} {io}")
+
+
+@pytest.mark.parametrize("flags", [dict(conv=False), dict(gate=False), dict(skip=False, bias=False),
+                                   dict(conv=False, gate=False, skip=False, bias=False)],
+                         ids=lambda f: "-".join(f"no_{k}" for k in f))
+def test_bwd_zoh_optional_pieces(ss, flags):
+    spec = W.ScanSpec("bwdzflags", 2, 90, 72, 16, io_dtype="f32", delta_mode="bias", seed=96)
+    check_bwd(ss, W.gen_scan_inputs(spec), "f32", flags=flags, zoh=True, label=f"bwd zoh flags {flags}")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [dict(batch=1, seqlen=4096, d_inner=64, d_state=16),
+                                   dict(batch=2, seqlen=3001, d_inner=100, d_state=8)],
+                         ids=["chunked_even", "chunked_ragged"])
+def test_bwd_zoh_chunked(ss, io, shape):
+    spec = W.ScanSpec("bwdzchunk", 1, 1, 1, 4, io_dtype=io, delta_mode="bias", seed=78)
+    check_bwd(ss, W.gen_scan_inputs(spec, **shape), io, zoh=True, label=f"bwd zoh chunked {shape} {io}")
+
+
+def test_bwd_zoh_small_and_zero_A(ss):
+    """States with A = 0 (coefficient Delta, dW/dA = Delta^2 / 2), with |A Delta| on both
+    sides of the series threshold, and growing states (A > 0)."""
+    spec = W.ScanSpec("bwdzA", 2, 300, 40, 16, io_dtype="f32", delta_mode="direct", seed=79)
+    inp = W.gen_scan_inputs(spec)
+    inp["A"][0::4, :4] = np.float32(0.0)
+    inp["A"][1::4, :] = -np.float32(1e-3) * (1 + np.arange(16, dtype=np.float32))
+    inp["A"][2::4, 4:8] = np.float32(0.05)
+    check_bwd(ss, inp, "f32", zoh=True, label="bwd zoh small A")
+
+
+def test_bwd_zoh_train_full_size(ss):
+    check_bwd(ss, W.gen_scan_inputs(W.WORKLOADS["train"]), "bf16", zoh=True, label="bwd zoh train")
