@@ -287,3 +287,46 @@ def test_chunked_growing_state_channels(ss):
     inp["A"][::7] = np.float32(0.002)
     inp["A"][1::7, :4] = np.float32(0.0)
     _long_chunk_case(ss, inp, "f32", np.array([0, 1, 7, 8, 14, 2047]), "growing state", states=False)
+
+
+# ----------------------------------------------------------------------------- limits
+
+def test_single_channel(ss):
+    """d_inner 1: the only workgroup's other 255 lanes repeat the last channel."""
+    spec = W.ScanSpec("one", 1, 1, 1, 4, io_dtype="f32", delta_mode="bias", seed=61)
+    _check_fwd(ss, spec, shape=dict(batch=3, seqlen=300, d_inner=1, d_state=16), states=True, label="one channel")
+
+
+def test_max_batch_forward_and_step(ss):
+    """batch 65535, the largest accepted (the launch grid's z extent), forward with
+    states and two decode steps of 65535 streams."""
+    spec = W.ScanSpec("maxb", 1, 1, 1, 4, io_dtype="f32", delta_mode="bias", seed=62)
+    _check_fwd(ss, spec, shape=dict(batch=65535, seqlen=5, d_inner=4, d_state=4), states=True, label="max batch")
+    inp = W.gen_scan_inputs(spec, batch=65535, seqlen=2, d_inner=4, d_state=4)
+    st = W.gen_states(65535, 4, 4, seed=63)
+    g = to_dev(inp, "f32")
+    h = torch.from_numpy(st["ssm_state"]).cuda()
+    c = torch.from_numpy(st["conv_state"]).cuda()
+    hr, cr = st["ssm_state"].astype(np.float64), st["conv_state"].astype(np.float64)
+    for t in range(2):
+        y = ss.ss_step(g["x"][:, t].contiguous(), g["delta"][:, t].contiguous(), g["A"], g["B"][:, t].contiguous(),
+                       g["C"][:, t].contiguous(), h, conv_state=c, conv_w=g["conv_w"], conv_b=g["conv_b"],
+                       delta_bias=g["delta_bias"], D=g["D"], z=g["z"][:, t].contiguous())
+        yr, hr, cr = oracle.step(inp["x"][:, t], inp["delta"][:, t], inp["A"], inp["B"][:, t], inp["C"][:, t], hr,
+                                 conv_w=inp["conv_w"], conv_b=inp["conv_b"], delta_bias=inp["delta_bias"],
+                                 D=inp["D"], z=inp["z"][:, t], conv_state=cr)
+        assert maxrel(host(y), yr) <= TOL["f32"], t
+    torch.cuda.synchronize()
+    assert maxrel(host(h), hr) <= TOL["f32"]
+    assert np.array_equal(host(c).astype(np.float64), cr)
+
+
+def test_max_d_inner(ss):
+    """d_inner 2^26, the largest accepted: the kernels' 32-bit per-lane and per-row
+    byte offsets are at their widest (bf16, 8 tokens = two prefetch groups), checked
+    on channels at both ends and around the last workgroup."""
+    Dn = 1 << 26
+    spec = W.ScanSpec("maxd", 1, 1, 1, 4, io_dtype="bf16", delta_mode="bias", seed=64)
+    dsel = np.array([0, 1, 255, 256, Dn // 2 + 7, Dn - 257, Dn - 256, Dn - 2, Dn - 1])
+    _check_fwd(ss, spec, shape=dict(batch=1, seqlen=8, d_inner=Dn, d_state=4), states=True, dsel=dsel,
+               label="max d_inner")
