@@ -349,12 +349,6 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     };
     const int64_t rowoff = rowbase * D;            // element offset of the chunk's first token
     auto ld = [&](const T* base, int r) -> T { return (base + rowoff + (int64_t)r * D)[du]; };
-    // x at chunk-relative row r (r >= -3): before token 0 it is the initial history
-    auto xat = [&](int r) -> float {
-        const int64_t t = t0 + r;
-        if (t >= 0) return IO<T>::cvt(ld(x, r));
-        return conv_state0 ? conv_state0[bd * 3 + (3 + t)] : 0.0f;
-    };
 
     const int ntiles = (clen + R - 1) / R;
     tile_fetch((ntiles - 1) * R);
@@ -369,17 +363,46 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
         for (int s = rlo + ((rhi - 1 - rlo) / S) * S; s >= rlo; s -= S) {
             const int ns = (s + S < rhi) ? S : rhi - s;      // tokens in this segment (uniform)
             const int64_t gs = t0 + s;
-            // inputs of the segment; xw[j] = x at row s - 3 + j
+            // inputs of the segment, every load issued before any is used: xw[j] = x at
+            // row s - 3 + j (rows before the sequence start come from the initial
+            // history, rows past the segment are not needed), delta, dy, z of its
+            // tokens, and the state before it (the checkpoint, or the initial state)
             float xw[S + 3];
-            T draw[S], zraw[S], yraw[S];
+            T xraw[S + 3], draw[S], zraw[S], yraw[S];
 #pragma unroll
-            for (int j = 0; j < S + 3; ++j) xw[j] = (CONV || j >= 3) && j < ns + 3 ? xat(s - 3 + j) : 0.0f;
+            for (int j = 0; j < S + 3; ++j) {
+                int r = s - 3 + j;
+                r = r < clen ? r : clen - 1;
+                r = t0 + r >= 0 ? r : (int)-t0;
+                xraw[j] = ld(x, r);
+            }
 #pragma unroll
             for (int i = 0; i < S; ++i) {
                 const int r = s + (i < ns ? i : ns - 1);
                 draw[i] = ld(delta, r);
                 yraw[i] = ld(dy, r);
                 zraw[i] = GATE ? ld(z, r) : T(0);
+            }
+            constexpr bool CK_AHEAD = N <= 16;            // all of the state loaded at once
+            const vf4* ck = reinterpret_cast<const vf4*>(ckpt) + ((int64_t)b * ba.nck + (gs > 0 ? gs / S - 1 : 0)) * (N / 4) * D + d;
+            vf4 ckv[CK_AHEAD ? N / 4 : 1];
+            if constexpr (CK_AHEAD) {
+                if (gs > 0) {
+#pragma unroll
+                    for (int q = 0; q < N / 4; ++q) ckv[q] = ck[(int64_t)q * D];
+                } else {
+#pragma unroll
+                    for (int q = 0; q < N / 4; ++q)
+                        ckv[q] = ssm_state0 ? vf4{ssm_state0[bd * N + 4 * q], ssm_state0[bd * N + 4 * q + 1],
+                                                  ssm_state0[bd * N + 4 * q + 2], ssm_state0[bd * N + 4 * q + 3]}
+                                            : vf4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < S + 3; ++j) {
+                const int64_t t = t0 + s - 3 + j;
+                const bool need = (CONV || j >= 3) && j < ns + 3;
+                xw[j] = !need ? 0.0f : t >= 0 ? IO<T>::cvt(xraw[j]) : (conv_state0 ? conv_state0[bd * 3 + (3 + t)] : 0.0f);
             }
             // per-token forward quantities and the gradient of the pre-gate output
             float dtv[S], uv[S], cv[S], vv[S], dyg[S], szv[S];
@@ -411,14 +434,18 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
             for (int i = 0; i < S; ++i) { yacc[i] = dsk * uv[i]; sgB[i] = 0.0f; sA[i] = 0.0f; }
 #pragma unroll
             for (int i = 0; i < (ZOH ? S : 1); ++i) sgaB[i] = 0.0f;
-            // checkpoint slot of the state before the segment: [.., N/4, D, 4]
-            const vf4* ck = reinterpret_cast<const vf4*>(ckpt) + ((int64_t)b * ba.nck + (gs > 0 ? gs / S - 1 : 0)) * (N / 4) * D + d;
             // states in blocks of NBK: recompute the block over the segment from the
             // state before it, then sweep the block backward
 #pragma unroll
             for (int j0 = 0; j0 < N; j0 += NBK) {
                 float hs[S + 1][NBK];
-                if (gs == 0) {
+                if constexpr (CK_AHEAD) {
+#pragma unroll
+                    for (int q = 0; q < NBK / 4; ++q) {
+                        const vf4 v = ckv[j0 / 4 + q];
+                        hs[0][4 * q] = v.x; hs[0][4 * q + 1] = v.y; hs[0][4 * q + 2] = v.z; hs[0][4 * q + 3] = v.w;
+                    }
+                } else if (gs == 0) {
 #pragma unroll
                     for (int n = 0; n < NBK; ++n) hs[0][n] = ssm_state0 ? ssm_state0[bd * N + j0 + n] : 0.0f;
                 } else {
