@@ -169,31 +169,62 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
     const T* db = delta + rowbase * D;
     const T* zb = GATE ? z + rowbase * D : nullptr;
     const T* yb = dy + rowbase * D;
-    auto ld = [&](const T* base, int r) -> T { return (base + (int64_t)r * D)[du]; };
 
     // rows go in groups of U aligned to the chunk start (so a group never crosses a
-    // tile), from the last group down; each group's loads are issued one group ahead
-    static_assert(R % U == 0, "groups do not cross tiles");
-    T cd[U], cz[U], cy[U], nd[U], nz[U], ny[U];
-    auto load_group = [&](int j, T* pd, T* pz, T* py) {
+    // tile), from the last group down. Even-numbered groups are loaded into one
+    // buffer and odd-numbered ones into the other, each one group ahead of its use;
+    // the loop takes a pair (odd, even) per iteration so neither buffer is copied
+    // and nothing waits for a load before the group that uses it. Tiles start at
+    // even group numbers, so a pair never crosses one. The raw I/O bits are held
+    // zero-extended in 32-bit registers.
+    static_assert(R % (2 * U) == 0, "pairs of groups do not cross tiles");
+    uint32_t ed[U], ez[U], ey[U], od[U], oz[U], oy[U];
+    auto raw = [&](const T* base, int r) -> uint32_t {
+        const T v = (base + (int64_t)r * D)[du];
+        if constexpr (sizeof(T) == 2) return (uint32_t)v;
+        else return __builtin_bit_cast(uint32_t, v);
+    };
+    auto val = [](uint32_t v) -> float {
+        if constexpr (sizeof(T) == 2) return __builtin_bit_cast(float, v << 16);
+        else return __builtin_bit_cast(float, v);
+    };
+    auto load_group = [&](int j, uint32_t* pd, uint32_t* pz, uint32_t* py) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             int r = U * j + U - 1 - i;                // rows of the group, last first
             r = r < clen ? r : clen - 1;
-            pd[i] = ld(db, r);
-            pz[i] = GATE ? ld(zb, r) : T(0);
-            py[i] = ld(yb, r);
+            pd[i] = raw(db, r);
+            pz[i] = GATE ? raw(zb, r) : 0u;
+            py[i] = raw(yb, r);
         }
     };
     float q[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) q[n] = 0.0f;
     double sdt = 0.0;
+    auto group = [&](int j, const uint32_t* cd, const uint32_t* cz, const uint32_t* cy, const float* tile, int rhi) {
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int r = U * j + U - 1 - i;
+            const bool valid = r < clen;               // only the chunk's last group can be short
+            const float dt = valid ? softplus(val(cd[i]) + dbias) : 0.0f;
+            float dyg = valid ? val(cy[i]) : 0.0f;
+            if (GATE) dyg *= silu(val(cz[i]));
+            const float* crow = tile + (int64_t)(valid ? r : rhi - 1) * N;
+#pragma unroll
+            for (int n = 0; n < N; ++n) q[n] = exp2_fast(dt * A2[n]) * __builtin_fmaf(crow[n], dyg, q[n]);
+            part += dt;
+        }
+        sdt += (double)part;
+    };
     const int ntiles = (clen + R - 1) / R;
     const int ngroups = (clen + U - 1) / U;
+    int j = ngroups - 1;                          // the next group to process
     tile_fetch((ntiles - 1) * R);
     tile_store(0);
-    load_group(ngroups - 1, cd, cz, cy);
+    if (j & 1) load_group(j, od, oz, oy);
+    else load_group(j, ed, ez, ey);
     __syncthreads();
     int buf = 0;
     for (int k = ntiles - 1; k >= 0; --k) {
@@ -201,24 +232,19 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
         const int rlo = k * R;
         const int rhi = (rlo + R < clen) ? rlo + R : clen;
         const float* tile = &sC[buf][0][0] - (int64_t)rlo * N;
-        for (int j = (rhi - 1) / U; j >= rlo / U; --j) {
-            if (j > 0) load_group(j - 1, nd, nz, ny);
-            float part = 0.0f;
-#pragma unroll
-            for (int i = 0; i < U; ++i) {
-                const int r = U * j + U - 1 - i;
-                const bool valid = r < clen;           // only the chunk's last group can be short
-                const float dt = valid ? softplus(IO<T>::cvt(cd[i]) + dbias) : 0.0f;
-                float dyg = valid ? IO<T>::cvt(cy[i]) : 0.0f;
-                if (GATE) dyg *= silu(IO<T>::cvt(cz[i]));
-                const float* crow = tile + (int64_t)(valid ? r : rhi - 1) * N;
-#pragma unroll
-                for (int n = 0; n < N; ++n) q[n] = exp2_fast(dt * A2[n]) * __builtin_fmaf(crow[n], dyg, q[n]);
-                part += dt;
-            }
-            sdt += (double)part;
-#pragma unroll
-            for (int i = 0; i < U; ++i) { cd[i] = nd[i]; cz[i] = nz[i]; cy[i] = ny[i]; }
+        const int jlo = rlo / U;                  // even
+        // the loads ahead are unconditional (group 0 again at the end, unused), so no
+        // buffer is ever merged from two paths
+        if ((j & 1) == 0 && j >= jlo) {           // an odd group count: the first group alone
+            load_group(j > 0 ? j - 1 : 0, od, oz, oy);
+            group(j, ed, ez, ey, tile, rhi);
+            --j;
+        }
+        for (; j > jlo; j -= 2) {                 // j odd, j - 1 >= jlo even
+            load_group(j - 1, ed, ez, ey);
+            group(j, od, oz, oy, tile, rhi);
+            load_group(j > 1 ? j - 2 : 0, od, oz, oy);
+            group(j - 1, ed, ez, ey, tile, rhi);
         }
         if (k > 0) tile_store(buf ^ 1);
         __syncthreads();
