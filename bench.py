@@ -447,11 +447,17 @@ def cpu_baseline(sample, spec, target_s=12.0):
     k = int(min(avail, max(k0, k0 * target_s / max(t_cal, 1e-3))))
     k = max(nthreads, (k // nthreads) * nthreads) if k >= nthreads else k
     k = min(k, avail)
-    dt = run(k)
+    # when the whole sample takes less than target_s, repeat it (up to 10 runs) and
+    # report the median rate
+    times = [run(k)]
+    while sum(times) < target_s and len(times) < 10:
+        times.append(run(k))
+    dt = float(np.median(times))
     elems = spec.batch * spec.seqlen * k * spec.d_state
     return {"value": round(elems / dt / 1e9, 4), "unit": "Gelem/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{k} of {spec.d_inner} channels (every 2nd from channel 0), all {spec.batch}x{spec.seqlen} "
-                      f"tokens, d_state {spec.d_state}, fp64 OpenMP over channels, {dt:.1f} s"}
+                      f"tokens, d_state {spec.d_state}, fp64 OpenMP over channels; median of {len(times)} runs of "
+                      f"{dt:.2f} s ({sum(times):.1f} s in total)"}
 
 
 def main():
