@@ -3,20 +3,21 @@
 // "How the Mamba Block Works": the input and output projections and the small step-size,
 // B and C projections; ai360xpert.com "Mamba", "The selection mechanism").
 //
-// Both operands are contiguous along K, so a workgroup stages a 128 x BK tile of X and of W
-// in LDS (16-byte rows chunks, double buffered) and each of its four waves multiplies a
-// 64 x 64 block of Y as 2 x 2 MFMA tiles of 32 x 32: v_mfma_f32_32x32x16_bf16 for bf16
-// (8 consecutive k per lane and half-wave) and v_mfma_f32_32x32x2_f32 for fp32. Lane l of a
-// 32 x 32 result holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4, v = 0..15.
-// Edges (M, Nout, K not multiples of the tile) are zero-filled on load and masked on store.
+// Both operands are contiguous along K, so a workgroup stages a TILE x BK tile of X and of W
+// in LDS (16-byte row chunks, double buffered) and each of its four waves multiplies a
+// TILE/2 x TILE/2 block of Y as MFMA tiles of 32 x 32 (2 x 2 of them for TILE = 128, one for
+// TILE = 64, the size taken when the larger tiles would leave the GPU short of workgroups):
+// v_mfma_f32_32x32x16_bf16 for bf16 (8 consecutive k per lane and half-wave) and
+// v_mfma_f32_32x32x2_f32 for fp32. Lane l of a 32 x 32 result holds column l % 32 and rows
+// 8 (v / 4) + 4 (l / 32) + v % 4, v = 0..15. Edges (M, Nout, K not multiples of the tile)
+// are zero-filled on load and masked on store.
 #pragma once
 #include "selscan_device.h"
 
 namespace selscan {
 
-constexpr int kGemmBM = 128;     // rows of X (and Y) per workgroup
-constexpr int kGemmBN = 128;     // rows of W (columns of Y) per workgroup
 constexpr int kGemmThreads = 256;
+constexpr int kGemmFillGroups = 512;     // below this many 128-tiles, use 64-tiles
 
 typedef __bf16 gemm_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float gemm_f32x16 __attribute__((ext_vector_type(16)));
@@ -32,21 +33,23 @@ template <> struct GemmCfg<float> {       // fp32: 16 k per tile, 4 per 16-byte 
 
 // VEC: K is a multiple of KV and the row starts are 16-byte aligned, so whole chunks
 // are loaded with one 16-byte access (else element by element).
-template <typename T, bool RES, bool VEC>
+template <typename T, bool RES, bool VEC, int TILE>
 __global__ void __launch_bounds__(kGemmThreads)
 k_gemm(const T* __restrict__ X, const T* __restrict__ W, const T* Rsd, T* Y, int64_t M, int64_t Nout, int64_t K) {
     using C = GemmCfg<T>;
     constexpr int BK = C::BK, KV = C::KV, LD = BK + C::PAD;       // LDS row stride in elements
     constexpr int CPR = BK / KV;                                   // 16-byte chunks per tile row
-    constexpr int CH = kGemmBM * CPR / kGemmThreads;               // chunks per thread per operand
-    static_assert(kGemmBM == kGemmBN && CH * kGemmThreads == kGemmBM * CPR, "tile shape");
-    __shared__ __attribute__((aligned(16))) T sX[2][kGemmBM][LD];
-    __shared__ __attribute__((aligned(16))) T sW[2][kGemmBN][LD];
+    constexpr int CH = TILE * CPR / kGemmThreads;                  // chunks per thread per operand
+    constexpr int NT = TILE / 64;                                  // 32 x 32 MFMA tiles per wave and dimension
+    constexpr int HW = TILE / 2;                                   // rows and columns per wave
+    static_assert((TILE == 64 || TILE == 128) && CH * kGemmThreads == TILE * CPR, "tile shape");
+    __shared__ __attribute__((aligned(16))) T sX[2][TILE][LD];
+    __shared__ __attribute__((aligned(16))) T sW[2][TILE][LD];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;                       // this wave's 64 x 64 block
-    const int64_t m0 = (int64_t)blockIdx.y * kGemmBM, n0 = (int64_t)blockIdx.x * kGemmBN;
+    const int wm = wave >> 1, wn = wave & 1;                       // this wave's HW x HW block
+    const int64_t m0 = (int64_t)blockIdx.y * TILE, n0 = (int64_t)blockIdx.x * TILE;
 
     gemm_u32x4 rx[CH], rw[CH];                                     // one tile of each operand in flight
     auto fetch = [&](const T* P, int64_t r0, int64_t rows, int64_t k0, gemm_u32x4* reg) {
@@ -74,11 +77,11 @@ k_gemm(const T* __restrict__ X, const T* __restrict__ W, const T* Rsd, T* Y, int
         }
     };
 
-    gemm_f32x16 acc[2][2];
+    gemm_f32x16 acc[NT][NT];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NT; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NT; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
@@ -99,31 +102,31 @@ k_gemm(const T* __restrict__ X, const T* __restrict__ W, const T* Rsd, T* Y, int
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
             for (int ks = 0; ks < BK; ks += 16) {
-                gemm_bf16x8 fa[2], fb[2];
+                gemm_bf16x8 fa[NT], fb[NT];
 #pragma unroll
-                for (int a = 0; a < 2; ++a)
-                    fa[a] = *reinterpret_cast<const gemm_bf16x8*>(&sX[buf][wm * 64 + a * 32 + l32][ks + 8 * half]);
+                for (int a = 0; a < NT; ++a)
+                    fa[a] = *reinterpret_cast<const gemm_bf16x8*>(&sX[buf][wm * HW + a * 32 + l32][ks + 8 * half]);
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
-                    fb[b] = *reinterpret_cast<const gemm_bf16x8*>(&sW[buf][wn * 64 + b * 32 + l32][ks + 8 * half]);
+                for (int b = 0; b < NT; ++b)
+                    fb[b] = *reinterpret_cast<const gemm_bf16x8*>(&sW[buf][wn * HW + b * 32 + l32][ks + 8 * half]);
 #pragma unroll
-                for (int a = 0; a < 2; ++a)
+                for (int a = 0; a < NT; ++a)
 #pragma unroll
-                    for (int b = 0; b < 2; ++b)
+                    for (int b = 0; b < NT; ++b)
                         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
             }
         } else {
 #pragma unroll
             for (int ks = 0; ks < BK; ks += 2) {
-                float fa[2], fb[2];
+                float fa[NT], fb[NT];
 #pragma unroll
-                for (int a = 0; a < 2; ++a) fa[a] = sX[buf][wm * 64 + a * 32 + l32][ks + half];
+                for (int a = 0; a < NT; ++a) fa[a] = sX[buf][wm * HW + a * 32 + l32][ks + half];
 #pragma unroll
-                for (int b = 0; b < 2; ++b) fb[b] = sW[buf][wn * 64 + b * 32 + l32][ks + half];
+                for (int b = 0; b < NT; ++b) fb[b] = sW[buf][wn * HW + b * 32 + l32][ks + half];
 #pragma unroll
-                for (int a = 0; a < 2; ++a)
+                for (int a = 0; a < NT; ++a)
 #pragma unroll
-                    for (int b = 0; b < 2; ++b)
+                    for (int b = 0; b < NT; ++b)
                         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[a], fb[b], acc[a][b], 0, 0, 0);
             }
         }
@@ -136,13 +139,13 @@ k_gemm(const T* __restrict__ X, const T* __restrict__ W, const T* Rsd, T* Y, int
 
     // epilogue: lane holds column l32 and rows 8 (v / 4) + 4 half + v % 4 of each 32 x 32 tile
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NT; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int64_t n = n0 + wn * 64 + b * 32 + l32;
+        for (int b = 0; b < NT; ++b) {
+            const int64_t n = n0 + wn * HW + b * 32 + l32;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t m = m0 + wm * 64 + a * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+                const int64_t m = m0 + wm * HW + a * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
                 if (m < M && n < Nout) {
                     float val = acc[a][b][v];
                     if (RES) val += IO<T>::ld(Rsd + m * Nout + n);
@@ -152,22 +155,29 @@ k_gemm(const T* __restrict__ X, const T* __restrict__ W, const T* Rsd, T* Y, int
         }
 }
 
-template <typename T>
-static hipError_t launch_gemm_t(const LaunchGemm& p) {
-    hipStream_t st = static_cast<hipStream_t>(p.stream);
-    const dim3 grid((unsigned)((p.N + kGemmBN - 1) / kGemmBN), (unsigned)((p.M + kGemmBM - 1) / kGemmBM));
+template <typename T, int TILE>
+static void launch_gemm_tile(const LaunchGemm& p, bool vec, hipStream_t st) {
+    const dim3 grid((unsigned)((p.N + TILE - 1) / TILE), (unsigned)((p.M + TILE - 1) / TILE));
     const T* X = static_cast<const T*>(p.X);
     const T* W = static_cast<const T*>(p.W);
     const T* R = static_cast<const T*>(p.R);
     T* Y = static_cast<T*>(p.Y);
-    const bool vec = p.K % GemmCfg<T>::KV == 0 && ((uintptr_t)X & 15u) == 0 && ((uintptr_t)W & 15u) == 0;
     if (vec) {
-        if (R) hipLaunchKernelGGL((k_gemm<T, true, true>), grid, dim3(kGemmThreads), 0, st, X, W, R, Y, p.M, p.N, p.K);
-        else hipLaunchKernelGGL((k_gemm<T, false, true>), grid, dim3(kGemmThreads), 0, st, X, W, R, Y, p.M, p.N, p.K);
+        if (R) hipLaunchKernelGGL((k_gemm<T, true, true, TILE>), grid, dim3(kGemmThreads), 0, st, X, W, R, Y, p.M, p.N, p.K);
+        else hipLaunchKernelGGL((k_gemm<T, false, true, TILE>), grid, dim3(kGemmThreads), 0, st, X, W, R, Y, p.M, p.N, p.K);
     } else {
-        if (R) hipLaunchKernelGGL((k_gemm<T, true, false>), grid, dim3(kGemmThreads), 0, st, X, W, R, Y, p.M, p.N, p.K);
-        else hipLaunchKernelGGL((k_gemm<T, false, false>), grid, dim3(kGemmThreads), 0, st, X, W, R, Y, p.M, p.N, p.K);
+        if (R) hipLaunchKernelGGL((k_gemm<T, true, false, TILE>), grid, dim3(kGemmThreads), 0, st, X, W, R, Y, p.M, p.N, p.K);
+        else hipLaunchKernelGGL((k_gemm<T, false, false, TILE>), grid, dim3(kGemmThreads), 0, st, X, W, R, Y, p.M, p.N, p.K);
     }
+}
+
+template <typename T>
+static hipError_t launch_gemm_t(const LaunchGemm& p) {
+    hipStream_t st = static_cast<hipStream_t>(p.stream);
+    const bool vec = p.K % GemmCfg<T>::KV == 0 && ((uintptr_t)p.X & 15u) == 0 && ((uintptr_t)p.W & 15u) == 0;
+    const int64_t tiles128 = ((p.N + 127) / 128) * ((p.M + 127) / 128);
+    if (tiles128 < kGemmFillGroups) launch_gemm_tile<T, 64>(p, vec, st);
+    else launch_gemm_tile<T, 128>(p, vec, st);
     return hipGetLastError();
 }
 

@@ -77,6 +77,19 @@ def test_block_fwd_ragged(ss, io):
     run_case(ss, spec, states=True, label=f"block ragged {io}")
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_block_fwd_wide_tiles(ss, io):
+    """Enough rows (batch 3 x 1500 tokens = 4500, not a multiple of 128) that the input
+    projection takes the 128-wide GEMM tiles with a ragged last row of tiles, while the
+    narrower projections keep the 64-wide ones. Carried states are checked with fp32 I/O
+    only: with bf16 I/O the final state after 1500 tokens differs from the fp64 block by
+    about 2e-2 (measured 2.15e-2), set by the bf16 rounding of the step-size projection
+    that every later decay factor compounds, not by the tile shape (both tile sizes
+    accumulate over K in the same order)."""
+    spec = W.BLOCKS["block_f32" if io == "f32" else "block_bf16"]
+    run_case(ss, spec, states=io == "f32", Bsz=3, L=1500, label=f"block wide tiles {io}")
+
+
 def test_block_fwd_chunked_long(ss):
     """A long sequence with few channels takes the scan's chunked path inside the block."""
     spec = W.BlockSpec("longblock", 1, 8192, 64, expand=2, d_state=16, io_dtype="f32", seed=778)
