@@ -598,14 +598,21 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     float M = 0.0f;                               // sum |Delta u| max|B| over swept rows (full mode)
     float Mh = 0.0f;                              // sum Delta max|B| over rows swept after every n was dropped
     float xmax = 0.0f;                            // max |x| feeding those rows
-    // state indices are dropped in blocks of four; a block goes once its least
-    // negative exponent A2 * R is below the cut on every lane
-    constexpr int NBLK = N / 4;
+    // state indices are dropped in blocks of BS (one state each up to d_state 16, so that
+    // a fast-decaying state stops as soon as it alone is below the cut); a block goes
+    // once its least negative exponent A2 * R is below the cut on every lane
+    constexpr int BS = N <= 16 ? 1 : N / 16;
+    constexpr int NBLK = N / BS;
+    static_assert(NBLK <= 32, "one mask bit per block");
     float A2blk[NBLK];
 #pragma unroll
-    for (int j = 0; j < NBLK; ++j)
-        A2blk[j] = __builtin_fmaxf(__builtin_fmaxf(A2[4 * j], A2[4 * j + 1]), __builtin_fmaxf(A2[4 * j + 2], A2[4 * j + 3]));
-    uint32_t act = (1u << NBLK) - 1u;
+    for (int j = 0; j < NBLK; ++j) {
+        float m = A2[BS * j];
+#pragma unroll
+        for (int q = 1; q < BS; ++q) m = __builtin_fmaxf(m, A2[BS * j + q]);
+        A2blk[j] = m;
+    }
+    uint32_t act = NBLK == 32 ? 0xffffffffu : (1u << NBLK) - 1u;
     const float cut = -(float)kAggCutLog2;
 
     // initial conv history (x_{-3}, x_{-2}, x_{-1}) in registers
@@ -690,8 +697,8 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
 #pragma unroll
                     for (int i = 0; i < U; ++i) {
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int n = 4 * j + q;
+                        for (int q = 0; q < BS; ++q) {
+                            const int n = BS * j + q;
                             if constexpr (ZOH) {
                                 const float e = exp2_fast(A2[n] * Ri[i]);
                                 const float ts = dt[i] * A2[n];
