@@ -59,9 +59,12 @@ template <int V> struct WaveSum {
 __device__ __forceinline__ unsigned fbits(float v) { return __builtin_bit_cast(unsigned, v); }
 __device__ __forceinline__ float bitsf(unsigned v) { return __builtin_bit_cast(float, v); }
 
+// Every control used here permutes lanes within a row of 16 (or a quad), so no source
+// lane is out of range, and the sweep runs with all lanes active: bound_ctrl is set
+// only because it lets the compiler fold the move into the add that consumes it.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 constexpr int kDppRowMirror = 0x140;       // lane l of a 16-lane row takes lane 15 - l
