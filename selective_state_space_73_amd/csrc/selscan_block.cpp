@@ -32,13 +32,17 @@ ss_status failf(ss_status s, const char* fmt, ...) {
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Y[M, Nout] (+)= X[M, K] * W[Nout, K]^T, all row-major; Cres (if not null) is added
-// and may equal Y.
+// and may equal Y0. The Nout columns go to Y0 (c0 of them), Y1 (c1) and Y2 (the rest);
+// part is the fp32 split-K workspace (selscan::gemm_plan).
 ss_status gemm(bool bf16, int64_t M, int64_t Nout, int64_t K, const void* W, const void* X, const void* Cres,
-               void* Y, hipStream_t st) {
+               void* Y0, int64_t c0, void* Y1, int64_t c1, void* Y2, float* part, hipStream_t st) {
     selscan::LaunchGemm g{};
     g.bf16 = bf16;
-    g.X = X; g.W = W; g.R = Cres; g.Y = Y;
+    g.X = X; g.W = W; g.R = Cres;
+    g.Y[0] = Y0; g.Y[1] = Y1; g.Y[2] = Y2;
+    g.cols[0] = c0; g.cols[1] = c1; g.cols[2] = Nout - c0 - c1;
     g.M = M; g.N = Nout; g.K = K;
+    g.part = part;
     g.stream = st;
     const hipError_t e = selscan::launch_gemm(g);
     if (e != hipSuccess)
@@ -48,7 +52,7 @@ ss_status gemm(bool bf16, int64_t M, int64_t Nout, int64_t K, const void* W, con
 }
 
 struct BlockLayout {
-    size_t xn, xi, z, u, dr, bm, cm, delta, y, scan, total;
+    size_t xn, xi, z, u, dr, bm, cm, delta, y, scan, part, total;
 };
 
 ss_dims scan_dims(const ss_block_dims& d, bool step) {
@@ -81,6 +85,16 @@ BlockLayout block_layout(const ss_block_dims& d, bool step) {
     l.y = take(M * di * es);
     const ss_dims sd = scan_dims(d, step);
     l.scan = take(step ? 0 : ss_workspace_bytes(&sd));
+    // fp32 partials of the projections that split K (the largest of them; one at a time)
+    const bool bf16 = d.io_dtype == SS_BF16;
+    const int64_t Mi = (int64_t)M;
+    size_t part = 0;
+    const size_t cand[] = {selscan::gemm_plan(Mi, 2 * (int64_t)di, (int64_t)dm, bf16).part_bytes,
+                           selscan::gemm_plan(Mi, (int64_t)(R + 2 * N), (int64_t)di, bf16).part_bytes,
+                           selscan::gemm_plan(Mi, (int64_t)di, (int64_t)R, bf16).part_bytes,
+                           selscan::gemm_plan(Mi, (int64_t)dm, (int64_t)di, bf16).part_bytes};
+    for (size_t c : cand) part = c > part ? c : part;
+    l.part = take(part);
     l.total = off;
     return l;
 }
@@ -127,10 +141,10 @@ ss_status run_block(const ss_block_dims* d, const ss_block_weights* w, const voi
         return failf(SS_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, l.total);
     if ((uintptr_t)workspace & 255u) return failf(SS_ERR_INVALID_ARG, "workspace not 256-byte aligned");
     const bool bf16 = d->io_dtype == SS_BF16;
-    const size_t es = bf16 ? 2 : 4;
     char* ws = static_cast<char*>(workspace);
     void* xn = ws + l.xn; void* xi = ws + l.xi; void* z = ws + l.z; void* u = ws + l.u; void* dr = ws + l.dr;
     void* bm = ws + l.bm; void* cm = ws + l.cm; void* delta = ws + l.delta; void* y = ws + l.y;
+    float* part = reinterpret_cast<float*>(ws + l.part);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t L = step ? 1 : d->seqlen;
     const int64_t M = d->batch * L;
@@ -143,9 +157,8 @@ ss_status run_block(const ss_block_dims* d, const ss_block_weights* w, const voi
     op.in = x; op.out = xn; op.w = w->norm_w; op.eps = d->norm_eps; op.rows = M; op.cols = (int)dm;
     if (selscan::launch_block_op(op) != hipSuccess) return failf(SS_ERR_HIP, "RMSNorm launch failed");
 
-    const char* W_in = static_cast<const char*>(w->W_in);
-    if ((s = gemm(bf16, M, di, dm, W_in, xn, nullptr, xi, st)) != SS_OK) return s;
-    if ((s = gemm(bf16, M, di, dm, W_in + (size_t)di * dm * es, xn, nullptr, z, st)) != SS_OK) return s;
+    // in_proj: the first d_inner rows of W_in give the main branch, the next the gate
+    if ((s = gemm(bf16, M, 2 * di, dm, w->W_in, xn, nullptr, xi, di, z, di, nullptr, part, st)) != SS_OK) return s;
 
     op = selscan::LaunchBlockOps{};
     op.bf16 = bf16;
@@ -164,11 +177,10 @@ ss_status run_block(const ss_block_dims* d, const ss_block_weights* w, const voi
         }
     }
 
-    const char* W_x = static_cast<const char*>(w->W_x);
-    if ((s = gemm(bf16, M, R, di, W_x, u, nullptr, dr, st)) != SS_OK) return s;
-    if ((s = gemm(bf16, M, N, di, W_x + (size_t)R * di * es, u, nullptr, bm, st)) != SS_OK) return s;
-    if ((s = gemm(bf16, M, N, di, W_x + (size_t)(R + N) * di * es, u, nullptr, cm, st)) != SS_OK) return s;
-    if ((s = gemm(bf16, M, di, R, w->W_dt, dr, nullptr, delta, st)) != SS_OK) return s;
+    // x_proj: rows [0, R) of W_x give the step-size rank, then N rows for B and N for C
+    if ((s = gemm(bf16, M, R + 2 * N, di, w->W_x, u, nullptr, dr, R, bm, N, cm, part, st)) != SS_OK) return s;
+    if ((s = gemm(bf16, M, di, R, w->W_dt, dr, nullptr, delta, di, nullptr, 0, nullptr, part, st)) != SS_OK)
+        return s;
 
     ss_args a{};
     a.x = u; a.delta = delta; a.delta_bias = w->dt_bias; a.A = w->A; a.B = bm; a.C = cm; a.Dskip = w->Dskip;
@@ -176,7 +188,7 @@ ss_status run_block(const ss_block_dims* d, const ss_block_weights* w, const voi
     s = step ? ss_step(&sd, &a, stream) : ss_conv_scan_fwd(&sd, &a, ws + l.scan, ss_workspace_bytes(&sd), stream);
     if (s != SS_OK) return s;
 
-    return gemm(bf16, M, dm, di, w->W_out, y, x, out, st);
+    return gemm(bf16, M, dm, di, w->W_out, y, x, out, dm, nullptr, 0, nullptr, part, st);
 }
 
 }  // namespace

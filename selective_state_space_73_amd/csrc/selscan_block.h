@@ -32,9 +32,13 @@ k_rmsnorm(const T* __restrict__ x, const float* __restrict__ w, T* __restrict__ 
 
 // Causal depthwise conv (width 4, tap 3 on the current token) + SiLU over a run of
 // kBlockConvRun tokens per lane: u[b,t,d] = SiLU(cb + sum_k w_k xi[b,t-3+k,d]), with
-// the initial history (oldest first) before token 0, or zeros. Reads the history
-// only; k_conv_history writes the new one afterwards.
-constexpr int kBlockConvRun = 64;
+// the initial history (oldest first) before token 0, or zeros. A lane loads its run and
+// the three inputs before it at once (the runs overlap by three rows, re-read from
+// cache), so short runs give the grid enough lanes to hide the load latency. Token runs
+// beyond the grid's y extent are taken in a strided loop. Reads the history only;
+// k_conv_history writes the new one afterwards.
+constexpr int kBlockConvRun = 8;
+constexpr int64_t kBlockConvMaxGridY = 65535;
 
 template <typename T>
 __global__ void __launch_bounds__(256)
@@ -43,21 +47,27 @@ k_conv_silu(const T* __restrict__ xi, const float* __restrict__ conv_w, const fl
     const int d = blockIdx.x * 256 + threadIdx.x;
     if (d >= D) return;
     const int b = blockIdx.z;
-    const int64_t t0 = (int64_t)blockIdx.y * kBlockConvRun;
-    const int64_t t1 = (t0 + kBlockConvRun < L) ? t0 + kBlockConvRun : L;
     const float w0 = conv_w[d * 4 + 0], w1 = conv_w[d * 4 + 1], w2 = conv_w[d * 4 + 2], w3 = conv_w[d * 4 + 3];
     const float cb = conv_b ? conv_b[d] : 0.0f;
     const int64_t bd = (int64_t)b * D + d;
-    auto xat = [&](int64_t t) -> float {
-        if (t >= 0) return IO<T>::ld(xi + ((int64_t)b * L + t) * D + d);
-        return hist ? hist[bd * 3 + (3 + t)] : 0.0f;
-    };
-    float x3 = xat(t0 - 3), x2 = xat(t0 - 2), x1 = xat(t0 - 1);
-    for (int64_t t = t0; t < t1; ++t) {
-        const float xt = IO<T>::ld(xi + ((int64_t)b * L + t) * D + d);
-        const float c = __builtin_fmaf(w3, xt, __builtin_fmaf(w2, x1, __builtin_fmaf(w1, x2, __builtin_fmaf(w0, x3, cb))));
-        IO<T>::st(u + ((int64_t)b * L + t) * D + d, silu(c));
-        x3 = x2; x2 = x1; x1 = xt;
+    const T* xb = xi + (int64_t)b * L * D + d;
+    T* ub = u + (int64_t)b * L * D + d;
+    const int64_t nrun = (L + kBlockConvRun - 1) / kBlockConvRun;
+    for (int64_t run = blockIdx.y; run < nrun; run += gridDim.y) {
+        const int64_t t0 = run * kBlockConvRun;
+        float xv[kBlockConvRun + 3];
+#pragma unroll
+        for (int j = 0; j < kBlockConvRun + 3; ++j) {
+            const int64_t t = t0 - 3 + j;
+            xv[j] = t >= L ? 0.0f : (t >= 0 ? IO<T>::ld(xb + t * D) : (hist ? hist[bd * 3 + (3 + t)] : 0.0f));
+        }
+#pragma unroll
+        for (int j = 0; j < kBlockConvRun; ++j) {
+            const int64_t t = t0 + j;
+            const float c = __builtin_fmaf(w3, xv[j + 3], __builtin_fmaf(w2, xv[j + 2],
+                            __builtin_fmaf(w1, xv[j + 1], __builtin_fmaf(w0, xv[j], cb))));
+            if (t < L) IO<T>::st(ub + t * D, silu(c));
+        }
     }
 }
 
@@ -105,10 +115,13 @@ static hipError_t launch_block_kernels_t(const LaunchBlockOps& p) {
                                static_cast<const T*>(p.in), p.w, static_cast<T*>(p.out), p.rows, p.cols, p.eps);
             break;
         case LaunchBlockOps::kConvSilu:
+        {
+            const int64_t runs = (p.L + kBlockConvRun - 1) / kBlockConvRun;
             hipLaunchKernelGGL((k_conv_silu<T>), dim3((unsigned)((p.cols + 255) / 256),
-                               (unsigned)((p.L + kBlockConvRun - 1) / kBlockConvRun), (unsigned)p.batch), dim3(256), 0,
-                               st, static_cast<const T*>(p.in), p.conv_w, p.conv_b, p.hist, static_cast<T*>(p.out), p.L,
-                               p.cols);
+                               (unsigned)(runs < kBlockConvMaxGridY ? runs : kBlockConvMaxGridY), (unsigned)p.batch),
+                               dim3(256), 0, st, static_cast<const T*>(p.in), p.conv_w, p.conv_b, p.hist,
+                               static_cast<T*>(p.out), p.L, p.cols);
+        }
             break;
         case LaunchBlockOps::kConvHistory:
             hipLaunchKernelGGL((k_conv_history<T>), dim3((unsigned)((p.batch * p.cols + 255) / 256)), dim3(256), 0, st,

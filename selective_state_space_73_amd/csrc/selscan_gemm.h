@@ -6,37 +6,58 @@
 // Both operands are contiguous along K, so a workgroup stages a TILE x BK tile of X and of W
 // in LDS (16-byte row chunks, double buffered) and each of its four waves multiplies a
 // TILE/2 x TILE/2 block of Y as MFMA tiles of 32 x 32 (2 x 2 of them for TILE = 128, one for
-// TILE = 64, the size taken when the larger tiles would leave the GPU short of workgroups):
-// v_mfma_f32_32x32x16_bf16 for bf16 (8 consecutive k per lane and half-wave) and
-// v_mfma_f32_32x32x2_f32 for fp32. Lane l of a 32 x 32 result holds column l % 32 and rows
-// 8 (v / 4) + 4 (l / 32) + v % 4, v = 0..15. Edges (M, Nout, K not multiples of the tile)
-// are zero-filled on load and masked on store.
+// TILE = 64, the size taken when the larger tiles would leave the GPU short of workgroups;
+// the 64-wide tiles take twice the K depth per stage, so a short grid waits on half as many
+// load round trips): v_mfma_f32_32x32x16_bf16 for bf16 (8 consecutive k per lane and
+// half-wave) and v_mfma_f32_32x32x2_f32 for fp32. Lane l of a 32 x 32 result holds column
+// l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4, v = 0..15. Edges (M, Nout, K not
+// multiples of the tile) are zero-filled on load and masked on store.
+//
+// Output columns can be routed to up to three matrices (the block's fused projections:
+// in_proj into the main branch and the gate, x_proj into the step-size rank, B and C).
+// A grid short of workgroups splits K (gemm_plan): split s multiplies its K range and
+// writes fp32 partials, and k_gemm_reduce sums the splits in order (deterministic), adds
+// the residual and stores in the I/O dtype.
 #pragma once
 #include "selscan_device.h"
 
 namespace selscan {
 
 constexpr int kGemmThreads = 256;
-constexpr int kGemmFillGroups = 512;     // below this many 128-tiles, use 64-tiles
 
 typedef __bf16 gemm_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float gemm_f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t gemm_u32x4 __attribute__((ext_vector_type(4)));
 
-template <typename T> struct GemmCfg;
-template <> struct GemmCfg<uint16_t> {    // bf16: 32 k per tile, 8 per 16-byte chunk
-    static constexpr int BK = 32, KV = 8, PAD = 8;
+template <typename T, int TILE> struct GemmCfg;
+template <int TILE> struct GemmCfg<uint16_t, TILE> {    // bf16: 8 k per 16-byte chunk
+    static constexpr int BK = TILE == 64 ? 64 : 32, KV = 8, PAD = 8;
 };
-template <> struct GemmCfg<float> {       // fp32: 16 k per tile, 4 per 16-byte chunk
-    static constexpr int BK = 16, KV = 4, PAD = 4;
+template <int TILE> struct GemmCfg<float, TILE> {       // fp32: 4 k per 16-byte chunk
+    static constexpr int BK = TILE == 64 ? 32 : 16, KV = 4, PAD = 4;
 };
 
+// Destination of output column n (< Nout) of row m: three row-major matrices side by side.
+struct GemmOut {
+    void* y0; void* y1; void* y2;
+    int64_t c0, c1, c2;
+};
+template <typename T>
+__device__ __forceinline__ T* gemm_dst(const GemmOut& o, int64_t m, int64_t n) {
+    if (n < o.c0) return static_cast<T*>(o.y0) + m * o.c0 + n;
+    n -= o.c0;
+    if (n < o.c1) return static_cast<T*>(o.y1) + m * o.c1 + n;
+    return static_cast<T*>(o.y2) + m * o.c2 + (n - o.c1);
+}
+
 // VEC: K is a multiple of KV and the row starts are 16-byte aligned, so whole chunks
-// are loaded with one 16-byte access (else element by element).
-template <typename T, bool RES, bool VEC, int TILE>
+// are loaded with one 16-byte access (else element by element). PART: write the fp32
+// partial of K split blockIdx.z (K range [z kper, (z + 1) kper)) to part[z, M, Nout].
+template <typename T, bool RES, bool VEC, int TILE, bool PART>
 __global__ void __launch_bounds__(kGemmThreads)
-k_gemm(const T* __restrict__ X, const T* __restrict__ W, const T* Rsd, T* Y, int64_t M, int64_t Nout, int64_t K) {
-    using C = GemmCfg<T>;
+k_gemm(const T* __restrict__ X, const T* __restrict__ W, const T* Rsd, GemmOut out, float* __restrict__ part,
+       int64_t M, int64_t Nout, int64_t K, int64_t kper) {
+    using C = GemmCfg<T, TILE>;
     constexpr int BK = C::BK, KV = C::KV, LD = BK + C::PAD;       // LDS row stride in elements
     constexpr int CPR = BK / KV;                                   // 16-byte chunks per tile row
     constexpr int CH = TILE * CPR / kGemmThreads;                  // chunks per thread per operand
@@ -86,15 +107,18 @@ k_gemm(const T* __restrict__ X, const T* __restrict__ W, const T* Rsd, T* Y, int
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
     const int l32 = lane & 31, half = lane >> 5;
-    const int64_t nk = (K + BK - 1) / BK;
-    fetch(X, m0, M, 0, rx);
-    fetch(W, n0, Nout, 0, rw);
+    // this workgroup's K stages: [kt0, kt1) (every split is non-empty: gemm_plan)
+    const int64_t kall = (K + BK - 1) / BK;
+    const int64_t kt0 = PART ? (int64_t)blockIdx.z * (kper / BK) : 0;
+    const int64_t kt1 = PART ? (kt0 + kper / BK < kall ? kt0 + kper / BK : kall) : kall;
+    fetch(X, m0, M, kt0 * BK, rx);
+    fetch(W, n0, Nout, kt0 * BK, rw);
     stash(sX[0], rx);
     stash(sW[0], rw);
     __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int buf = (int)(kt & 1);
-        const bool more = kt + 1 < nk;
+    for (int64_t kt = kt0; kt < kt1; ++kt) {
+        const int buf = (int)((kt - kt0) & 1);
+        const bool more = kt + 1 < kt1;
         if (more) {
             fetch(X, m0, M, (kt + 1) * BK, rx);
             fetch(W, n0, Nout, (kt + 1) * BK, rw);
@@ -148,36 +172,70 @@ k_gemm(const T* __restrict__ X, const T* __restrict__ W, const T* Rsd, T* Y, int
                 const int64_t m = m0 + wm * HW + a * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
                 if (m < M && n < Nout) {
                     float val = acc[a][b][v];
-                    if (RES) val += IO<T>::ld(Rsd + m * Nout + n);
-                    IO<T>::st(Y + m * Nout + n, val);
+                    if (PART) {
+                        part[((int64_t)blockIdx.z * M + m) * Nout + n] = val;
+                    } else {
+                        if (RES) val += IO<T>::ld(Rsd + m * Nout + n);
+                        IO<T>::st(gemm_dst<T>(out, m, n), val);
+                    }
                 }
             }
         }
 }
 
-template <typename T, int TILE>
-static void launch_gemm_tile(const LaunchGemm& p, bool vec, hipStream_t st) {
-    const dim3 grid((unsigned)((p.N + TILE - 1) / TILE), (unsigned)((p.M + TILE - 1) / TILE));
+// Sum of the K splits' fp32 partials in split order (+ residual), stored in the I/O dtype.
+template <typename T, bool RES>
+__global__ void __launch_bounds__(256)
+k_gemm_reduce(const float* __restrict__ part, int splits, const T* Rsd, GemmOut out, int64_t M, int64_t Nout) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = M * Nout;
+    if (i >= total) return;
+    float v = part[i];
+    for (int s = 1; s < splits; ++s) v += part[(int64_t)s * total + i];
+    if (RES) v += IO<T>::ld(Rsd + i);
+    IO<T>::st(gemm_dst<T>(out, i / Nout, i % Nout), v);
+}
+
+template <typename T, int TILE, bool PART>
+static void launch_gemm_tile(const LaunchGemm& p, const GemmPlan& g, bool vec, const GemmOut& o, hipStream_t st) {
+    const dim3 grid((unsigned)((p.N + TILE - 1) / TILE), (unsigned)((p.M + TILE - 1) / TILE), (unsigned)g.splits);
     const T* X = static_cast<const T*>(p.X);
     const T* W = static_cast<const T*>(p.W);
     const T* R = static_cast<const T*>(p.R);
-    T* Y = static_cast<T*>(p.Y);
-    if (vec) {
-        if (R) hipLaunchKernelGGL((k_gemm<T, true, true, TILE>), grid, dim3(kGemmThreads), 0, st, X, W, R, Y, p.M, p.N, p.K);
-        else hipLaunchKernelGGL((k_gemm<T, false, true, TILE>), grid, dim3(kGemmThreads), 0, st, X, W, R, Y, p.M, p.N, p.K);
+    // a split launch adds the residual in k_gemm_reduce
+    const bool res = !PART && R != nullptr;
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(kGemmThreads), 0, st, X, W, R, o, p.part, p.M, p.N, p.K, g.kper);
+    };
+    if constexpr (PART) {
+        if (vec) go(k_gemm<T, false, true, TILE, true>);
+        else go(k_gemm<T, false, false, TILE, true>);
     } else {
-        if (R) hipLaunchKernelGGL((k_gemm<T, true, false, TILE>), grid, dim3(kGemmThreads), 0, st, X, W, R, Y, p.M, p.N, p.K);
-        else hipLaunchKernelGGL((k_gemm<T, false, false, TILE>), grid, dim3(kGemmThreads), 0, st, X, W, R, Y, p.M, p.N, p.K);
+        if (vec) res ? go(k_gemm<T, true, true, TILE, false>) : go(k_gemm<T, false, true, TILE, false>);
+        else res ? go(k_gemm<T, true, false, TILE, false>) : go(k_gemm<T, false, false, TILE, false>);
     }
 }
 
 template <typename T>
 static hipError_t launch_gemm_t(const LaunchGemm& p) {
     hipStream_t st = static_cast<hipStream_t>(p.stream);
-    const bool vec = p.K % GemmCfg<T>::KV == 0 && ((uintptr_t)p.X & 15u) == 0 && ((uintptr_t)p.W & 15u) == 0;
-    const int64_t tiles128 = ((p.N + 127) / 128) * ((p.M + 127) / 128);
-    if (tiles128 < kGemmFillGroups) launch_gemm_tile<T, 64>(p, vec, st);
-    else launch_gemm_tile<T, 128>(p, vec, st);
+    const bool vec = p.K % GemmCfg<T, 64>::KV == 0 && ((uintptr_t)p.X & 15u) == 0 && ((uintptr_t)p.W & 15u) == 0;
+    const GemmPlan g = gemm_plan(p.M, p.N, p.K, sizeof(T) == 2);
+    if (g.bk != (g.tile == 64 ? GemmCfg<T, 64>::BK : GemmCfg<T, 128>::BK)) return hipErrorInvalidValue;
+    if (g.splits > 1 && !p.part) return hipErrorInvalidValue;
+    const GemmOut o{p.Y[0], p.Y[1], p.Y[2], p.cols[0], p.cols[1], p.N - p.cols[0] - p.cols[1]};
+    if (g.splits > 1) {
+        if (g.tile == 64) launch_gemm_tile<T, 64, true>(p, g, vec, o, st);
+        else launch_gemm_tile<T, 128, true>(p, g, vec, o, st);
+        const int64_t total = p.M * p.N;
+        const dim3 rg((unsigned)((total + 255) / 256));
+        const T* R = static_cast<const T*>(p.R);
+        if (R) hipLaunchKernelGGL((k_gemm_reduce<T, true>), rg, dim3(256), 0, st, p.part, g.splits, R, o, p.M, p.N);
+        else hipLaunchKernelGGL((k_gemm_reduce<T, false>), rg, dim3(256), 0, st, p.part, g.splits, R, o, p.M, p.N);
+    } else {
+        if (g.tile == 64) launch_gemm_tile<T, 64, false>(p, g, vec, o, st);
+        else launch_gemm_tile<T, 128, false>(p, g, vec, o, st);
+    }
     return hipGetLastError();
 }
 

@@ -73,14 +73,49 @@ struct LaunchBlockOps {
 hipError_t launch_block_op(const LaunchBlockOps& p);
 
 // Y[M, N] = X[M, K] W[N, K]^T (+ R[M, N]), row-major, in the I/O dtype, fp32 accumulation
-// (selscan_gemm.h). R may equal Y.
+// (selscan_gemm.h). The N output columns may go to up to three separate row-major
+// matrices: columns [0, cols[0]) to Y[0], the next cols[1] to Y[1], the rest to Y[2]
+// (cols[1] = cols[2] = 0 for a single output). R (one output only) may equal Y[0].
 struct LaunchGemm {
     bool bf16;
-    const void* X; const void* W; const void* R; void* Y;
+    const void* X; const void* W; const void* R;
+    void* Y[3]; int64_t cols[3];
     int64_t M, N, K;
+    float* part;          // fp32 workspace of gemm_plan(...).part_bytes for split-K launches
     void* stream;
 };
 hipError_t launch_gemm(const LaunchGemm& p);
+
+// Tile width, K depth per split and split count of a GEMM launch. Launches that would
+// give the GPU few workgroups split K over up to kGemmMaxSplits workgroups per output
+// tile; each writes an fp32 partial and a second kernel sums them in split order.
+constexpr int kGemmTargetGroups = 1024;
+constexpr int kGemmMaxSplits = 16;
+struct GemmPlan {
+    int tile;             // 64 or 128
+    int bk;               // K depth of one LDS stage
+    int splits;           // >= 1
+    int64_t kper;         // K range of one split (a multiple of bk)
+    size_t part_bytes;    // fp32 partials [splits, M, N] (0 when splits == 1)
+};
+inline GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, bool bf16) {
+    GemmPlan g{};
+    const int64_t t128 = ((N + 127) / 128) * ((M + 127) / 128);
+    g.tile = t128 < 512 ? 64 : 128;
+    g.bk = g.tile == 64 ? (bf16 ? 64 : 32) : (bf16 ? 32 : 16);
+    const int64_t tiles = ((N + g.tile - 1) / g.tile) * ((M + g.tile - 1) / g.tile);
+    const int64_t steps = (K + g.bk - 1) / g.bk;
+    int64_t s = 1;
+    // split while the grid is short of workgroups and every split keeps >= 2 stages
+    // (a single row of output tiles, as in decode, keeps one launch: there the split's
+    // second kernel would cost more than it saves)
+    while (M > g.tile && s < kGemmMaxSplits && tiles * s * 2 <= kGemmTargetGroups && steps >= 4 * s) s *= 2;
+    g.kper = ((steps + s - 1) / s) * g.bk;
+    g.splits = (int)((K + g.kper - 1) / g.kper);
+    if (g.splits < 1) g.splits = 1;
+    g.part_bytes = g.splits > 1 ? (size_t)g.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
+    return g;
+}
 
 // Records the calling thread's error detail (ss_last_error) and returns s.
 ss_status set_error(ss_status s, const char* msg);
