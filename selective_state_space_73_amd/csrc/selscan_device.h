@@ -944,6 +944,261 @@ k_step(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 }
 
 // ---------------------------------------------------------------------------
+// Forward scan on grids that one lane per channel cannot fill (few batch rows x
+// channels, and sequences too short for enough chunks of at least one B/C tile):
+// four lanes (a quad) per (batch row, channel), lane q holding state entries
+// [q N/4, (q+1) N/4) as in the decode step, so the chip holds four times as many
+// waves. Every lane of a quad computes its channel's conv, step size and gate; the
+// readout is summed over the quad with DPP. Chunks, aggregates and workspace are
+// those of k_agg / k_scan, and the fold of the carry-in is the same. A chunk's
+// aggregate is its end state by the forward recurrence, exactly (chunks on these
+// grids are a few tiles long, where the truncated backward sweep would drop little).
+// x, delta, z, B and C of a group of kQuadGroup tokens are loaded one group ahead
+// (two register buffers used alternately). Lanes past the last channel repeat it
+// but store nothing: with no barrier between the waves of a workgroup, such a lane
+// could otherwise read an in-place state after its owner has written it.
+constexpr int kQuadGroup = 4;
+constexpr int64_t kQuadMaxGroups = 512;     // quad path below this many one-lane-per-channel workgroups
+
+template <typename T, int NQ, bool GATE, bool CB>
+struct QuadGroup {
+    T x[kQuadGroup], dl[kQuadGroup], z[GATE ? kQuadGroup : 1];
+    T b[kQuadGroup][NQ], c[CB ? kQuadGroup : 1][CB ? NQ : 1];
+};
+
+// Loads of rows r0 .. r0 + kQuadGroup - 1 of the chunk (clamped to its last row).
+template <typename T, int N, bool GATE, bool CB>
+__device__ __forceinline__ void quad_load(QuadGroup<T, N / 4, GATE, CB>& g, int r0, int nrows, const T* xb,
+                                          const T* db, const T* zb, const T* Bb, const T* Cb, int64_t D, int q) {
+    constexpr int NQ = N / 4;
+#pragma unroll
+    for (int i = 0; i < kQuadGroup; ++i) {
+        const int64_t r = r0 + i < nrows ? r0 + i : nrows - 1;
+        g.x[i] = xb[r * D];
+        g.dl[i] = db[r * D];
+        if constexpr (GATE) g.z[i] = zb[r * D];
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            g.b[i][k] = Bb[r * N + q * NQ + k];
+            if constexpr (CB) g.c[i][k] = Cb[r * N + q * NQ + k];
+        }
+    }
+}
+
+// Per-channel parameters and the conv window of a quad lane.
+template <int NQ, bool CONV, bool ZOH>
+struct QuadChannel {
+    float A2[NQ], iA[ZOH ? NQ : 1];
+    float dbias, w0, w1, w2, w3, cb;
+    float x3, x2, x1;                            // x_{t-3}, x_{t-2}, x_{t-1}
+    __device__ __forceinline__ void init(const float* A, const float* delta_bias, const float* conv_w,
+                                         const float* conv_b, int d, int q) {
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            const float av = A[(int64_t)d * (4 * NQ) + q * NQ + k];
+            const bool zero = ZOH && __builtin_fabsf(av) < kZohZeroA;
+            A2[k] = zero ? 0.0f : av * kLog2e;            // ZOH: an A = 0 state decays by exactly 1
+            if (ZOH) iA[k] = zero ? 0.0f : 1.0f / av;
+        }
+        dbias = delta_bias ? delta_bias[d] : 0.0f;
+        w0 = w1 = w2 = cb = 0.0f; w3 = 1.0f;
+        if (CONV) {
+            w0 = conv_w[d * 4 + 0]; w1 = conv_w[d * 4 + 1]; w2 = conv_w[d * 4 + 2]; w3 = conv_w[d * 4 + 3];
+            cb = conv_b ? conv_b[d] : 0.0f;
+        }
+        x3 = x2 = x1 = 0.0f;
+    }
+    // u of the token with input xt (conv + SiLU, or xt itself), shifting the window
+    __device__ __forceinline__ float input(float xt) {
+        if (!CONV) return xt;
+        const float cv = __builtin_fmaf(w3, xt, __builtin_fmaf(w2, x1, __builtin_fmaf(w1, x2, __builtin_fmaf(w0, x3, cb))));
+        x3 = x2; x2 = x1; x1 = xt;
+        return silu(cv);
+    }
+    // state update with step dt, input u and B row values braw; returns sum_k C_k h_k
+    template <typename T, bool READ>
+    __device__ __forceinline__ float update(float* h, float dt, float u, const T* braw, const T* craw) {
+        const float wv = dt * u;
+        float yp = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            const float tk = dt * A2[k];
+            const float a = exp2_fast(tk);
+            const float coef = ZOH ? zoh_coef(a, tk, dt, iA[ZOH ? k : 0]) * u : wv;
+            h[k] = __builtin_fmaf(a, h[k], coef * IO<T>::cvt(braw[k]));
+            if (READ) yp = __builtin_fmaf(IO<T>::cvt(craw[k]), h[k], yp);
+        }
+        return yp;
+    }
+};
+
+// The conv window x_{t0-3}, x_{t0-2}, x_{t0-1} of a chunk starting at t0.
+template <typename T>
+__device__ __forceinline__ void quad_window(float& x3, float& x2, float& x1, const T* xcol, int64_t t0, int64_t D,
+                                            const float* hist, int64_t bd) {
+    float xh[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int64_t tt = t0 - 3 + j;
+        xh[j] = tt >= 0 ? IO<T>::ld(xcol + tt * D) : (hist ? hist[bd * 3 + (3 + tt)] : 0.0f);
+    }
+    x3 = xh[0]; x2 = xh[1]; x1 = xh[2];
+}
+
+// Aggregates of every chunk but the last: its end state from its initial state (zero,
+// or the caller's state for chunk 0) and its summed step size (accumulated in fp64);
+// chunk 0 also copies the initial states for the main pass, whose last chunk
+// overwrites them.
+template <typename T, int N, bool CONV, bool ZOH>
+__global__ void __launch_bounds__(kScanThreads)
+k_agg_q(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
+        const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
+        const T* __restrict__ Bm, const float* __restrict__ ssm_state, const float* __restrict__ conv_state,
+        float* __restrict__ ws_S, float* __restrict__ ws_sdt, float* __restrict__ ws_h0, float* __restrict__ ws_c0,
+        ScanArgs sa) {
+    constexpr int NQ = N / 4;
+    const int D = sa.D;
+    const int q = threadIdx.x & 3;
+    const int d_raw = (blockIdx.x * kScanThreads + threadIdx.x) >> 2;
+    const bool live = d_raw < D;
+    const int d = live ? d_raw : D - 1;
+    const int c = blockIdx.y, b = blockIdx.z;
+    const int64_t t0 = (int64_t)c * sa.chunk_len;
+    const int nrows = (int)sa.chunk_len;         // every chunk but the last is full
+    const int64_t bd = (int64_t)b * D + d;
+    QuadChannel<NQ, CONV, ZOH> ch;
+    ch.init(A, delta_bias, conv_w, conv_b, d, q);
+    float h[NQ];
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) h[k] = (c == 0 && ssm_state) ? ssm_state[bd * N + q * NQ + k] : 0.0f;
+    if (c == 0 && live) {
+#pragma unroll
+        for (int k = 0; k < NQ; ++k)
+            if (ssm_state) ws_h0[bd * N + q * NQ + k] = h[k];
+        if (CONV && conv_state && q == 0) {
+            ws_c0[bd * 3 + 0] = conv_state[bd * 3 + 0];
+            ws_c0[bd * 3 + 1] = conv_state[bd * 3 + 1];
+            ws_c0[bd * 3 + 2] = conv_state[bd * 3 + 2];
+        }
+    }
+    const T* xcol = x + (int64_t)b * sa.L * D + d;              // channel d of batch row b, token 0
+    if (CONV) quad_window<T>(ch.x3, ch.x2, ch.x1, xcol, t0, D, conv_state, bd);
+    const T* xb = xcol + t0 * D;
+    const T* db = delta + ((int64_t)b * sa.L + t0) * D + d;
+    const T* Bb = Bm + ((int64_t)b * sa.L + t0) * N;
+    double sdt = 0.0;
+    QuadGroup<T, NQ, false, false> g0, g1;
+    auto group = [&](const QuadGroup<T, NQ, false, false>& g, int r0) {
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kQuadGroup; ++i) {
+            if (r0 + i >= nrows) break;                            // uniform
+            const float u = ch.input(IO<T>::cvt(g.x[i]));
+            const float dt = softplus(IO<T>::cvt(g.dl[i]) + ch.dbias);
+            part += dt;
+            ch.template update<T, false>(h, dt, u, g.b[i], nullptr);
+        }
+        sdt += (double)part;
+    };
+    quad_load<T, N, false, false>(g0, 0, nrows, xb, db, nullptr, Bb, nullptr, D, q);
+    for (int r = 0; r < nrows; r += 2 * kQuadGroup) {
+        quad_load<T, N, false, false>(g1, r + kQuadGroup, nrows, xb, db, nullptr, Bb, nullptr, D, q);
+        group(g0, r);
+        quad_load<T, N, false, false>(g0, r + 2 * kQuadGroup, nrows, xb, db, nullptr, Bb, nullptr, D, q);
+        group(g1, r + kQuadGroup);
+    }
+    if (live) {
+        const int64_t ai = ((int64_t)b * (sa.nchunks - 1) + c) * D + d;
+        if (q == 0) ws_sdt[ai] = (float)sdt;
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) ws_S[ai * N + q * NQ + k] = h[k];
+    }
+}
+
+template <typename T, int N, bool CONV, bool GATE, bool ZOH>
+__global__ void __launch_bounds__(kScanThreads)
+k_scan_q(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
+         const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
+         const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
+         const T* __restrict__ z, T* __restrict__ y, float* __restrict__ ssm_state, float* __restrict__ conv_state,
+         const float* __restrict__ ws_S, const float* __restrict__ ws_sdt, const float* __restrict__ ws_h0,
+         const float* __restrict__ ws_c0, ScanArgs sa) {
+    constexpr int NQ = N / 4;
+    const int D = sa.D;
+    const int q = threadIdx.x & 3;
+    const int d_raw = (blockIdx.x * kScanThreads + threadIdx.x) >> 2;
+    const bool live = d_raw < D;
+    const int d = live ? d_raw : D - 1;
+    const int c = blockIdx.y, b = blockIdx.z;
+    const int64_t t0 = (int64_t)c * sa.chunk_len;
+    const int64_t t1 = (t0 + sa.chunk_len < sa.L) ? t0 + sa.chunk_len : sa.L;
+    const int nrows = (int)(t1 - t0);
+    const int nagg = sa.nchunks - 1;
+    const bool multi = sa.nchunks > 1;
+    const int64_t bd = (int64_t)b * D + d;
+    QuadChannel<NQ, CONV, ZOH> ch;
+    ch.init(A, delta_bias, conv_w, conv_b, d, q);
+    const float dsk = Dskip ? Dskip[d] : 0.0f;
+
+    // initial state: the caller's (or its copy) for chunk 0, else the fold of the
+    // aggregates of chunks 0 .. c-1
+    float h[NQ];
+    if (c == 0) {
+        const float* src = (ssm_state && multi) ? ws_h0 : ssm_state;
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) h[k] = src ? src[bd * N + q * NQ + k] : 0.0f;
+    } else {
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) h[k] = 0.0f;
+        for (int cc = 0; cc < c; ++cc) {
+            const int64_t ai = ((int64_t)b * nagg + cc) * D + d;
+            const float sdt = ws_sdt[ai];
+#pragma unroll
+            for (int k = 0; k < NQ; ++k)
+                h[k] = __builtin_fmaf(exp2_fast(sdt * ch.A2[k]), h[k], ws_S[ai * N + q * NQ + k]);
+        }
+    }
+    const T* xcol = x + (int64_t)b * sa.L * D + d;
+    if (CONV) quad_window<T>(ch.x3, ch.x2, ch.x1, xcol, t0, D, conv_state ? (multi ? ws_c0 : conv_state) : nullptr, bd);
+    const int64_t row0 = (int64_t)b * sa.L + t0;
+    const T* xb = xcol + t0 * D;
+    const T* db = delta + row0 * D + d;
+    const T* zb = GATE ? z + row0 * D + d : nullptr;
+    T* yb = y + row0 * D + d;
+    const T* Bb = Bm + row0 * N;
+    const T* Cb = Cm + row0 * N;
+    QuadGroup<T, NQ, GATE, true> g0, g1;
+    auto group = [&](const QuadGroup<T, NQ, GATE, true>& g, int r0) {
+#pragma unroll
+        for (int i = 0; i < kQuadGroup; ++i) {
+            if (r0 + i >= nrows) break;                            // uniform
+            const float u = ch.input(IO<T>::cvt(g.x[i]));
+            const float dt = softplus(IO<T>::cvt(g.dl[i]) + ch.dbias);
+            const float yp = ch.template update<T, true>(h, dt, u, g.b[i], g.c[i]);
+            float yv = quad_sum(yp) + dsk * u;
+            if constexpr (GATE) yv *= silu(IO<T>::cvt(g.z[i]));
+            if (live && q == 0) IO<T>::st(yb + (int64_t)(r0 + i) * D, yv);
+        }
+    };
+    quad_load<T, N, GATE, true>(g0, 0, nrows, xb, db, zb, Bb, Cb, D, q);
+    for (int r = 0; r < nrows; r += 2 * kQuadGroup) {
+        quad_load<T, N, GATE, true>(g1, r + kQuadGroup, nrows, xb, db, zb, Bb, Cb, D, q);
+        group(g0, r);
+        quad_load<T, N, GATE, true>(g0, r + 2 * kQuadGroup, nrows, xb, db, zb, Bb, Cb, D, q);
+        group(g1, r + kQuadGroup);
+    }
+    if (live && c == sa.nchunks - 1) {
+        if (ssm_state) {
+#pragma unroll
+            for (int k = 0; k < NQ; ++k) ssm_state[bd * N + q * NQ + k] = h[k];
+        }
+        if (CONV && conv_state && q == 0) {
+            conv_state[bd * 3 + 0] = ch.x3; conv_state[bd * 3 + 1] = ch.x2; conv_state[bd * 3 + 2] = ch.x1;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launchers (templates; each instantiation unit calls dispatch_n for its dtype and rule)
 
 template <typename T, int N, bool CONV, bool GATE, bool ZOH, bool REV = false, bool PART = false>
@@ -955,6 +1210,25 @@ static hipError_t launch_scan_t(const LaunchScan& p) {
     hipStream_t st = static_cast<hipStream_t>(p.stream);
     ScanArgs sa{p.L, p.chunk_len, (int)p.D, p.nchunks, 0};
     const unsigned gx = (unsigned)((p.D + kScanThreads - 1) / kScanThreads);
+    if constexpr (!REV && !PART && N <= 16) {
+        if ((int64_t)gx * p.nchunks * p.batch < kQuadMaxGroups) {
+            // few channels: a lane quad per channel (k_agg_q / k_scan_q)
+            const unsigned gq = (unsigned)((4 * p.D + kScanThreads - 1) / kScanThreads);
+            if (p.nchunks > 1) {
+                hipExtLaunchKernelGGL((k_agg_q<T, N, CONV, ZOH>), dim3(gq, p.nchunks - 1, (unsigned)p.batch),
+                                      dim3(kScanThreads), 0, st, static_cast<hipEvent_t>(p.ev_agg[0]),
+                                      static_cast<hipEvent_t>(p.ev_agg[1]), 0, x, p.conv_w, p.conv_b, dl,
+                                      p.delta_bias, p.A, static_cast<const T*>(p.B), p.ssm_state, p.conv_state,
+                                      p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, sa);
+            }
+            hipExtLaunchKernelGGL((k_scan_q<T, N, CONV, GATE, ZOH>), dim3(gq, p.nchunks, (unsigned)p.batch),
+                                  dim3(kScanThreads), 0, st, static_cast<hipEvent_t>(p.ev_main[0]),
+                                  static_cast<hipEvent_t>(p.ev_main[1]), 0, x, p.conv_w, p.conv_b, dl, p.delta_bias,
+                                  p.A, static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip, z, y,
+                                  p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, sa);
+            return hipGetLastError();
+        }
+    }
     if (p.nchunks > 1) {
         hipExtLaunchKernelGGL((k_agg<T, N, CONV, ZOH, REV>), dim3(gx, p.nchunks - 1, (unsigned)p.batch),
                               dim3(kScanThreads), 0, st, static_cast<hipEvent_t>(p.ev_agg[0]),
