@@ -81,18 +81,42 @@ int choose_chunks(const ss_dims& d) {
     return (int)((d.seqlen + len - 1) / len);
 }
 
+// The forward's lane-quad path (k_agg_q / k_scan_q): d_state <= 16 and fewer than
+// kQuadMaxGroups one-lane-per-channel workgroups even with the chunks above.
+bool quad_path(const ss_dims& d) {
+    if (d.d_state > 16) return false;
+    const int64_t col_groups = (d.d_inner + selscan::kScanThreads - 1) / selscan::kScanThreads;
+    return d.batch * col_groups * choose_chunks(d) < selscan::kQuadMaxGroups;
+}
+
+// Its chunk count: about kQuadTargetLanes lanes (4 per channel), chunks of at least
+// kQuadMinChunk tokens, at most kQuadMaxChunks; every chunk but the last is full.
+int quad_chunks(const ss_dims& d) {
+    const int64_t lanes = 4 * d.batch * d.d_inner;
+    int64_t nc = (selscan::kQuadTargetLanes + lanes - 1) / lanes;
+    if (nc > selscan::kQuadMaxChunks) nc = selscan::kQuadMaxChunks;
+    if (nc > d.seqlen / selscan::kQuadMinChunk) nc = d.seqlen / selscan::kQuadMinChunk;
+    if (nc < 1) nc = 1;
+    const int64_t len = (d.seqlen + nc - 1) / nc;
+    return (int)((d.seqlen + len - 1) / len);
+}
+
 struct Layout {
     int nchunks = 1;
     int64_t chunk_len = 0;
+    bool quad = false;
     size_t off_S = 0, off_sdt = 0, off_h0 = 0, off_c0 = 0, total = 0;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-Layout layout(const ss_dims& d) {
+// fwd: the plain forward (ss_conv_scan_fwd), which may take the lane-quad path; the
+// bidirectional and backward passes keep whole-tile chunks.
+Layout layout(const ss_dims& d, bool fwd = false) {
     Layout l;
-    l.nchunks = choose_chunks(d);
-    l.chunk_len = chunk_len_for(d.seqlen, l.nchunks);
+    l.quad = fwd && quad_path(d);
+    l.nchunks = l.quad ? quad_chunks(d) : choose_chunks(d);
+    l.chunk_len = l.quad ? (d.seqlen + l.nchunks - 1) / l.nchunks : chunk_len_for(d.seqlen, l.nchunks);
     const size_t B = (size_t)d.batch, D = (size_t)d.d_inner, N = (size_t)d.d_state;
     size_t off = 0;
     if (l.nchunks > 1) {
@@ -293,6 +317,7 @@ void attach_workspace(selscan::LaunchScan& p, const Layout& l, void* workspace) 
     char* ws = static_cast<char*>(workspace);
     p.nchunks = l.nchunks;
     p.chunk_len = l.chunk_len;
+    p.quad = l.quad;
     if (l.nchunks > 1) {
         p.ws_S = reinterpret_cast<float*>(ws + l.off_S);
         p.ws_sdt = reinterpret_cast<float*>(ws + l.off_sdt);
@@ -315,7 +340,7 @@ extern "C" {
 
 size_t ss_workspace_bytes(const ss_dims* dims) {
     if (check_dims(dims, false) != SS_OK) return 0;
-    return layout(*dims).total;
+    return layout(*dims, true).total;
 }
 
 size_t ss_bidir_workspace_bytes(const ss_dims* dims) {
@@ -327,7 +352,7 @@ ss_status ss_conv_scan_fwd(const ss_dims* dims, const ss_args* args, void* works
                            size_t workspace_bytes, void* stream) {
     ss_status s = check_dims(dims, false);
     if (s == SS_OK) s = check_args(*dims, args, false);
-    const Layout l = s == SS_OK ? layout(*dims) : Layout{};
+    const Layout l = s == SS_OK ? layout(*dims, true) : Layout{};
     if (s == SS_OK) s = check_workspace(l, *args, workspace, workspace_bytes);
     if (s != SS_OK) { drop_events(); return s; }
 

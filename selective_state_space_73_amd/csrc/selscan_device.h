@@ -949,16 +949,18 @@ k_step(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 // four lanes (a quad) per (batch row, channel), lane q holding state entries
 // [q N/4, (q+1) N/4) as in the decode step, so the chip holds four times as many
 // waves. Every lane of a quad computes its channel's conv, step size and gate; the
-// readout is summed over the quad with DPP. Chunks, aggregates and workspace are
-// those of k_agg / k_scan, and the fold of the carry-in is the same. A chunk's
-// aggregate is its end state by the forward recurrence, exactly (chunks on these
-// grids are a few tiles long, where the truncated backward sweep would drop little).
+// readout is summed over the quad with DPP. The aggregates and their workspace are
+// those of k_agg / k_scan and the carry-in is the same fold, with the aggregates of
+// 8 chunks loaded before any is folded; chunks need not be whole B/C tiles (nothing
+// is staged in LDS), so the forward chunks these grids more finely. A chunk's
+// aggregate is its end state by the forward recurrence, exactly (the chunks here are
+// short, where the truncated backward sweep would drop little).
 // x, delta, z, B and C of a group of kQuadGroup tokens are loaded one group ahead
 // (two register buffers used alternately). Lanes past the last channel repeat it
 // but store nothing: with no barrier between the waves of a workgroup, such a lane
 // could otherwise read an in-place state after its owner has written it.
 constexpr int kQuadGroup = 4;
-constexpr int64_t kQuadMaxGroups = 512;     // quad path below this many one-lane-per-channel workgroups
+constexpr int kQuadFold = 8;               // aggregates loaded per step of the carry fold
 
 template <typename T, int NQ, bool GATE, bool CB>
 struct QuadGroup {
@@ -1150,12 +1152,23 @@ k_scan_q(const T* __restrict__ x, const float* __restrict__ conv_w, const float*
     } else {
 #pragma unroll
         for (int k = 0; k < NQ; ++k) h[k] = 0.0f;
-        for (int cc = 0; cc < c; ++cc) {
-            const int64_t ai = ((int64_t)b * nagg + cc) * D + d;
-            const float sdt = ws_sdt[ai];
+        for (int c0 = 0; c0 < c; c0 += kQuadFold) {
+            float sd[kQuadFold], sv[kQuadFold][NQ];
 #pragma unroll
-            for (int k = 0; k < NQ; ++k)
-                h[k] = __builtin_fmaf(exp2_fast(sdt * ch.A2[k]), h[k], ws_S[ai * N + q * NQ + k]);
+            for (int j = 0; j < kQuadFold; ++j) {
+                const int cc = c0 + j < c ? c0 + j : c - 1;      // past c: a repeated load, unused
+                const int64_t ai = ((int64_t)b * nagg + cc) * D + d;
+                sd[j] = ws_sdt[ai];
+#pragma unroll
+                for (int k = 0; k < NQ; ++k) sv[j][k] = ws_S[ai * N + q * NQ + k];
+            }
+#pragma unroll
+            for (int j = 0; j < kQuadFold; ++j) {
+                if (c0 + j < c) {                                 // uniform
+#pragma unroll
+                    for (int k = 0; k < NQ; ++k) h[k] = __builtin_fmaf(exp2_fast(sd[j] * ch.A2[k]), h[k], sv[j][k]);
+                }
+            }
         }
     }
     const T* xcol = x + (int64_t)b * sa.L * D + d;
@@ -1211,7 +1224,7 @@ static hipError_t launch_scan_t(const LaunchScan& p) {
     ScanArgs sa{p.L, p.chunk_len, (int)p.D, p.nchunks, 0};
     const unsigned gx = (unsigned)((p.D + kScanThreads - 1) / kScanThreads);
     if constexpr (!REV && !PART && N <= 16) {
-        if ((int64_t)gx * p.nchunks * p.batch < kQuadMaxGroups) {
+        if (p.quad) {
             // few channels: a lane quad per channel (k_agg_q / k_scan_q)
             const unsigned gq = (unsigned)((4 * p.D + kScanThreads - 1) / kScanThreads);
             if (p.nchunks > 1) {

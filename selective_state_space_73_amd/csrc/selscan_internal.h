@@ -17,6 +17,15 @@ constexpr int kScanThreads = 256;   // channels per workgroup of the scan kernel
 constexpr int kStepThreads = SELSCAN_STEP_THREADS;   // lanes per workgroup of the decode-step kernel (4 per channel)
 constexpr int kStepStreams = SELSCAN_STEP_STREAMS;   // streams each lane quad of the decode-step kernel handles
 constexpr int kScanTile = 64;       // tokens of B/C staged in LDS at a time
+// Lane-quad forward path (k_agg_q / k_scan_q): taken for d_state <= 16 when one lane
+// per channel gives fewer than kQuadMaxGroups workgroups even with 64-token chunks.
+// It chunks for about kQuadTargetLanes lanes (four waves per SIMD), with chunks of at
+// least kQuadMinChunk tokens and at most kQuadMaxChunks chunks (a chunk folds the
+// aggregates of every earlier one).
+constexpr int64_t kQuadMaxGroups = 512;
+constexpr int64_t kQuadTargetLanes = 4 * 1024 * 64;
+constexpr int64_t kQuadMinChunk = 16;
+constexpr int64_t kQuadMaxChunks = 128;
 
 // Everything a launch needs, already validated by the C-ABI layer.
 struct LaunchScan {
@@ -25,6 +34,7 @@ struct LaunchScan {
     bool bf16;
     bool zoh;       // zero-order-hold write term instead of Euler
     bool reverse;   // the reversed pass of a bidirectional scan: reads ypart, adds its output, writes y
+    bool quad;      // forward only: the lane-quad kernels (chunking of the quad rule)
     float* ypart;   // [B, L, D] fp32 forward output of a bidirectional scan (written by the
                     // forward pass when reverse is false, read by the reversed pass)
     const void* x; const float* conv_w; const float* conv_b; const void* delta; const float* delta_bias;
