@@ -955,12 +955,25 @@ k_step(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 // is staged in LDS), so the forward chunks these grids more finely. A chunk's
 // aggregate is its end state by the forward recurrence, exactly (the chunks here are
 // short, where the truncated backward sweep would drop little).
-// x, delta, z, B and C of a group of kQuadGroup tokens are loaded one group ahead
-// (two register buffers used alternately). Lanes past the last channel repeat it
+// x, delta, z, B and C of a group of kQuadGroup = 4 tokens are loaded one group ahead
+// (two register buffers used alternately). The per-token work that does not depend on
+// the state index (conv + SiLU, softplus, SiLU(z)) is split over the quad: lane q
+// computes it for token q of the group and DPP broadcasts the results to the others. Lanes past the last channel repeat it
 // but store nothing: with no barrier between the waves of a workgroup, such a lane
 // could otherwise read an in-place state after its owner has written it.
-constexpr int kQuadGroup = 4;
+constexpr int kQuadGroup = 4;              // one token of a group per lane of the quad
 constexpr int kQuadFold = 8;               // aggregates loaded per step of the carry fold
+
+// lane i's value on every lane of its quad
+template <int I>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return quad_dpp<I | (I << 2) | (I << 4) | (I << 6)>(v);
+}
+// lane q's pick among four per-token values
+template <typename V>
+__device__ __forceinline__ V quad_pick(int q, V a0, V a1, V a2, V a3) {
+    return q == 0 ? a0 : (q == 1 ? a1 : (q == 2 ? a2 : a3));
+}
 
 template <typename T, int NQ, bool GATE, bool CB>
 struct QuadGroup {
@@ -1010,12 +1023,36 @@ struct QuadChannel {
         }
         x3 = x2 = x1 = 0.0f;
     }
-    // u of the token with input xt (conv + SiLU, or xt itself), shifting the window
-    __device__ __forceinline__ float input(float xt) {
-        if (!CONV) return xt;
-        const float cv = __builtin_fmaf(w3, xt, __builtin_fmaf(w2, x1, __builtin_fmaf(w1, x2, __builtin_fmaf(w0, x3, cb))));
-        x3 = x2; x2 = x1; x1 = xt;
-        return silu(cv);
+    // Input u (conv + SiLU, or x itself), step size and gate factor SiLU(z) of the
+    // group's tokens 0..3: lane q computes those of token q, then every lane gets all
+    // four by broadcast. The window advances by the m (1..4) valid tokens.
+    template <typename T, bool GATE, typename G>
+    __device__ __forceinline__ void group_prologue(const G& g, int q, int m, float* u, float* dt, float* gz) {
+        static_assert(kQuadGroup == 4, "one token per lane of the quad");
+        const float xs[7] = {x3, x2, x1, IO<T>::cvt(g.x[0]), IO<T>::cvt(g.x[1]), IO<T>::cvt(g.x[2]),
+                             IO<T>::cvt(g.x[3])};
+        float uq;
+        if constexpr (CONV) {
+            float cv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                cv[i] = __builtin_fmaf(w3, xs[i + 3], __builtin_fmaf(w2, xs[i + 2], __builtin_fmaf(w1, xs[i + 1],
+                                       __builtin_fmaf(w0, xs[i], cb))));
+            uq = silu(quad_pick(q, cv[0], cv[1], cv[2], cv[3]));
+            if (m == 4) { x3 = xs[4]; x2 = xs[5]; x1 = xs[6]; }
+            else if (m == 3) { x3 = xs[3]; x2 = xs[4]; x1 = xs[5]; }
+            else if (m == 2) { x3 = xs[2]; x2 = xs[3]; x1 = xs[4]; }
+            else { x3 = xs[1]; x2 = xs[2]; x1 = xs[3]; }
+        } else {
+            uq = quad_pick(q, xs[3], xs[4], xs[5], xs[6]);
+        }
+        const float dq = softplus(IO<T>::cvt(quad_pick(q, g.dl[0], g.dl[1], g.dl[2], g.dl[3])) + dbias);
+        u[0] = quad_bcast<0>(uq); u[1] = quad_bcast<1>(uq); u[2] = quad_bcast<2>(uq); u[3] = quad_bcast<3>(uq);
+        dt[0] = quad_bcast<0>(dq); dt[1] = quad_bcast<1>(dq); dt[2] = quad_bcast<2>(dq); dt[3] = quad_bcast<3>(dq);
+        if constexpr (GATE) {
+            const float gq = silu(IO<T>::cvt(quad_pick(q, g.z[0], g.z[1], g.z[2], g.z[3])));
+            gz[0] = quad_bcast<0>(gq); gz[1] = quad_bcast<1>(gq); gz[2] = quad_bcast<2>(gq); gz[3] = quad_bcast<3>(gq);
+        }
     }
     // state update with step dt, input u and B row values braw; returns sum_k C_k h_k
     template <typename T, bool READ>
@@ -1091,14 +1128,16 @@ k_agg_q(const T* __restrict__ x, const float* __restrict__ conv_w, const float* 
     double sdt = 0.0;
     QuadGroup<T, NQ, false, false> g0, g1;
     auto group = [&](const QuadGroup<T, NQ, false, false>& g, int r0) {
+        if (r0 >= nrows) return;                                   // uniform
+        const int m = nrows - r0 < kQuadGroup ? nrows - r0 : kQuadGroup;
+        float u[kQuadGroup], dt[kQuadGroup];
+        ch.template group_prologue<T, false>(g, q, m, u, dt, nullptr);
         float part = 0.0f;
 #pragma unroll
         for (int i = 0; i < kQuadGroup; ++i) {
-            if (r0 + i >= nrows) break;                            // uniform
-            const float u = ch.input(IO<T>::cvt(g.x[i]));
-            const float dt = softplus(IO<T>::cvt(g.dl[i]) + ch.dbias);
-            part += dt;
-            ch.template update<T, false>(h, dt, u, g.b[i], nullptr);
+            if (i >= m) break;                                     // uniform
+            part += dt[i];
+            ch.template update<T, false>(h, dt[i], u[i], g.b[i], nullptr);
         }
         sdt += (double)part;
     };
@@ -1182,14 +1221,16 @@ k_scan_q(const T* __restrict__ x, const float* __restrict__ conv_w, const float*
     const T* Cb = Cm + row0 * N;
     QuadGroup<T, NQ, GATE, true> g0, g1;
     auto group = [&](const QuadGroup<T, NQ, GATE, true>& g, int r0) {
+        if (r0 >= nrows) return;                                   // uniform
+        const int m = nrows - r0 < kQuadGroup ? nrows - r0 : kQuadGroup;
+        float u[kQuadGroup], dt[kQuadGroup], gz[kQuadGroup];
+        ch.template group_prologue<T, GATE>(g, q, m, u, dt, gz);
 #pragma unroll
         for (int i = 0; i < kQuadGroup; ++i) {
-            if (r0 + i >= nrows) break;                            // uniform
-            const float u = ch.input(IO<T>::cvt(g.x[i]));
-            const float dt = softplus(IO<T>::cvt(g.dl[i]) + ch.dbias);
-            const float yp = ch.template update<T, true>(h, dt, u, g.b[i], g.c[i]);
-            float yv = quad_sum(yp) + dsk * u;
-            if constexpr (GATE) yv *= silu(IO<T>::cvt(g.z[i]));
+            if (i >= m) break;                                     // uniform
+            const float yp = ch.template update<T, true>(h, dt[i], u[i], g.b[i], g.c[i]);
+            float yv = quad_sum(yp) + dsk * u[i];
+            if constexpr (GATE) yv *= gz[i];
             if (live && q == 0) IO<T>::st(yb + (int64_t)(r0 + i) * D, yv);
         }
     };
