@@ -147,6 +147,33 @@ def test_workspace_query_and_check():
     assert ss.ss_workspace_bytes(_dims(batch=0)) == 0
 
 
+def _scan_ws(B, L, D, N, nc):
+    """Forward workspace for nc chunks: aggregates S [B, nc-1, D, N], summed steps
+    [B, nc-1, D], copies of the initial state [B, D, N] and conv history [B, D, 3]."""
+    a = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    if nc == 1:
+        return 0
+    return a(B * (nc - 1) * D * N * 4) + a(B * (nc - 1) * D * 4) + a(B * D * N * 4) + a(B * D * 3 * 4)
+
+
+def test_forward_chunk_rules():
+    """Host chunk rules, seen through the workspace size. Few channels and d_state <= 16
+    take the lane-quad kernels, chunked for about 2^18 lanes (four per channel) with
+    chunks of at least 16 tokens and at most 128 chunks: batch 2 x 1024 channels ->
+    32 chunks of 32 tokens; one row of 64 channels over 4096 tokens -> 128 chunks.
+    d_state 32 keeps one lane per channel and whole 64-token tiles, aiming at 512
+    workgroups of 256 lanes: 2 rows x 4 groups -> 64 chunks, capped at 1024 / 64 = 16.
+    The bidirectional passes keep the tile rule for every d_state."""
+    assert ss.ss_workspace_bytes(ss.make_dims(2, 1024, 1024, 16, ss.SS_F32)) == _scan_ws(2, 1024, 1024, 16, 32)
+    assert ss.ss_workspace_bytes(ss.make_dims(1, 4096, 64, 16, ss.SS_BF16)) == _scan_ws(1, 4096, 64, 16, 128)
+    assert ss.ss_workspace_bytes(ss.make_dims(2, 1024, 1024, 32, ss.SS_F32)) == _scan_ws(2, 1024, 1024, 32, 16)
+    a = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    assert ss.ss_bidir_workspace_bytes(ss.make_dims(2, 1024, 1024, 16, ss.SS_F32)) == \
+        a(_scan_ws(2, 1024, 1024, 16, 16)) + 2 * 1024 * 1024 * 4
+    # sequences shorter than two 16-token chunks stay in one chunk (no workspace)
+    assert ss.ss_workspace_bytes(ss.make_dims(2, 31, 1024, 16, ss.SS_F32)) == 0
+
+
 def test_workspace_alignment_and_overlap_checked():
     d = _dims(batch=1, seqlen=1 << 14, d_inner=64)
     need = ss.ss_workspace_bytes(d)
