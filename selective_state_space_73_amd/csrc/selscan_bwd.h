@@ -120,10 +120,20 @@ __device__ __forceinline__ void wave_sum(float (&v)[V], int lane) {
 }
 
 // --------------------------------------------------------------------------
-// Adjoint chunk aggregates (chunks 1 .. nchunks-1): swept backward over the chunk,
-// q <- exp(Delta_t A) (q + C_t dyg_t), so that q ends as the adjoint that the
-// chunk's own tokens send to the state before it, and the chunk's summed step
-// size (fp64 running total) for its decay exp(A sum Delta).
+// Adjoint chunk aggregates (chunks 1 .. nchunks-1): the adjoint that a chunk's own
+// tokens send to the state before it,
+//     Q_n = sum_t exp(A_n P_t) C_t[n] dyg_t,   P_t = sum of Delta over the chunk's
+//                                               tokens up to and including t,
+// and the chunk's summed step size (fp64 running total) for its decay exp(A sum Delta).
+// The sweep runs forward from the chunk start, so the weights exp(A_n P_t) only
+// shrink (A <= 0): a state index n is dropped (wave-uniformly; one index at a time up
+// to d_state 16, blocks of d_state/16 above) once exp(A_n P) < 2^-kAggCutLog2 on every
+// lane. Rows after the first drop add to a bound M = sum_t max_n |C_t[n]| |dyg_t|
+// (with |dy z| for |dyg| once every index is dropped, as |SiLU(z)| < |z|), and
+//     |dropped part of Q_n| <= 2^-kAggCutLog2 M.
+// Rows after every index is dropped only add their Delta. If that bound exceeds
+// 2^-24 max_n |Q_n| (one unit roundoff of the aggregate) on any lane, the wave
+// recomputes Q exactly by the backward (Horner) sweep q <- exp(Delta_t A) (q + C_t dyg_t).
 template <typename T, int N, bool GATE>
 __global__ void __launch_bounds__(kScanThreads)
 k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
@@ -145,10 +155,13 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
 
     constexpr int R = kScanTile;
     constexpr int U = 4;
-    __shared__ float sC[2][R][N];
+    constexpr int NB = N + 1;                     // C values and max_n |C| per row
+    static_assert(R % (2 * U) == 0, "a tile holds whole pairs of groups");
+    __shared__ float sC[2][R][NB];
     const int tid = threadIdx.x;
     constexpr int TILE_ELEMS = R * N;
     constexpr int PER_THREAD = (TILE_ELEMS + kScanThreads - 1) / kScanThreads;
+    static_assert(kScanThreads % N == 0 && 64 % N == 0, "a row's N values sit in consecutive lanes of a wave");
     const int64_t rowbase = (int64_t)b * ba.L + t0;
     const T* Cc = Cm + rowbase * N;
     T tc[PER_THREAD];
@@ -158,7 +171,7 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
             const int e0 = tid + k * kScanThreads;
             const int e = e0 < TILE_ELEMS ? e0 : TILE_ELEMS - 1;
             int r = rlo + e / N;
-            r = r < 0 ? 0 : (r > clen - 1 ? clen - 1 : r);
+            r = r > clen - 1 ? clen - 1 : r;
             tc[k] = Cc[(int64_t)r * N + e % N];
         }
     };
@@ -166,21 +179,23 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
 #pragma unroll
         for (int k = 0; k < PER_THREAD; ++k) {
             const int e = tid + k * kScanThreads;
-            if (e < TILE_ELEMS) sC[buf][e / N][e % N] = IO<T>::cvt(tc[k]);
+            const float v = IO<T>::cvt(tc[k]);
+            float m = __builtin_fabsf(v);
+#pragma unroll
+            for (int o = 1; o < N; o <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o, N));
+            if (e < TILE_ELEMS) {
+                sC[buf][e / N][e % N] = v;
+                if (e % N == 0) sC[buf][e / N][N] = m;
+            }
         }
     };
     const T* db = delta + rowbase * D;
     const T* zb = GATE ? z + rowbase * D : nullptr;
     const T* yb = dy + rowbase * D;
 
-    // rows go in groups of U aligned to the chunk start (so a group never crosses a
-    // tile), from the last group down. Even-numbered groups are loaded into one
-    // buffer and odd-numbered ones into the other, each one group ahead of its use;
-    // the loop takes a pair (odd, even) per iteration so neither buffer is copied
-    // and nothing waits for a load before the group that uses it. Tiles start at
-    // even group numbers, so a pair never crosses one. The raw I/O bits are held
-    // zero-extended in 32-bit registers.
-    static_assert(R % (2 * U) == 0, "pairs of groups do not cross tiles");
+    // group j holds rows 4j .. 4j+3 (chunk-relative; rows past the chunk end are
+    // padding with zero weight), loaded one group ahead into two buffers used
+    // alternately; raw I/O bits zero-extended in 32-bit registers
     uint32_t ed[U], ez[U], ey[U], od[U], oz[U], oy[U];
     auto raw = [&](const T* base, int r) -> uint32_t {
         const T v = (base + (int64_t)r * D)[du];
@@ -194,67 +209,129 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
     auto load_group = [&](int j, uint32_t* pd, uint32_t* pz, uint32_t* py) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            int r = U * j + U - 1 - i;                // rows of the group, last first
+            int r = U * j + i;
             r = r < clen ? r : clen - 1;
             pd[i] = raw(db, r);
             pz[i] = GATE ? raw(zb, r) : 0u;
             py[i] = raw(yb, r);
         }
     };
+
+    // state indices drop in blocks of BS (one each up to d_state 16); a block goes once
+    // its least negative exponent A2 * P is below the cut on every lane
+    constexpr int BS = N <= 16 ? 1 : N / 16;
+    constexpr int NBLK = N / BS;
+    static_assert(NBLK <= 32, "one mask bit per block");
+    float A2blk[NBLK];
+#pragma unroll
+    for (int j = 0; j < NBLK; ++j) {
+        float m = A2[BS * j];
+#pragma unroll
+        for (int k = 1; k < BS; ++k) m = __builtin_fmaxf(m, A2[BS * j + k]);
+        A2blk[j] = m;
+    }
+    const uint32_t full = NBLK == 32 ? 0xffffffffu : (1u << NBLK) - 1u;
+    uint32_t act = full;
+    const float cut = -(float)kAggCutLog2;
+
     float q[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) q[n] = 0.0f;
-    double sdt = 0.0;
-    auto group = [&](int j, const uint32_t* cd, const uint32_t* cz, const uint32_t* cy, const float* tile, int rhi) {
-        float part = 0.0f;
+    double Psum = 0.0;                            // sum of Delta over the rows swept so far
+    float M = 0.0f;                               // bound on the dropped part (rows after the first drop)
+    auto group = [&](int j, const uint32_t* cd, const uint32_t* cz, const uint32_t* cy, const float* tile) {
+        float dt[U], dyg[U];
+        bool valid[U];
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            const int r = U * j + U - 1 - i;
-            const bool valid = r < clen;               // only the chunk's last group can be short
-            const float dt = valid ? softplus(val(cd[i]) + dbias) : 0.0f;
-            float dyg = valid ? val(cy[i]) : 0.0f;
-            if (GATE) dyg *= silu(val(cz[i]));
-            const float* crow = tile + (int64_t)(valid ? r : rhi - 1) * N;
-#pragma unroll
-            for (int n = 0; n < N; ++n) q[n] = exp2_fast(dt * A2[n]) * __builtin_fmaf(crow[n], dyg, q[n]);
-            part += dt;
+            valid[i] = U * j + i < clen;
+            dt[i] = valid[i] ? softplus(val(cd[i]) + dbias) : 0.0f;
         }
-        sdt += (double)part;
+        const float pbase = (float)Psum;
+        float P[U], part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < U; ++i) { part += dt[i]; P[i] = pbase + part; }
+        Psum += (double)part;
+        const float* rowp = tile + (int64_t)(U * j) * NB;    // row 4j of the chunk
+        if (act) {
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                float g = valid[i] ? val(cy[i]) : 0.0f;
+                if (GATE) g *= silu(val(cz[i]));
+                dyg[i] = g;
+            }
+            if (act != full) {
+#pragma unroll
+                for (int i = 0; i < U; ++i) M = __builtin_fmaf(__builtin_fabsf(dyg[i]), rowp[i * NB + N], M);
+            }
+#pragma unroll
+            for (int jb = 0; jb < NBLK; ++jb) {
+                if ((act >> jb) & 1u) {
+#pragma unroll
+                    for (int i = 0; i < U; ++i) {
+#pragma unroll
+                        for (int k = 0; k < BS; ++k) {
+                            const int n = BS * jb + k;
+                            q[n] = __builtin_fmaf(exp2_fast(A2[n] * P[i]), rowp[i * NB + n] * dyg[i], q[n]);
+                        }
+                    }
+                    // weights only shrink further on: drop the block once every lane is below the cut
+                    if (!__any(A2blk[jb] * (float)Psum > cut)) act &= ~(1u << jb);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                float g = valid[i] ? __builtin_fabsf(val(cy[i])) : 0.0f;
+                if (GATE) g *= __builtin_fabsf(val(cz[i]));
+                M = __builtin_fmaf(g, rowp[i * NB + N], M);
+            }
+        }
     };
+
     const int ntiles = (clen + R - 1) / R;
-    const int ngroups = (clen + U - 1) / U;
-    int j = ngroups - 1;                          // the next group to process
-    tile_fetch((ntiles - 1) * R);
+    tile_fetch(0);
     tile_store(0);
-    if (j & 1) load_group(j, od, oz, oy);
-    else load_group(j, ed, ez, ey);
+    load_group(0, ed, ez, ey);
     __syncthreads();
     int buf = 0;
-    for (int k = ntiles - 1; k >= 0; --k) {
-        if (k > 0) tile_fetch((k - 1) * R);
-        const int rlo = k * R;
-        const int rhi = (rlo + R < clen) ? rlo + R : clen;
-        const float* tile = &sC[buf][0][0] - (int64_t)rlo * N;
-        const int jlo = rlo / U;                  // even
-        // the loads ahead are unconditional (group 0 again at the end, unused), so no
-        // buffer is ever merged from two paths
-        if ((j & 1) == 0 && j >= jlo) {           // an odd group count: the first group alone
-            load_group(j > 0 ? j - 1 : 0, od, oz, oy);
-            group(j, ed, ez, ey, tile, rhi);
-            --j;
+    for (int k = 0; k < ntiles; ++k) {
+        if (k + 1 < ntiles) tile_fetch((k + 1) * R);
+        const float* tile = &sC[buf][0][0] - (int64_t)(k * R) * NB;   // chunk row r at tile + r * NB
+        const int jend = (k + 1) * (R / U);
+        for (int j = k * (R / U); j < jend && U * j < clen; j += 2) {
+            load_group(j + 1, od, oz, oy);
+            group(j, ed, ez, ey, tile);
+            load_group(j + 2, ed, ez, ey);
+            group(j + 1, od, oz, oy, tile);
         }
-        for (; j > jlo; j -= 2) {                 // j odd, j - 1 >= jlo even
-            load_group(j - 1, ed, ez, ey);
-            group(j, od, oz, oy, tile, rhi);
-            load_group(j > 1 ? j - 2 : 0, od, oz, oy);
-            group(j - 1, ed, ez, ey, tile, rhi);
-        }
-        if (k > 0) tile_store(buf ^ 1);
+        if (k + 1 < ntiles) tile_store(buf ^ 1);
         __syncthreads();
         buf ^= 1;
     }
+
+    float qmax = 0.0f;
+#pragma unroll
+    for (int n = 0; n < N; ++n) qmax = __builtin_fmaxf(qmax, __builtin_fabsf(q[n]));
+    const bool bad = !(M * 0x1p-40f <= qmax * 0x1p-24f);
+    if (__any(bad)) {
+        // exact backward sweep over the chunk (rare: the dropped part was not negligible)
+#pragma unroll
+        for (int n = 0; n < N; ++n) q[n] = 0.0f;
+        double sd = 0.0;
+        for (int r = clen - 1; r >= 0; --r) {
+            const float dt = softplus(val(raw(db, r)) + dbias);
+            float g = val(raw(yb, r));
+            if (GATE) g *= silu(val(raw(zb, r)));
+            sd += (double)dt;
+            const T* crow = Cc + (int64_t)r * N;
+#pragma unroll
+            for (int n = 0; n < N; ++n) q[n] = exp2_fast(dt * A2[n]) * __builtin_fmaf(IO<T>::cvt(crow[n]), g, q[n]);
+        }
+        Psum = sd;
+    }
     const int64_t ai = ((int64_t)b * (ba.nchunks - 1) + (c - 1)) * D + d;
-    ws_qsdt[ai] = (float)sdt;
+    ws_qsdt[ai] = (float)Psum;
 #pragma unroll
     for (int n = 0; n < N; ++n) ws_Q[ai * N + n] = q[n];
 }

@@ -39,13 +39,16 @@ def _cotangents(Bsz, L, Dn, N, seed, io):
                 dconv_final=rng.standard_normal((Bsz, Dn, 3)).astype(np.float32))
 
 
-def check_bwd(ss, inp, io, *, states=True, finals=True, flags=None, label="", seed=900, full_sums=True, zoh=False):
+def check_bwd(ss, inp, io, *, states=True, finals=True, flags=None, label="", seed=900, full_sums=True, zoh=False,
+              dy_fn=None):
     f = dict(conv=True, gate=True, skip=True, bias=True)
     f.update(flags or {})
     Bsz, L, Dn = inp["x"].shape
     N = inp["A"].shape[1]
     st = W.gen_states(Bsz, Dn, N, seed=seed + 1) if states else None
     cot = _cotangents(Bsz, L, Dn, N, seed, io)
+    if dy_fn is not None:
+        cot["dy"] = dy_fn(cot["dy"])
     g = to_dev(inp, io)
     tdt = torch.bfloat16 if io == "bf16" else torch.float32
     kw = dict(conv_w=g["conv_w"] if f["conv"] else None, conv_b=g["conv_b"] if f["conv"] else None,
@@ -144,6 +147,38 @@ def test_bwd_train_full_size(ss):
 
 def test_bwd_long_full_size(ss):
     check_bwd(ss, W.gen_scan_inputs(W.WORKLOADS["long"]), "bf16", label="bwd long")
+
+
+def _bwd_long_chunks(ss):
+    """2 x 65536 tokens x 1024 channels: 64 chunks of 1024 tokens, long enough for the
+    adjoint-aggregate pass to drop state indices whose weight fell below 2^-40."""
+    spec = W.ScanSpec("bwdlc", 2, 65536, 1024, 16, io_dtype="f32", delta_mode="direct", seed=126)
+    inp = W.gen_scan_inputs(spec)
+    dims = ss.make_dims(2, 65536, 1024, 16, ss.SS_F32)
+    assert ss.ss_bwd_workspace_bytes(dims) > ss.ss_workspace_bytes(dims) > 0
+    return inp
+
+
+def test_bwd_long_chunks_truncated_adjoint_aggregates(ss):
+    """Step sizes in [1e-3, 1e-1]: the truncated adjoint aggregates keep every gradient
+    within the fp32 bar."""
+    check_bwd(ss, _bwd_long_chunks(ss), "f32", label="bwd long chunks")
+
+
+def test_bwd_adjoint_aggregate_bound_fallback(ss):
+    """Constant step 0.1 drops every state index within the first ~280 tokens of a
+    chunk, while the output gradient is 1e6 times larger in the last quarter of every
+    1024-token chunk: the bound on the dropped part then exceeds one unit roundoff of
+    the adjoint aggregate, the exact sweep takes over, and every gradient holds."""
+    inp = _bwd_long_chunks(ss)
+    inp["delta"][:] = np.float32(np.log(np.expm1(0.1)))
+    tail = (np.arange(65536) % 1024) >= 768
+
+    def loud_tail(dy):
+        dy = dy.copy()
+        dy[:, tail, :] *= np.float32(1e6)
+        return dy
+    check_bwd(ss, inp, "f32", label="bwd aggregate fallback", dy_fn=loud_tail)
 
 
 # ----------------------------------------------------------------------------- zero-order hold
