@@ -454,7 +454,17 @@ def cpu_baseline(sample, spec, target_s=12.0):
         times.append(run(k))
     dt = float(np.median(times))
     elems = spec.batch * spec.seqlen * k * spec.d_state
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(elems / dt / 1e9, 4), "unit": "Gelem/s", "cores": nthreads, "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": f"{k} of {spec.d_inner} channels (every 2nd from channel 0), all {spec.batch}x{spec.seqlen} "
                       f"tokens, d_state {spec.d_state}, fp64 OpenMP over channels; median of {len(times)} runs of "
                       f"{dt:.2f} s ({sum(times):.1f} s in total)"}
