@@ -649,8 +649,15 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     };
     bool cut_seen = false;                                // the window at the switch enters xmax once
 
-    // one group of U rows (gr-1 .. gr-U), B/C row of gr-1 at rowp
-    auto group = [&](int gr, const T* cd, const T* cx, const float* rowp) {
+    // one group of U rows (gr-1 .. gr-U); rowref is the staged row group_row(gr). Up to
+    // d_state 16 that is row gr-U and the B row of gr-1-i (and its max |B|) is read at
+    // rowref + (U-1-i) * NB, so every LDS read is one base register plus a non-negative
+    // immediate offset (a negative one cannot be encoded and costs an address move per
+    // read). Larger d_state passes row gr-1 and reads downward from it: with the cheaper
+    // reads the compiler keeps more of them in flight, which the zero-order-hold kernel
+    // at d_state 64 has no registers for.
+    auto group = [&](int gr, const T* cd, const T* cx, const float* rowref) {
+        auto brow = [&](int i) -> const float* { return N <= 16 ? rowref + (U - 1 - i) * NB : rowref - i * NB; };
         // x_{r-3} of each row, and which rows are padding; only the group that reaches
         // down to rel < 3 needs the selects
         float xd[U];
@@ -690,7 +697,7 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
             for (int i = 0; i < U; ++i) { Rf[i] = rbase + part; part += dt[i]; Ri[i] = rbase + part; }
             Rsum += (double)part;
 #pragma unroll
-            for (int i = 0; i < U; ++i) M = __builtin_fmaf(__builtin_fabsf(wv[i]), rowp[-i * NB + N], M);
+            for (int i = 0; i < U; ++i) M = __builtin_fmaf(__builtin_fabsf(wv[i]), brow(i)[N], M);
 #pragma unroll
             for (int j = 0; j < NBLK; ++j) {
                 if ((act >> j) & 1u) {
@@ -705,10 +712,10 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                                 const float big = (e - Ep[n]) * iA[n];                 // (E - E') / A
                                 const float small = Ep[n] * (dt[i] * phi_series(ts));   // E' Delta phi
                                 const float cf = __builtin_fabsf(ts) < kZohSeriesT ? small : big;
-                                S[n] = __builtin_fmaf(cf, uu[i] * rowp[-i * NB + n], S[n]);
+                                S[n] = __builtin_fmaf(cf, uu[i] * brow(i)[n], S[n]);
                                 Ep[n] = e;
                             } else {
-                                S[n] = __builtin_fmaf(exp2_fast(A2[n] * Rf[i]), wv[i] * rowp[-i * NB + n], S[n]);
+                                S[n] = __builtin_fmaf(exp2_fast(A2[n] * Rf[i]), wv[i] * brow(i)[n], S[n]);
                             }
                         }
                     }
@@ -729,12 +736,13 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                 xmax = __builtin_fmaxf(xmax, pad[i] ? 0.0f : __builtin_fabsf(xd[i]));
                 const float dtv = pad[i] ? 0.0f : softplus(IO<T>::cvt(cd[i]) + dbias);
                 part += dtv;
-                Mh = __builtin_fmaf(dtv, rowp[-i * NB + N], Mh);
+                Mh = __builtin_fmaf(dtv, brow(i)[N], Mh);
             }
             Rsum += (double)part;
         }
     };
 
+    auto group_row = [](int gr) { return N <= 16 ? gr - U : gr - 1; };
     const int ntiles = (clen + R - 1) / R;
     tile_fetch(clen - R);
     tile_store(0);
@@ -747,9 +755,9 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
         const float* tbase = &sB[buf][0][0] - (int64_t)(rhi - R) * NB;   // row r of this tile at tbase + r*NB
         for (int gr = rhi; gr > rhi - R; gr -= 2 * U) {
             load_group(gr - U, pd1, px1);
-            group(gr, pd0, px0, tbase + (gr - 1) * NB);
+            group(gr, pd0, px0, tbase + group_row(gr) * NB);
             load_group(gr - 2 * U, pd0, px0);
-            group(gr - U, pd1, px1, tbase + (gr - U - 1) * NB);
+            group(gr - U, pd1, px1, tbase + group_row(gr - U) * NB);
         }
         if (k + 1 < ntiles) tile_store(buf ^ 1);
         __syncthreads();
