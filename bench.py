@@ -492,7 +492,7 @@ def main():
                          "hardware traffic counters)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+        print(f"bench.py runs on one GPU: the library has no multi-GPU path (asked for --gpus {a.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
