@@ -81,16 +81,8 @@ int choose_chunks(const ss_dims& d) {
     return (int)((d.seqlen + len - 1) / len);
 }
 
-// The forward's lane-quad path (k_agg_q / k_scan_q): d_state <= 16 and fewer than
-// kQuadMaxGroups one-lane-per-channel workgroups even with the chunks above.
-bool quad_path(const ss_dims& d) {
-    if (d.d_state > 16) return false;
-    const int64_t col_groups = (d.d_inner + selscan::kScanThreads - 1) / selscan::kScanThreads;
-    return d.batch * col_groups * choose_chunks(d) < selscan::kQuadMaxGroups;
-}
-
-// Its chunk count: about kQuadTargetLanes lanes (4 per channel), chunks of at least
-// kQuadMinChunk tokens, at most kQuadMaxChunks; every chunk but the last is full.
+// The lane-quad chunk count: about kQuadTargetLanes lanes (4 per channel), chunks of
+// at least kQuadMinChunk tokens, at most kQuadMaxChunks; every chunk but the last is full.
 int quad_chunks(const ss_dims& d) {
     const int64_t lanes = 4 * d.batch * d.d_inner;
     int64_t nc = (selscan::kQuadTargetLanes + lanes - 1) / lanes;
@@ -99,6 +91,17 @@ int quad_chunks(const ss_dims& d) {
     if (nc < 1) nc = 1;
     const int64_t len = (d.seqlen + nc - 1) / nc;
     return (int)((d.seqlen + len - 1) / len);
+}
+
+// The forward's lane-quad path (k_agg_q / k_scan_q): d_state <= 16, fewer than
+// kQuadMaxTileWaves channel-holding waves on the one-lane kernels with the chunks
+// above, and at least twice as many on the quad kernels.
+bool quad_path(const ss_dims& d) {
+    if (d.d_state > 16) return false;
+    const int64_t tile_waves = d.batch * ((d.d_inner + 63) / 64) * choose_chunks(d);
+    if (tile_waves >= selscan::kQuadMaxTileWaves) return false;
+    const int64_t quad_waves = d.batch * ((4 * d.d_inner + 63) / 64) * quad_chunks(d);
+    return quad_waves >= 2 * tile_waves;
 }
 
 struct Layout {

@@ -17,12 +17,14 @@ constexpr int kScanThreads = 256;   // channels per workgroup of the scan kernel
 constexpr int kStepThreads = SELSCAN_STEP_THREADS;   // lanes per workgroup of the decode-step kernel (4 per channel)
 constexpr int kStepStreams = SELSCAN_STEP_STREAMS;   // streams each lane quad of the decode-step kernel handles
 constexpr int kScanTile = 64;       // tokens of B/C staged in LDS at a time
-// Lane-quad forward path (k_agg_q / k_scan_q): taken for d_state <= 16 when one lane
-// per channel gives fewer than kQuadMaxGroups workgroups even with 64-token chunks.
-// It chunks for about kQuadTargetLanes lanes (four waves per SIMD), with chunks of at
-// least kQuadMinChunk tokens and at most kQuadMaxChunks chunks (a chunk folds the
-// aggregates of every earlier one).
-constexpr int64_t kQuadMaxGroups = 512;
+// Lane-quad forward path (k_agg_q / k_scan_q), for d_state <= 16: taken when one lane
+// per channel, even with 64-token chunks, gives fewer than kQuadMaxTileWaves waves that
+// hold a channel (two per SIMD) and the quad layout at least doubles that count (its
+// lanes repeat the per-token work, about 1.6 times the instructions per row). It chunks
+// for about kQuadTargetLanes lanes (four waves per SIMD), with chunks of at least
+// kQuadMinChunk tokens and at most kQuadMaxChunks chunks (a chunk folds the aggregates
+// of every earlier one).
+constexpr int64_t kQuadMaxTileWaves = 2048;
 constexpr int64_t kQuadTargetLanes = 4 * 1024 * 64;
 constexpr int64_t kQuadMinChunk = 16;
 constexpr int64_t kQuadMaxChunks = 128;

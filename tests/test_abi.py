@@ -157,15 +157,19 @@ def _scan_ws(B, L, D, N, nc):
 
 
 def test_forward_chunk_rules():
-    """Host chunk rules, seen through the workspace size. Few channels and d_state <= 16
-    take the lane-quad kernels, chunked for about 2^18 lanes (four per channel) with
-    chunks of at least 16 tokens and at most 128 chunks: batch 2 x 1024 channels ->
-    32 chunks of 32 tokens; one row of 64 channels over 4096 tokens -> 128 chunks.
-    d_state 32 keeps one lane per channel and whole 64-token tiles, aiming at 512
-    workgroups of 256 lanes: 2 rows x 4 groups -> 64 chunks, capped at 1024 / 64 = 16.
+    """Host chunk rules, seen through the workspace size. One lane per channel takes
+    whole 64-token tiles, aiming at 512 workgroups of 256 lanes. With d_state <= 16,
+    when that gives fewer than 2048 waves holding a channel and the lane-quad kernels
+    at least double them, the quad kernels run, chunked for about 2^18 lanes (four per
+    channel) with chunks of at least 16 tokens and at most 128 chunks: batch 2 x 1024
+    channels -> 32 chunks of 32 tokens (tiles: 16 chunks, 512 waves); one row of 64
+    channels over 4096 tokens -> 128 chunks. One row of 256 channels over 24576 tokens
+    keeps the tiles: 384 chunks hold 1536 waves, the quad cap of 128 chunks 2048.
+    d_state 32 keeps the tiles: 2 rows x 4 groups -> 64 chunks, capped at 1024 / 64.
     The bidirectional passes keep the tile rule for every d_state."""
     assert ss.ss_workspace_bytes(ss.make_dims(2, 1024, 1024, 16, ss.SS_F32)) == _scan_ws(2, 1024, 1024, 16, 32)
     assert ss.ss_workspace_bytes(ss.make_dims(1, 4096, 64, 16, ss.SS_BF16)) == _scan_ws(1, 4096, 64, 16, 128)
+    assert ss.ss_workspace_bytes(ss.make_dims(1, 24576, 256, 16, ss.SS_BF16)) == _scan_ws(1, 24576, 256, 16, 384)
     assert ss.ss_workspace_bytes(ss.make_dims(2, 1024, 1024, 32, ss.SS_F32)) == _scan_ws(2, 1024, 1024, 32, 16)
     a = lambda v: (v + 255) // 256 * 256  # noqa: E731
     assert ss.ss_bidir_workspace_bytes(ss.make_dims(2, 1024, 1024, 16, ss.SS_F32)) == \
