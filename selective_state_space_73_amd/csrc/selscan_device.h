@@ -965,8 +965,12 @@ k_step(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 // short, where the truncated backward sweep would drop little).
 // x, delta, z, B and C of a group of kQuadGroup = 4 tokens are loaded one group ahead
 // (two register buffers used alternately). The per-token work that does not depend on
-// the state index (conv + SiLU, softplus, SiLU(z)) is split over the quad: lane q
-// computes it for token q of the group and DPP broadcasts the results to the others. Lanes past the last channel repeat it
+// the state index (conv + SiLU, softplus, SiLU(z)) is split over the quad: lane q loads
+// x, delta and z of token q of the group only, takes the earlier inputs of its conv
+// window from the lanes before it (DPP shifts within the quad, the carried window where
+// the shift would reach before the group), computes that token's terms and DPP
+// broadcasts them to the other lanes. The B and C quarter-rows of all four tokens are
+// loaded by every lane. Lanes past the last channel repeat it
 // but store nothing: with no barrier between the waves of a workgroup, such a lane
 // could otherwise read an in-place state after its owner has written it.
 constexpr int kQuadGroup = 4;              // one token of a group per lane of the quad
@@ -977,29 +981,30 @@ template <int I>
 __device__ __forceinline__ float quad_bcast(float v) {
     return quad_dpp<I | (I << 2) | (I << 4) | (I << 6)>(v);
 }
-// lane q's pick among four per-token values
-template <typename V>
-__device__ __forceinline__ V quad_pick(int q, V a0, V a1, V a2, V a3) {
-    return q == 0 ? a0 : (q == 1 ? a1 : (q == 2 ? a2 : a3));
-}
+// lane q takes lane q-1's value (quad_perm 0,0,1,2) and lane q-2's (quad_perm 0,0,0,1);
+// lanes without such a predecessor get lane 0's, which the caller replaces
+constexpr int kQuadPrev1 = 0 | (0 << 2) | (1 << 4) | (2 << 6);
+constexpr int kQuadPrev2 = 0 | (0 << 2) | (0 << 4) | (1 << 6);
 
 template <typename T, int NQ, bool GATE, bool CB>
 struct QuadGroup {
-    T x[kQuadGroup], dl[kQuadGroup], z[GATE ? kQuadGroup : 1];
+    T x, dl, z;                                  // token q of the group (lane q)
     T b[kQuadGroup][NQ], c[CB ? kQuadGroup : 1][CB ? NQ : 1];
 };
 
-// Loads of rows r0 .. r0 + kQuadGroup - 1 of the chunk (clamped to its last row).
+// Loads of rows r0 .. r0 + kQuadGroup - 1 of the chunk (clamped to its last row): x,
+// delta and z of row r0 + q on lane q, the B and C quarter-rows of all four rows.
 template <typename T, int N, bool GATE, bool CB>
 __device__ __forceinline__ void quad_load(QuadGroup<T, N / 4, GATE, CB>& g, int r0, int nrows, const T* xb,
                                           const T* db, const T* zb, const T* Bb, const T* Cb, int64_t D, int q) {
     constexpr int NQ = N / 4;
+    const int64_t rq = r0 + q < nrows ? r0 + q : nrows - 1;
+    g.x = xb[rq * D];
+    g.dl = db[rq * D];
+    if constexpr (GATE) g.z = zb[rq * D];
 #pragma unroll
     for (int i = 0; i < kQuadGroup; ++i) {
         const int64_t r = r0 + i < nrows ? r0 + i : nrows - 1;
-        g.x[i] = xb[r * D];
-        g.dl[i] = db[r * D];
-        if constexpr (GATE) g.z[i] = zb[r * D];
 #pragma unroll
         for (int k = 0; k < NQ; ++k) {
             g.b[i][k] = Bb[r * N + q * NQ + k];
@@ -1037,28 +1042,31 @@ struct QuadChannel {
     template <typename T, bool GATE, typename G>
     __device__ __forceinline__ void group_prologue(const G& g, int q, int m, float* u, float* dt, float* gz) {
         static_assert(kQuadGroup == 4, "one token per lane of the quad");
-        const float xs[7] = {x3, x2, x1, IO<T>::cvt(g.x[0]), IO<T>::cvt(g.x[1]), IO<T>::cvt(g.x[2]),
-                             IO<T>::cvt(g.x[3])};
+        const float xq = IO<T>::cvt(g.x);            // x of token q
         float uq;
         if constexpr (CONV) {
-            float cv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                cv[i] = __builtin_fmaf(w3, xs[i + 3], __builtin_fmaf(w2, xs[i + 2], __builtin_fmaf(w1, xs[i + 1],
-                                       __builtin_fmaf(w0, xs[i], cb))));
-            uq = silu(quad_pick(q, cv[0], cv[1], cv[2], cv[3]));
-            if (m == 4) { x3 = xs[4]; x2 = xs[5]; x1 = xs[6]; }
-            else if (m == 3) { x3 = xs[3]; x2 = xs[4]; x1 = xs[5]; }
-            else if (m == 2) { x3 = xs[2]; x2 = xs[3]; x1 = xs[4]; }
-            else { x3 = xs[1]; x2 = xs[2]; x1 = xs[3]; }
+            // token q's window x_{t-3}, x_{t-2}, x_{t-1}: earlier tokens of the group from
+            // the lanes before q, the rest from the window carried into the group
+            const float s1 = quad_dpp<kQuadPrev1>(xq), s2 = quad_dpp<kQuadPrev2>(xq), s3 = quad_bcast<0>(xq);
+            const float p1 = q >= 1 ? s1 : x1;
+            const float p2 = q >= 2 ? s2 : (q == 1 ? x1 : x2);
+            const float p3 = q == 3 ? s3 : (q == 2 ? x1 : (q == 1 ? x2 : x3));
+            uq = silu(__builtin_fmaf(w3, xq, __builtin_fmaf(w2, p1, __builtin_fmaf(w1, p2, __builtin_fmaf(w0, p3, cb)))));
+            // the window after the group's m valid tokens
+            const float l0 = s3, l1 = quad_bcast<1>(xq), l2 = quad_bcast<2>(xq), l3 = quad_bcast<3>(xq);
+            const float o1 = x1, o2 = x2;
+            if (m == 4) { x3 = l1; x2 = l2; x1 = l3; }
+            else if (m == 3) { x3 = l0; x2 = l1; x1 = l2; }
+            else if (m == 2) { x3 = o1; x2 = l0; x1 = l1; }
+            else { x3 = o2; x2 = o1; x1 = l0; }
         } else {
-            uq = quad_pick(q, xs[3], xs[4], xs[5], xs[6]);
+            uq = xq;
         }
-        const float dq = softplus(IO<T>::cvt(quad_pick(q, g.dl[0], g.dl[1], g.dl[2], g.dl[3])) + dbias);
+        const float dq = softplus(IO<T>::cvt(g.dl) + dbias);
         u[0] = quad_bcast<0>(uq); u[1] = quad_bcast<1>(uq); u[2] = quad_bcast<2>(uq); u[3] = quad_bcast<3>(uq);
         dt[0] = quad_bcast<0>(dq); dt[1] = quad_bcast<1>(dq); dt[2] = quad_bcast<2>(dq); dt[3] = quad_bcast<3>(dq);
         if constexpr (GATE) {
-            const float gq = silu(IO<T>::cvt(quad_pick(q, g.z[0], g.z[1], g.z[2], g.z[3])));
+            const float gq = silu(IO<T>::cvt(g.z));
             gz[0] = quad_bcast<0>(gq); gz[1] = quad_bcast<1>(gq); gz[2] = quad_bcast<2>(gq); gz[3] = quad_bcast<3>(gq);
         }
     }
