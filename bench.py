@@ -27,7 +27,8 @@ parameters. Prints one JSON line:
   the zero-order hold (whole-call and sweep-kernel time).
 * block: the Mamba block
   (ss_block_fwd, the library's MFMA projections around the scan) at d_model 512
-  (B2 L1024), random weights, with its decode step (ss_block_step) for 8 streams.
+  (B2 L1024), random weights, with its decode step (ss_block_step) for 8 streams,
+  eager and replayed from a HIP graph.
 * decode: 64 streams x 32 layers x 256 token steps (d_inner 8192, d_state 16),
   one ss_step per layer and token, timed end to end eagerly and replayed from
   HIP graphs (one graph per token step over the 32 layers); its roofline is
@@ -322,7 +323,36 @@ def run_block(ss, torch, hip, spec, steps, warmup, decode_steps, streams):
         ss.ss_block_step(xs, w, spec.rank, hs, cs, out=so, workspace=sws)
     torch.cuda.synchronize()
     dwall = time.perf_counter() - t0
-    return dict(ms=wall / steps * 1e3, scan_ms=scan_ms, decode_ms=dwall / decode_steps * 1e3, streams=S)
+    # the same step replayed from a HIP graph (the step issues no memset, nothing is
+    # allocated inside it); one replay from saved states must reproduce the eager step
+    gph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(gph, stream=cap):
+            ss.ss_block_step(xs, w, spec.rank, hs, cs, out=so, workspace=sws)
+    torch.cuda.synchronize()
+    h0, c0 = hs.clone(), cs.clone()
+    ss.ss_block_step(xs, w, spec.rank, hs, cs, out=so, workspace=sws)
+    torch.cuda.synchronize()
+    ref = (so.clone(), hs.clone(), cs.clone())
+    hs.copy_(h0)
+    cs.copy_(c0)
+    torch.cuda.synchronize()
+    gph.replay()
+    torch.cuda.synchronize()
+    if not (torch.equal(so, ref[0]) and torch.equal(hs, ref[1]) and torch.equal(cs, ref[2])):
+        raise RuntimeError("block decode step: graph replay differs from the eager step")
+    for _ in range(3):
+        gph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(decode_steps):
+        gph.replay()
+    torch.cuda.synchronize()
+    gwall = time.perf_counter() - t0
+    del gph
+    return dict(ms=wall / steps * 1e3, scan_ms=scan_ms, decode_ms=dwall / decode_steps * 1e3,
+                decode_graph_ms=gwall / decode_steps * 1e3, streams=S)
 
 
 def run_decode(ss, torch, hip, spec: W.DecodeSpec, token_steps: int):
@@ -646,7 +676,9 @@ def main():
                 "gemm_tflops_lower_bound": round(fl / (rest_ms / 1e3) / 1e12, 1) if rest_ms > 0 else None,
                 "mfma_peak_tflops": 2500.0,
                 "decode": {"streams": rb["streams"], "ms_per_token_step": round(rb["decode_ms"], 4),
-                           "tokens_per_s": round(rb["streams"] / (rb["decode_ms"] / 1e3), 1)},
+                           "tokens_per_s": round(rb["streams"] / (rb["decode_ms"] / 1e3), 1),
+                           "ms_per_token_step_graph": round(rb["decode_graph_ms"], 4),
+                           "tokens_per_s_graph": round(rb["streams"] / (rb["decode_graph_ms"] / 1e3), 1)},
             }
         out["block"] = blocks
     if not a.no_cpu and sample is not None:
