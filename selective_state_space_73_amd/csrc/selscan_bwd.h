@@ -14,7 +14,9 @@
 //   3. k_bagg       per chunk (after the first): the adjoint arriving at its start
 //                   from its own tokens, Q_c = sum_t prod_{k<=t} a_k C_t dyg_t, and its
 //                   summed step size, so that chunk c's adjoint carry-in is the fold
-//                   gamma_c = Q_{c+1} + exp(A sum Delta_{c+1}) gamma_{c+1};
+//                   gamma_c = Q_{c+1} + exp(A sum Delta_{c+1}) gamma_{c+1}; swept from
+//                   the chunk start, dropping state indices whose weight fell below
+//                   2^-40, with an exact fallback when the dropped part may matter;
 //   4. k_bwd        per chunk, 4-token segments from the end: recompute the segment
 //                   forward from its checkpoint (states kept in registers), then sweep
 //                   it backward; channel sums of dB/dC are reduced across the lanes of

@@ -15,7 +15,8 @@
 // values in VGPRs for a run of consecutive tokens (a chunk). Loads of x, delta,
 // z and stores of y are coalesced along d. B_t and C_t are the same for every
 // channel: each workgroup stages them through LDS in fp32 tiles and every wave
-// reads them back as broadcasts.
+// reads them back as broadcasts. Grids with too few channels for that mapping use
+// a lane quad per channel instead (k_agg_q / k_scan_q, further down).
 //
 // Long sequences with few channels are split into chunks so the grid fills the
 // GPU. The recurrence h_t = a_t h_{t-1} + b_t is associative in the pair (a, b)
@@ -956,23 +957,22 @@ k_step(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 // channels, and sequences too short for enough chunks of at least one B/C tile):
 // four lanes (a quad) per (batch row, channel), lane q holding state entries
 // [q N/4, (q+1) N/4) as in the decode step, so the chip holds four times as many
-// waves. Every lane of a quad computes its channel's conv, step size and gate; the
-// readout is summed over the quad with DPP. The aggregates and their workspace are
-// those of k_agg / k_scan and the carry-in is the same fold, with the aggregates of
-// 8 chunks loaded before any is folded; chunks need not be whole B/C tiles (nothing
-// is staged in LDS), so the forward chunks these grids more finely. A chunk's
-// aggregate is its end state by the forward recurrence, exactly (the chunks here are
-// short, where the truncated backward sweep would drop little).
-// x, delta, z, B and C of a group of kQuadGroup = 4 tokens are loaded one group ahead
-// (two register buffers used alternately). The per-token work that does not depend on
-// the state index (conv + SiLU, softplus, SiLU(z)) is split over the quad: lane q loads
-// x, delta and z of token q of the group only, takes the earlier inputs of its conv
-// window from the lanes before it (DPP shifts within the quad, the carried window where
-// the shift would reach before the group), computes that token's terms and DPP
-// broadcasts them to the other lanes. The B and C quarter-rows of all four tokens are
-// loaded by every lane. Lanes past the last channel repeat it
-// but store nothing: with no barrier between the waves of a workgroup, such a lane
-// could otherwise read an in-place state after its owner has written it.
+// waves; the readout is summed over the quad with DPP. The aggregates and their
+// workspace are those of k_agg / k_scan and the carry-in is the same fold, with the
+// aggregates of 8 chunks loaded before any is folded; chunks need not be whole B/C
+// tiles (nothing is staged in LDS), so the forward chunks these grids more finely. A
+// chunk's aggregate is its end state by the forward recurrence, exactly (the chunks
+// here are short, where the truncated backward sweep would drop little).
+// Tokens go in groups of kQuadGroup = 4, loaded one group ahead (two register buffers
+// used alternately). The per-token work that does not depend on the state index
+// (conv + SiLU, softplus, SiLU(z)) is split over the quad: lane q loads x, delta and z
+// of token q of the group only, takes the earlier inputs of its conv window from the
+// lanes before it (DPP shifts within the quad, the carried window where the shift
+// would reach before the group), computes that token's terms and DPP broadcasts them
+// to the other lanes. Every lane loads the B and C quarter-rows of all four tokens.
+// Lanes past the last channel repeat it but store nothing: with no barrier between
+// the waves of a workgroup, such a lane could otherwise read an in-place state after
+// its owner has written it.
 constexpr int kQuadGroup = 4;              // one token of a group per lane of the quad
 constexpr int kQuadFold = 8;               // aggregates loaded per step of the carry fold
 
