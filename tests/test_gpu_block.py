@@ -90,6 +90,16 @@ def test_block_fwd_wide_tiles(ss, io):
     run_case(ss, spec, states=io == "f32", Bsz=3, L=1500, label=f"block wide tiles {io}")
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_block_fwd_split_k_elementwise_loads(ss, io):
+    """d_model 1001: K of in_proj (1001) and of x_proj (2002) is no multiple of the
+    16-byte load chunk, so the projections load element by element, and with 200
+    rows their grids are short enough that they split K (in_proj 4 ways, x_proj and
+    out_proj 16 ways), summed by the reduce kernel, which also adds the residual."""
+    spec = W.BlockSpec("splitk", 1, 200, 1001, io_dtype=io, seed=779)
+    run_case(ss, spec, states=True, label=f"block split-K element loads {io}")
+
+
 def test_block_fwd_chunked_long(ss):
     """A long sequence with few channels takes the scan's chunked path inside the block."""
     spec = W.BlockSpec("longblock", 1, 8192, 64, expand=2, d_state=16, io_dtype="f32", seed=778)
