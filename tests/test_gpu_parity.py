@@ -177,13 +177,18 @@ def test_steps_match_scan(ss, io):
     assert torch.equal(c, c_s)
 
 
-def test_bitwise_deterministic(ss):
+@pytest.mark.parametrize("shape", [(1, 8192, 256), (2, 16384, 1024)], ids=["lane-quad", "one-lane"])
+def test_bitwise_deterministic(ss, shape):
+    """Three calls give bit-identical outputs and states, on a shape of each forward
+    path (1 x 8192 x 256 channels takes the lane-quad kernels, 2 x 16384 x 1024 the
+    one-lane chunked ones)."""
+    Bsz, L, Dn = shape
     spec = W.ScanSpec("det", 1, 1, 1, 16, io_dtype="bf16", delta_mode="direct", seed=3)
-    inp = W.gen_scan_inputs(spec, batch=1, seqlen=8192, d_inner=256)
+    inp = W.gen_scan_inputs(spec, batch=Bsz, seqlen=L, d_inner=Dn)
     g = to_dev(inp, "bf16")
     outs = []
     for _ in range(3):
-        h = torch.zeros(1, 256, 16, device="cuda")
+        h = torch.zeros(Bsz, Dn, 16, device="cuda")
         outs.append((gpu_fwd(ss, g, h), h))
     for y, h in outs[1:]:
         assert torch.equal(y, outs[0][0]) and torch.equal(h, outs[0][1])
