@@ -3,7 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|train|block]
                     [--no-decode] [--no-cpu] [--zoh-steps K] [--bidir-steps K] [--bwd-steps K]
-                    [--block-steps K]
+                    [--block-scan-steps K] [--block-steps K]
 
 A step is one ss_conv_scan_fwd call over the whole workload (conv1d + SiLU,
 softplus step, discretisation, scan, C.h + D.u readout, SiLU(z) gate), with
@@ -25,6 +25,8 @@ parameters. Prints one JSON line:
 * bwd: the backward (ss_conv_scan_bwd) on the same inputs with a seeded output
   gradient: whole-call time and the backward-sweep kernel's roofline; the same for
   the zero-order hold (whole-call and sweep-kernel time).
+* block_scan: the scan alone on the block-shaped workload (batch 2, L = 1024,
+  d_inner 1024, d_state 16, fp32, conv on), which takes the lane-quad kernels.
 * block: the Mamba block
   (ss_block_fwd, the library's MFMA projections around the scan) at d_model 512
   (B2 L1024), random weights, with its decode step (ss_block_step) for 8 streams,
@@ -515,6 +517,8 @@ def main():
                     help="timed bidirectional calls on the same inputs, parameters shared (0: skip)")
     ap.add_argument("--bwd-steps", type=int, default=5,
                     help="timed backward calls on the same inputs (0: skip)")
+    ap.add_argument("--block-scan-steps", type=int, default=20,
+                    help="timed scan calls on the block-shaped workload, B2 L1024 D1024 fp32 (0: skip)")
     ap.add_argument("--block-steps", type=int, default=10,
                     help="timed calls of the Mamba block at d_model 512 (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -655,6 +659,22 @@ def main():
                              "unit": "Gelem/s", "sweep_kernel_ms": round(rbz["kernel_ms"], 4),
                              "ratio_to_zoh_forward": round(bzms / out["zoh"]["ms_per_step"], 3) if "zoh" in out else None}
     del g
+    if a.block_scan_steps > 0 and a.workload != "block":
+        # the block-shaped scan (few channels: the lane-quad kernels), fp32 with conv
+        bsp = W.WORKLOADS["block"]
+        progress(f"scan {bsp.name}: {a.block_scan_steps} steps")
+        gb, _ = prepare_scan(torch, bsp, False)
+        rbs = run_scan(ss, torch, hip, bsp, gb, a.block_scan_steps, a.warmup)
+        bms = rbs["wall_s"] / a.block_scan_steps * 1e3
+        brows = bsp.batch * bsp.seqlen * bsp.d_inner
+        out["block_scan"] = {
+            "workload": f"{bsp.name}: batch {bsp.batch}, L={bsp.seqlen}, d_inner {bsp.d_inner}, d_state "
+                        f"{bsp.d_state}, d_conv 4, {bsp.io_dtype} I/O and state (lane-quad kernels)",
+            "value": round(brows * bsp.d_state / (bms / 1e3) / 1e9, 2), "unit": "Gelem/s",
+            "ms_per_step": round(bms, 4), "main_kernel_ms": round(rbs["main_ms"], 4),
+            "aggregate_kernel_ms": round(rbs["agg_ms"], 4),
+        }
+        del gb
     if a.block_steps > 0:
         torch.cuda.empty_cache()
         blocks = {}
