@@ -464,13 +464,13 @@ def cpu_baseline(sample, spec, target_s=12.0):
     orc = oracle.default()
     nthreads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
 
-    def run(k):
+    def run(k, threads=None):
         sl = slice(0, k)
         t0 = time.perf_counter()
         orc.conv_scan_fwd(sample["x"][:, :, sl], sample["delta"][:, :, sl], sample["A"][sl], sample["B"],
                           sample["C"], conv_w=sample["conv_w"][sl], conv_b=sample["conv_b"][sl],
                           delta_bias=sample["delta_bias"][sl], D=sample["D"][sl], z=sample["z"][:, :, sl],
-                          nthreads=nthreads)
+                          nthreads=threads or nthreads)
         return time.perf_counter() - t0
 
     avail = len(sample["dsel"])
@@ -486,6 +486,11 @@ def cpu_baseline(sample, spec, target_s=12.0):
         times.append(run(k))
     dt = float(np.median(times))
     elems = spec.batch * spec.seqlen * k * spec.d_state
+    # one thread, on about 4 s of the same sample
+    t1 = run(1, threads=1)
+    k1 = int(min(avail, max(1, 4.0 / max(t1, 1e-3))))
+    dt1 = run(k1, threads=1)
+    single = spec.batch * spec.seqlen * k1 * spec.d_state / dt1 / 1e9
     cpu_model = None
     try:
         with open("/proc/cpuinfo") as f:
@@ -497,6 +502,7 @@ def cpu_baseline(sample, spec, target_s=12.0):
         pass
     return {"value": round(elems / dt / 1e9, 4), "unit": "Gelem/s", "cores": nthreads, "kind": "oracle",
             "cpu_model": cpu_model,
+            "single_core": {"value": round(single, 4), "unit": "Gelem/s", "sample": f"{k1} channels, one thread"},
             "sample": f"{k} of {spec.d_inner} channels (every 2nd from channel 0), all {spec.batch}x{spec.seqlen} "
                       f"tokens, d_state {spec.d_state}, fp64 OpenMP over channels; median of {len(times)} runs of "
                       f"{dt:.2f} s ({sum(times):.1f} s in total)"}
