@@ -473,12 +473,17 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 // The sweep runs backward from the chunk end; a state index n is dropped
 // (wave-uniformly) once exp(A_n * R) < 2^-kAggCutLog2 for every lane, because R
 // only grows from there. Rows after every n is dropped only add Delta to the
-// chunk's sum (needed exactly for its decay exp(A*sum)) and to a bound M on
-// everything dropped (both write coefficients are at most Delta for A <= 0):
-//     |dropped part of S_n| <= 2^-kAggCutLog2 * sum_t |Delta_t u_t| * max_n |B_t[n]|.
-// If 2^-kAggCutLog2 * M exceeds 2^-24 * max_n |S_n| (one unit roundoff of the
-// aggregate) for any lane, the wave recomputes S exactly with the forward
-// recurrence. R is accumulated in fp64.
+// chunk's sum (needed exactly for its decay exp(A*sum)) and to a bound on what was
+// dropped (both write coefficients are at most Delta for A <= 0):
+//     |dropped part of S_n| <= 2^-kAggCutLog2 * M + umax * Mh,
+//     M  = sum over rows after the first drop, while some state is still active,
+//          of |Delta_t u_t| max_n |B_t[n]|,
+//     Mh = sum over rows after every state is dropped of exp(A_max R_t) Delta_t
+//          max_n |B_t[n]|, A_max the least negative A (bounding every dropped weight),
+// umax a bound on |u| over those rows (from their inputs, which need no SiLU).
+// If it exceeds 2^-24 * max_n |S_n| (one unit roundoff of the aggregate) for any
+// lane, the wave recomputes S exactly with the forward recurrence. R is
+// accumulated in fp64.
 
 constexpr int kAggCutLog2 = 40;
 
@@ -613,8 +618,14 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
         for (int q = 1; q < BS; ++q) m = __builtin_fmaxf(m, A2[BS * j + q]);
         A2blk[j] = m;
     }
-    uint32_t act = NBLK == 32 ? 0xffffffffu : (1u << NBLK) - 1u;
+    const uint32_t full = NBLK == 32 ? 0xffffffffu : (1u << NBLK) - 1u;
+    uint32_t act = full;
     const float cut = -(float)kAggCutLog2;
+    // the least negative exponent of all states: once every state is dropped (all of
+    // them negative then), exp2(A2max * R) bounds each dropped state's weight at R
+    float A2max = A2blk[0];
+#pragma unroll
+    for (int j = 1; j < NBLK; ++j) A2max = __builtin_fmaxf(A2max, A2blk[j]);
 
     // initial conv history (x_{-3}, x_{-2}, x_{-1}) in registers
     float hist0 = 0.f, hist1 = 0.f, hist2 = 0.f;
@@ -698,7 +709,10 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
             for (int i = 0; i < U; ++i) { Rf[i] = rbase + part; part += dt[i]; Ri[i] = rbase + part; }
             Rsum += (double)part;
 #pragma unroll
-            for (int i = 0; i < U; ++i) M = __builtin_fmaf(__builtin_fabsf(wv[i]), brow(i)[N], M);
+            for (int i = 0; i < U; ++i) {
+                // rows after the first drop (a group with every state still active drops nothing)
+                if (act != full) M = __builtin_fmaf(__builtin_fabsf(wv[i]), brow(i)[N], M);
+            }
 #pragma unroll
             for (int j = 0; j < NBLK; ++j) {
                 if ((act >> j) & 1u) {
@@ -730,15 +744,19 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                 xmax = __builtin_fmaxf(__builtin_fabsf(xa), __builtin_fmaxf(__builtin_fabsf(xb), __builtin_fabsf(xc)));
                 cut_seen = true;
             }
-            float part = 0.0f;
+            // every row of the group has weight at most exp2(A2max * R) at the group's
+            // first R, since R only grows (one exponential per group)
+            const float wt = exp2_fast(A2max * (float)Rsum);
+            float part = 0.0f, mg = 0.0f;
 #pragma unroll
             for (int i = 0; i < U; ++i) {
                 // each x enters the bound once, as the newest input of the row that loads it
                 xmax = __builtin_fmaxf(xmax, pad[i] ? 0.0f : __builtin_fabsf(xd[i]));
                 const float dtv = pad[i] ? 0.0f : softplus(IO<T>::cvt(cd[i]) + dbias);
                 part += dtv;
-                Mh = __builtin_fmaf(dtv, brow(i)[N], Mh);
+                mg = __builtin_fmaf(dtv, brow(i)[N], mg);
             }
+            Mh = __builtin_fmaf(wt, mg, Mh);
             Rsum += (double)part;
         }
     };
@@ -777,7 +795,7 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     float smax = 0.0f;
 #pragma unroll
     for (int n = 0; n < N; ++n) smax = __builtin_fmaxf(smax, __builtin_fabsf(S[n]));
-    const float bound = (M + umax * Mh) * 0x1p-40f;
+    const float bound = M * 0x1p-40f + umax * Mh;
     const bool bad = !(bound <= smax * 0x1p-24f);
     if (__any(bad)) {
         // exact forward recurrence over the chunk (rare: the dropped part was not negligible)
