@@ -130,9 +130,13 @@ __device__ __forceinline__ void wave_sum(float (&v)[V], int lane) {
 // The sweep runs forward from the chunk start, so the weights exp(A_n P_t) only
 // shrink (A <= 0): a state index n is dropped (wave-uniformly; one index at a time up
 // to d_state 16, blocks of d_state/16 above) once exp(A_n P) < 2^-kAggCutLog2 on every
-// lane. Rows after the first drop add to a bound M = sum_t max_n |C_t[n]| |dyg_t|
-// (with |dy z| for |dyg| once every index is dropped, as |SiLU(z)| < |z|), and
-//     |dropped part of Q_n| <= 2^-kAggCutLog2 M.
+// lane. The dropped part is bounded by
+//     |dropped part of Q_n| <= 2^-kAggCutLog2 M + Mh,
+//     M  = sum over rows after the first drop, while some index is still active, of
+//          max_n |C_t[n]| |dyg_t|,
+//     Mh = sum over rows after every index is dropped of exp(A_max P_t) max_n |C_t[n]|
+//          |dy_t z_t| (A_max the least negative A, bounding every dropped weight;
+//          |SiLU(z)| < |z|), taken per 4-row group at the group's first P.
 // Rows after every index is dropped only add their Delta. If that bound exceeds
 // 2^-24 max_n |Q_n| (one unit roundoff of the aggregate) on any lane, the wave
 // recomputes Q exactly by the backward (Horner) sweep q <- exp(Delta_t A) (q + C_t dyg_t).
@@ -235,12 +239,18 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
     const uint32_t full = NBLK == 32 ? 0xffffffffu : (1u << NBLK) - 1u;
     uint32_t act = full;
     const float cut = -(float)kAggCutLog2;
+    // the least negative exponent: once every index is dropped (all negative then),
+    // exp2(A2max * P) bounds each dropped weight at P
+    float A2max = A2blk[0];
+#pragma unroll
+    for (int j = 1; j < NBLK; ++j) A2max = __builtin_fmaxf(A2max, A2blk[j]);
 
     float q[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) q[n] = 0.0f;
     double Psum = 0.0;                            // sum of Delta over the rows swept so far
-    float M = 0.0f;                               // bound on the dropped part (rows after the first drop)
+    float M = 0.0f;                               // rows after the first drop, some index still active
+    float Mh = 0.0f;                              // rows after every index is dropped, weighted
     auto group = [&](int j, const uint32_t* cd, const uint32_t* cz, const uint32_t* cy, const float* tile) {
         float dt[U], dyg[U];
         bool valid[U];
@@ -282,12 +292,17 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
                 }
             }
         } else {
+            // every row of the group weighs at most exp2(A2max * P) at the group's first
+            // P (P only grows): one exponential per group
+            const float wt = exp2_fast(A2max * pbase);
+            float mg = 0.0f;
 #pragma unroll
             for (int i = 0; i < U; ++i) {
                 float g = valid[i] ? __builtin_fabsf(val(cy[i])) : 0.0f;
                 if (GATE) g *= __builtin_fabsf(val(cz[i]));
-                M = __builtin_fmaf(g, rowp[i * NB + N], M);
+                mg = __builtin_fmaf(g, rowp[i * NB + N], mg);
             }
+            Mh = __builtin_fmaf(wt, mg, Mh);
         }
     };
 
@@ -315,7 +330,7 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
     float qmax = 0.0f;
 #pragma unroll
     for (int n = 0; n < N; ++n) qmax = __builtin_fmaxf(qmax, __builtin_fabsf(q[n]));
-    const bool bad = !(M * 0x1p-40f <= qmax * 0x1p-24f);
+    const bool bad = !(M * 0x1p-40f + Mh <= qmax * 0x1p-24f);
     if (__any(bad)) {
         // exact backward sweep over the chunk (rare: the dropped part was not negligible)
 #pragma unroll
