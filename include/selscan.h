@@ -242,7 +242,9 @@ typedef struct {             /* DEVICE pointers, row-major, y = v W^T convention
 } ss_block_weights;
 
 /* Bytes of device workspace for ss_block_fwd (step = 0) or ss_block_step (step != 0):
- * the block's intermediate activations and the scan's workspace. 0 for invalid sizes. */
+ * the block's intermediate activations, the scan's workspace and the fp32 partial
+ * sums of the projections that split their reduction dimension over several
+ * workgroups. 0 for invalid sizes. */
 size_t ss_block_workspace_bytes(const ss_block_dims* dims, int step);
 
 /* Block forward over a sequence: out [B,L,d_model] from x [B,L,d_model]. ssm_state
