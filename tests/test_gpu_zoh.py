@@ -121,13 +121,17 @@ def test_zoh_long_chunks_fp32_truncated_aggregates(ss):
 
 
 def test_zoh_aggregate_bound_fallback(ss):
-    """As for Euler: constant step 0.1 and inputs of 1e6 in the first quarter of each
-    1024-token chunk force the exact recurrence in the aggregate pass."""
+    """As for Euler, on this shape's 512-token chunks: constant step 0.1 drops every
+    state about 280 tokens before a chunk's end, inputs 1e10 times larger sit just
+    before that point (chunk rows 185-224; their carry is 8e-3 of the chunk's end state,
+    which the truncated sweep would miss), so the exact recurrence must take over; the
+    gate is shut (z = -30) over the rows the large inputs would otherwise dominate."""
     spec = W.ScanSpec("zfb", 1, 65536, 1024, 16, io_dtype="f32", delta_mode="direct", seed=128)
     inp = W.gen_scan_inputs(spec)
     inp["delta"][:] = np.float32(np.log(np.expm1(0.1)))
-    head = (np.arange(65536) % 1024) < 256
-    inp["x"][:, head, :] *= np.float32(1e6)
+    r = np.arange(65536) % 512
+    inp["x"][:, (r >= 185) & (r < 225), :] *= np.float32(1e10)
+    inp["z"][:, (r >= 185) & (r < 490), :] = np.float32(-30.0)
     check_inputs(ss, inp, "f32", states=True, dsel=np.array([0, 3, 512, 1023]), zoh=True,
                  label="zoh bound fallback")
 
