@@ -111,6 +111,29 @@ typedef struct {
  * possible). Returns 0 also for invalid dims; ss_conv_scan_fwd then rejects them. */
 size_t ss_workspace_bytes(const ss_dims* dims);
 
+/* How a full-sequence call splits its work, for tests and tuning (the recurrence
+ * composes over chunks of consecutive tokens: ai360xpert.com "Mamba", "Why this
+ * breaks the parallel form"; ozercemkelahmet.com "Mamba", "Deployment notes", long
+ * prompts processed in pieces that pass the state on). `pass` names the call:
+ * SS_PASS_FWD for ss_conv_scan_fwd, SS_PASS_BIDIR for each pass of
+ * ss_conv_scan_bidir_fwd (the reversed pass counts chunks in reversed token order),
+ * SS_PASS_BWD for ss_conv_scan_bwd. On SS_OK *plan holds: nchunks, the chunk count
+ * (1: the call runs no chunk-aggregate pass); chunk_len, the tokens of every chunk
+ * but the last (chunk c starts at token c * chunk_len); lane_quad, 1 when four lanes
+ * share a channel (the forward on grids with few channels), 0 for one lane per
+ * channel. Invalid dims or pass return SS_ERR_INVALID_ARG / SS_ERR_UNSUPPORTED as the
+ * calls themselves would, and leave *plan untouched. Host only; touches no device. */
+typedef enum { SS_PASS_FWD = 0, SS_PASS_BIDIR = 1, SS_PASS_BWD = 2 } ss_pass;
+
+typedef struct {
+    int64_t nchunks;
+    int64_t chunk_len;
+    int32_t lane_quad;
+    int32_t reserved;   /* 0 */
+} ss_plan;
+
+ss_status ss_scan_plan(const ss_dims* dims, int32_t pass, ss_plan* plan);
+
 /* Full-sequence forward: y = gate(scan(conv(x))) for every (b, t, d), reading
  * the initial state from ssm_state / conv_state when given and overwriting them
  * with the state after token L-1 (so a long sequence can be processed in

@@ -39,6 +39,14 @@ class ss_args(ctypes.Structure):
                                    "z", "y", "ssm_state", "conv_state")]
 
 
+class ss_plan(ctypes.Structure):
+    _fields_ = [("nchunks", ctypes.c_int64), ("chunk_len", ctypes.c_int64), ("lane_quad", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+SS_PASS_FWD, SS_PASS_BIDIR, SS_PASS_BWD = 0, 1, 2
+
+
 class ss_dir_args(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("conv_w", "conv_b", "delta", "delta_bias", "A", "B", "C", "Dskip")]
 
@@ -72,6 +80,8 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     lib.ss_workspace_bytes.argtypes = [ctypes.POINTER(ss_dims)]
     lib.ss_workspace_bytes.restype = ctypes.c_size_t
+    lib.ss_scan_plan.argtypes = [ctypes.POINTER(ss_dims), ctypes.c_int32, ctypes.POINTER(ss_plan)]
+    lib.ss_scan_plan.restype = ctypes.c_int
     lib.ss_conv_scan_fwd.argtypes = [ctypes.POINTER(ss_dims), ctypes.POINTER(ss_args), _vp, ctypes.c_size_t, _vp]
     lib.ss_conv_scan_fwd.restype = ctypes.c_int
     lib.ss_conv_scan_bidir_fwd.argtypes = [ctypes.POINTER(ss_dims), ctypes.POINTER(ss_args),
@@ -152,6 +162,14 @@ def make_dims(batch: int, seqlen: int, d_inner: int, d_state: int, io_dtype: int
 
 def ss_workspace_bytes(dims: ss_dims) -> int:
     return int(lib.ss_workspace_bytes(ctypes.byref(dims)))
+
+
+def ss_scan_plan(dims: ss_dims, pass_: int = SS_PASS_FWD) -> dict:
+    """How a call with these dims splits the sequence: {"nchunks", "chunk_len",
+    "lane_quad"} (pass_: SS_PASS_FWD, SS_PASS_BIDIR or SS_PASS_BWD)."""
+    p = ss_plan()
+    _check(lib.ss_scan_plan(ctypes.byref(dims), int(pass_), ctypes.byref(p)))
+    return {"nchunks": int(p.nchunks), "chunk_len": int(p.chunk_len), "lane_quad": bool(p.lane_quad)}
 
 
 def _stream_handle(stream) -> Optional[int]:
@@ -399,5 +417,6 @@ def ss_block_step(x: torch.Tensor, W: dict, dt_rank: int, ssm_state: torch.Tenso
 
 
 __all__ = ["ss_conv_scan_bidir_fwd", "ss_bidir_workspace_bytes", "ss_dir_args", "DIR_KEYS", "ss_block_fwd", "ss_block_step", "ss_block_workspace_bytes", "block_dims", "ss_block_dims",
-           "ss_block_weights", "BLOCK_WEIGHTS", "ss_conv_scan_fwd", "ss_conv_scan_bwd", "ss_bwd_workspace_bytes", "ss_grads", "ss_step", "ss_workspace_bytes", "ss_version", "ss_time_next_call", "make_dims", "ss_dims", "ss_args",
+           "ss_block_weights", "BLOCK_WEIGHTS", "ss_conv_scan_fwd", "ss_conv_scan_bwd", "ss_bwd_workspace_bytes", "ss_grads", "ss_step", "ss_workspace_bytes", "ss_scan_plan", "ss_plan",
+           "SS_PASS_FWD", "SS_PASS_BIDIR", "SS_PASS_BWD", "ss_version", "ss_time_next_call", "make_dims", "ss_dims", "ss_args",
            "SelscanError", "SS_F32", "SS_BF16", "SS_EULER", "SS_ZOH", "LIB_PATH", "lib"]

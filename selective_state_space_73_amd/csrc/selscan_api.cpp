@@ -346,6 +346,20 @@ size_t ss_workspace_bytes(const ss_dims* dims) {
     return layout(*dims, true).total;
 }
 
+ss_status ss_scan_plan(const ss_dims* dims, int32_t pass, ss_plan* plan) {
+    if (!plan) return fail(SS_ERR_INVALID_ARG, "plan is NULL");
+    if (pass != SS_PASS_FWD && pass != SS_PASS_BIDIR && pass != SS_PASS_BWD)
+        return fail(SS_ERR_INVALID_ARG, "pass %d unknown", pass);
+    const ss_status s = check_dims(dims, false);
+    if (s != SS_OK) return s;
+    const Layout l = layout(*dims, pass == SS_PASS_FWD);
+    plan->nchunks = l.nchunks;
+    plan->chunk_len = l.chunk_len;
+    plan->lane_quad = l.quad ? 1 : 0;
+    plan->reserved = 0;
+    return SS_OK;
+}
+
 size_t ss_bidir_workspace_bytes(const ss_dims* dims) {
     if (check_dims(dims, false) != SS_OK) return 0;
     return bidir_layout(*dims).total;

@@ -25,7 +25,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["ss_workspace_bytes", "ss_conv_scan_fwd", "ss_step", "ss_status_str",
                                            "ss_last_error", "ss_version", "ss_time_next_call",
                                            "ss_bwd_workspace_bytes", "ss_conv_scan_bwd", "ss_conv_scan_bidir_fwd",
-                                           "ss_bidir_workspace_bytes",
+                                           "ss_bidir_workspace_bytes", "ss_scan_plan",
                                            "ss_block_workspace_bytes", "ss_block_fwd", "ss_block_step"])
 
 
@@ -50,6 +50,7 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(ss.ss_block_dims) == 56
     assert ctypes.sizeof(ss.ss_block_weights) == 10 * ctypes.sizeof(ctypes.c_void_p)
     assert ctypes.sizeof(ss.ss_dir_args) == 8 * ctypes.sizeof(ctypes.c_void_p)
+    assert ctypes.sizeof(ss.ss_plan) == 24
 
 
 def _dims(**kw):
@@ -176,6 +177,37 @@ def test_forward_chunk_rules():
         a(_scan_ws(2, 1024, 1024, 16, 16)) + 2 * 1024 * 1024 * 4
     # sequences shorter than two 16-token chunks stay in one chunk (no workspace)
     assert ss.ss_workspace_bytes(ss.make_dims(2, 31, 1024, 16, ss.SS_F32)) == 0
+
+
+def test_scan_plan_matches_the_chunk_rules():
+    """ss_scan_plan reports the chunking the workspace sizes above imply, per pass."""
+    P = ss.ss_scan_plan
+    assert P(ss.make_dims(2, 1024, 1024, 16, ss.SS_F32)) == dict(nchunks=32, chunk_len=32, lane_quad=True)
+    assert P(ss.make_dims(2, 1024, 1024, 16, ss.SS_F32), ss.SS_PASS_BIDIR) == \
+        dict(nchunks=16, chunk_len=64, lane_quad=False)
+    assert P(ss.make_dims(2, 1024, 1024, 16, ss.SS_F32), ss.SS_PASS_BWD) == \
+        dict(nchunks=16, chunk_len=64, lane_quad=False)
+    assert P(ss.make_dims(1, 24576, 256, 16, ss.SS_BF16)) == dict(nchunks=384, chunk_len=64, lane_quad=False)
+    # the long workload: 2048 channels = 8 workgroups, 64 chunks of 2048 tokens
+    assert P(ss.make_dims(1, 131072, 2048, 16, ss.SS_BF16)) == dict(nchunks=64, chunk_len=2048, lane_quad=False)
+    # enough channels for the GPU: one chunk
+    assert P(ss.make_dims(8, 2048, 5120, 16, ss.SS_BF16))["nchunks"] == 4
+    assert P(ss.make_dims(64, 2048, 5120, 16, ss.SS_BF16)) == dict(nchunks=1, chunk_len=2048, lane_quad=False)
+    for L, D, B in ((4096, 64, 1), (3001, 100, 2), (65536, 1024, 2), (65536, 1024, 1)):
+        for pas in (ss.SS_PASS_FWD, ss.SS_PASS_BIDIR, ss.SS_PASS_BWD):
+            p = P(ss.make_dims(B, L, D, 16, ss.SS_F32), pas)
+            assert (p["nchunks"] - 1) * p["chunk_len"] < L <= p["nchunks"] * p["chunk_len"], (L, D, B, pas, p)
+
+
+def test_scan_plan_rejects_bad_input():
+    d = ss.make_dims(1, 64, 8, 16, ss.SS_F32)
+    p = ss.ss_plan()
+    assert ss.lib.ss_scan_plan(ctypes.byref(d), 3, ctypes.byref(p)) == 1
+    assert ss.lib.ss_scan_plan(ctypes.byref(d), 0, None) == 1
+    bad = ss.make_dims(1, 64, 8, 12, ss.SS_F32)
+    assert ss.lib.ss_scan_plan(ctypes.byref(bad), 0, ctypes.byref(p)) == 2
+    zero = ss.make_dims(1, 0, 8, 16, ss.SS_F32)
+    assert ss.lib.ss_scan_plan(ctypes.byref(zero), 0, ctypes.byref(p)) == 1
 
 
 def test_workspace_alignment_and_overlap_checked():

@@ -173,20 +173,24 @@ def test_bidir_zoh_workloads(ss, name):
 
 
 def test_bidir_long_chunks_truncated_and_fallback(ss):
-    """fp32, 1024-token chunks: the reversed aggregate pass drops state indices below
-    2^-40 like the forward one. Then constant step 0.1 with inputs 1e10 times larger at
-    positions 290-329 of each 1024-position block, just past the point where the
-    reversed pass (which ends its chunks at the block's low positions) drops its last
-    state: their reversed carry into the previous block's last outputs is about 1e-3 of
-    the outputs' rms, which the truncated sweep would miss, so its exact fallback must
-    take over. The gate is shut (z = -30) over positions 24-599, where either
-    direction's state is dominated by those inputs."""
+    """fp32, one-lane chunks (1024 tokens on this shape, from the library's plan): the
+    reversed aggregate pass drops state indices below 2^-40 like the forward one. Then
+    constant step 0.1 with inputs 1e10 times larger at positions 290-329 of each
+    chunk-long block, just past the point where the reversed pass (which ends its
+    chunks at the block's low positions) drops its last state: their reversed carry
+    into the previous block's last outputs is about 1e-3 of the outputs' rms, which the
+    truncated sweep would miss, so its exact fallback must take over. The gate is shut
+    (z = -30) over positions 24-599 of each block, where either direction's state is
+    dominated by those inputs."""
+    from test_gpu_parity import one_lane_chunk_len
     spec = W.ScanSpec("lcb", 2, 65536, 1024, 16, io_dtype="f32", delta_mode="direct", seed=126)
     inp, _ = _inputs(spec)
+    cl = one_lane_chunk_len(ss, inp, "f32", pass_=ss.SS_PASS_BIDIR)
+    assert cl >= 1024 and 65536 % cl == 0, cl
     dsel = np.array([0, 5, 511, 700, 1023])
     check_bidir(ss, inp, "f32", dsel=dsel, label="bidir long chunks")
     inp["delta"][:] = np.float32(np.log(np.expm1(0.1)))
-    r = np.arange(65536) % 1024
+    r = np.arange(65536) % cl
     inp["x"][:, (r >= 290) & (r < 330), :] *= np.float32(1e10)
     inp["z"][:, (r >= 24) & (r < 600), :] = np.float32(-30.0)
     check_bidir(ss, inp, "f32", dsel=dsel, label="bidir fallback")

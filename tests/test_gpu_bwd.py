@@ -156,6 +156,8 @@ def _bwd_long_chunks(ss):
     inp = W.gen_scan_inputs(spec)
     dims = ss.make_dims(2, 65536, 1024, 16, ss.SS_F32)
     assert ss.ss_bwd_workspace_bytes(dims) > ss.ss_workspace_bytes(dims) > 0
+    p = ss.ss_scan_plan(dims, ss.SS_PASS_BWD)
+    assert p["nchunks"] > 1 and not p["lane_quad"], p
     return inp
 
 
@@ -167,15 +169,17 @@ def test_bwd_long_chunks_truncated_adjoint_aggregates(ss):
 
 def test_bwd_adjoint_aggregate_bound_fallback(ss):
     """Constant step 0.1 drops every state index of the adjoint aggregates within
-    about 280 tokens of each 1024-token chunk's start. Just past that point (chunk rows
-    285-324) the output gradient is 1e10 times larger and z = -30: the bound on the
-    dropped part, which takes |dy z| for |dy SiLU(z)|, then exceeds one unit roundoff
-    of the aggregate and the exact sweep runs, while dy SiLU(z) itself stays on the
-    scale of the other rows, so every gradient is checked at the fp32 bar with a
-    sensitive metric."""
+    278 tokens of each chunk's start. Just past that point (chunk rows 285-324; the
+    chunk length, 1024 tokens on this shape, is the library's plan) the output
+    gradient is 1e10 times larger and z = -30: the bound on the dropped part, which
+    takes |dy z| for |dy SiLU(z)|, then exceeds one unit roundoff of the aggregate and
+    the exact sweep runs, while dy SiLU(z) itself stays on the scale of the other rows,
+    so every gradient is checked at the fp32 bar with a sensitive metric."""
     inp = _bwd_long_chunks(ss)
     inp["delta"][:] = np.float32(np.log(np.expm1(0.1)))
-    r = np.arange(65536) % 1024
+    cl = ss.ss_scan_plan(ss.make_dims(2, 65536, 1024, 16, ss.SS_F32), ss.SS_PASS_BWD)["chunk_len"]
+    assert cl >= 512, cl
+    r = np.arange(65536) % cl
     loud = (r >= 285) & (r < 325)
     inp["z"][:, loud, :] = np.float32(-30.0)
 

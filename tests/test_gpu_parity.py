@@ -256,10 +256,20 @@ def test_step_without_conv_or_gate(ss, S, Dn, N):
     assert maxrel(host(h), hr) <= TOL["f32"]
 
 
-def _long_chunk_case(ss, inp, io, dsel, label, states=True):
+def one_lane_chunk_len(ss, inp, io, zoh=False, pass_=0):
+    """Chunk length of the one-lane chunked kernels for these inputs' shape; fails when
+    the shape would run unchunked or on the lane-quad kernels (whose aggregates are
+    exact, so a truncation test there would test nothing)."""
     Bsz, L, Dn = inp["x"].shape
-    dims = ss.make_dims(Bsz, L, Dn, inp["A"].shape[1], 0 if io == "f32" else 1)
-    assert ss.ss_workspace_bytes(dims) > 0, "shape does not select the chunked path"
+    dims = ss.make_dims(Bsz, L, Dn, inp["A"].shape[1], 0 if io == "f32" else 1,
+                        discretization=ss.SS_ZOH if zoh else ss.SS_EULER)
+    p = ss.ss_scan_plan(dims, pass_)
+    assert p["nchunks"] > 1 and not p["lane_quad"], ("shape does not select the one-lane chunked path", p)
+    return p["chunk_len"]
+
+
+def _long_chunk_case(ss, inp, io, dsel, label, states=True):
+    one_lane_chunk_len(ss, inp, io)
     check_inputs(ss, inp, io, states=states, dsel=dsel, label=label, state_tol=TOL["f32"])
 
 
@@ -272,22 +282,25 @@ def test_long_chunks_fp32_truncated_aggregates(ss):
 
 
 def test_aggregate_bound_fallback(ss):
-    """Constant step 0.1: the aggregate pass drops the slowest state (A = -1) about
-    280 tokens before each 1024-token chunk's end. Inputs 1e10 times larger sit just
-    before that point (chunk rows 694-733), where the state weights are e^-29 to e^-33:
-    their contribution to the chunk's end state is about 2e-3 of it, which the
-    truncated sweep would miss. The bound on the dropped part (those rows' weights
-    times the largest input) then exceeds one unit roundoff of the aggregate, the
-    exact recurrence takes over, and the next chunk's outputs and the final state
-    hold the fp32 bar. The gate is shut (z = -30) over the rows the large inputs would
-    otherwise dominate, so every output stays on the scale of the others and the
-    error metric stays sensitive to the carry."""
+    """Constant step 0.1: the aggregate pass drops the slowest state (A = -1) 278
+    tokens before each chunk's end (0.1 * 278 > 40 ln 2). Inputs 1e10 times larger
+    sit just before that point (290-329 tokens before the chunk end), where the state
+    weights are e^-29 to e^-33: their contribution to the chunk's end state is about
+    2e-3 of it, which the truncated sweep would miss. The bound on the dropped part
+    (those rows' weights times the largest input) then exceeds one unit roundoff of
+    the aggregate, the exact recurrence takes over, and the next chunk's outputs and
+    the final state hold the fp32 bar. The gate is shut (z = -30) over the rows the
+    large inputs would otherwise dominate, so every output stays on the scale of the
+    others and the error metric stays sensitive to the carry. The rows are placed from
+    the chunk length the library reports for this shape."""
     spec = W.ScanSpec("fb", 2, 65536, 1024, 16, io_dtype="f32", delta_mode="direct", seed=124)
     inp = W.gen_scan_inputs(spec)
     inp["delta"][:] = np.float32(np.log(np.expm1(0.1)))
-    r = np.arange(65536) % 1024
-    inp["x"][:, (r >= 694) & (r < 734), :] *= np.float32(1e10)
-    inp["z"][:, (r >= 694) & (r < 1000), :] = np.float32(-30.0)
+    cl = one_lane_chunk_len(ss, inp, "f32")
+    assert cl >= 512, cl
+    r = np.arange(65536) % cl
+    inp["x"][:, (r >= cl - 330) & (r < cl - 290), :] *= np.float32(1e10)
+    inp["z"][:, (r >= cl - 330) & (r < cl - 24), :] = np.float32(-30.0)
     _long_chunk_case(ss, inp, "f32", np.array([0, 3, 512, 1023]), "bound fallback")
 
 
