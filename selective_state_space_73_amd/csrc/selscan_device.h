@@ -83,6 +83,61 @@ __device__ __forceinline__ float zoh_coef(float a, float t, float dt, float iA) 
     return __builtin_fabsf(t) < kZohSeriesT ? small : big;
 }
 
+// Runtime-checked fast path for A[d, n] = (n + 1) * A[d, 0] (the A = -(1..N)
+// initialisation of ozercemkelahmet.com "Mamba", "A minimal selective scan in PyTorch",
+// and the benchmark workloads): then exp(Delta A[d, n]) = exp(Delta A[d, 0])^(n+1), so
+// one exponential and N - 1 multiplies give every state's decay. a_n carries about
+// n + 1 roundings of a_0 plus n of its own, the same order as the error an
+// exponential of the (n + 1)-fold argument makes over the state's (n + 1)-fold shorter
+// memory. The kernels that take it are launched twice, with POW = false and true;
+// each workgroup votes on the identity over its channels and runs in exactly one of
+// the two launches (the other returns at once).
+constexpr int kPowMinN = 8;              // below this the saved exponentials do not pay for a second launch
+
+// a[n] = a0^(n+1): squares for even exponents, one more factor of a0 for odd ones
+template <int N>
+__device__ __forceinline__ void pow_chain(float a0, float* a) {
+    a[0] = a0;
+#pragma unroll
+    for (int n = 1; n < N; ++n) {
+        const int p = n + 1;
+        a[n] = (p % 2 == 0) ? a[p / 2 - 1] * a[p / 2 - 1] : a[n - 1] * a0;
+    }
+}
+
+// true on this lane when A[d, n] == (n + 1) * A[d, 0] holds exactly in fp32 for every n
+// (its own loads, not merged with the kernel's later loads of A, so that these raw
+// values are not kept live)
+template <int N>
+__device__ __forceinline__ bool pow_structured(const float* Arow) {
+    const float a0 = __builtin_nontemporal_load(Arow);
+    bool ok = true;
+#pragma unroll
+    for (int n = 1; n < N; ++n) ok = ok && (__builtin_nontemporal_load(Arow + n) == (float)(n + 1) * a0);
+    return ok;
+}
+
+// Workgroup vote of the power fast path, taken at the start of a kernel launched once
+// with POW = false and once with POW = true: returns true when this workgroup belongs
+// to the other launch and must exit (uniformly, before any other barrier).
+template <int N, bool POW>
+__device__ __forceinline__ bool pow_skip(const float* Arow) {
+    if constexpr (N < kPowMinN) {
+        return POW;                                  // only the general launch exists
+    } else {
+        // one flag per wave in LDS, one barrier, then every lane reads all of them
+        static_assert(kScanThreads % 64 == 0 && kScanThreads / 64 <= 32, "one vote bit per wave");
+        __shared__ uint32_t votes;
+        const bool mine = __all(pow_structured<N>(Arow));
+        if (threadIdx.x == 0) votes = 0;
+        __syncthreads();
+        if ((threadIdx.x & 63) == 0 && !mine) atomicOr(&votes, 1u);
+        __syncthreads();
+        const bool all = votes == 0;
+        return all != POW;
+    }
+}
+
 typedef float vf4 __attribute__((ext_vector_type(4)));
 
 template <typename T> struct IO;
@@ -173,7 +228,8 @@ template <int N, bool CONV, bool ZOH, bool CK, bool REV> constexpr int scan_wave
 // gated output as fp32 to ypart [B, L, D] instead of y. REV: the same layer over the
 // time-reversed sequence, so chunk-relative token r of chunk c is position
 // L-1-(c*chunk_len + r); it adds its gated output to ypart's and writes the sum to y.
-template <typename T, int N, bool CONV, bool GATE, bool ZOH, bool CK = false, bool REV = false, bool PART = false>
+template <typename T, int N, bool CONV, bool GATE, bool ZOH, bool CK = false, bool REV = false, bool PART = false,
+          bool POW = false>
 __global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<N, CONV, ZOH, CK, REV>())))
 k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
        const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
@@ -190,11 +246,13 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
        ScanArgs sa) {
     static_assert(!(CK && GATE), "checkpoint mode has no gate");
     static_assert(!(CK && (REV || PART)) && !(REV && PART), "one mode per pass");
+    static_assert(!POW || N >= kPowMinN, "power path only from kPowMinN states");
     const int D = sa.D;
     const int d_raw = blockIdx.x * kScanThreads + threadIdx.x;
     // lanes past the last channel work on the last channel: they compute and store
     // bit-identical values, so no store needs a branch
     const int d = d_raw < D ? d_raw : D - 1;
+    if (pow_skip<N, POW>(A + (int64_t)d * N)) return;       // the workgroup runs in the other launch
     const unsigned du = (unsigned)d;              // zero-extended lane offset: uniform-base addressing
     const int c = blockIdx.y;
     const int b = blockIdx.z;
@@ -245,9 +303,15 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         for (int cc = 0; cc < c; ++cc) {
             const int64_t ai = ((int64_t)b * nagg + cc) * D + d;
             const float sdt = ws_sdt[ai];
+            float dec[N];
+            if constexpr (POW) {
+                pow_chain<N>(exp2_fast(sdt * A2[0]), dec);
+            } else {
 #pragma unroll
-            for (int n = 0; n < N; ++n)
-                h[n] = __builtin_fmaf(exp2_fast(sdt * A2[n]), h[n], ws_S[ai * N + n]);
+                for (int n = 0; n < N; ++n) dec[n] = exp2_fast(sdt * A2[n]);
+            }
+#pragma unroll
+            for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(dec[n], h[n], ws_S[ai * N + n]);
         }
     }
 
@@ -351,18 +415,33 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 #pragma unroll
             for (int n = 0; n < N; ++n) cv[n] = bct[N + n];
         }
+        if constexpr (POW) {
+            // power chain, one factor per state (a_n = a_{n-1} a_0), each decay used at
+            // once so that only two of them are live
+            const float a0 = exp2_fast(p.dt * A2[0]);
+            float an = a0;
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            t[n] = p.dt * A2[n];
-            a[n] = exp2_fast(t[n]);
-        }
-        if constexpr (ZOH) {
-#pragma unroll
-            for (int n = 0; n < N; ++n)
-                h[n] = __builtin_fmaf(a[n], h[n], zoh_coef(a[n], t[n], p.dt, iA[n]) * (p.u * bv[n]));
+            for (int n = 0; n < N; ++n) {
+                if (n > 0) an *= a0;
+                if constexpr (ZOH)
+                    h[n] = __builtin_fmaf(an, h[n], zoh_coef(an, p.dt * A2[n], p.dt, iA[n]) * (p.u * bv[n]));
+                else
+                    h[n] = __builtin_fmaf(an, h[n], p.wv * bv[n]);
+            }
         } else {
 #pragma unroll
-            for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(a[n], h[n], p.wv * bv[n]);
+            for (int n = 0; n < N; ++n) {
+                t[n] = p.dt * A2[n];
+                a[n] = exp2_fast(t[n]);
+            }
+            if constexpr (ZOH) {
+#pragma unroll
+                for (int n = 0; n < N; ++n)
+                    h[n] = __builtin_fmaf(a[n], h[n], zoh_coef(a[n], t[n], p.dt, iA[n]) * (p.u * bv[n]));
+            } else {
+#pragma unroll
+                for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(a[n], h[n], p.wv * bv[n]);
+            }
         }
         if constexpr (!CK) {
             float ya = dsk * p.u, yc = 0.0f;
@@ -393,7 +472,12 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 #pragma unroll
         for (int i = 0; i < U; ++i) p[i] = prologue(gx[i], gd[i], gz[i], gy[i]);
 #pragma unroll
-        for (int i = 0; i < U; ++i) update(p[i], tile_rows + i * NB, r0 + i);
+        for (int i = 0; i < U; ++i) {
+            update(p[i], tile_rows + i * NB, r0 + i);
+            // power path: keep each token's chain of decays with its own update (hoisting
+            // the next tokens' chains above it would hold N more values per token)
+            if constexpr (POW) __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (CK) store_ckpt(r0 + U - 1);      // r0 + U is a multiple of kCkptEvery
     };
     T gx0[U], gd0[U], gz0[U], gx1[U], gd1[U], gz1[U];
@@ -1289,6 +1373,22 @@ k_scan_q(const T* __restrict__ x, const float* __restrict__ conv_w, const float*
 // ---------------------------------------------------------------------------
 // launchers (templates; each instantiation unit calls dispatch_n for its dtype and rule)
 
+// k_scan over `grid`: once with the general decays and, from kPowMinN states on, once
+// more with the power chain (each workgroup runs in one of the two, by its vote). The
+// optional start event is recorded before the first launch, the stop event after the last.
+template <typename T, int N, bool CONV, bool GATE, bool ZOH, bool CK, bool REV, bool PART, typename... Args>
+static void launch_k_scan(dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, Args... args) {
+    if constexpr (N >= kPowMinN) {
+        hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, ZOH, CK, REV, PART, false>), grid, dim3(kScanThreads), 0, st,
+                              ev0, nullptr, 0, args...);
+        hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, ZOH, CK, REV, PART, true>), grid, dim3(kScanThreads), 0, st,
+                              nullptr, ev1, 0, args...);
+    } else {
+        hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, ZOH, CK, REV, PART, false>), grid, dim3(kScanThreads), 0, st,
+                              ev0, ev1, 0, args...);
+    }
+}
+
 template <typename T, int N, bool CONV, bool GATE, bool ZOH, bool REV = false, bool PART = false>
 static hipError_t launch_scan_t(const LaunchScan& p) {
     const T* x = static_cast<const T*>(p.x);
@@ -1324,11 +1424,11 @@ static hipError_t launch_scan_t(const LaunchScan& p) {
                               static_cast<const T*>(p.B), p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0,
                               p.ws_c0, sa);
     }
-    hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, ZOH, false, REV, PART>), dim3(gx, p.nchunks, (unsigned)p.batch),
-                          dim3(kScanThreads), 0, st, static_cast<hipEvent_t>(p.ev_main[0]),
-                          static_cast<hipEvent_t>(p.ev_main[1]), 0, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
-                          static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip, z, y, p.ssm_state,
-                          p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, nullptr, p.ypart, sa);
+    launch_k_scan<T, N, CONV, GATE, ZOH, false, REV, PART>(
+        dim3(gx, p.nchunks, (unsigned)p.batch), st, static_cast<hipEvent_t>(p.ev_main[0]),
+        static_cast<hipEvent_t>(p.ev_main[1]), x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
+        static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip, z, y, p.ssm_state, p.conv_state, p.ws_S,
+        p.ws_sdt, p.ws_h0, p.ws_c0, static_cast<float*>(nullptr), p.ypart, sa);
     return hipGetLastError();
 }
 
