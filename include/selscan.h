@@ -143,6 +143,21 @@ ss_status ss_scan_plan(const ss_dims* dims, int32_t pass, ss_plan* plan);
 ss_status ss_conv_scan_fwd(const ss_dims* dims, const ss_args* args,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * allocation-free serving loops, harnesses that forbid hipMalloc): ss_conv_scan_fwd
+ * with its workspace taken from a device array built into the library, of
+ * SS_NOALLOC_MAX_WORKSPACE bytes on every GPU it runs on (held from the first call
+ * on that GPU until the process ends). The call itself allocates nothing and
+ * enqueues the same kernels as ss_conv_scan_fwd, with identical results. Dims whose
+ * ss_workspace_bytes exceeds the maximum are rejected with SS_ERR_WORKSPACE before
+ * anything is enqueued (the long sequence B1 L131072 D2048 N16 needs about 9 MB).
+ * Every call on one GPU uses that GPU's one array: calls that may run at the same
+ * time on one GPU (different streams without ordering between them) race and must
+ * not be issued; calls ordered on one stream are fine. Other arguments and errors as
+ * for ss_conv_scan_fwd. */
+#define SS_NOALLOC_MAX_WORKSPACE (16u << 20)
+ss_status ss_conv_scan_fwd_noalloc(const ss_dims* dims, const ss_args* args, void* stream);
+
 /* One decode step for every stream b: the same computation for a single token
  * (x, delta, z, y: [B,D]; B, C: [B,N]) from the carried state, updating
  * ssm_state [B,D,N] and conv_state [B,D,K-1] in place. dims->seqlen is ignored. */

@@ -84,6 +84,8 @@ def _load() -> ctypes.CDLL:
     lib.ss_scan_plan.restype = ctypes.c_int
     lib.ss_conv_scan_fwd.argtypes = [ctypes.POINTER(ss_dims), ctypes.POINTER(ss_args), _vp, ctypes.c_size_t, _vp]
     lib.ss_conv_scan_fwd.restype = ctypes.c_int
+    lib.ss_conv_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ss_dims), ctypes.POINTER(ss_args), _vp]
+    lib.ss_conv_scan_fwd_noalloc.restype = ctypes.c_int
     lib.ss_conv_scan_bidir_fwd.argtypes = [ctypes.POINTER(ss_dims), ctypes.POINTER(ss_args),
                                            ctypes.POINTER(ss_dir_args), _vp, ctypes.c_size_t, _vp]
     lib.ss_conv_scan_bidir_fwd.restype = ctypes.c_int
@@ -219,6 +221,31 @@ def ss_conv_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: t
         raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
     _check(lib.ss_conv_scan_fwd(ctypes.byref(dims), ctypes.byref(args), workspace.data_ptr() if need else None,
                                 workspace.numel(), _stream_handle(stream)))
+    return y
+
+
+NOALLOC_MAX_WORKSPACE = 16 << 20   # SS_NOALLOC_MAX_WORKSPACE
+
+
+def ss_conv_scan_fwd_noalloc(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                             C: torch.Tensor, *, conv_w: Optional[torch.Tensor] = None,
+                             conv_b: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                             D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                             ssm_state: Optional[torch.Tensor] = None, conv_state: Optional[torch.Tensor] = None,
+                             y: Optional[torch.Tensor] = None, zoh: bool = False, stream=None) -> torch.Tensor:
+    """ss_conv_scan_fwd with the library's built-in device workspace (no workspace
+    argument; the C call allocates nothing). Pass y to keep this wrapper from
+    allocating the output as well."""
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, d_inner]")
+    Bsz, L, Dn = x.shape
+    dims = make_dims(Bsz, L, Dn, A.shape[1] if A.dim() == 2 else 0, _io_dtype(x),
+                     discretization=SS_ZOH if zoh else SS_EULER)
+    if y is None:
+        y = torch.empty_like(x)
+    args = _build_args(x, delta, A, B, C, conv_w, conv_b, delta_bias, D, z, y, ssm_state, conv_state,
+                       (Bsz, L), dims)
+    _check(lib.ss_conv_scan_fwd_noalloc(ctypes.byref(dims), ctypes.byref(args), _stream_handle(stream)))
     return y
 
 
@@ -417,6 +444,7 @@ def ss_block_step(x: torch.Tensor, W: dict, dt_rank: int, ssm_state: torch.Tenso
 
 
 __all__ = ["ss_conv_scan_bidir_fwd", "ss_bidir_workspace_bytes", "ss_dir_args", "DIR_KEYS", "ss_block_fwd", "ss_block_step", "ss_block_workspace_bytes", "block_dims", "ss_block_dims",
-           "ss_block_weights", "BLOCK_WEIGHTS", "ss_conv_scan_fwd", "ss_conv_scan_bwd", "ss_bwd_workspace_bytes", "ss_grads", "ss_step", "ss_workspace_bytes", "ss_scan_plan", "ss_plan",
+           "ss_block_weights", "BLOCK_WEIGHTS", "ss_conv_scan_fwd", "ss_conv_scan_fwd_noalloc", "NOALLOC_MAX_WORKSPACE",
+           "ss_conv_scan_bwd", "ss_bwd_workspace_bytes", "ss_grads", "ss_step", "ss_workspace_bytes", "ss_scan_plan", "ss_plan",
            "SS_PASS_FWD", "SS_PASS_BIDIR", "SS_PASS_BWD", "ss_version", "ss_time_next_call", "make_dims", "ss_dims", "ss_args",
            "SelscanError", "SS_F32", "SS_BF16", "SS_EULER", "SS_ZOH", "LIB_PATH", "lib"]

@@ -25,7 +25,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["ss_workspace_bytes", "ss_conv_scan_fwd", "ss_step", "ss_status_str",
                                            "ss_last_error", "ss_version", "ss_time_next_call",
                                            "ss_bwd_workspace_bytes", "ss_conv_scan_bwd", "ss_conv_scan_bidir_fwd",
-                                           "ss_bidir_workspace_bytes", "ss_scan_plan",
+                                           "ss_bidir_workspace_bytes", "ss_scan_plan", "ss_conv_scan_fwd_noalloc",
                                            "ss_block_workspace_bytes", "ss_block_fwd", "ss_block_step"])
 
 
@@ -208,6 +208,23 @@ def test_scan_plan_rejects_bad_input():
     assert ss.lib.ss_scan_plan(ctypes.byref(bad), 0, ctypes.byref(p)) == 2
     zero = ss.make_dims(1, 0, 8, 16, ss.SS_F32)
     assert ss.lib.ss_scan_plan(ctypes.byref(zero), 0, ctypes.byref(p)) == 1
+
+
+def test_noalloc_rejects_dims_beyond_its_array():
+    """The allocation-free forward takes its workspace from a built-in array of
+    SS_NOALLOC_MAX_WORKSPACE bytes; dims needing more are rejected on the host."""
+    text = open(HEADER).read()
+    assert "#define SS_NOALLOC_MAX_WORKSPACE (16u << 20)" in text
+    assert ss.NOALLOC_MAX_WORKSPACE == 16 << 20
+    big = _dims(batch=1, seqlen=1 << 20, d_inner=4096, d_state=64)
+    assert ss.ss_workspace_bytes(big) > ss.NOALLOC_MAX_WORKSPACE
+    assert ss.lib.ss_conv_scan_fwd_noalloc(ctypes.byref(big), ctypes.byref(_fake_args()), None) == 3
+    assert b"built-in array" in ss.lib.ss_last_error()
+    # bad dims are reported as such, not as a workspace problem
+    assert ss.lib.ss_conv_scan_fwd_noalloc(ctypes.byref(_dims(d_state=12)), ctypes.byref(_fake_args()), None) == 2
+    # the bench workloads fit: long (B1 L131072 D2048) and train (B8 L2048 D5120)
+    assert ss.ss_workspace_bytes(ss.make_dims(1, 131072, 2048, 16, ss.SS_BF16)) <= ss.NOALLOC_MAX_WORKSPACE
+    assert ss.ss_workspace_bytes(ss.make_dims(8, 2048, 5120, 16, ss.SS_BF16)) <= ss.NOALLOC_MAX_WORKSPACE
 
 
 def test_workspace_alignment_and_overlap_checked():

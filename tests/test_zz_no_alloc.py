@@ -1,0 +1,65 @@
+"""The allocation-free forward (ss_conv_scan_fwd_noalloc, workspace in the library's
+built-in device array) against ss_conv_scan_fwd with a caller-supplied workspace:
+bit-identical outputs and states on consecutive calls, the second with a smaller
+input on a different kernel path (the array keeps the first call's contents), and a
+third with initial states, so the copies of the initial states in the array are
+checked too."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import TOL, host, maxrel, oracle_fwd, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ss():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_73_amd as mod
+    return mod
+
+
+def _call(ss, fn, g, h=None, c=None, **kw):
+    return fn(g["x"], g["delta"], g["A"], g["B"], g["C"], conv_w=g["conv_w"], conv_b=g["conv_b"],
+              delta_bias=g["delta_bias"], D=g["D"], z=g["z"], ssm_state=h, conv_state=c, **kw)
+
+
+CASES = [  # (batch, seqlen, d_inner, io, states): one-lane chunked, then lane-quad, then with states
+    (1, 65536, 1024, "bf16", False),
+    (1, 8192, 256, "f32", False),
+    (2, 6000, 512, "f32", True),
+]
+
+
+def test_noalloc_matches_the_workspace_entry_point(ss):
+    for i, (Bsz, L, Dn, io, states) in enumerate(CASES):
+        dims = ss.make_dims(Bsz, L, Dn, 16, 0 if io == "f32" else 1)
+        need = ss.ss_workspace_bytes(dims)
+        assert 0 < need <= ss.NOALLOC_MAX_WORKSPACE, need
+        print(f"case {i}: B{Bsz} L{L} D{Dn} {io} states={states} plan={ss.ss_scan_plan(dims)}", flush=True)
+        spec = W.ScanSpec("noalloc", Bsz, L, Dn, 16, io_dtype=io, delta_mode="bias", seed=900 + i)
+        inp = W.gen_scan_inputs(spec)
+        g = to_dev(inp, io)
+        st = W.gen_states(Bsz, Dn, 16, seed=950 + i) if states else None
+        def fresh():
+            if not states:
+                return None, None
+            return torch.from_numpy(st["ssm_state"]).cuda(), torch.from_numpy(st["conv_state"]).cuda()
+        h1, c1 = fresh()
+        y1 = _call(ss, ss.ss_conv_scan_fwd, g, h1, c1)
+        h2, c2 = fresh()
+        y2 = torch.full_like(y1, float("nan"))
+        _call(ss, ss.ss_conv_scan_fwd_noalloc, g, h2, c2, y=y2)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2), i
+        if states:
+            assert torch.equal(h1, h2) and torch.equal(c1, c2), i
+        dsel = np.array([0, 1, 255, Dn - 1])
+        yr, hr, _ = oracle_fwd(inp, st["ssm_state"] if states else None, st["conv_state"] if states else None,
+                               dsel=dsel)
+        e = maxrel(host(y2)[:, :, dsel], yr)
+        print(f"case {i}: identical to ss_conv_scan_fwd; y maxrel vs oracle {e:.3e}", flush=True)
+        assert e <= TOL[io]
