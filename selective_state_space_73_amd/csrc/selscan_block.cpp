@@ -8,7 +8,11 @@
 // D skip and SiLU gate, the projection back to the model width and the residual.
 // Every step runs in this library's kernels: the projections are its MFMA GEMM
 // (row-major activations times transposed row-major weights, fp32 accumulation), with
-// the residual fused into the output projection's epilogue.
+// the residual fused into the output projection's epilogue. The activations between the
+// steps are fp32 whatever the I/O dtype, and the scan runs on its fp32 kernels: only the
+// block's input, its output and the GEMM weights have the I/O dtype. With bf16 weights
+// the GEMM feeds each fp32 activation to the matrix cores as two bf16 terms (hi + lo), so
+// no step rounds an activation to bf16.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -31,13 +35,15 @@ ss_status failf(ss_status s, const char* fmt, ...) {
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Y[M, Nout] (+)= X[M, K] * W[Nout, K]^T, all row-major; Cres (if not null) is added
-// and may equal Y0. The Nout columns go to Y0 (c0 of them), Y1 (c1) and Y2 (the rest);
-// part is the fp32 split-K workspace (selscan::gemm_plan).
-ss_status gemm(bool bf16, int64_t M, int64_t Nout, int64_t K, const void* W, const void* X, const void* Cres,
-               void* Y0, int64_t c0, void* Y1, int64_t c1, void* Y2, float* part, hipStream_t st) {
+// Y[M, Nout] (+)= X[M, K] * W[Nout, K]^T, all row-major; X fp32, W bf16 (bf16) or fp32,
+// Y and Cres bf16 (y_bf16) or fp32. Cres (if not null) is added and may equal Y0. The Nout
+// columns go to Y0 (c0 of them), Y1 (c1) and Y2 (the rest); part is the fp32 split-K
+// workspace (selscan::gemm_plan).
+ss_status gemm(bool bf16, bool y_bf16, int64_t M, int64_t Nout, int64_t K, const void* W, const void* X,
+               const void* Cres, void* Y0, int64_t c0, void* Y1, int64_t c1, void* Y2, float* part, hipStream_t st) {
     selscan::LaunchGemm g{};
     g.bf16 = bf16;
+    g.y_bf16 = y_bf16;
     g.X = X; g.W = W; g.R = Cres;
     g.Y[0] = Y0; g.Y[1] = Y1; g.Y[2] = Y2;
     g.cols[0] = c0; g.cols[1] = c1; g.cols[2] = Nout - c0 - c1;
@@ -55,6 +61,7 @@ struct BlockLayout {
     size_t xn, xi, z, u, dr, bm, cm, delta, y, scan, part, total;
 };
 
+// the scan inside the block: fp32 activations whatever the block's I/O dtype
 ss_dims scan_dims(const ss_block_dims& d, bool step) {
     ss_dims s{};
     s.batch = d.batch;
@@ -62,14 +69,14 @@ ss_dims scan_dims(const ss_block_dims& d, bool step) {
     s.d_inner = d.d_inner;
     s.d_state = d.d_state;
     s.d_conv = d.d_conv;
-    s.io_dtype = d.io_dtype;
+    s.io_dtype = SS_F32;
     s.discretization = d.discretization;
     return s;
 }
 
 BlockLayout block_layout(const ss_block_dims& d, bool step) {
     BlockLayout l{};
-    const size_t es = d.io_dtype == SS_BF16 ? 2 : 4;
+    const size_t es = 4;                                 // every activation is fp32
     const size_t M = (size_t)d.batch * (size_t)(step ? 1 : d.seqlen);
     const size_t dm = (size_t)d.d_model, di = (size_t)d.d_inner, N = (size_t)d.d_state, R = (size_t)d.dt_rank;
     size_t off = 0;
@@ -126,6 +133,8 @@ ss_status check_block(const ss_block_dims* d, const ss_block_weights* w, const v
         if ((uintptr_t)p & 3u) return failf(SS_ERR_INVALID_ARG, "parameters and states must be 4-byte aligned");
     if (ssm_state && ((uintptr_t)ssm_state & 15u)) return failf(SS_ERR_INVALID_ARG, "ssm_state not 16-byte aligned");
     if (d->d_conv != 4) return failf(SS_ERR_UNSUPPORTED, "d_conv %d: only 4 is built", d->d_conv);
+    if (d->io_dtype != SS_F32 && d->io_dtype != SS_BF16)
+        return failf(SS_ERR_UNSUPPORTED, "io_dtype %d unknown", d->io_dtype);
     // the scan's own checks (sizes, d_state, dtype, discretization) before anything is enqueued
     const ss_dims sd = scan_dims(*d, step);
     return selscan::validate_dims(&sd, step);
@@ -158,7 +167,8 @@ ss_status run_block(const ss_block_dims* d, const ss_block_weights* w, const voi
     if (selscan::launch_block_op(op) != hipSuccess) return failf(SS_ERR_HIP, "RMSNorm launch failed");
 
     // in_proj: the first d_inner rows of W_in give the main branch, the next the gate
-    if ((s = gemm(bf16, M, 2 * di, dm, w->W_in, xn, nullptr, xi, di, z, di, nullptr, part, st)) != SS_OK) return s;
+    if ((s = gemm(bf16, false, M, 2 * di, dm, w->W_in, xn, nullptr, xi, di, z, di, nullptr, part, st)) != SS_OK)
+        return s;
 
     op = selscan::LaunchBlockOps{};
     op.bf16 = bf16;
@@ -178,8 +188,9 @@ ss_status run_block(const ss_block_dims* d, const ss_block_weights* w, const voi
     }
 
     // x_proj: rows [0, R) of W_x give the step-size rank, then N rows for B and N for C
-    if ((s = gemm(bf16, M, R + 2 * N, di, w->W_x, u, nullptr, dr, R, bm, N, cm, part, st)) != SS_OK) return s;
-    if ((s = gemm(bf16, M, di, R, w->W_dt, dr, nullptr, delta, di, nullptr, 0, nullptr, part, st)) != SS_OK)
+    if ((s = gemm(bf16, false, M, R + 2 * N, di, w->W_x, u, nullptr, dr, R, bm, N, cm, part, st)) != SS_OK)
+        return s;
+    if ((s = gemm(bf16, false, M, di, R, w->W_dt, dr, nullptr, delta, di, nullptr, 0, nullptr, part, st)) != SS_OK)
         return s;
 
     ss_args a{};
@@ -188,7 +199,7 @@ ss_status run_block(const ss_block_dims* d, const ss_block_weights* w, const voi
     s = step ? ss_step(&sd, &a, stream) : ss_conv_scan_fwd(&sd, &a, ws + l.scan, ss_workspace_bytes(&sd), stream);
     if (s != SS_OK) return s;
 
-    return gemm(bf16, M, dm, di, w->W_out, y, x, out, dm, nullptr, 0, nullptr, part, st);
+    return gemm(bf16, bf16, M, dm, di, w->W_out, y, x, out, dm, nullptr, 0, nullptr, part, st);
 }
 
 }  // namespace

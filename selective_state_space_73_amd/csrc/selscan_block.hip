@@ -10,7 +10,8 @@ hipError_t launch_block_op(const LaunchBlockOps& p) {
 }
 
 hipError_t launch_gemm(const LaunchGemm& p) {
-    return p.bf16 ? launch_gemm_t<uint16_t>(p) : launch_gemm_t<float>(p);
+    if (!p.bf16) return p.y_bf16 ? hipErrorInvalidValue : launch_gemm_t<float, float>(p);
+    return p.y_bf16 ? launch_gemm_t<uint16_t, uint16_t>(p) : launch_gemm_t<uint16_t, float>(p);
 }
 
 }  // namespace selscan
