@@ -55,22 +55,13 @@ int64_t chunk_len_for(int64_t L, int64_t nc) {
 // Chunk count for the full-sequence scan. One chunk when batch x channel
 // workgroups already fill the GPU; otherwise enough chunks (each at least
 // kMinChunk tokens) to reach about kTargetGroups workgroups.
-// SELSCAN_CHUNKS=<n> overrides the count (tuning only).
 int choose_chunks(const ss_dims& d) {
     const int64_t col_groups = (d.d_inner + selscan::kScanThreads - 1) / selscan::kScanThreads;
     const int64_t base = d.batch * col_groups;
     int64_t nc = 1;
-    static const int64_t env = [] {
-        const char* e = std::getenv("SELSCAN_CHUNKS");
-        return e ? std::atoll(e) : int64_t(0);
-    }();
-    if (env > 0) {
-        nc = env;
-    } else if (base < 256) {
-        nc = (kTargetGroups + base - 1) / base;
-    }
+    if (base < 256) nc = (kTargetGroups + base - 1) / base;
     const int64_t max_by_len = d.seqlen / kMinChunk > 0 ? d.seqlen / kMinChunk : 1;
-    if (env <= 0 && nc > max_by_len) nc = max_by_len;
+    if (nc > max_by_len) nc = max_by_len;
     if (nc > d.seqlen) nc = d.seqlen;
     if (nc > kMaxGridYZ) nc = kMaxGridYZ;
     if (nc < 1) nc = 1;

@@ -1,0 +1,9 @@
+// Kernel instantiations of libselscan: bfloat16 I/O, Euler write term; backward (in a unit of
+// its own so that it compiles in parallel with the forward).
+#include "selscan_bwd.h"
+
+namespace selscan {
+
+hipError_t launch_bwd_bf16_euler(const LaunchBwd& p) { return dispatch_bwd<uint16_t, false>(p); }
+
+}  // namespace selscan

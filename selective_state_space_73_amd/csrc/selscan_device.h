@@ -93,6 +93,7 @@ __device__ __forceinline__ float zoh_coef(float a, float t, float dt, float iA) 
 // each workgroup votes on the identity over its channels and runs in exactly one of
 // the two launches (the other returns at once).
 constexpr int kPowMinN = 8;              // below this the saved exponentials do not pay for a second launch
+constexpr int kPowLanes = 4;             // interleaved multiply chains of the scan's per-token decays
 
 // a[n] = a0^(n+1): squares for even exponents, one more factor of a0 for odd ones
 template <int N>
@@ -416,13 +417,19 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
             for (int n = 0; n < N; ++n) cv[n] = bct[N + n];
         }
         if constexpr (POW) {
-            // power chain, one factor per state (a_n = a_{n-1} a_0), each decay used at
-            // once so that only two of them are live
-            const float a0 = exp2_fast(p.dt * A2[0]);
-            float an = a0;
+            // four interleaved power chains: a_0..a_3 (powers 1..4), then a_{n+4} = a_n a_3,
+            // so the dependent multiplies are 3 + N/4 - 1 deep and each decay is used at
+            // once (about five values live)
+            float c[kPowLanes];
+            c[0] = exp2_fast(p.dt * A2[0]);
+            c[1] = c[0] * c[0];
+            c[2] = c[1] * c[0];
+            c[3] = c[1] * c[1];
+            const float step = c[3];
 #pragma unroll
             for (int n = 0; n < N; ++n) {
-                if (n > 0) an *= a0;
+                const float an = c[n % kPowLanes];
+                if (n + kPowLanes < N) c[n % kPowLanes] = an * step;
                 if constexpr (ZOH)
                     h[n] = __builtin_fmaf(an, h[n], zoh_coef(an, p.dt * A2[n], p.dt, iA[n]) * (p.u * bv[n]));
                 else
@@ -571,25 +578,15 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 
 constexpr int kAggCutLog2 = 40;
 
-// Tuning knobs of the aggregate pass: rows per prefetched group for N <= 16 and the
-// minimum resident waves per SIMD the register allocation must allow (0: the
-// compiler's own). Larger N keeps groups of 4: with 8 the per-state arrays of the
-// zero-order-hold form at N = 64 no longer fit in registers and go to scratch memory.
-#ifndef SELSCAN_AGG_U
-#define SELSCAN_AGG_U 8
-#endif
-#ifndef SELSCAN_AGG_WAVES
-#define SELSCAN_AGG_WAVES 0
-#endif
-#if SELSCAN_AGG_WAVES > 0
-#define SELSCAN_AGG_ATTR __attribute__((amdgpu_waves_per_eu(SELSCAN_AGG_WAVES)))
-#else
-#define SELSCAN_AGG_ATTR
-#endif
+// Rows per prefetched group of the aggregate pass: 8 up to d_state 16, 4 above (with 8,
+// the zero-order-hold form at d_state 64 kept its per-state arrays in scratch memory; that
+// configuration once ended in a memory-aperture fault, though a host transcription of its
+// index arithmetic finds every row, tile and LDS index in bounds, so it stays excluded).
+template <int N> constexpr int agg_group_rows() { return N <= 16 ? 8 : 4; }
 
 // REV: the aggregates of the reversed scan order (see k_scan), no initial states.
 template <typename T, int N, bool CONV, bool ZOH, bool REV = false>
-__global__ void __launch_bounds__(kScanThreads) SELSCAN_AGG_ATTR
+__global__ void __launch_bounds__(kScanThreads)
 k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
       const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
       const T* __restrict__ Bm, const float* __restrict__ ssm_state, const float* __restrict__ conv_state,
@@ -641,7 +638,8 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
             ws_c0[bd * 3 + 2] = conv_state[bd * 3 + 2];
         }
     }
-    constexpr int U = N <= 16 ? SELSCAN_AGG_U : 4;
+    constexpr int U = agg_group_rows<N>();
+    static_assert(U == 4 || N <= 16, "8-row groups only up to d_state 16");
     constexpr int R = kScanTile;
     static_assert(R % (2 * U) == 0, "tiles hold whole pairs of groups");
     constexpr int NB = N + 1;                     // B values and max_n |B| per token

@@ -8,14 +8,8 @@
 namespace selscan {
 
 constexpr int kScanThreads = 256;   // channels per workgroup of the scan kernels (4 waves)
-#ifndef SELSCAN_STEP_THREADS
-#define SELSCAN_STEP_THREADS 256
-#endif
-#ifndef SELSCAN_STEP_STREAMS
-#define SELSCAN_STEP_STREAMS 4
-#endif
-constexpr int kStepThreads = SELSCAN_STEP_THREADS;   // lanes per workgroup of the decode-step kernel (4 per channel)
-constexpr int kStepStreams = SELSCAN_STEP_STREAMS;   // streams each lane quad of the decode-step kernel handles
+constexpr int kStepThreads = 256;   // lanes per workgroup of the decode-step kernel (4 per channel)
+constexpr int kStepStreams = 4;     // streams each lane quad of the decode-step kernel handles
 constexpr int kScanTile = 64;       // tokens of B/C staged in LDS at a time
 // Lane-quad forward path (k_agg_q / k_scan_q), for d_state <= 16: taken when one lane
 // per channel, even with 64-token chunks, gives fewer than kQuadMaxTileWaves waves that
@@ -72,6 +66,7 @@ struct LaunchBwd {
 };
 
 // Elementwise kernels of the block (selscan_block.h): one launch description for all.
+// The norm reads the block input in the I/O dtype (bf16 or not); everything else is fp32.
 struct LaunchBlockOps {
     enum Op { kRmsNorm, kConvSilu, kConvHistory, kConvStep } op;
     bool bf16;
@@ -84,12 +79,15 @@ struct LaunchBlockOps {
 };
 hipError_t launch_block_op(const LaunchBlockOps& p);
 
-// Y[M, N] = X[M, K] W[N, K]^T (+ R[M, N]), row-major, in the I/O dtype, fp32 accumulation
-// (selscan_gemm.h). The N output columns may go to up to three separate row-major
-// matrices: columns [0, cols[0]) to Y[0], the next cols[1] to Y[1], the rest to Y[2]
-// (cols[1] = cols[2] = 0 for a single output). R (one output only) may equal Y[0].
+// Y[M, N] = X[M, K] W[N, K]^T (+ R[M, N]), row-major, fp32 accumulation (selscan_gemm.h).
+// X is fp32; W is bf16 (bf16 = true: X enters the matrix cores as two bf16 terms) or fp32;
+// Y and R are bf16 (y_bf16, only with bf16 weights) or fp32. The N output columns may go
+// to up to three separate row-major matrices: columns [0, cols[0]) to Y[0], the next
+// cols[1] to Y[1], the rest to Y[2] (cols[1] = cols[2] = 0 for a single output). R (one
+// output only) may equal Y[0].
 struct LaunchGemm {
     bool bf16;
+    bool y_bf16;
     const void* X; const void* W; const void* R;
     void* Y[3]; int64_t cols[3];
     int64_t M, N, K;
