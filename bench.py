@@ -1,42 +1,43 @@
 #!/usr/bin/env python3
 """Benchmark of the selective-scan (S6) forward path and decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|train|block]
-                    [--no-decode] [--no-cpu] [--zoh-steps K] [--bidir-steps K] [--bwd-steps K]
-                    [--block-scan-steps K] [--block-steps K]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+                    [--train-steps K] [--zoh-steps K] [--bidir-steps K] [--bwd-steps K]
+                    [--block-scan-steps K] [--block-steps K] [--no-probes]
 
 A step is one ss_conv_scan_fwd call over the whole workload (conv1d + SiLU,
 softplus step, discretisation, scan, C.h + D.u readout, SiLU(z) gate), with
-inputs resident in HBM. The default workload is the long sequence: batch 1,
+inputs resident in HBM. The headline workload is the long sequence: batch 1,
 L = 131072, d_inner 2048, d_state 16, bf16 x/delta/z/B/C, fp32 state and
 parameters. Prints one JSON line:
 
-* value: Gelem/s = B*L*D*N / step time, whole step (all kernels of the call).
-* roofline: the main scan kernel, timed live with HIP events recorded around
-  that kernel on its own stream; it is bound by VALU issue, so achieved is its
-  algorithmic fp32 VALU instructions per launch / its average duration against
-  the chip's VALU issue rate (see instr_per_row below). The same kernel's HBM
-  view (algorithmic bytes / duration vs 8 TB/s) is given as hbm_view.
-* zoh: the same workload and inputs with the zero-order-hold write term, its
-  step rate and main-kernel roofline on the same model.
-* bidir: the bidirectional scan (ss_conv_scan_bidir_fwd) on the same inputs, both
-  directions sharing the parameters: whole-call time and the reversed main pass's
-  roofline on the same model.
-* bwd: the backward (ss_conv_scan_bwd) on the same inputs with a seeded output
-  gradient: whole-call time and the backward-sweep kernel's roofline; the same for
-  the zero-order hold (whole-call and sweep-kernel time).
-* block_scan: the scan alone on the block-shaped workload (batch 2, L = 1024,
-  d_inner 1024, d_state 16, fp32, conv on), which takes the lane-quad kernels.
-* block: the Mamba block
-  (ss_block_fwd, the library's MFMA projections around the scan) at d_model 512
-  (B2 L1024), random weights, with its decode step (ss_block_step) for 8 streams,
-  eager and replayed from a HIP graph.
-* decode: 64 streams x 32 layers x 256 token steps (d_inner 8192, d_state 16),
-  one ss_step per layer and token, timed end to end eagerly and replayed from
-  HIP graphs (one graph per token step over the 32 layers); its roofline is
-  the step kernel's algorithmic bytes / average duration against 8 TB/s.
-* cpu_baseline: the fp64 oracle on a channel sample of the same workload, on
-  the host cores.
+* value: Gelem/s = B*L*D*N / step time, whole step (all kernels of the call), on the
+  general decay path: A[d, n] = -(n+1) with every n >= 1 scaled by (1 + 2^-20), so the
+  kernels' check for A[d, n] = (n+1) A[d, 0] fails and every decay is its own
+  exponential (same work and bytes; the results move by rounding only).
+* roofline: the main scan kernel on that path, timed live with HIP events recorded at
+  the kernel's own start and end on its stream: its algorithmic HBM bytes per launch
+  / its average duration against 8 TB/s (bound "hbm"), with the rocprofv3-measured
+  HBM bytes per launch as traffic when the committed counters match the sources.
+* valu_view: the same kernel against the VALU issue rate it actually hits: fp32
+  lane-instructions per row (ISA counts from the committed SQ counters when they match
+  the sources, else the algorithmic model), transcendentals priced at the issue cost
+  the calibration probe measured in this run.
+* power_path: the same workload with A[d, n] = -(n+1) exactly, which the kernels run as
+  one exponential and a multiply chain per token (their runtime-checked fast path).
+* train: the training-shaped workload (batch 8, L 2048, d_inner 5120) on both paths.
+* zoh, bidir, bwd: the zero-order-hold write term, the bidirectional scan and the
+  backward on the long workload's inputs (power path, the workload's own A).
+* calibration: measured ceilings of this GPU: a plain device copy, a decode-step-sized
+  nontemporal read-modify-write (libselscan_probes ssp_rmw) and the VALU issue rate of
+  fmas and exponentials (ssp_issue).
+* decode: 64 streams x 32 layers x 256 token steps (d_inner 8192, d_state 16), one
+  ss_step per layer and token, eager and replayed from HIP graphs; its roofline is the
+  step kernel's algorithmic bytes / average duration against 8 TB/s.
+* block_scan, block: the scan on the block-shaped workload (lane-quad kernels) and the
+  Mamba block at d_model 512 with its decode step.
+* cpu_baseline: the fp64 oracle on host cores: a channel sample of the long workload
+  (headline), and per workload (tiny and block in full, train and long sampled).
 """
 from __future__ import annotations
 
@@ -55,10 +56,12 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E
-# fp32 VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3e12 lane-instructions/s
-# (a wave64 instruction holds a SIMD16 for 4 cycles; no packed fp32). Transcendentals
-# issue in one slot too; measured interleaved with fmas they cost 1.3-1.9 slots.
-VALU_INSTR_PER_S = 256 * 4 * 16 * 2.4e9
+# fp32 VALU issue rate: 256 CUs x 4 SIMDs x 32 lanes per clock x 2.4 GHz = 78.6e12
+# lane-instructions/s, the spec's 157.3 TFLOP/s fp32 vector counted as fmas. On gfx950 a
+# wave64 fp32 fma (not packed) takes two cycles: the calibration probe sustains 61 T/s of
+# plain v_fmamk_f32, above the 39.3 T a four-cycle issue would allow. Transcendentals run
+# at a quarter of that rate; their cost in fma issue slots is measured by the probe.
+VALU_INSTR_PER_S = 256 * 4 * 32 * 2.4e9
 BLOCK_DECODE_STREAMS = 8                    # streams of the block's decode leg
 METRIC = "selective-scan fwd Gelem(B·L·D·N)/s + achieved HBM GB/s vs peak; decode tokens/s"
 
@@ -83,6 +86,26 @@ def measured_traffic(key: str, digest: str):
     if t.get("kernel_source_sha256") != digest:
         return None
     return t.get("traffic_bytes_per_dispatch", {}).get(key)
+
+
+def measured_counters(key: str, digest: str):
+    """Per-dispatch SQ counters of a kernel (profiles/counters.json, rocprofv3 --pmc
+    passes), or None when the kernel sources have changed since."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "counters.json")) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    if t.get("kernel_source_sha256") != digest:
+        return None
+    return t.get("per_dispatch", {}).get(key)
+
+
+def instr_per_row_power(N: int) -> int:
+    """Algorithmic fp32 VALU instructions per row on the power path: the 24 per-row ones,
+    Delta*A[0] and its exponential, then per state index the chain multiply (none for
+    n = 0), Delta*u*B, the state fma and the readout fma: 24 + 2 + 4N - 1."""
+    return 25 + 4 * N
 
 
 def instr_per_row(N: int, zoh: bool = False) -> int:
@@ -140,6 +163,87 @@ class Hip:
         self.lib.hipEventDestroy(ctypes.c_void_p(e))
 
 
+class Probes:
+    """The calibration kernels (libselscan_probes, include/selscan_probes.h) via ctypes."""
+
+    def __init__(self):
+        path = os.path.join(ROOT, "selective_state_space_73_amd", "libselscan_probes.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built: run __graft_entry__.build()")
+        self.lib = ctypes.CDLL(path)
+        self.lib.ssp_rmw.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        self.lib.ssp_rmw.restype = ctypes.c_int
+        self.lib.ssp_issue.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        self.lib.ssp_issue.restype = ctypes.c_int
+
+
+def rmw_probe(torch, probes, spec: W.DecodeSpec, rounds: int = 4):
+    """Read-modify-write rate of one buffer per layer of the decode workload's state and
+    conv history (S*D*(N+3) floats each, 32 distinct buffers, so nothing stays in the
+    256 MB MALL), launched back to back like the decode's 32 layers."""
+    n = spec.streams * spec.d_inner * (spec.d_state + 3)
+    bufs = [torch.zeros(n, dtype=torch.float32, device="cuda") for _ in range(spec.layers)]
+    sh = torch.cuda.current_stream().cuda_stream or None
+    for b in bufs:
+        if probes.lib.ssp_rmw(b.data_ptr(), n, sh) != 0:
+            raise RuntimeError("ssp_rmw launch failed")
+    torch.cuda.synchronize()
+    ev_start = torch.cuda.Event(enable_timing=True)
+    ev_stop = torch.cuda.Event(enable_timing=True)
+    ev_start.record()
+    for _ in range(rounds):
+        for b in bufs:
+            probes.lib.ssp_rmw(b.data_ptr(), n, sh)
+    ev_stop.record()
+    torch.cuda.synchronize()
+    us = ev_start.elapsed_time(ev_stop) * 1e3 / (rounds * len(bufs))
+    del bufs
+    torch.cuda.empty_cache()
+    nbytes = 8 * n
+    return {"bytes_per_launch": nbytes, "us_per_launch": round(us, 3), "gbps": round(nbytes / (us / 1e6) / 1e9, 1),
+            "what": f"in-place fp32 read-modify-write of {n} floats (the decode's state and conv history of one "
+                    f"layer), 16-byte nontemporal accesses, {spec.layers} buffers launched back to back"}
+
+
+def issue_probe(torch, probes):
+    """VALU issue rates (fp32 lane-instructions per second): fmas alone, v_exp_f32 alone,
+    and an exponential interleaved with k fmas, from which its cost in fma issue slots
+    follows (slots = t_mix / t_slot - k, t_slot the time of one fma from the fma-only run)."""
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    sh = torch.cuda.current_stream().cuda_stream or None
+    lanes = 2048 * 256
+    chains = 8
+
+    def timed(mode, k, iters):
+        if probes.lib.ssp_issue(out.data_ptr(), iters, mode, k, sh) != 0:
+            raise RuntimeError("ssp_issue launch failed")
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        probes.lib.ssp_issue(out.data_ptr(), iters, mode, k, sh)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+
+    iters = 4096
+    t_fma = timed(0, 8, iters)
+    fma_instr = lanes * chains * 8 * iters
+    t_slot = t_fma / (chains * 8 * iters)                    # seconds per fma per lane-chain
+    t_exp = timed(1, 1, iters * 4)
+    exp_instr = lanes * chains * iters * 4
+    res = {"fma_T_per_s": round(fma_instr / t_fma / 1e12, 2), "exp_alone_T_per_s": round(exp_instr / t_exp / 1e12, 2),
+           "exp_slots_interleaved": {}}
+    for k in (1, 3, 7):
+        t_mix = timed(2, k, iters)
+        res["exp_slots_interleaved"][f"with_{k}_fma"] = round(t_mix / (chains * iters) / t_slot - k, 3)
+    res["fma_frac_of_peak"] = round(res["fma_T_per_s"] * 1e12 / VALU_INSTR_PER_S, 4)
+    res["what"] = ("8 independent chains per lane, 8 waves per SIMD (2048 x 256 lanes); 1 T = 1e12 fp32 "
+                   "lane-instructions; the chip's issue peak is 78.6 T (256 CU x 4 SIMD x 32 lanes x 2.4 GHz); "
+                   "exp slots with k fmas: (time of one exp and k fmas) / (time of one fma) - k")
+    del out
+    return res
+
+
 def scan_bytes(spec: W.ScanSpec) -> int:
     """Algorithmic HBM bytes of one forward call: x, delta, z read and y written at the
     I/O size, B and C read, parameters read once, fp32 state and conv history read and
@@ -159,14 +263,22 @@ def decode_bytes(spec: W.DecodeSpec) -> int:
     return S * D * (2 * (N + 3) * 4 + 4 * 2) + S * N * 2 * 2 + D * (N + 4 + 3) * 4
 
 
-def prepare_scan(torch, spec, want_sample):
-    """Seeded inputs of the workload, resident in HBM; plus a host channel sample for
-    the CPU baseline."""
+def break_power_identity(A):
+    """A[d, n] = -(n+1) with every n >= 1 scaled by (1 + 2^-20): the kernels' check for
+    A[d, n] = (n+1) A[d, 0] fails, so every decay is its own exponential."""
+    A = A.clone()
+    A[:, 1:] *= 1.0 + 2.0 ** -20
+    return A
+
+
+def prepare_scan(torch, spec, keep=None):
+    """Seeded inputs of the workload, resident in HBM; plus host inputs for the CPU
+    baseline: keep="sample", every 2nd channel; keep="full", all of them."""
     t0 = time.time()
     inp = W.gen_scan_inputs(spec)
     log(f"[bench] generated {spec.name} inputs in {time.time() - t0:.1f}s")
     sample = None
-    if want_sample:
+    if keep == "sample":
         # channel sample kept on the host for the CPU baseline (every 2nd channel;
         # the baseline itself times a prefix of it sized to about 12 s)
         dsel = np.arange(0, spec.d_inner, 2)
@@ -175,6 +287,8 @@ def prepare_scan(torch, spec, want_sample):
                       z=np.ascontiguousarray(inp["z"][:, :, dsel]), B=inp["B"], C=inp["C"],
                       A=inp["A"][dsel], conv_w=inp["conv_w"][dsel], conv_b=inp["conv_b"][dsel],
                       delta_bias=inp["delta_bias"][dsel], D=inp["D"][dsel])
+    elif keep == "full":
+        sample = dict(inp, dsel=np.arange(spec.d_inner))
     tdt = torch.bfloat16 if spec.io_dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
     g = {}
@@ -508,15 +622,75 @@ def cpu_baseline(sample, spec, target_s=12.0):
                       f"{dt:.2f} s ({sum(times):.1f} s in total)"}
 
 
+def cpu_oracle_full(inp, spec, max_runs=5, target_s=3.0):
+    """The fp64 oracle over every channel and token of a (small) workload on all host
+    cores: median of up to max_runs runs, stopping after about target_s seconds."""
+    import oracle
+    orc = oracle.default()
+    nthreads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    times = []
+    while len(times) < max_runs and sum(times) < target_s:
+        t0 = time.perf_counter()
+        orc.conv_scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], conv_w=inp["conv_w"],
+                          conv_b=inp["conv_b"], delta_bias=inp["delta_bias"], D=inp["D"], z=inp["z"],
+                          nthreads=nthreads)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    elems = spec.batch * spec.seqlen * spec.d_inner * spec.d_state
+    return {"value": round(elems / dt / 1e9, 4), "unit": "Gelem/s", "cores": nthreads,
+            "sample": f"all {spec.batch}x{spec.seqlen} tokens x {spec.d_inner} channels, median of {len(times)}"}
+
+
+def hbm_roofline(kernel, nbytes, kernel_ms, traffic, extra=None):
+    a = nbytes / (kernel_ms / 1e3) / 1e9
+    r = {"kernel": kernel, "bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+         "frac": round(a / PEAK_HBM_GBS, 4), "traffic": traffic, "bytes_per_launch": nbytes,
+         "kernel_ms": round(kernel_ms, 4)}
+    r.update(extra or {})
+    return r
+
+
+def valu_view(kernel, rows, kernel_ms, counters, model_instr, model_trans, issue):
+    """Issue-slot use of a VALU-bound kernel: fp32 lane-instructions per row from the ISA
+    (SQ_INSTS_VALU, SQ_INSTS_VALU_TRANS_F32 per dispatch, 64 lanes each) when the
+    committed counters match the sources, else the algorithmic model; a transcendental
+    costs the fma issue slots the calibration probe measured in this run with the fma
+    count per exponential nearest the kernel's own (1, 3 or 7; 4 slots without the probe).
+    With counters, the measured VALU busy fraction (SQ_ACTIVE_INST_VALU quad-cycles over
+    the SIMDs' cycles) is given as well."""
+    if counters and counters.get("SQ_INSTS_VALU"):
+        instr = counters["SQ_INSTS_VALU"] * 64 / rows
+        trans = counters.get("SQ_INSTS_VALU_TRANS_F32", 0) * 64 / rows
+        source = "isa (rocprofv3 SQ counters)"
+    else:
+        instr, trans, source = float(model_instr), float(model_trans), "algorithmic model"
+    exp_slots = 4.0
+    if issue:
+        ratio = (instr - trans) / max(trans, 1e-9)
+        k = min((1, 3, 7), key=lambda v: abs(v - ratio))
+        exp_slots = issue["exp_slots_interleaved"][f"with_{k}_fma"]
+    slots = instr - trans + trans * exp_slots
+    t = kernel_ms / 1e3
+    v = {"kernel": kernel, "instr_per_row": round(instr, 2), "trans_per_row": round(trans, 2),
+         "exp_cost_slots": round(exp_slots, 3), "slots_per_row": round(slots, 2), "counted": source,
+         "achieved": round(rows * slots / t / 1e12, 3), "peak": round(VALU_INSTR_PER_S / 1e12, 3),
+         "unit": "T fp32 issue slots/s", "frac": round(rows * slots / t / VALU_INSTR_PER_S, 4)}
+    if counters and counters.get("valu_busy_frac") is not None:
+        v["valu_busy_frac_counters"] = counters["valu_busy_frac"]
+    return v
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="long", choices=["long", "train", "block", "tiny"])
     ap.add_argument("--decode-steps", type=int, default=W.DECODE.steps)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-probes", action="store_true", help="skip the calibration probes")
+    ap.add_argument("--train-steps", type=int, default=20,
+                    help="timed calls of the training-shaped workload, each decay path (0: skip)")
     ap.add_argument("--zoh-steps", type=int, default=10,
                     help="timed calls of the zero-order-hold variant on the same inputs (0: skip)")
     ap.add_argument("--bidir-steps", type=int, default=5,
@@ -550,56 +724,85 @@ def main():
         del src, dst
     from selective_state_space_73_amd import build as ss_build
     digest = ss_build.kernel_digest()
-    spec = W.WORKLOADS[a.workload]
+    spec = W.WORKLOADS["long"]
     log(f"[bench] workload {spec}")
-    progress("device-to-device copy rate")
+
+    # calibration: copy rate, decode-sized read-modify-write, VALU issue rates
+    progress("calibration: device-to-device copy rate")
     copy_gbps = copy_bandwidth(torch)
-    g, sample = prepare_scan(torch, spec, not a.no_cpu)
-    progress(f"scan {spec.name}: {a.steps} steps")
-    r = run_scan(ss, torch, hip, spec, g, a.steps, a.warmup)
+    calib = {"copy_gbps": round(copy_gbps, 1)}
+    issue = None
+    if not a.no_probes:
+        probes = Probes()
+        progress("calibration: read-modify-write probe")
+        calib["rmw"] = rmw_probe(torch, probes, W.DECODE)
+        progress("calibration: VALU issue probe")
+        calib["issue"] = issue = issue_probe(torch, probes)
+
+    g, sample = prepare_scan(torch, spec, None if a.no_cpu else "sample")
     Bz, L, D, N = spec.batch, spec.seqlen, spec.d_inner, spec.d_state
     rows = Bz * L * D
+    nbytes = scan_bytes(spec)
+    A_pow = g["A"]
+    A_gen = break_power_identity(A_pow)
+
+    # warm-up: the headline call for about a second, so clocks and caches have settled
+    # before the first timed leg (the legs after it are each preceded by their own warm-up)
+    g["A"] = A_gen
+    progress("warm-up")
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < 1.0:
+        run_scan(ss, torch, hip, spec, g, 1, 0)
+    # headline: the general decay path
+    progress(f"scan {spec.name}, general decays: {a.steps} steps")
+    r = run_scan(ss, torch, hip, spec, g, a.steps, a.warmup)
     ms_step = r["wall_s"] / a.steps * 1e3
     gelem = rows * N / (ms_step / 1e3) / 1e9
-    nbytes = scan_bytes(spec)
-    main_s = r["main_ms"] / 1e3
-    instrs = rows * instr_per_row(N)
     out = {
         "metric": METRIC, "value": round(gelem, 2), "unit": "Gelem/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{spec.name}: batch {Bz}, L={L}, d_inner {D}, d_state {N}, d_conv 4, "
-                               f"{spec.io_dtype} x/delta/z/B/C/y, fp32 state and parameters",
+                               f"{spec.io_dtype} x/delta/z/B/C/y, fp32 state and parameters; general decay path "
+                               f"(A = -(n+1), n >= 1 scaled by 1 + 2^-20)",
                    "batch": Bz, "seq_len": L, "d_inner": D, "d_state": N, "io_dtype": spec.io_dtype},
         "hbm_gbps_step": round(nbytes / (ms_step / 1e3) / 1e9, 1),
-        "roofline": {"kernel": "k_scan main pass", "bound": "alu",
-                     "achieved": round(instrs / main_s / 1e12, 3), "peak": round(VALU_INSTR_PER_S / 1e12, 3),
-                     "unit": "T fp32 VALU instr/s", "frac": round(instrs / main_s / VALU_INSTR_PER_S, 4),
-                     "traffic": measured_traffic("k_scan_main", digest) if a.workload == "long" else None,
-                     "kernel_ms": round(r["main_ms"], 4), "kernel_ms_min": round(r["main_ms_min"], 4),
-                     "valu_instr_per_row": instr_per_row(N),
-                     "of_which_transcendental": trans_per_row(N), "rows_per_launch": rows},
-        "hbm_view": {"achieved": round(nbytes / main_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac_of_measured_copy": round(nbytes / main_s / 1e9 / copy_gbps, 4),
-                     "frac": round(nbytes / main_s / 1e9 / PEAK_HBM_GBS, 4), "bytes_per_launch": nbytes},
+        "roofline": hbm_roofline("k_scan main pass, general decays", nbytes, r["main_ms"],
+                                 measured_traffic("k_scan_main_general", digest),
+                                 {"kernel_ms_min": round(r["main_ms_min"], 4),
+                                  "frac_of_measured_copy": round(nbytes / (r["main_ms"] / 1e3) / 1e9 / copy_gbps, 4)}),
+        "valu_view": valu_view("k_scan main pass, general decays", rows, r["main_ms"],
+                               measured_counters("k_scan_main_general", digest), instr_per_row(N), trans_per_row(N),
+                               issue),
         "aggregate_kernel_ms": round(r["agg_ms"], 4),
-        "measured_copy_gbps": round(copy_gbps, 1),
+        "aggregate_roofline": hbm_roofline("k_agg chunk aggregates (x and delta of every chunk but the last)",
+                                           rows * 2 * (2 if spec.io_dtype == "bf16" else 4) * 63 // 64,
+                                           max(r["agg_ms"], 1e-9), measured_traffic("k_agg", digest)),
+    }
+    # the same inputs with A exactly -(n+1): the power path
+    g["A"] = A_pow
+    progress(f"scan {spec.name}, power path: {a.steps} steps")
+    rp = run_scan(ss, torch, hip, spec, g, a.steps, a.warmup)
+    pms = rp["wall_s"] / a.steps * 1e3
+    out["power_path"] = {
+        "workload": "same inputs with A[d, n] = -(n+1) exactly: decays exp(Delta A[d, 0])^(n+1)",
+        "value": round(rows * N / (pms / 1e3) / 1e9, 2), "unit": "Gelem/s", "ms_per_step": round(pms, 4),
+        "aggregate_kernel_ms": round(rp["agg_ms"], 4),
+        "roofline": hbm_roofline("k_scan main pass, power path", nbytes, rp["main_ms"],
+                                 measured_traffic("k_scan_main_power", digest)),
+        "valu_view": valu_view("k_scan main pass, power path", rows, rp["main_ms"],
+                               measured_counters("k_scan_main_power", digest), instr_per_row_power(N), 7,
+                               issue),
     }
     if a.zoh_steps > 0:
         progress(f"scan {spec.name} zero-order hold: {a.zoh_steps} steps")
         rz = run_scan(ss, torch, hip, spec, g, a.zoh_steps, a.warmup, zoh=True)
         zms = rz["wall_s"] / a.zoh_steps * 1e3
-        zinstr = rows * instr_per_row(N, zoh=True)
         out["zoh"] = {
-            "workload": "same inputs, zero-order-hold write term (exp(Delta A) - 1) / A",
+            "workload": "same inputs (power path), zero-order-hold write term (exp(Delta A) - 1) / A",
             "value": round(rows * N / (zms / 1e3) / 1e9, 2), "unit": "Gelem/s", "ms_per_step": round(zms, 4),
-            "roofline": {"kernel": "k_scan main pass (ZOH)", "bound": "alu",
-                         "achieved": round(zinstr / (rz["main_ms"] / 1e3) / 1e12, 3),
-                         "peak": round(VALU_INSTR_PER_S / 1e12, 3), "unit": "T fp32 VALU instr/s",
-                         "frac": round(zinstr / (rz["main_ms"] / 1e3) / VALU_INSTR_PER_S, 4),
-                         "traffic": measured_traffic("k_scan_main_zoh", digest) if a.workload == "long" else None,
-                         "kernel_ms": round(rz["main_ms"], 4), "valu_instr_per_row": instr_per_row(N, zoh=True),
-                         "of_which_transcendental": trans_per_row(N), "rows_per_launch": rows},
+            "roofline": hbm_roofline("k_scan main pass (ZOH)", nbytes, rz["main_ms"],
+                                     measured_traffic("k_scan_main_zoh", digest)),
             "aggregate_kernel_ms": round(rz["agg_ms"], 4),
         }
     if a.bidir_steps > 0:
@@ -607,56 +810,25 @@ def main():
         rbd = run_scan(ss, torch, hip, spec, g, a.bidir_steps, a.warmup, bidir=True)
         bdms = rbd["wall_s"] / a.bidir_steps * 1e3
         out["bidir"] = {
-            "workload": "same inputs, forward scan plus the reversed scan sharing the parameters, outputs summed",
+            "workload": "same inputs (power path), forward scan plus the reversed scan sharing the parameters, "
+                        "outputs summed",
             "value": round(rows * N / (bdms / 1e3) / 1e9, 2), "unit": "Gelem/s", "ms_per_call": round(bdms, 4),
-            "ratio_to_forward": round(bdms / ms_step, 3),
-            "roofline": {"kernel": "k_scan main pass, reversed order", "bound": "alu",
-                         "achieved": round(instrs / (rbd["main_ms"] / 1e3) / 1e12, 3),
-                         "peak": round(VALU_INSTR_PER_S / 1e12, 3), "unit": "T fp32 VALU instr/s",
-                         "frac": round(instrs / (rbd["main_ms"] / 1e3) / VALU_INSTR_PER_S, 4),
-                         "traffic": measured_traffic("k_scan_main_reversed", digest) if a.workload == "long" else None,
-                         "kernel_ms": round(rbd["main_ms"], 4), "valu_instr_per_row": instr_per_row(N),
-                         "rows_per_launch": rows},
+            "ratio_to_forward": round(bdms / pms, 3),
+            "roofline": hbm_roofline("k_scan main pass, reversed order", nbytes + rows * 4, rbd["main_ms"],
+                                     measured_traffic("k_scan_main_reversed", digest)),
             "aggregate_kernel_ms": round(rbd["agg_ms"], 4),
-        }
-    if not a.no_decode:
-        dspec = W.DECODE
-        progress(f"decode: {dspec.streams} streams x {dspec.layers} layers x {a.decode_steps} steps")
-        dr = run_decode(ss, torch, hip, dspec, a.decode_steps)
-        tokens = dspec.streams * a.decode_steps
-        dbytes = decode_bytes(dspec)
-        ks = dr["kernel_ms"] / 1e3
-        out["decode"] = {
-            "workload": f"{dspec.streams} streams x {dspec.layers} layers x {a.decode_steps} token steps, "
-                        f"d_inner {dspec.d_inner}, d_state {dspec.d_state}, bf16 token inputs, fp32 states",
-            "tokens_per_s_graph": round(tokens / dr["graph_s"], 1),
-            "tokens_per_s_eager": round(tokens / dr["eager_s"], 1),
-            "ms_per_token_step_graph": round(dr["graph_s"] / a.decode_steps * 1e3, 4),
-            "roofline": {"kernel": "k_step", "bound": "hbm", "achieved": round(dbytes / ks / 1e9, 1),
-                         "frac_of_measured_copy": round(dbytes / ks / 1e9 / copy_gbps, 4),
-                         "kernel_us_min": round(dr["kernel_ms_min"] * 1e3, 3),
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dbytes / ks / 1e9 / PEAK_HBM_GBS, 4),
-                         "traffic": measured_traffic("k_step", digest), "kernel_us": round(dr["kernel_ms"] * 1e3, 3),
-                         "bytes_per_launch": dbytes},
-            "hbm_gbps_end_to_end_graph": round(dbytes * dspec.layers * a.decode_steps / dr["graph_s"] / 1e9, 1),
         }
     if a.bwd_steps > 0:
         progress(f"backward {spec.name}: {a.bwd_steps} calls")
         rb = run_bwd(ss, torch, hip, spec, g, a.bwd_steps, 1)
         bms = rb["wall_s"] / a.bwd_steps * 1e3
-        binstr = rows * bwd_instr_per_row(N)
         out["bwd"] = {
-            "workload": "same inputs, gradients of every input for a seeded output gradient",
+            "workload": "same inputs (power path), gradients of every input for a seeded output gradient",
             "value": round(rows * N / (bms / 1e3) / 1e9, 2), "unit": "Gelem/s", "ms_per_call": round(bms, 4),
-            "ratio_to_forward": round(bms / ms_step, 3),
-            "roofline": {"kernel": "k_bwd backward sweep", "bound": "alu",
-                         "achieved": round(binstr / (rb["kernel_ms"] / 1e3) / 1e12, 3),
-                         "peak": round(VALU_INSTR_PER_S / 1e12, 3), "unit": "T fp32 VALU instr/s",
-                         "frac": round(binstr / (rb["kernel_ms"] / 1e3) / VALU_INSTR_PER_S, 4),
-                         "traffic": measured_traffic("k_bwd", digest) if a.workload == "long" else None,
-                         "kernel_ms": round(rb["kernel_ms"], 4), "valu_instr_per_row": bwd_instr_per_row(N),
-                         "rows_per_launch": rows},
-            "workspace_bytes": rb["workspace_bytes"],
+            "ratio_to_forward": round(bms / pms, 3),
+            "valu_view": valu_view("k_bwd backward sweep", rows, rb["kernel_ms"], measured_counters("k_bwd", digest),
+                                   bwd_instr_per_row(N), 4 + N, issue),
+            "kernel_ms": round(rb["kernel_ms"], 4), "workspace_bytes": rb["workspace_bytes"],
         }
         progress(f"backward {spec.name} zero-order hold: {a.bwd_steps} calls")
         rbz = run_bwd(ss, torch, hip, spec, g, a.bwd_steps, 1, zoh=True)
@@ -665,22 +837,93 @@ def main():
                              "unit": "Gelem/s", "sweep_kernel_ms": round(rbz["kernel_ms"], 4),
                              "ratio_to_zoh_forward": round(bzms / out["zoh"]["ms_per_step"], 3) if "zoh" in out else None}
     del g
-    if a.block_scan_steps > 0 and a.workload != "block":
+    torch.cuda.empty_cache()
+    cpu_per = {}
+    if a.train_steps > 0:
+        tsp = W.WORKLOADS["train"]
+        progress(f"scan {tsp.name}: {a.train_steps} steps on each decay path")
+        gt, tin = prepare_scan(torch, tsp, None if a.no_cpu else "full")
+        trows = tsp.batch * tsp.seqlen * tsp.d_inner
+        tbytes = scan_bytes(tsp)
+        tA = gt["A"]
+        gt["A"] = break_power_identity(tA)
+        rt = run_scan(ss, torch, hip, tsp, gt, a.train_steps, a.warmup)
+        gt["A"] = tA
+        rtp = run_scan(ss, torch, hip, tsp, gt, a.train_steps, a.warmup)
+        tms, tpms = rt["wall_s"] / a.train_steps * 1e3, rtp["wall_s"] / a.train_steps * 1e3
+        out["train"] = {
+            "workload": f"train: batch {tsp.batch}, L={tsp.seqlen}, d_inner {tsp.d_inner}, d_state {tsp.d_state}, "
+                        f"bf16 I/O; value on the general decay path, power_path with A = -(n+1)",
+            "value": round(trows * tsp.d_state / (tms / 1e3) / 1e9, 2), "unit": "Gelem/s",
+            "ms_per_step": round(tms, 4), "aggregate_kernel_ms": round(rt["agg_ms"], 4),
+            "roofline": hbm_roofline("k_scan main pass, general decays", tbytes, rt["main_ms"], None),
+            "power_path": {"value": round(trows * tsp.d_state / (tpms / 1e3) / 1e9, 2), "ms_per_step": round(tpms, 4),
+                           "aggregate_kernel_ms": round(rtp["agg_ms"], 4),
+                           "roofline": hbm_roofline("k_scan main pass, power path", tbytes, rtp["main_ms"], None)},
+        }
+        del gt
+        torch.cuda.empty_cache()
+        if tin is not None:
+            progress("oracle on the train workload (all channels)")
+            cpu_per["train"] = cpu_oracle_full(tin, tsp, max_runs=3, target_s=2.0)
+            cpu_per["train"]["gpu_over_oracle"] = round(out["train"]["value"] / cpu_per["train"]["value"], 1)
+            del tin
+    if not a.no_decode:
+        dspec = W.DECODE
+        progress(f"decode: {dspec.streams} streams x {dspec.layers} layers x {a.decode_steps} steps")
+        dr = run_decode(ss, torch, hip, dspec, a.decode_steps)
+        tokens = dspec.streams * a.decode_steps
+        dbytes = decode_bytes(dspec)
+        ks = dr["kernel_ms"] / 1e3
+        extra = {"frac_of_measured_copy": round(dbytes / ks / 1e9 / copy_gbps, 4),
+                 "kernel_us_min": round(dr["kernel_ms_min"] * 1e3, 3), "kernel_us": round(dr["kernel_ms"] * 1e3, 3)}
+        if "rmw" in calib:
+            extra["frac_of_rmw_probe"] = round(dbytes / ks / 1e9 / calib["rmw"]["gbps"], 4)
+        out["decode"] = {
+            "workload": f"{dspec.streams} streams x {dspec.layers} layers x {a.decode_steps} token steps, "
+                        f"d_inner {dspec.d_inner}, d_state {dspec.d_state}, bf16 token inputs, fp32 states",
+            "tokens_per_s_graph": round(tokens / dr["graph_s"], 1),
+            "tokens_per_s_eager": round(tokens / dr["eager_s"], 1),
+            "ms_per_token_step_graph": round(dr["graph_s"] / a.decode_steps * 1e3, 4),
+            "ms_per_token_step_eager": round(dr["eager_s"] / a.decode_steps * 1e3, 4),
+            "roofline": hbm_roofline("k_step", dbytes, dr["kernel_ms"], measured_traffic("k_step", digest), extra),
+            "hbm_gbps_end_to_end_graph": round(dbytes * dspec.layers * a.decode_steps / dr["graph_s"] / 1e9, 1),
+        }
+    if a.block_scan_steps > 0:
         # the block-shaped scan (few channels: the lane-quad kernels), fp32 with conv
         bsp = W.WORKLOADS["block"]
         progress(f"scan {bsp.name}: {a.block_scan_steps} steps")
-        gb, _ = prepare_scan(torch, bsp, False)
+        gb, bin_ = prepare_scan(torch, bsp, None if a.no_cpu else "full")
         rbs = run_scan(ss, torch, hip, bsp, gb, a.block_scan_steps, a.warmup)
         bms = rbs["wall_s"] / a.block_scan_steps * 1e3
         brows = bsp.batch * bsp.seqlen * bsp.d_inner
+        # the same call prepared once (argument structures built and validated once)
+        yb = torch.empty_like(gb["x"])
+        pc = ss.prepare_conv_scan_fwd(gb["x"], gb["delta"], gb["A"], gb["B"], gb["C"], conv_w=gb["conv_w"],
+                                      conv_b=gb["conv_b"], delta_bias=gb["delta_bias"], D=gb["D"], z=gb["z"], y=yb)
+        for _ in range(a.warmup):
+            pc()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(a.block_scan_steps):
+            pc()
+        torch.cuda.synchronize()
+        pms = (time.perf_counter() - t0) / a.block_scan_steps * 1e3
+        kern = rbs["main_ms"] + rbs["agg_ms"]
         out["block_scan"] = {
             "workload": f"{bsp.name}: batch {bsp.batch}, L={bsp.seqlen}, d_inner {bsp.d_inner}, d_state "
                         f"{bsp.d_state}, d_conv 4, {bsp.io_dtype} I/O and state (lane-quad kernels)",
             "value": round(brows * bsp.d_state / (bms / 1e3) / 1e9, 2), "unit": "Gelem/s",
             "ms_per_step": round(bms, 4), "main_kernel_ms": round(rbs["main_ms"], 4),
             "aggregate_kernel_ms": round(rbs["agg_ms"], 4),
+            "prepared_call": {"ms_per_step": round(pms, 4), "value": round(brows * bsp.d_state / (pms / 1e3) / 1e9, 2),
+                              "us_above_kernels": round((pms - kern) * 1e3, 2),
+                              "plain_call_us_above_kernels": round((bms - kern) * 1e3, 2)},
         }
         del gb
+        if bin_ is not None:
+            cpu_per["block"] = cpu_oracle_full(bin_, bsp)
+            cpu_per["block"]["gpu_over_oracle"] = round(out["block_scan"]["value"] / cpu_per["block"]["value"], 1)
     if a.block_steps > 0:
         torch.cuda.empty_cache()
         blocks = {}
@@ -707,8 +950,15 @@ def main():
                            "tokens_per_s_graph": round(rb["streams"] / (rb["decode_graph_ms"] / 1e3), 1)},
             }
         out["block"] = blocks
+    out["calibration"] = calib
     if not a.no_cpu and sample is not None:
-        out["cpu_baseline"] = cpu_baseline(sample, spec)
+        progress("oracle on a channel sample of the long workload")
+        cb = cpu_baseline(sample, spec)
+        cb["gpu_over_oracle"] = round(out["value"] / cb["value"], 1)
+        tiny = W.WORKLOADS["tiny"]
+        cpu_per["tiny"] = cpu_oracle_full(W.gen_scan_inputs(tiny), tiny, max_runs=20, target_s=0.5)
+        cb["per_workload"] = cpu_per
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
 

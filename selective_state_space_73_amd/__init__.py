@@ -224,6 +224,52 @@ def ss_conv_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: t
     return y
 
 
+class PreparedCall:
+    """One C-ABI call with its argument structures built and validated once: calling the
+    object re-issues it on the same tensors (whose contents the caller may change in
+    place between calls) at the cost of one ctypes call. The tensors are kept alive by
+    the object. Built by prepare_conv_scan_fwd."""
+
+    def __init__(self, fn, dims, args, ws, ws_bytes, stream, keep):
+        self._fn, self._dims, self._args = fn, dims, args
+        self._ws, self._ws_bytes, self._stream = ws, ws_bytes, stream
+        self._dref, self._aref = ctypes.byref(dims), ctypes.byref(args)
+        self._keep = keep
+
+    def __call__(self):
+        _check(self._fn(self._dref, self._aref, self._ws, self._ws_bytes, self._stream))
+        return self._keep["y"]
+
+
+def prepare_conv_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, *,
+                          conv_w: Optional[torch.Tensor] = None, conv_b: Optional[torch.Tensor] = None,
+                          delta_bias: Optional[torch.Tensor] = None, D: Optional[torch.Tensor] = None,
+                          z: Optional[torch.Tensor] = None, ssm_state: Optional[torch.Tensor] = None,
+                          conv_state: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, zoh: bool = False, stream=None) -> PreparedCall:
+    """ss_conv_scan_fwd prepared for repeated calls on the same tensors (arguments as for
+    ss_conv_scan_fwd; the stream is fixed at preparation). Returns a PreparedCall whose
+    call enqueues the forward and returns y."""
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, d_inner]")
+    Bsz, L, Dn = x.shape
+    dims = make_dims(Bsz, L, Dn, A.shape[1] if A.dim() == 2 else 0, _io_dtype(x),
+                     discretization=SS_ZOH if zoh else SS_EULER)
+    if y is None:
+        y = torch.empty_like(x)
+    args = _build_args(x, delta, A, B, C, conv_w, conv_b, delta_bias, D, z, y, ssm_state, conv_state,
+                       (Bsz, L), dims)
+    need = ss_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
+    keep = dict(x=x, delta=delta, A=A, B=B, C=C, conv_w=conv_w, conv_b=conv_b, delta_bias=delta_bias, D=D, z=z,
+                y=y, ssm_state=ssm_state, conv_state=conv_state, workspace=workspace)
+    return PreparedCall(lib.ss_conv_scan_fwd, dims, args, workspace.data_ptr() if need else None,
+                        workspace.numel(), _stream_handle(stream), keep)
+
+
 NOALLOC_MAX_WORKSPACE = 16 << 20   # SS_NOALLOC_MAX_WORKSPACE
 
 
@@ -444,7 +490,7 @@ def ss_block_step(x: torch.Tensor, W: dict, dt_rank: int, ssm_state: torch.Tenso
 
 
 __all__ = ["ss_conv_scan_bidir_fwd", "ss_bidir_workspace_bytes", "ss_dir_args", "DIR_KEYS", "ss_block_fwd", "ss_block_step", "ss_block_workspace_bytes", "block_dims", "ss_block_dims",
-           "ss_block_weights", "BLOCK_WEIGHTS", "ss_conv_scan_fwd", "ss_conv_scan_fwd_noalloc", "NOALLOC_MAX_WORKSPACE",
+           "ss_block_weights", "BLOCK_WEIGHTS", "ss_conv_scan_fwd", "ss_conv_scan_fwd_noalloc", "prepare_conv_scan_fwd", "PreparedCall", "NOALLOC_MAX_WORKSPACE",
            "ss_conv_scan_bwd", "ss_bwd_workspace_bytes", "ss_grads", "ss_step", "ss_workspace_bytes", "ss_scan_plan", "ss_plan",
            "SS_PASS_FWD", "SS_PASS_BIDIR", "SS_PASS_BWD", "ss_version", "ss_time_next_call", "make_dims", "ss_dims", "ss_args",
            "SelscanError", "SS_F32", "SS_BF16", "SS_EULER", "SS_ZOH", "LIB_PATH", "lib"]

@@ -13,6 +13,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libselscan.so")
+# the benchmark's calibration kernels (include/selscan_probes.h), a library of their own
+PROBE_LIB = os.path.join(PKG, "libselscan_probes.so")
+PROBE_SOURCES = [os.path.join(PKG, "csrc", "probes.hip")]
 # kernel units (one per I/O dtype and write rule, plus the block's kernels; compiled in
 # parallel) + the C ABI layer and the block pipeline (host code)
 KERNEL_UNITS = sorted(glob.glob(os.path.join(CSRC, "selscan_*.hip")))
@@ -71,14 +74,22 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
             print(" ".join(cmd))
         cmds.append(cmd)
         objs.append(obj)
+    probe_objs = []
+    for src in PROBE_SOURCES:
+        obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+        cmds.append([HIPCC, *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj])
+        probe_objs.append(obj)
     jobs = jobs or min(len(cmds), os.cpu_count() or 1, 16)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         reports = [r.stderr for r in ex.map(_run, cmds)]
     with open(RESOURCES, "w") as f:
-        f.write("\n".join(reports))
+        f.write("\n".join(reports[:len(objs)]))
     tmp = LIB + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs, *LIBS])
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *probe_objs])
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -354,3 +354,24 @@ def test_max_d_inner(ss):
     dsel = np.array([0, 1, 255, 256, Dn // 2 + 7, Dn - 257, Dn - 256, Dn - 2, Dn - 1])
     _check_fwd(ss, spec, shape=dict(batch=1, seqlen=8, d_inner=Dn, d_state=4), states=True, dsel=dsel,
                label="max d_inner")
+
+
+def test_prepared_call_matches_and_follows_in_place_inputs(ss):
+    """prepare_conv_scan_fwd: the prepared call gives the plain call's result bit for bit,
+    and after the inputs are overwritten in place the next call uses the new values."""
+    spec = W.ScanSpec("prep", 2, 1024, 1024, 16, io_dtype="f32", delta_mode="bias", seed=71)
+    inp = W.gen_scan_inputs(spec)
+    g = to_dev(inp, "f32")
+    y_plain = gpu_fwd(ss, g)
+    pc = ss.prepare_conv_scan_fwd(g["x"], g["delta"], g["A"], g["B"], g["C"], conv_w=g["conv_w"],
+                                  conv_b=g["conv_b"], delta_bias=g["delta_bias"], D=g["D"], z=g["z"])
+    y1 = pc().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y_plain)
+    inp2 = W.gen_scan_inputs(spec, seed=72)
+    g["x"].copy_(torch.from_numpy(inp2["x"]).cuda())
+    y2 = pc()
+    torch.cuda.synchronize()
+    inp["x"] = inp2["x"]
+    yr, _, _ = oracle_fwd(inp)
+    assert maxrel(host(y2), yr) <= TOL["f32"]
