@@ -80,12 +80,13 @@ k_conv_history(const float* __restrict__ xi, float* __restrict__ hist, int64_t L
     if (i >= (int64_t)Bsz * D) return;
     const int d = (int)(i % D);
     const int64_t b = i / D;
-    float h[3] = {hist[i * 3 + 0], hist[i * 3 + 1], hist[i * 3 + 2]};
+    const float h0 = hist[i * 3 + 0], h1 = hist[i * 3 + 1], h2 = hist[i * 3 + 2];
     float n[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         const int64_t t = L - 3 + k;                 // sequence position of new entry k
-        n[k] = t >= 0 ? xi[(b * L + t) * D + d] : h[3 + t];
+        // before the sequence: old entry 3 + t (selects, not an indexed private array)
+        n[k] = t >= 0 ? xi[(b * L + t) * D + d] : (t == -1 ? h2 : (t == -2 ? h1 : h0));
     }
     hist[i * 3 + 0] = n[0]; hist[i * 3 + 1] = n[1]; hist[i * 3 + 2] = n[2];
 }

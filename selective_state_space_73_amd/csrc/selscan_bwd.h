@@ -128,8 +128,8 @@ __device__ __forceinline__ void wave_sum(float (&v)[V], int lane) {
 //                                               tokens up to and including t,
 // and the chunk's summed step size (fp64 running total) for its decay exp(A sum Delta).
 // The sweep runs forward from the chunk start, so the weights exp(A_n P_t) only
-// shrink (A <= 0): a state index n is dropped (wave-uniformly; one index at a time up
-// to d_state 16, blocks of d_state/16 above) once exp(A_n P) < 2^-kAggCutLog2 on every
+// shrink (A <= 0): a state index n is dropped (wave-uniformly; in pairs up to d_state
+// 32, blocks of d_state/16 above) once exp(A_n P) < 2^-kAggCutLog2 on every
 // lane. The dropped part is bounded by
 //     |dropped part of Q_n| <= 2^-kAggCutLog2 M + Mh,
 //     M  = sum over rows after the first drop, while some index is still active, of
@@ -223,9 +223,9 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
         }
     };
 
-    // state indices drop in blocks of BS (one each up to d_state 16); a block goes once
-    // its least negative exponent A2 * P is below the cut on every lane
-    constexpr int BS = N <= 16 ? 1 : N / 16;
+    // state indices drop in blocks of BS (pairs up to d_state 32, as in k_agg); a block
+    // goes once its least negative exponent A2 * P is below the cut on every lane
+    constexpr int BS = N <= 32 ? 2 : N / 16;
     constexpr int NBLK = N / BS;
     static_assert(NBLK <= 32, "one mask bit per block");
     float A2blk[NBLK];
@@ -808,10 +808,11 @@ static hipError_t launch_bwd_t(const LaunchBwd& q) {
     const int nC = p.nchunks;
     ScanArgs sa{p.L, p.chunk_len, (int)p.D, nC, q.nck};
     BwdArgs ba{p.L, p.chunk_len, (int)p.D, nC, q.nck, (int)gx};
+    if (nC > 1 && (p.chunk_len % kScanTile != 0 || p.chunk_len < kScanTile)) return hipErrorInvalidValue;
     if (nC > 1) {
-        hipLaunchKernelGGL((k_agg<T, N, CONV, ZOH>), dim3(gx, nC - 1, (unsigned)p.batch), dim3(kScanThreads), 0, st,
-                           x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A, Bm, p.ssm_state, p.conv_state, p.ws_S,
-                           p.ws_sdt, p.ws_h0, p.ws_c0, sa);
+        launch_k_agg<T, N, CONV, ZOH, false>(dim3(gx, nC - 1, (unsigned)p.batch), st, nullptr, nullptr, x, p.conv_w,
+                                             p.conv_b, dl, p.delta_bias, p.A, Bm, p.ssm_state, p.conv_state, p.ws_S,
+                                             p.ws_sdt, p.ws_h0, p.ws_c0, sa);
     }
     launch_k_scan<T, N, CONV, false, ZOH, true, false, false>(
         dim3(gx, nC, (unsigned)p.batch), st, nullptr, nullptr, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A, Bm, Cm,

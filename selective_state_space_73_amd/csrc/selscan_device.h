@@ -49,6 +49,9 @@ constexpr float kZohSeriesT = 0.14426950408889634f;   // |t| below this (|x| < 0
 // ---------------------------------------------------------------------------
 // elementwise pieces (fp32)
 
+// compile-time flag passed to generic lambdas
+template <bool B> struct Tag { static constexpr bool value = B; };
+
 __device__ __forceinline__ float exp2_fast(float v) { return __builtin_amdgcn_exp2f(v); }
 __device__ __forceinline__ float log2_fast(float v) { return __builtin_amdgcn_logf(v); }
 __device__ __forceinline__ float rcp_fast(float v) { return __builtin_amdgcn_rcpf(v); }
@@ -567,8 +570,9 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 // chunk's sum (needed exactly for its decay exp(A*sum)) and to a bound on what was
 // dropped (both write coefficients are at most Delta for A <= 0):
 //     |dropped part of S_n| <= 2^-kAggCutLog2 * M + umax * Mh,
-//     M  = sum over rows after the first drop, while some state is still active,
-//          of |Delta_t u_t| max_n |B_t[n]|,
+//     M  = sum over the rows swept while some state is still active of
+//          |Delta_t u_t| max_n |B_t[n]| (the rows that can hold a dropped term, and
+//          the few before the first drop),
 //     Mh = sum over rows after every state is dropped of exp(A_max R_t) Delta_t
 //          max_n |B_t[n]|, A_max the least negative A (bounding every dropped weight),
 // umax a bound on |u| over those rows (from their inputs, which need no SiLU).
@@ -578,23 +582,37 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 
 constexpr int kAggCutLog2 = 40;
 
-// Rows per prefetched group of the aggregate pass: 8 up to d_state 16, 4 above (with 8,
-// the zero-order-hold form at d_state 64 kept its per-state arrays in scratch memory; that
-// configuration once ended in a memory-aperture fault, though a host transcription of its
-// index arithmetic finds every row, tile and LDS index in bounds, so it stays excluded).
-template <int N> constexpr int agg_group_rows() { return N <= 16 ? 8 : 4; }
+// Rows per prefetched group of the aggregate pass: 8 up to d_state 16, 4 at 32 and 2 at 64,
+// where the zero-order-hold form fills the register file with its four per-state arrays
+// (with 8, that form kept its per-state arrays in scratch memory and once ended in a
+// memory-aperture fault, though a host transcription of its index arithmetic finds
+// every row, tile and LDS index in bounds, so it stays excluded).
+template <int N> constexpr int agg_group_rows() { return N <= 16 ? 8 : (N <= 32 ? 4 : 2); }
+
+// Whether the aggregate pass has a power launch: the Euler form from kPowMinN states.
+template <int N, bool ZOH> constexpr bool kAggPowLaunch = N >= kPowMinN && !ZOH;
 
 // REV: the aggregates of the reversed scan order (see k_scan), no initial states.
-template <typename T, int N, bool CONV, bool ZOH, bool REV = false>
+// POW: the power fast path (launched twice, as k_scan): each row's decays
+// exp(A_n R) = exp(A_0 R)^(n+1) from one exponential and a chain of multiplies. Under
+// the identity A_n = (n+1) A_0 the drop order follows n (a block's least negative
+// exponent falls with n, and every block is tested at the same R), so the active
+// blocks are always a prefix and the chain stops at the first dropped one.
+template <typename T, int N, bool CONV, bool ZOH, bool REV = false, bool POW = false>
 __global__ void __launch_bounds__(kScanThreads)
 k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
       const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
       const T* __restrict__ Bm, const float* __restrict__ ssm_state, const float* __restrict__ conv_state,
       float* __restrict__ ws_S, float* __restrict__ ws_sdt, float* __restrict__ ws_h0, float* __restrict__ ws_c0,
       ScanArgs sa) {
+    static_assert(!(POW && ZOH), "the aggregate pass's power path is Euler only");
     const int D = sa.D;
     const int d_raw = blockIdx.x * kScanThreads + threadIdx.x;
     const int d = d_raw < D ? d_raw : D - 1;      // clamped lanes repeat the last channel
+    // the vote only where launch_k_agg makes both launches
+    if constexpr (kAggPowLaunch<N, ZOH>) {
+        if (pow_skip<N, POW>(A + (int64_t)d * N)) return;   // the workgroup runs in the other launch
+    }
     const unsigned du = (unsigned)d;              // zero-extended lane offset: uniform-base addressing
     const int c = blockIdx.y;                     // chunk, < nchunks - 1
     const int b = blockIdx.z;
@@ -639,7 +657,7 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
         }
     }
     constexpr int U = agg_group_rows<N>();
-    static_assert(U == 4 || N <= 16, "8-row groups only up to d_state 16");
+    static_assert(U <= 4 || N <= 16, "8-row groups only up to d_state 16");
     constexpr int R = kScanTile;
     static_assert(R % (2 * U) == 0, "tiles hold whole pairs of groups");
     constexpr int NB = N + 1;                     // B values and max_n |B| per token
@@ -649,16 +667,14 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     constexpr int PER_THREAD = (TILE_ELEMS + kScanThreads - 1) / kScanThreads;
     static_assert(kScanThreads % N == 0 && 64 % N == 0, "a token's N values sit in consecutive lanes of a wave");
     T tb[PER_THREAD];
-    // tile with chunk-relative rows [rlo, rlo + R); rows before the chunk start are
-    // clamped to it (they are zero-weight padding)
+    // tile with chunk-relative rows [rlo, rlo + R), rlo >= 0
     const T* Bc = Bm + prow(t0) * N;                      // uniform: B of the chunk's first token
     auto tile_fetch = [&](int rlo) {
 #pragma unroll
         for (int k = 0; k < PER_THREAD; ++k) {
             const int e0 = tid + k * kScanThreads;
             const int e = e0 < TILE_ELEMS ? e0 : TILE_ELEMS - 1;
-            const int r = rlo + e / N;
-            tb[k] = Bc[(r < 0 ? 0 : r) * sN + e % N];
+            tb[k] = Bc[(rlo + e / N) * sN + e % N];
         }
     };
     auto tile_store = [&](int buf) {
@@ -686,10 +702,11 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     float M = 0.0f;                               // sum |Delta u| max|B| over swept rows (full mode)
     float Mh = 0.0f;                              // sum Delta max|B| over rows swept after every n was dropped
     float xmax = 0.0f;                            // max |x| feeding those rows
-    // state indices are dropped in blocks of BS (one state each up to d_state 16, so that
-    // a fast-decaying state stops as soon as it alone is below the cut); a block goes
-    // once its least negative exponent A2 * R is below the cut on every lane
-    constexpr int BS = N <= 16 ? 1 : N / 16;
+    // state indices are dropped in blocks of BS (pairs up to d_state 32: single states
+    // save some exponentials but cost a branch and a register copy per state and group,
+    // measured slower); a block goes once its least negative exponent A2 * R is below
+    // the cut on every lane
+    constexpr int BS = N <= 32 ? 2 : N / 16;
     constexpr int NBLK = N / BS;
     static_assert(NBLK <= 32, "one mask bit per block");
     float A2blk[NBLK];
@@ -713,33 +730,43 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     float hist0 = 0.f, hist1 = 0.f, hist2 = 0.f;
     if (CONV && conv_state) { hist0 = conv_state[bd * 3 + 0]; hist1 = conv_state[bd * 3 + 1]; hist2 = conv_state[bd * 3 + 2]; }
 
-    // Token indices below are relative to the chunk start (int32). Rows at rel < 0
-    // are zero-weight padding; x at global token < 0 comes from the history.
+    // Token indices below are relative to the chunk start (int32). Every chunk this
+    // kernel sweeps is full and a whole number of B tiles long (the host's chunking),
+    // so no row is padding. x before the chunk start is the previous chunk's, except in
+    // chunk 0, whose rows 0..2 take x_{-3..-1} from the initial history.
     const int clen = (int)(t1 - t0);
-    // lowest chunk-relative row of x this sweep reads from memory: rows down to -(3+U)
-    // are touched (x_{r-3} of the padding rows); below global token 0 nothing exists
-    const int minrel = t0 >= 3 + U ? -(3 + U) : (int)-t0;
+    const bool first = t0 == 0;
+    // lowest chunk-relative row of x the sweep loads: x_{r-3} of rows down to -U (the
+    // prefetch past the chunk start); t0 >= kScanTile > 3 + U when it is not chunk 0
+    const int xlo = first ? 0 : -(3 + U);
     const T* xrow0 = x + prow(t0) * D;                    // uniform: token t0 of this batch row
     const T* drow0 = delta + prow(t0) * D;
-    auto xrel = [&](int r) -> float {                     // x at chunk-relative row r (may be < 0)
-        if (r >= minrel) return IO<T>::cvt(xrow0[(int64_t)r * sD + d]);
-        const int64_t tt = t0 + r;                       // < 0 here
-        return tt == -1 ? hist2 : (tt == -2 ? hist1 : (tt == -3 ? hist0 : 0.0f));
-    };
+    const unsigned voff = du * (unsigned)sizeof(T);       // lane byte offset within a token row
+    const unsigned rowb = (unsigned)D * (unsigned)sizeof(T);
+    auto hist_x = [&](int r) -> float { return r == -1 ? hist2 : (r == -2 ? hist1 : hist0); };   // r in -3..-1
+    auto xmem = [&](int r) -> float { return IO<T>::ld(xrow0 + (int64_t)r * sD + d); };
     // conv window for the token about to be processed (r): xa = x_r, xb = x_{r-1}, xc = x_{r-2}
-    float xa = xrel(clen - 1), xb = xrel(clen - 2), xc = xrel(clen - 3);
+    // (clen >= kScanTile, so these rows are the chunk's own)
+    float xa = xmem(clen - 1), xb = xmem(clen - 2), xc = xmem(clen - 3);
+    // rows top, top-1, .., top-U+1 (each clamped to >= lo) of a [., D] tensor whose
+    // chunk-relative row 0 is at p0: one uniform base at the group's lowest address and
+    // uniform byte offsets from it
+    auto load_rows = [&](const T* p0, int top, int lo, T* out) {
+        const int hi = top > lo ? top : lo;
+        const int bot = top - (U - 1) > lo ? top - (U - 1) : lo;
+        const Buf<T> bf(p0 + (int64_t)(REV ? hi : bot) * sD);
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int r = top - i > lo ? top - i : lo;
+            out[i] = bf.ld(voff, (unsigned)(REV ? hi - r : r - bot) * rowb);
+        }
+    };
     // prefetch of a group (rows gr-1 .. gr-U): delta of those rows, x of rows gr-4 .. gr-U-3;
     // two buffers used alternately
     T pd0[U], px0[U], pd1[U], px1[U];
     auto load_group = [&](int gr, T* pd, T* px) {
-#pragma unroll
-        for (int i = 0; i < U; ++i) {
-            const int r = gr - 1 - i;
-            const int rd = r < 0 ? 0 : r;
-            const int rx = (r - 3) < minrel ? minrel : r - 3;
-            pd[i] = (drow0 + (int64_t)rd * sD)[du];
-            px[i] = (xrow0 + (int64_t)rx * sD)[du];
-        }
+        load_rows(drow0, gr - 1, 0, pd);
+        load_rows(xrow0, gr - 4, xlo, px);
     };
     bool cut_seen = false;                                // the window at the switch enters xmax once
 
@@ -749,23 +776,32 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     // immediate offset (a negative one cannot be encoded and costs an address move per
     // read). Larger d_state passes row gr-1 and reads downward from it: with the cheaper
     // reads the compiler keeps more of them in flight, which the zero-order-hold kernel
-    // at d_state 64 has no registers for.
-    auto group = [&](int gr, const T* cd, const T* cx, const float* rowref) {
+    // at d_state 64 has no registers for. EDGE: chunk 0's last group (gr = U), whose rows
+    // 0..2 take their oldest conv input from the initial history.
+    // Up to d_state 16 (8-row groups) that group is a separate copy of the code; above,
+    // the history enters through a few selects under a uniform branch (a second copy of
+    // the larger kernels' group would not fit their registers), in the last group or, with
+    // 2-row groups, the last two.
+    constexpr bool PEEL = N <= 16;
+    auto group = [&](auto edge, int gr, const T* cd, const T* cx, const float* rowref) {
+        constexpr bool EDGE = decltype(edge)::value;
         auto brow = [&](int i) -> const float* { return N <= 16 ? rowref + (U - 1 - i) * NB : rowref - i * NB; };
-        // x_{r-3} of each row, and which rows are padding; only the group that reaches
-        // down to rel < 3 needs the selects
-        float xd[U];
-        bool pad[U];
-        if (gr - U < 3) {
+        float xd[U];                                      // x_{r-3} of each row r = gr-1-i
 #pragma unroll
-            for (int i = 0; i < U; ++i) {
-                const int r = gr - 1 - i;
-                xd[i] = (r - 3) >= minrel ? IO<T>::cvt(cx[i]) : xrel(r - 3);
-                pad[i] = r < 0;
+        for (int i = 0; i < U; ++i) xd[i] = (EDGE && U - 4 - i < 0) ? hist_x(U - 4 - i) : IO<T>::cvt(cx[i]);
+        if (!PEEL && first && gr - U < 3) {
+            // the group of rows U-1..0, and with 2-row groups also rows 3..2 (row 2 takes x_{-1})
+            if (gr == U) {
+#pragma unroll
+                for (int i = 0; i < U; ++i) {
+                    if (U - 4 - i < 0) xd[i] = hist_x(U - 4 - i);
+                }
+            } else if (U < 3 && gr == 2 * U) {
+#pragma unroll
+                for (int i = 0; i < U; ++i) {
+                    if (2 * U - 4 - i < 0) xd[i] = hist_x(2 * U - 4 - i);
+                }
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < U; ++i) { xd[i] = IO<T>::cvt(cx[i]); pad[i] = false; }
         }
         if (act) {
             float dt[U], wv[U], uu[U];
@@ -779,7 +815,7 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                     u = xa;
                 }
                 xa = xb; xb = xc; xc = xd[i];
-                dt[i] = pad[i] ? 0.0f : softplus(IO<T>::cvt(cd[i]) + dbias);
+                dt[i] = softplus(IO<T>::cvt(cd[i]) + dbias);
                 wv[i] = dt[i] * u;
                 uu[i] = u;
             }
@@ -790,11 +826,31 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
 #pragma unroll
             for (int i = 0; i < U; ++i) { Rf[i] = rbase + part; part += dt[i]; Ri[i] = rbase + part; }
             Rsum += (double)part;
+            // every row swept while a state is active enters M (a superset of the rows
+            // after the first drop, which loosens the bound only slightly)
 #pragma unroll
-            for (int i = 0; i < U; ++i) {
-                // rows after the first drop (a group with every state still active drops nothing)
-                if (act != full) M = __builtin_fmaf(__builtin_fabsf(wv[i]), brow(i)[N], M);
-            }
+            for (int i = 0; i < U; ++i) M = __builtin_fmaf(__builtin_fabsf(wv[i]), brow(i)[N], M);
+            if constexpr (POW) {
+                // running power e0^(BS j) of each row's base decay, advanced through the
+                // active prefix of blocks
+                float e0[U], pw[U];
+#pragma unroll
+                for (int i = 0; i < U; ++i) { e0[i] = exp2_fast(A2[0] * Rf[i]); pw[i] = 1.0f; }
+#pragma unroll
+                for (int j = 0; j < NBLK; ++j) {
+                    if ((act >> j) & 1u) {                // then so is every block before it
+#pragma unroll
+                        for (int i = 0; i < U; ++i) {
+#pragma unroll
+                            for (int q = 0; q < BS; ++q) {
+                                pw[i] *= e0[i];
+                                S[BS * j + q] = __builtin_fmaf(pw[i], wv[i] * brow(i)[BS * j + q], S[BS * j + q]);
+                            }
+                        }
+                        if (!__any(A2blk[j] * (float)Rsum > cut)) act &= ~(1u << j);
+                    }
+                }
+            } else {
 #pragma unroll
             for (int j = 0; j < NBLK; ++j) {
                 if ((act >> j) & 1u) {
@@ -820,6 +876,7 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                     if (!__any(A2blk[j] * (float)Rsum > cut)) act &= ~(1u << j);
                 }
             }
+            }
         } else {
             if (!cut_seen) {
                 // the window entering the first row after the cut
@@ -833,8 +890,8 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
 #pragma unroll
             for (int i = 0; i < U; ++i) {
                 // each x enters the bound once, as the newest input of the row that loads it
-                xmax = __builtin_fmaxf(xmax, pad[i] ? 0.0f : __builtin_fabsf(xd[i]));
-                const float dtv = pad[i] ? 0.0f : softplus(IO<T>::cvt(cd[i]) + dbias);
+                xmax = __builtin_fmaxf(xmax, __builtin_fabsf(xd[i]));
+                const float dtv = softplus(IO<T>::cvt(cd[i]) + dbias);
                 part += dtv;
                 mg = __builtin_fmaf(dtv, brow(i)[N], mg);
             }
@@ -844,7 +901,7 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     };
 
     auto group_row = [](int gr) { return N <= 16 ? gr - U : gr - 1; };
-    const int ntiles = (clen + R - 1) / R;
+    const int ntiles = clen / R;
     tile_fetch(clen - R);
     tile_store(0);
     load_group(clen, pd0, px0);
@@ -854,11 +911,13 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
         const int rhi = clen - k * R;                     // tile rows [rhi - R, rhi)
         if (k + 1 < ntiles) tile_fetch(rhi - 2 * R);
         const float* tbase = &sB[buf][0][0] - (int64_t)(rhi - R) * NB;   // row r of this tile at tbase + r*NB
+        const bool edge = first && k + 1 == ntiles;      // the tile holding chunk 0's rows 0..2
         for (int gr = rhi; gr > rhi - R; gr -= 2 * U) {
             load_group(gr - U, pd1, px1);
-            group(gr, pd0, px0, tbase + group_row(gr) * NB);
+            group(Tag<false>{}, gr, pd0, px0, tbase + group_row(gr) * NB);
             load_group(gr - 2 * U, pd0, px0);
-            group(gr - U, pd1, px1, tbase + group_row(gr - U) * NB);
+            if (PEEL && edge && gr - U == U) group(Tag<PEEL>{}, U, pd1, px1, tbase + group_row(U) * NB);
+            else group(Tag<false>{}, gr - U, pd1, px1, tbase + group_row(gr - U) * NB);
         }
         if (k + 1 < ntiles) tile_store(buf ^ 1);
         __syncthreads();
@@ -885,7 +944,10 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
         const float* src = (c == 0) ? ssm_state : nullptr;
 #pragma unroll
         for (int n = 0; n < N; ++n) h[n] = src ? src[bd * N + n] : 0.0f;
-        float x3 = xrel(-3), x2 = xrel(-2), x1 = xrel(-1);
+        // x_{-3..-1}: the history in chunk 0, else the previous chunk's last rows (the
+        // loads read row 0 in chunk 0 and the value is selected afterwards)
+        const float m3 = xmem(first ? 0 : -3), m2 = xmem(first ? 0 : -2), m1 = xmem(first ? 0 : -1);
+        float x3 = first ? hist0 : m3, x2 = first ? hist1 : m2, x1 = first ? hist2 : m1;
         double sd = 0.0;
         for (int64_t t = t0; t < t1; ++t) {
             const float xt = IO<T>::ld(x + prow(t) * D + d);
@@ -1387,6 +1449,21 @@ static void launch_k_scan(dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t 
     }
 }
 
+// The aggregate pass: as k_scan, general and power launches for the Euler form from
+// kPowMinN states.
+template <typename T, int N, bool CONV, bool ZOH, bool REV, typename... Args>
+static void launch_k_agg(dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, Args... args) {
+    if constexpr (kAggPowLaunch<N, ZOH>) {
+        hipExtLaunchKernelGGL((k_agg<T, N, CONV, ZOH, REV, false>), grid, dim3(kScanThreads), 0, st, ev0, nullptr, 0,
+                              args...);
+        hipExtLaunchKernelGGL((k_agg<T, N, CONV, ZOH, REV, true>), grid, dim3(kScanThreads), 0, st, nullptr, ev1, 0,
+                              args...);
+    } else {
+        hipExtLaunchKernelGGL((k_agg<T, N, CONV, ZOH, REV, false>), grid, dim3(kScanThreads), 0, st, ev0, ev1, 0,
+                              args...);
+    }
+}
+
 template <typename T, int N, bool CONV, bool GATE, bool ZOH, bool REV = false, bool PART = false>
 static hipError_t launch_scan_t(const LaunchScan& p) {
     const T* x = static_cast<const T*>(p.x);
@@ -1415,12 +1492,13 @@ static hipError_t launch_scan_t(const LaunchScan& p) {
             return hipGetLastError();
         }
     }
+    // the aggregate pass sweeps whole B tiles of full chunks (no padding rows)
+    if (p.nchunks > 1 && (p.chunk_len % kScanTile != 0 || p.chunk_len < kScanTile)) return hipErrorInvalidValue;
     if (p.nchunks > 1) {
-        hipExtLaunchKernelGGL((k_agg<T, N, CONV, ZOH, REV>), dim3(gx, p.nchunks - 1, (unsigned)p.batch),
-                              dim3(kScanThreads), 0, st, static_cast<hipEvent_t>(p.ev_agg[0]),
-                              static_cast<hipEvent_t>(p.ev_agg[1]), 0, x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
-                              static_cast<const T*>(p.B), p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0,
-                              p.ws_c0, sa);
+        launch_k_agg<T, N, CONV, ZOH, REV>(dim3(gx, p.nchunks - 1, (unsigned)p.batch), st,
+                                           static_cast<hipEvent_t>(p.ev_agg[0]), static_cast<hipEvent_t>(p.ev_agg[1]),
+                                           x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A, static_cast<const T*>(p.B),
+                                           p.ssm_state, p.conv_state, p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, sa);
     }
     launch_k_scan<T, N, CONV, GATE, ZOH, false, REV, PART>(
         dim3(gx, p.nchunks, (unsigned)p.batch), st, static_cast<hipEvent_t>(p.ev_main[0]),

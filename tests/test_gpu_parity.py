@@ -114,11 +114,15 @@ def test_optional_pieces(ss, flags, io):
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [dict(batch=1, seqlen=4096, d_inner=64, d_state=16),
-                                   dict(batch=2, seqlen=3001, d_inner=100, d_state=8)],
-                         ids=["chunked_even", "chunked_ragged"])
+                                   dict(batch=2, seqlen=3001, d_inner=100, d_state=8),
+                                   dict(batch=1, seqlen=2048, d_inner=64, d_state=32),
+                                   dict(batch=2, seqlen=1999, d_inner=48, d_state=64)],
+                         ids=["chunked_even", "chunked_ragged", "chunked_n32", "chunked_n64"])
 def test_chunked_path(ss, io, shape):
     """Few channels and a long sequence select the chunked scan (aggregate pass +
-    carry-in); it must agree with the oracle including the returned state."""
+    carry-in); it must agree with the oracle including the returned state. d_state 32
+    and 64 run the aggregate pass with 4- and 2-row groups, whose first chunk takes the
+    conv history into its last one or two groups."""
     dims = ss.make_dims(shape["batch"], shape["seqlen"], shape["d_inner"], shape["d_state"], 0)
     assert ss.ss_workspace_bytes(dims) > 0, "shape does not select the chunked path"
     spec = W.ScanSpec("chunk", 1, 1, 1, 4, io_dtype=io, delta_mode="bias", seed=7)

@@ -214,28 +214,34 @@ void agg_case(int64_t L, int64_t chunk_len, int nchunks, int N, int U, bool rev)
         const int64_t t0 = (int64_t)c * chunk_len;
         const int clen = (int)chunk_len;                       // every chunk but the last is full
         if (clen % R != 0) { std::printf("FAIL agg: chunk length not whole tiles\n"); ++bad; }
-        const int minrel = t0 >= 3 + U ? -(3 + U) : (int)-t0;
-        // tile_fetch(rlo): element e of the tile -> chunk-relative row rlo + e / N, clamped at 0
-        const int ntiles = (clen + R - 1) / R;
+        const bool first = t0 == 0;
+        if (!first && t0 < 3 + U) { std::printf("FAIL agg: a later chunk starts before row 3 + U\n"); ++bad; }
+        const int xlo = first ? 0 : -(3 + U);
+        // tile_fetch(rlo): element e of the tile -> chunk-relative row rlo + e / N (rlo >= 0)
+        const int ntiles = clen / R;
         for (int k = 0; k < ntiles; ++k) {
             const int rlo = clen - (k + 1) * R;
+            if (rlo < 0) { if (bad++ < 5) std::printf("FAIL agg: tile starts at row %d\n", rlo); }
             const int tile_elems = R * N;
-            for (int e = 0; e < tile_elems; ++e) {
-                const int r = rlo + e / N;
-                inL(t0 + (r < 0 ? 0 : r), "B tile row");
-            }
+            for (int e = 0; e < tile_elems; ++e) inL(t0 + rlo + e / N, "B tile row");
         }
-        // the sweep: groups of U rows gr-1 .. gr-U, prefetched one group ahead
-        auto load_group = [&](int gr) {
+        // load_rows(top, lo): rows max(top - i, lo), i < U, at byte offsets from the group's
+        // lowest-address row (non-negative, and below 2^32 for any d_inner up to 2^26)
+        auto load_rows = [&](int top, int lo, const char* what) {
+            const int hi = top > lo ? top : lo;
+            const int bot = top - (U - 1) > lo ? top - (U - 1) : lo;
             for (int i = 0; i < U; ++i) {
-                const int r = gr - 1 - i;
-                const int rd = r < 0 ? 0 : r;
-                const int rx = (r - 3) < minrel ? minrel : r - 3;
-                inL(t0 + rd, "delta row");
-                inL(t0 + rx, "x row");
+                const int r = top - i > lo ? top - i : lo;
+                const int64_t rel = rev ? hi - r : r - bot;
+                if (rel < 0 || rel >= U) { if (bad++ < 5) std::printf("FAIL agg: %s offset %" PRId64 " rows\n", what, rel); }
+                inL(t0 + r, what);
             }
         };
-        auto group = [&](int gr, int rhi) {
+        auto load_group = [&](int gr) {
+            load_rows(gr - 1, 0, "delta row");
+            load_rows(gr - 4, xlo, "x row");
+        };
+        auto group = [&](int gr, int rhi, bool edge) {
             for (int i = 0; i < U; ++i) {
                 // staged row of the B value (and max |B|) of row gr-1-i, relative to the tile
                 const int row = (gr - 1 - i) - (rhi - R);
@@ -245,29 +251,28 @@ void agg_case(int64_t L, int64_t chunk_len, int nchunks, int N, int U, bool rev)
                 const int idx_last = row * NB + N;              // max |B| entry, the row's last
                 if (idx_last >= R * NB) { if (bad++ < 5) std::printf("FAIL agg: LDS index %d\n", idx_last); }
                 const int r = gr - 1 - i;
-                if (gr - U < 3 && (r - 3) < minrel) {
-                    // window entry from the initial history: global token t0 + r - 3 in [-3, -1]
-                    const int64_t tt = t0 + r - 3;
-                    if (tt >= 0 || tt < -3) {
-                        // below -3 the kernel returns 0 (no history there); >= 0 must be read from x
-                        if (tt >= 0 && bad++ < 5) std::printf("FAIL agg: history read at token %" PRId64 "\n", tt);
-                    }
+                // x_{r-3}: from the initial history exactly where it precedes the sequence
+                // (the kernel's rule: chunk 0's last group, and with 2-row groups the one before)
+                const bool from_hist = first && ((gr == U && U - 4 - i < 0) || (U < 3 && gr == 2 * U && 2 * U - 4 - i < 0));
+                const bool needs_hist = t0 + r - 3 < 0;
+                if (from_hist != needs_hist) {
+                    if (bad++ < 5) std::printf("FAIL agg: x_{r-3} source wrong at token %" PRId64 "\n", t0 + r);
                 }
+                if (edge && gr != U) { if (bad++ < 5) std::printf("FAIL agg: edge group at row %d\n", gr); }
+                if (edge && U < 8) { if (bad++ < 5) std::printf("FAIL agg: separate edge group with %d-row groups\n", U); }
             }
         };
         // the conv window before the sweep: rows clen-1, clen-2, clen-3
-        for (int j = 1; j <= 3; ++j) {
-            const int r = clen - j;
-            if (r >= minrel) inL(t0 + r, "window row");
-        }
+        for (int j = 1; j <= 3; ++j) inL(t0 + clen - j, "window row");
         load_group(clen);
         for (int k = 0; k < ntiles; ++k) {
             const int rhi = clen - k * R;
+            const bool edge = first && k + 1 == ntiles;
             for (int gr = rhi; gr > rhi - R; gr -= 2 * U) {
                 load_group(gr - U);
-                group(gr, rhi);
+                group(gr, rhi, false);
                 load_group(gr - 2 * U);
-                group(gr - U, rhi);
+                group(gr - U, rhi, U == 8 && edge && gr - U == U);   // the separate copy: 8-row groups
             }
         }
     }
@@ -304,7 +309,7 @@ int main(int argc, char** argv) {
                     {2048, 512, 4}, {3001, 64, 47}, {200, 64, 4}, {192, 64, 3}};
     for (const A& a : ag)
         for (int N : {4, 8, 16, 32, 64})
-            for (int U : {4, 8})
+            for (int U : {2, 4, 8})
                 for (bool rev : {false, true}) agg_case(a.L, a.cl, a.nc, N, U, rev);
     std::printf("%s: %d violation(s)\n", failures ? "FAILED" : "ok", failures);
     return failures ? 1 : 0;
