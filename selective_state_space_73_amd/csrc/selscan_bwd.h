@@ -16,7 +16,7 @@
 //                   summed step size, so that chunk c's adjoint carry-in is the fold
 //                   gamma_c = Q_{c+1} + exp(A sum Delta_{c+1}) gamma_{c+1}; swept from
 //                   the chunk start, dropping state indices whose weight fell below
-//                   2^-40, with an exact fallback when the dropped part may matter;
+//                   2^-kAggCutLog2, with an exact fallback when the dropped part may matter;
 //   4. k_bwd        per chunk, 4-token segments from the end: recompute the segment
 //                   forward from its checkpoint (states kept in registers), then sweep
 //                   it backward; channel sums of dB/dC are reduced across the lanes of
@@ -330,7 +330,7 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
     float qmax = 0.0f;
 #pragma unroll
     for (int n = 0; n < N; ++n) qmax = __builtin_fmaxf(qmax, __builtin_fabsf(q[n]));
-    const bool bad = !(M * 0x1p-40f + Mh <= qmax * 0x1p-24f);
+    const bool bad = !(__builtin_ldexpf(M, -kAggCutLog2) + Mh <= qmax * 0x1p-24f);
     if (__any(bad)) {
         // exact backward sweep over the chunk (rare: the dropped part was not negligible)
 #pragma unroll
