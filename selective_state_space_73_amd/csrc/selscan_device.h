@@ -379,12 +379,16 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
             if (!CK) tc[k] = Ct[off];
         }
     };
+    // zero-order hold on the power path: B[n] is staged as B[n] / (n+1), the factor its
+    // write coefficient takes from the geometric sum below (one rounding per value)
     auto tile_store = [&](int buf) {
 #pragma unroll
         for (int k = 0; k < PER_THREAD; ++k) {
             const int e = tid + k * kScanThreads;
             if (e < TILE_ELEMS) {
-                sbc[buf][e / N][e % N] = IO<T>::cvt(tb[k]);
+                float bvs = IO<T>::cvt(tb[k]);
+                if constexpr (ZOH && POW) bvs = bvs / (float)(e % N + 1);
+                sbc[buf][e / N][e % N] = bvs;
                 if (!CK) sbc[buf][e / N][N + e % N] = IO<T>::cvt(tc[k]);
             }
         }
@@ -429,14 +433,36 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
             c[2] = c[1] * c[0];
             c[3] = c[1] * c[1];
             const float step = c[3];
+            if constexpr (ZOH) {
+                // (a_n - 1) / A_n = [(a_0 - 1) / A_0] G_n / (n+1) with A_n = (n+1) A_0 and
+                // G_n = 1 + a_0 + ... + a_0^n: the coefficient of state 0 (with its series
+                // near A_0 Delta = 0) once per token, G_n as four interleaved sums
+                // G_{n+4} = G_n + a_n G_3 of positive terms (no cancellation for any n),
+                // and 1/(n+1) already in the staged B
+                const float cz = zoh_coef(c[0], p.dt * A2[0], p.dt, iA[0]) * p.u;
+                float g[kPowLanes];
+                g[0] = 1.0f;
+                g[1] = 1.0f + c[0];
+                g[2] = g[1] + c[1];
+                g[3] = g[2] + c[2];
+                const float q = g[3];
 #pragma unroll
-            for (int n = 0; n < N; ++n) {
-                const float an = c[n % kPowLanes];
-                if (n + kPowLanes < N) c[n % kPowLanes] = an * step;
-                if constexpr (ZOH)
-                    h[n] = __builtin_fmaf(an, h[n], zoh_coef(an, p.dt * A2[n], p.dt, iA[n]) * (p.u * bv[n]));
-                else
+                for (int n = 0; n < N; ++n) {
+                    const float an = c[n % kPowLanes];
+                    const float gn = g[n % kPowLanes];
+                    if (n + kPowLanes < N) {
+                        c[n % kPowLanes] = an * step;
+                        g[n % kPowLanes] = __builtin_fmaf(an, q, gn);
+                    }
+                    h[n] = __builtin_fmaf(an, h[n], (cz * gn) * bv[n]);
+                }
+            } else {
+#pragma unroll
+                for (int n = 0; n < N; ++n) {
+                    const float an = c[n % kPowLanes];
+                    if (n + kPowLanes < N) c[n % kPowLanes] = an * step;
                     h[n] = __builtin_fmaf(an, h[n], p.wv * bv[n]);
+                }
             }
         } else {
 #pragma unroll
