@@ -621,8 +621,8 @@ constexpr int kAggCutLog2 = 40;
 // every row, tile and LDS index in bounds, so it stays excluded).
 template <int N> constexpr int agg_group_rows() { return N <= 16 ? 8 : (N <= 32 ? 4 : 2); }
 
-// Whether the aggregate pass has a power launch: the Euler form from kPowMinN states.
-template <int N, bool ZOH> constexpr bool kAggPowLaunch = N >= kPowMinN && !ZOH;
+// Whether the aggregate pass has a power launch: from kPowMinN states.
+template <int N, bool ZOH> constexpr bool kAggPowLaunch = N >= kPowMinN;
 
 // REV: the aggregates of the reversed scan order (see k_scan), no initial states.
 // POW: the power fast path (launched twice, as k_scan): each row's decays
@@ -637,7 +637,6 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
       const T* __restrict__ Bm, const float* __restrict__ ssm_state, const float* __restrict__ conv_state,
       float* __restrict__ ws_S, float* __restrict__ ws_sdt, float* __restrict__ ws_h0, float* __restrict__ ws_c0,
       ScanArgs sa) {
-    static_assert(!(POW && ZOH), "the aggregate pass's power path is Euler only");
     const int D = sa.D;
     const int d_raw = blockIdx.x * kScanThreads + threadIdx.x;
     const int d = d_raw < D ? d_raw : D - 1;      // clamped lanes repeat the last channel
@@ -718,7 +717,9 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
 #pragma unroll
             for (int o = 1; o < N; o <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o, N));
             if (e < TILE_ELEMS) {
-                sB[buf][e / N][e % N] = v;
+                // zero-order hold on the power path: B[n] / (n+1), the factor its write
+                // coefficient takes from the geometric sum (the bound keeps max |B|)
+                sB[buf][e / N][e % N] = (ZOH && POW) ? v / (float)(e % N + 1) : v;
                 if (e % N == 0) sB[buf][e / N][N] = m;
             }
         }
@@ -864,10 +865,24 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
             for (int i = 0; i < U; ++i) M = __builtin_fmaf(__builtin_fabsf(wv[i]), brow(i)[N], M);
             if constexpr (POW) {
                 // running power e0^(BS j) of each row's base decay, advanced through the
-                // active prefix of blocks
-                float e0[U], pw[U];
+                // active prefix of blocks. Zero-order hold: the row's term for state n is
+                // exp(A_n R) (a_n - 1) / A_n u B[n] (R without the row's own step, a_n its
+                // decay), with (a_n - 1) / A_n = [(a_0 - 1) / A_0] G_n / (n+1) and
+                // G_n = 1 + a_0 + ... + a_0^n carried beside the running power; 1/(n+1)
+                // is in the staged B.
+                float e0[U], pw[U], a0[U], pa[U], gs[U], cz[U];
 #pragma unroll
-                for (int i = 0; i < U; ++i) { e0[i] = exp2_fast(A2[0] * Rf[i]); pw[i] = 1.0f; }
+                for (int i = 0; i < U; ++i) {
+                    e0[i] = exp2_fast(A2[0] * Rf[i]);
+                    pw[i] = 1.0f;
+                    if constexpr (ZOH) {
+                        const float t0 = dt[i] * A2[0];
+                        a0[i] = exp2_fast(t0);
+                        pa[i] = 1.0f;
+                        gs[i] = 0.0f;
+                        cz[i] = zoh_coef(a0[i], t0, dt[i], iA[0]) * uu[i];
+                    }
+                }
 #pragma unroll
                 for (int j = 0; j < NBLK; ++j) {
                     if ((act >> j) & 1u) {                // then so is every block before it
@@ -885,7 +900,13 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
 #pragma unroll
                             for (int q = 0; q < BS; ++q) {
                                 pw[i] *= e0[i];
-                                S[BS * j + q] = __builtin_fmaf(pw[i], wv[i] * bb[i][q], S[BS * j + q]);
+                                if constexpr (ZOH) {
+                                    gs[i] += pa[i];
+                                    pa[i] *= a0[i];
+                                    S[BS * j + q] = __builtin_fmaf(pw[i], (cz[i] * gs[i]) * bb[i][q], S[BS * j + q]);
+                                } else {
+                                    S[BS * j + q] = __builtin_fmaf(pw[i], wv[i] * bb[i][q], S[BS * j + q]);
+                                }
                             }
                         }
                         if (!__any(A2blk[j] * (float)Rsum > cut)) act &= ~(1u << j);
