@@ -90,11 +90,16 @@ __device__ __forceinline__ float zoh_coef(float a, float t, float dt, float iA) 
 // initialisation of ozercemkelahmet.com "Mamba", "A minimal selective scan in PyTorch",
 // and the benchmark workloads): then exp(Delta A[d, n]) = exp(Delta A[d, 0])^(n+1), so
 // one exponential and N - 1 multiplies give every state's decay. a_n carries about
-// n + 1 roundings of a_0 plus n of its own, the same order as the error an
-// exponential of the (n + 1)-fold argument makes over the state's (n + 1)-fold shorter
-// memory. The kernels that take it are launched twice, with POW = false and true;
-// each workgroup votes on the identity over its channels and runs in exactly one of
-// the two launches (the other returns at once).
+// n + 1 roundings of a_0 plus n of its own, so state n's accumulated rounding is
+// about (n + 1) eps min(M_n, T) for a memory of M_n = 1 / |A_n Delta| tokens over a
+// run of T: at most eps / |A_0 Delta|, the bound of state 0 on either path, but up to
+// N times the exponentials' own error where the memory outlasts the run (small
+// |A_0 Delta| over short sequences). So the identity must hold with A[d, 0] = 0 (no
+// decay, the chain is exact) or A[d, 0] <= -1/2 (memories of at most 2 / Delta
+// tokens); other channels take the general decays. The kernels that take it are
+// launched twice, with POW = false and true; each workgroup votes on the identity over
+// its channels and runs in exactly one of the two launches (the other returns at
+// once).
 constexpr int kPowMinN = 8;              // below this the saved exponentials do not pay for a second launch
 constexpr int kPowLanes = 4;             // interleaved multiply chains of the scan's per-token decays
 
@@ -110,12 +115,13 @@ __device__ __forceinline__ void pow_chain(float a0, float* a) {
 }
 
 // true on this lane when A[d, n] == (n + 1) * A[d, 0] holds exactly in fp32 for every n
-// (its own loads, not merged with the kernel's later loads of A, so that these raw
-// values are not kept live)
+// and A[d, 0] is 0 or at most -1/2 (its own loads, not merged with the kernel's later
+// loads of A, so that these raw values are not kept live)
+constexpr float kPowMaxA0 = -0.5f;
 template <int N>
 __device__ __forceinline__ bool pow_structured(const float* Arow) {
     const float a0 = __builtin_nontemporal_load(Arow);
-    bool ok = true;
+    bool ok = a0 == 0.0f || a0 <= kPowMaxA0;
 #pragma unroll
     for (int n = 1; n < N; ++n) ok = ok && (__builtin_nontemporal_load(Arow + n) == (float)(n + 1) * a0);
     return ok;

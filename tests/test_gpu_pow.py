@@ -5,7 +5,10 @@ exp(Delta A[d, 0])^(n+1), one exponential and a chain of multiplies; otherwise t
 general decays exp(Delta A[d, n]) run. Both against the fp64 oracle, for d_state 8,
 16 and 64 (4 never takes the fast path), fp32 and bf16 I/O, unchunked and chunked
 shapes, workgroups of either kind side by side, and the forward recompute of the
-backward and the reversed pass of the bidirectional scan. The error of the final
+backward and the reversed pass of the bidirectional scan. Under the zero-order hold the
+power path also forms every write coefficient (exp(Delta A_n) - 1) / A_n from the first
+one and the geometric sum 1 + a_0 + ... + a_0^n. The path is taken only where A[d, 0] is
+0 or at most -1/2; channels with A[d, 0] = -1e-3, 0 and +1e-4 check that gate. The error of the final
 state is reported per state index n, where the chain's rounding would grow with n."""
 import numpy as np
 import pytest
@@ -35,7 +38,7 @@ def _break_identity(A, rows):
     return A
 
 
-def _per_state_errors(ss, inp, io, label, dsel=None):
+def _per_state_errors(ss, inp, io, label, dsel=None, zoh=False):
     """One forward with initial states; y and the final state against the oracle, the
     state's error per state index n."""
     Bsz, L, Dn = inp["x"].shape
@@ -44,9 +47,9 @@ def _per_state_errors(ss, inp, io, label, dsel=None):
     g = to_dev(inp, io)
     hs = torch.from_numpy(st["ssm_state"]).cuda()
     cs = torch.from_numpy(st["conv_state"]).cuda()
-    y = gpu_fwd(ss, g, hs, cs)
+    y = gpu_fwd(ss, g, hs, cs, zoh=zoh)
     torch.cuda.synchronize()
-    yr, hr, cr = oracle_fwd(inp, st["ssm_state"], st["conv_state"], dsel=dsel)
+    yr, hr, cr = oracle_fwd(inp, st["ssm_state"], st["conv_state"], dsel=dsel, zoh=zoh)
     yg = host(y) if dsel is None else host(y)[:, :, dsel]
     hg = host(hs) if dsel is None else host(hs)[:, dsel]
     ey = maxrel(yg, yr)
@@ -133,3 +136,56 @@ def test_power_and_general_agree_closely(ss):
     e = maxrel(host(y_pow), host(y_gen))
     print(f"power vs general y maxrel {e:.2e}", flush=True)
     assert e <= TOL["f32"]
+
+
+def _special_power_A(Dn, N):
+    """A[d, n] = (n + 1) A[d, 0] exactly in fp32 on every channel, with A[d, 0] = -1 except
+    on some channels of the first three workgroups (256 channels each): 0 on channels
+    0, 37, .. of the first (no decay, an exact chain: that workgroup keeps the power path;
+    for the zero-order hold the coefficient is Delta), -1e-3 on channels of the second (a
+    memory far longer than the sequence, where the chain's rounding would grow with n: the
+    workgroup must take the general decays) and +1e-4 on channels of the third (a growing
+    state, general decays)."""
+    a0 = np.full(Dn, -1.0, dtype=np.float32)
+    a0[np.arange(0, 256, 37)] = np.float32(0.0)
+    a0[256 + np.arange(3, 256, 17)] = np.float32(-1e-3)
+    a0[512 + np.arange(5, 256, 41)] = np.float32(1e-4)
+    k = np.arange(1, N + 1, dtype=np.float32)
+    A = (k[None, :] * a0[:, None]).astype(np.float32)
+    assert np.array_equal(A[:, 1:], np.float32(k[1:])[None, :] * A[:, :1])
+    return A, np.flatnonzero(a0 != -1.0)
+
+
+@pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
+@pytest.mark.parametrize("N", [8, 16, 64])
+@pytest.mark.parametrize("shape", list(SHAPES), ids=str)
+@pytest.mark.parametrize("kind", ["power", "general", "mixed"])
+def test_power_path_special_channels(ss, kind, shape, N, zoh):
+    """fp32 I/O, both write terms: workgroups with channels of A[d, 0] = 0, -1e-3 and +1e-4
+    beside the usual -1 (see _special_power_A); "mixed" also breaks the identity on a fourth
+    workgroup. The zero-order hold's power path forms every write coefficient from the
+    first one and the geometric sum 1 + a_0 + ... + a_0^n (main pass and, chunked,
+    aggregate pass). Without the gate on A[d, 0], the -1e-3 channels at d_state 64 on the
+    short shape were 3.5e-4 from the oracle on the power path."""
+    Bsz, L, Dn = SHAPES[shape]
+    spec = W.ScanSpec("spow", Bsz, L, Dn, N, io_dtype="f32", delta_mode="direct", seed=700 + N)
+    inp = W.gen_scan_inputs(spec)
+    inp["A"], special = _special_power_A(Dn, N)
+    if kind == "general":
+        inp["A"] = _break_identity(inp["A"], slice(None))
+    elif kind == "mixed":
+        inp["A"] = _break_identity(inp["A"], np.r_[768:1024])
+    dsel = np.unique(np.r_[[0, 255, 256, 511, 512, Dn - 1], special])
+    _per_state_errors(ss, inp, "f32", f"{'zoh' if zoh else 'euler'} {kind} {shape} N{N}", dsel=dsel, zoh=zoh)
+
+
+def test_zoh_power_path_long_workload(ss):
+    """The long workload (B1 L131072 D2048 N16 bf16, 64 chunks) with the zero-order hold on
+    the power path and on the general path, sampled channels."""
+    spec = W.WORKLOADS["long"]
+    inp = W.gen_scan_inputs(spec)
+    dsel = np.array([0, 1, 63, 64, 255, 256, 1000, 1023, 1024, 2047])
+    per_n = _per_state_errors(ss, inp, "bf16", "zoh long power", dsel=dsel, zoh=True)
+    inp["A"] = _break_identity(inp["A"], slice(None))
+    per_g = _per_state_errors(ss, inp, "bf16", "zoh long general", dsel=dsel, zoh=True)
+    assert max(per_n) <= 10 * max(max(per_g), 1e-6), (per_n, per_g)
