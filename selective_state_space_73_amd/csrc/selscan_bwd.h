@@ -390,11 +390,13 @@ k_bagg(const T* __restrict__ delta, const float* __restrict__ delta_bias, const 
 // there as Delta^2 (1/2 + x/3 + x^2/8 + x^3/30), x = Delta A (the series of
 // (x e^x - e^x + 1) / x^2; truncation below 2e-6 for |x| < 0.1).
 //
-// POW (Euler, from kPowMinN states): the power fast path of the forward kernels, taken
-// by the workgroups whose channels all have A[d, n] = (n+1) A[d, 0] with A[d, 0] = 0 or
+// POW (from kPowMinN states): the power fast path of the forward kernels, taken by the
+// workgroups whose channels all have A[d, n] = (n+1) A[d, 0] with A[d, 0] = 0 or
 // <= -1/2 (launched twice, each workgroup running in one launch by its vote): the
 // recompute's decays are one exponential per token and a multiply chain across the
-// state blocks.
+// state blocks; under the zero-order hold the write coefficients are
+// [(a_0 - 1) / A_0] G_n / (n+1) with the geometric sum G_n = 1 + a_0 + ... + a_0^n carried
+// beside the chain, kept from the recompute for the sweep.
 template <typename T, int N, bool CONV, bool GATE, bool ZOH = false, bool POW = false>
 __global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(N <= 16 && !ZOH ? 2 : 1)))
 k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
@@ -409,7 +411,7 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
       float* __restrict__ ws_dxh,        // [B, nchunks, D, 3] dx of a chunk's last 3 tokens without the next chunk's share
       float* __restrict__ ws_dc3,        // [B, nchunks, D, 3] conv-input gradient of a chunk's first 3 tokens
       float* __restrict__ dstate_init, float* __restrict__ dconv_init, BwdArgs ba) {
-    static_assert(!POW || (N >= kPowMinN && !ZOH), "the sweep's power path is Euler only");
+    static_assert(!POW || N >= kPowMinN, "power path only from kPowMinN states");
     constexpr int S = kCkptEvery;
     constexpr int V = 2 * N;                      // per token: dB partials, then dC partials
     constexpr int NBK = N < 4 ? N : 4;            // states recomputed and swept together
@@ -418,9 +420,7 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
     const int d_raw = blockIdx.x * kScanThreads + tid;
     const float livef = d_raw < D ? 1.0f : 0.0f;
     const int d = d_raw < D ? d_raw : D - 1;
-    if constexpr (N >= kPowMinN && !ZOH) {
-        if (pow_skip<N, POW>(A + (int64_t)d * N)) return;   // the workgroup runs in the other launch
-    }
+    if (pow_skip<N, POW>(A + (int64_t)d * N)) return;       // the workgroup runs in the other launch
     const unsigned du = (unsigned)d;
     const int c = blockIdx.y, b = blockIdx.z;
     const int nC = ba.nchunks;
@@ -585,9 +585,20 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
             // power path: each token's base decay exp(Delta A[d, 0]) and the running power
             // a_0^(j0) carried from one state block to the next
             float pe[POW ? S : 1], pr[POW ? S : 1];
+            constexpr int SZ = POW && ZOH ? S : 1;
+            float pa[SZ], gsum[SZ], cz[SZ];              // zero-order hold: a_0^n, G_n, (a_0 - 1) / A_0
             if constexpr (POW) {
 #pragma unroll
-                for (int i = 0; i < S; ++i) { pe[i] = exp2_fast(dtv[i] * A2[0]); pr[i] = 1.0f; }
+                for (int i = 0; i < S; ++i) {
+                    const float t0 = dtv[i] * A2[0];
+                    pe[i] = exp2_fast(t0);
+                    pr[i] = 1.0f;
+                    if constexpr (ZOH) {
+                        pa[i] = 1.0f;
+                        gsum[i] = 0.0f;
+                        cz[i] = zoh_coef(pe[i], t0, dtv[i], iA[0]);
+                    }
+                }
             }
 #pragma unroll
             for (int i = 0; i < (ZOH ? S : 1); ++i) sgaB[i] = 0.0f;
@@ -613,6 +624,7 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                     }
                 }
                 float av[S][NBK];
+                float ww[SZ][POW && ZOH ? NBK : 1];         // power path: the coefficients, kept for the sweep
 #pragma unroll
                 for (int i = 0; i < S; ++i) {
                     const float* brow = tile + (int64_t)(s + i) * V + j0;
@@ -627,9 +639,17 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                             av[i][n] = exp2_fast(tn);
                         }
                         if constexpr (ZOH) {
-                            // the write coefficient is recomputed in the sweep below rather
-                            // than kept (registers)
-                            const float w = zoh_coef(av[i][n], tn, dtv[i], iA[j0 + n]);
+                            // general path: the write coefficient is recomputed in the sweep
+                            // below rather than kept (registers)
+                            float w;
+                            if constexpr (POW) {
+                                gsum[i] += pa[i];
+                                pa[i] *= pe[i];
+                                w = (cz[i] * gsum[i]) * (1.0f / (float)(j0 + n + 1));
+                                ww[i][n] = w;
+                            } else {
+                                w = zoh_coef(av[i][n], tn, dtv[i], iA[j0 + n]);
+                            }
                             hs[i + 1][n] = __builtin_fmaf(av[i][n], hs[i][n], w * (uv[i] * brow[n]));
                         } else {
                             hs[i + 1][n] = __builtin_fmaf(av[i][n], hs[i][n], wv * brow[n]);
@@ -657,7 +677,9 @@ k_bwd(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
                         sa = __builtin_fmaf(A2[m], gq, sa);
                         if constexpr (ZOH) {
                             const float tn = dtv[i] * A2[m];
-                            const float w = zoh_coef(av[i][n], tn, dtv[i], iA[m]);
+                            float w;
+                            if constexpr (POW) w = ww[i][n];
+                            else w = zoh_coef(av[i][n], tn, dtv[i], iA[m]);
                             const float gB = g * brow[n];
                             vals[n] = g * w * um;
                             gb = __builtin_fmaf(gB, w, gb);
@@ -865,8 +887,7 @@ static hipError_t launch_bwd_t(const LaunchBwd& q) {
             hipLaunchKernelGGL((k_bagg<T, N, GATE, true>), dim3(gx, nC - 1, (unsigned)p.batch), dim3(kScanThreads),
                                0, st, dl, p.delta_bias, p.A, Cm, z, dy, q.ws_Q, q.ws_qsdt, ba);
     }
-    // the sweep (general and, Euler from kPowMinN states, power launches; the events
-    // bracket both)
+    // the sweep (general and, from kPowMinN states, power launches; the events bracket both)
     auto sweep = [&](auto pow_tag, hipEvent_t e0, hipEvent_t e1) {
         constexpr bool P = decltype(pow_tag)::value;
         hipExtLaunchKernelGGL((k_bwd<T, N, CONV, GATE, ZOH, P>), dim3(gx, nC, (unsigned)p.batch), dim3(kScanThreads),
@@ -876,7 +897,7 @@ static hipError_t launch_bwd_t(const LaunchBwd& q) {
                               q.ws_dbc, q.ws_par, q.ws_dxh, q.ws_dc3, q.dstate_init, q.dconv_init, ba);
     };
     const hipEvent_t ev0 = static_cast<hipEvent_t>(p.ev_main[0]), ev1 = static_cast<hipEvent_t>(p.ev_main[1]);
-    if constexpr (N >= kPowMinN && !ZOH) {
+    if constexpr (N >= kPowMinN) {
         sweep(Tag<false>{}, ev0, nullptr);
         sweep(Tag<true>{}, nullptr, ev1);
     } else {

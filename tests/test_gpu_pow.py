@@ -101,14 +101,20 @@ def test_power_path_long_workload_per_state(ss):
     assert max(per_n) <= 10 * max(max(per_g), 1e-6), (per_n, per_g)
 
 
-@pytest.mark.parametrize("kind", ["power", "general"])
-def test_backward_recompute_both_paths(ss, kind):
-    """The backward's forward recompute (checkpoint mode of the scan) on either path."""
-    spec = W.ScanSpec("powbwd", 2, 8192, 512, 16, io_dtype="f32", delta_mode="direct", seed=611)
+@pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
+@pytest.mark.parametrize("kind", ["power", "general", "special"])
+def test_backward_both_paths(ss, kind, zoh):
+    """The backward on either path: the checkpoint pass, the sweep (whose power launch takes
+    its recompute's decays, and under the zero-order hold its coefficients, from the chain
+    and the geometric sum) and the adjoint aggregates. "special": the channels of
+    _special_power_A (A[d, 0] = 0 keeps the power path; -1e-3 and +1e-4 take the general one)."""
+    spec = W.ScanSpec("powbwd", 2, 8192, 1024, 16, io_dtype="f32", delta_mode="direct", seed=611)
     inp = W.gen_scan_inputs(spec)
     if kind == "general":
         inp["A"] = _break_identity(inp["A"], slice(None))
-    check_bwd(ss, inp, "f32", label=f"bwd {kind}")
+    elif kind == "special":
+        inp["A"], _ = _special_power_A(1024, 16)
+    check_bwd(ss, inp, "f32", label=f"bwd {kind} {'zoh' if zoh else 'euler'}", zoh=zoh)
 
 
 @pytest.mark.parametrize("kind", ["power", "general", "mixed"])
