@@ -53,6 +53,14 @@
  * (per calling thread). Faults inside a kernel surface at the caller's next
  * synchronisation. NaN/Inf inputs propagate and are not checked. Results are
  * deterministic for a given shape (no floating-point atomics).
+ *
+ * Decays: a group of 256 channels whose A rows all satisfy A[d,n] == (n+1) * A[d,0]
+ * exactly (fp32), with A[d,0] == 0 or A[d,0] <= -1/2 (the A_log = log(1..N)
+ * initialisation of ozercemkelahmet.com "Mamba", "A minimal selective scan in
+ * PyTorch", and its scalings), is computed with one exponential per token and a
+ * multiply chain, exp(Dt A[d,n]) = exp(Dt A[d,0])^(n+1) (and, for SS_ZOH, W from the
+ * geometric sum of that chain); other groups take one exponential per state. The two
+ * differ by rounding only; the choice is made on the device, per call.
  */
 #ifndef SELSCAN_H
 #define SELSCAN_H
