@@ -114,7 +114,9 @@ Layout layout(const ss_dims& d, bool fwd = false) {
     const size_t B = (size_t)d.batch, D = (size_t)d.d_inner, N = (size_t)d.d_state;
     size_t off = 0;
     if (l.nchunks > 1) {
-        const size_t na = (size_t)(l.nchunks - 1);
+        // a slot per chunk: the plain forward writes every chunk's end state and step sum,
+        // the aggregate pass (bidirectional and backward) those of all but the last
+        const size_t na = (size_t)l.nchunks;
         l.off_S = off;   off = align256(off + B * na * D * N * sizeof(float));
         l.off_sdt = off; off = align256(off + B * na * D * sizeof(float));
         l.off_h0 = off;  off = align256(off + B * D * N * sizeof(float));

@@ -224,11 +224,11 @@ constexpr int kCkptEvery = 4;
 // N <= 16, measured faster than the compiler's own choice (two waves at ~240
 // VGPRs) because more resident waves hide the long per-token dependency chains;
 // larger N needs the registers for the state and keeps one-wave-per-SIMD limits.
-// (Without the conv the schedule under that cap spills, so it is left free; the
+// (Without the conv the schedule under those caps spills, so it is left free; the
 // zero-order hold's longer per-state chain with N more registers of 1/A, and the
 // reversed pass's extra prefetched y, are held to two waves.)
 template <int N, bool CONV, bool ZOH, bool CK, bool REV> constexpr int scan_waves_per_eu() {
-    return N > 16 ? 1 : (ZOH || CK || REV) ? 2 : CONV ? 3 : 1;
+    return (N > 16 || !CONV) ? 1 : (ZOH || CK || REV) ? 2 : 3;
 }
 
 // Zero-order hold: the write coefficient (exp(Delta A) - 1) / A comes from the decay
@@ -247,8 +247,9 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
        const T* __restrict__ z, T* __restrict__ y,
        float* __restrict__ ssm_state,        // IN (nchunks == 1) and OUT (last chunk)
        float* __restrict__ conv_state,       // IN (nchunks == 1) and OUT (last chunk)
-       const float* __restrict__ ws_S,       // [B, nchunks-1, D, N] chunk end states (chunk 0 includes h0)
-       const float* __restrict__ ws_sdt,     // [B, nchunks-1, D] summed step sizes
+       float* __restrict__ ws_S,             // [B, nchunks-1, D, N] chunk end states (chunk 0 includes h0);
+                                             // written by the plain forward as [B, nchunks, D, N]
+       float* __restrict__ ws_sdt,           // [B, nchunks-1, D] summed step sizes (plain: written, [B, nchunks, D])
        const float* __restrict__ ws_h0,      // [B, D, N] copy of the initial state (nchunks > 1)
        const float* __restrict__ ws_c0,      // [B, D, K-1] copy of the initial conv history (nchunks > 1)
        float* __restrict__ ckpt,             // CK: [B, nck, N/4, D, 4] state checkpoints
@@ -256,6 +257,8 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
        ScanArgs sa) {
     static_assert(!(CK && GATE), "checkpoint mode has no gate");
     static_assert(!(CK && (REV || PART)) && !(REV && PART), "one mode per pass");
+    // the plain forward: several chunks run from zero and k_corr adds their carries
+    constexpr bool PLAIN = !CK && !REV && !PART;
     static_assert(!POW || N >= kPowMinN, "power path only from kPowMinN states");
     const int D = sa.D;
     const int d_raw = blockIdx.x * kScanThreads + threadIdx.x;
@@ -301,11 +304,16 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     float h[N];
     const int64_t bd = (int64_t)b * D + d;
     if (c == 0) {
-        // with several chunks, read the copy the aggregate pass made, because the
-        // last chunk overwrites ssm_state
-        const float* src = REV ? nullptr : (ssm_state && multi) ? ws_h0 : ssm_state;
+        // with several chunks, the checkpoint and bidirectional passes read the copy the
+        // aggregate pass made, because their last chunk overwrites ssm_state (the plain
+        // forward leaves it to k_corr)
+        const float* src = REV ? nullptr : (ssm_state && multi && !PLAIN) ? ws_h0 : ssm_state;
 #pragma unroll
         for (int n = 0; n < N; ++n) h[n] = src ? src[bd * N + n] : 0.0f;
+    } else if (PLAIN) {
+        // local run from a zero state; k_corr adds what the carry-in contributes
+#pragma unroll
+        for (int n = 0; n < N; ++n) h[n] = 0.0f;
     } else {
         // fold the aggregates of chunks 0..c-1 into the carry-in
 #pragma unroll
@@ -330,7 +338,7 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     // made, because the last chunk overwrites conv_state)
     float x3 = 0.f, x2 = 0.f, x1 = 0.f;
     if (CONV) {
-        const float* hsrc = (conv_state && !REV) ? (multi ? ws_c0 : conv_state) : nullptr;
+        const float* hsrc = (conv_state && !REV) ? ((multi && !PLAIN) ? ws_c0 : conv_state) : nullptr;
         float xh[3];
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
@@ -352,6 +360,8 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
     constexpr int NB = CK ? N : 2 * N;                  // staged values per token (B row, C row)
     __shared__ float sbc[2][R][NB];
     const int tid = threadIdx.x;
+    __shared__ double srsum[PLAIN ? kScanThreads : 1];
+    if constexpr (PLAIN) srsum[tid] = 0.0;
     const int nrows = (int)(t1 - t0);
     const unsigned voff = du * (unsigned)sizeof(T);               // lane byte offset within a token row
     const unsigned rowb = (unsigned)D * (unsigned)sizeof(T);      // bytes per token row
@@ -505,14 +515,20 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
 #pragma unroll
         for (int k = 0; k < N / 4; ++k) dst[(int64_t)k * D] = vf4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
     };
+    // PLAIN: the chunk's summed step size, for its total decay exp(A * sum Delta) in
+    // k_corr's fold: each group's fp32 sum is added (ds_add_f64, no return value) to an
+    // fp64 total in the lane's own LDS slot, because a total kept in registers costs the
+    // main pass a register spill at its three-waves-per-SIMD cap
     auto token = [&](T xraw, T draw, T zraw, float yprev, const float* bct, int r) {
         const Pro p = prologue(xraw, draw, zraw, yprev);
+        if constexpr (PLAIN) atomicAdd(&srsum[tid], (double)p.dt);
         update(p, bct, r);
     };
     auto group = [&](const T* gx, const T* gd, const T* gz, const float* gy, const float* tile_rows, int r0) {
         Pro p[U];
 #pragma unroll
         for (int i = 0; i < U; ++i) p[i] = prologue(gx[i], gd[i], gz[i], gy[i]);
+        if constexpr (PLAIN) atomicAdd(&srsum[tid], (double)((p[0].dt + p[1].dt) + (p[2].dt + p[3].dt)));
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             update(p[i], tile_rows + i * NB, r0 + i);
@@ -574,13 +590,25 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         buf ^= 1;
     }
 
-    if (!CK && !REV && !PART && c == sa.nchunks - 1) {
-        if (ssm_state) {
+    if constexpr (PLAIN) {
+        if (!multi) {
+            if (ssm_state) {
 #pragma unroll
-            for (int n = 0; n < N; ++n) ssm_state[bd * N + n] = h[n];
-        }
-        if (CONV && conv_state) {
-            conv_state[bd * 3 + 0] = x3; conv_state[bd * 3 + 1] = x2; conv_state[bd * 3 + 2] = x1;
+                for (int n = 0; n < N; ++n) ssm_state[bd * N + n] = h[n];
+            }
+            if (CONV && conv_state) {
+                // a uniform base and a 32-bit lane offset (d < 2^26): no 64-bit offset kept
+                // live across the token loop from the history read at the chunk start
+                const Buf<float> cs(conv_state + (int64_t)b * D * 3);
+                cs.st(x3, du * 12u, 0u); cs.st(x2, du * 12u, 4u); cs.st(x1, du * 12u, 8u);
+            }
+        } else {
+            // the chunk's end state from its own start state and its summed step size
+            // ([B, nchunks, D, N] and [B, nchunks, D]); k_corr writes the final states
+            const int64_t ai = ((int64_t)b * sa.nchunks + c) * D + d;
+#pragma unroll
+            for (int n = 0; n < N; ++n) ws_S[ai * N + n] = h[n];
+            ws_sdt[ai] = (float)srsum[tid];
         }
     }
 }
@@ -1071,6 +1099,296 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
 }
 
 // ---------------------------------------------------------------------------
+// Carry correction of the plain forward over several chunks. The main pass runs
+// every chunk but the first from a zero state and writes each chunk's end state
+// S_c and summed step size; k_fold (below) turns them into the carry-ins
+//     H_1 = S_0,   H_{c+1} = exp(A_n * sum Delta_c) H_c + S_c.
+// By linearity of the recurrence the true state at chunk-relative row r of chunk
+// c >= 1 is the local one plus E_r[n] H_c[n], E_r[n] = exp(A_n R_r) with R_r the
+// step sizes of rows 0..r summed (the decay alone carries the state; the write
+// term, Euler or zero-order hold, does not enter). So the output misses
+//     sum_n C_r[n] E_r[n] H_c[n]   (times SiLU(z_r) with the gate),
+// which k_corr adds to y. Where A_n <= 0, E only shrinks as r grows: a state index
+// is dropped (wave-uniformly, in blocks as in k_agg) once exp(A_n R) <= 2^-kCorrCutLog2
+// on every lane whose carry is not exactly zero, and that leaves every later state of
+// the chunk off by at most 2^-kCorrCutLog2 |H_c[n]| (below the rounding already in
+// H_c). A workgroup stops once its waves have dropped every index, so the pass reads
+// delta, z and y only over each chunk's head; channels whose states barely decay
+// (A_n > 0 or tiny steps) keep theirs to the chunk end.
+// POW: decays from exp(A_0 R)^(n+1); the per-row sum is then a polynomial in
+// exp(A_0 R), evaluated by Horner's rule over the states up to the highest one still
+// active (the drop order follows n, so dropped states below it add zero terms only
+// where their carry is exactly zero).
+constexpr int kCorrCutLog2 = 28;
+constexpr int kCorrDepth = 8;                 // prefetched 4-row groups of delta, z and y
+
+// The fold of the plain forward's chunk end states, one thread per (batch row,
+// channel, state): H_1 = S_0, H_{c+1} = exp(A sum Delta_c) H_c + S_c, each carry H_c
+// written over slot c-1 of the end states (already read by then), the final state
+// exp(A sum Delta_last) H_last + S_last to ssm_state and the conv history (the last
+// three inputs) to conv_state. Loads are issued kFoldBatch chunks at a time, so a
+// thread waits on about nchunks / kFoldBatch memory round trips rather than nchunks.
+constexpr int kFoldBatch = 16;
+template <typename T, int N>
+__global__ void __launch_bounds__(kScanThreads)
+k_fold(const T* __restrict__ x, const float* __restrict__ A, float* __restrict__ ssm_state,
+       float* __restrict__ conv_state, float* __restrict__ ws_S, const float* __restrict__ ws_sdt,
+       int64_t batch, ScanArgs sa) {
+    const int64_t D = sa.D;
+    const int64_t i = (int64_t)blockIdx.x * kScanThreads + threadIdx.x;   // (b, d, n)
+    if (i >= batch * D * N) return;                 // no barriers in this kernel
+    const int n = (int)(i % N);
+    const int64_t bd = i / N;
+    const int64_t b = bd / D, d = bd % D;
+    const float av = A[d * N + n];
+    const float a2 = __builtin_fabsf(av) < kZohZeroA ? 0.0f : av * kLog2e;
+    const int nc = sa.nchunks;
+    float* Sb = ws_S + (b * nc * D + d) * N + n;     // slot c at Sb[c * D * N]
+    const float* tb = ws_sdt + b * nc * D + d;       // slot c at tb[c * D]
+    float H = 0.0f;
+    for (int c0 = 0; c0 < nc; c0 += kFoldBatch) {
+        float sv[kFoldBatch], tv[kFoldBatch];
+#pragma unroll
+        for (int k = 0; k < kFoldBatch; ++k) {
+            const int c = c0 + k < nc ? c0 + k : nc - 1;
+            sv[k] = Sb[(int64_t)c * D * N];
+            tv[k] = tb[(int64_t)c * D];
+        }
+#pragma unroll
+        for (int k = 0; k < kFoldBatch; ++k) {
+            const int c = c0 + k;
+            if (c < nc) {
+                if (c > 0) Sb[(int64_t)(c - 1) * D * N] = H;     // carry into chunk c
+                H = __builtin_fmaf(exp2_fast(a2 * tv[k]), H, sv[k]);
+            }
+        }
+    }
+    if (ssm_state) ssm_state[bd * N + n] = H;
+    if (conv_state && n < 3) {
+        // the chunking keeps the last chunk at least one tile long, so L > 3
+        conv_state[bd * 3 + n] = IO<T>::cvt(x[(b * sa.L + sa.L - 3 + n) * D + d]);
+    }
+}
+
+template <typename T, int N, bool GATE, bool POW>
+__global__ void __launch_bounds__(kScanThreads)
+k_corr(const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
+       const T* __restrict__ Cm, const T* __restrict__ z, T* __restrict__ y, const float* __restrict__ ws_H,
+       ScanArgs sa) {
+    const int D = sa.D;
+    const int d_raw = blockIdx.x * kScanThreads + threadIdx.x;
+    const int d = d_raw < D ? d_raw : D - 1;      // clamped lanes repeat the last channel
+    // y is read, corrected and written back, so only the channel's own lane may store
+    // (the clamped lanes of the main pass write identical values; here each would add
+    // its correction again)
+    const bool owner = d_raw < D;
+    if (pow_skip<N, POW>(A + (int64_t)d * N)) return;   // the workgroup runs in the other launch
+    const unsigned du = (unsigned)d;
+    const int nc = sa.nchunks;
+    const int c = blockIdx.y + 1;                 // chunks 1 .. nchunks-1
+    const int b = blockIdx.z;
+    const int64_t t0 = (int64_t)c * sa.chunk_len;
+    const int64_t t1 = (t0 + sa.chunk_len < sa.L) ? t0 + sa.chunk_len : sa.L;
+
+    float A2[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const float av = A[(int64_t)d * N + n];
+        A2[n] = __builtin_fabsf(av) < kZohZeroA ? 0.0f : av * kLog2e;   // decays by exactly 1
+    }
+    const float dbias = delta_bias ? delta_bias[d] : 0.0f;
+    // carry-in of chunk c, written by k_fold over slot c-1 of the end states
+    float H[N];
+    const float* hc = ws_H + ((((int64_t)b * nc + (c - 1)) * D) + d) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) H[n] = hc[n];
+
+    // state blocks and the drop rule
+    constexpr int BS = N <= 32 ? 2 : N / 16;
+    constexpr int NBLK = N / BS;
+    static_assert(NBLK <= 32, "one mask bit per block");
+    float A2blk[NBLK];
+    uint32_t live = 0;                            // blocks with a nonzero carry on this lane
+#pragma unroll
+    for (int j = 0; j < NBLK; ++j) {
+        float m = A2[BS * j];
+        bool nz = H[BS * j] != 0.0f;
+#pragma unroll
+        for (int q = 1; q < BS; ++q) { m = __builtin_fmaxf(m, A2[BS * j + q]); nz = nz || H[BS * j + q] != 0.0f; }
+        A2blk[j] = m;
+        live |= nz ? (1u << j) : 0u;
+    }
+    const float cut = -(float)kCorrCutLog2;
+    uint32_t act = 0;
+#pragma unroll
+    for (int j = 0; j < NBLK; ++j) act |= __any((live >> j) & 1u) ? (1u << j) : 0u;
+
+    // workgroup-uniform exit: one flag word per wave, double-buffered by tile parity so
+    // that a wave writing the next tile's word never races a wave still reading this one
+    constexpr int NW = kScanThreads / 64;
+    __shared__ uint32_t wact[2][NW];
+    const int wave = threadIdx.x >> 6;
+    auto all_done = [&](int parity) -> bool {
+        if ((threadIdx.x & 63) == 0) wact[parity][wave] = act;
+        __syncthreads();
+        uint32_t any = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) any |= wact[parity][w];
+        return any == 0;
+    };
+    if (all_done(1)) return;
+
+    // C tiles through LDS (as k_scan's B/C), delta, z and y one U-row group ahead
+    constexpr int U = 4;
+    constexpr int R = kScanTile;
+    static_assert(R % (2 * U) == 0, "a tile holds whole pairs of groups");
+    __shared__ float sC[2][R][N];
+    const int tid = threadIdx.x;
+    const int nrows = (int)(t1 - t0);
+    const unsigned voff = du * (unsigned)sizeof(T);
+    const unsigned rowb = (unsigned)D * (unsigned)sizeof(T);
+    const int64_t rowbase = (int64_t)b * sa.L + t0;
+    const T* db = delta + rowbase * D;
+    const T* zb = GATE ? z + rowbase * D : nullptr;
+    T* yb = y + rowbase * D;
+    const T* Cb = Cm + rowbase * N;
+    constexpr int TILE_ELEMS = R * N;
+    constexpr int PER_THREAD = (TILE_ELEMS + kScanThreads - 1) / kScanThreads;
+    T tc[PER_THREAD];
+    auto tile_fetch = [&](int r0) {
+        const int rlast = nrows - 1 - r0;
+        const T* Ct = Cb + (int64_t)r0 * N;
+#pragma unroll
+        for (int k = 0; k < PER_THREAD; ++k) {
+            const int e0 = tid + k * kScanThreads;
+            const int e = e0 < TILE_ELEMS ? e0 : TILE_ELEMS - 1;
+            const int r = e / N < rlast ? e / N : rlast;
+            tc[k] = Ct[r * N + e % N];
+        }
+    };
+    auto tile_store = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < PER_THREAD; ++k) {
+            const int e = tid + k * kScanThreads;
+            if (e < TILE_ELEMS) sC[buf][e / N][e % N] = IO<T>::cvt(tc[k]);
+        }
+    };
+    // delta, z and y of kCorrDepth groups in flight: the grid gives a SIMD about two
+    // waves and a group's work is short, so one group ahead would leave each wave
+    // waiting on HBM latency
+    T gd[kCorrDepth][U], gz[kCorrDepth][U], gy[kCorrDepth][U];
+    auto load_group = [&](int r0, T* gd, T* gz, T* gy) {
+        const int rb = r0 < nrows ? r0 : nrows - 1;
+        const int64_t off = (int64_t)rb * D;
+        const Buf<T> bdl(db + off), by(yb + off);
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int r = (r0 + i < nrows) ? r0 + i : nrows - 1;
+            const unsigned so = (unsigned)(r - rb) * rowb;
+            gd[i] = bdl.ld(voff, so);
+            if (GATE) gz[i] = Buf<T>(zb + off).ld(voff, so);
+            gy[i] = by.ld(voff, so);
+        }
+    };
+
+    double rsum = 0.0;                            // step sizes of the rows swept so far
+    auto group = [&](const T* gd, const T* gz, const T* gy, const float* crow, int r0) {
+        float Rr[U], g[U], corr[U];
+        float part = 0.0f;
+        const float rbase = (float)rsum;
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            // rows past the chunk end (the last chunk's final group) add no step
+            const float dt = r0 + i < nrows ? softplus(IO<T>::cvt(gd[i]) + dbias) : 0.0f;
+            part += dt;
+            Rr[i] = rbase + part;                     // R of row r0+i, its own step included
+            g[i] = GATE ? silu(IO<T>::cvt(gz[i])) : 1.0f;
+            corr[i] = 0.0f;
+        }
+        rsum += (double)part;
+        if constexpr (POW) {
+            float e0[U];
+#pragma unroll
+            for (int i = 0; i < U; ++i) e0[i] = exp2_fast(A2[0] * Rr[i]);
+            // Horner from the highest active state down: acc = sum_n C[n] H[n] e0^n, times e0
+#pragma unroll
+            for (int j = NBLK - 1; j >= 0; --j) {
+                if ((act >> j) != 0u) {               // block j is at or below the highest active one
+#pragma unroll
+                    for (int q = BS - 1; q >= 0; --q) {
+                        const int n = BS * j + q;
+#pragma unroll
+                        for (int i = 0; i < U; ++i)
+                            corr[i] = __builtin_fmaf(corr[i], e0[i], crow[i * N + n] * H[n]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < U; ++i) corr[i] *= e0[i];
+        } else {
+#pragma unroll
+            for (int j = 0; j < NBLK; ++j) {
+                if ((act >> j) & 1u) {
+#pragma unroll
+                    for (int q = 0; q < BS; ++q) {
+                        const int n = BS * j + q;
+#pragma unroll
+                        for (int i = 0; i < U; ++i) {
+                            const float e = exp2_fast(A2[n] * Rr[i]);
+                            corr[i] = __builtin_fmaf(crow[i * N + n], H[n] * e, corr[i]);
+                        }
+                    }
+                }
+            }
+        }
+        const int64_t off = (int64_t)r0 * D;
+        const Buf<T> by(yb + off);
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            if (r0 + i < nrows && owner) {
+                const float yv = __builtin_fmaf(corr[i], g[i], IO<T>::cvt(gy[i]));
+                by.st(IO<T>::bits(yv), voff, (unsigned)i * rowb);
+            }
+        }
+        // drop blocks whose decay is below the cut on every lane that carries them
+        const float rl = Rr[U - 1];
+#pragma unroll
+        for (int j = 0; j < NBLK; ++j) {
+            if ((act >> j) & 1u) {
+                if (!__any(((live >> j) & 1u) && A2blk[j] * rl > cut)) act &= ~(1u << j);
+            }
+        }
+    };
+
+    int buf = 0;
+    tile_fetch(0);
+    tile_store(0);
+#pragma unroll
+    for (int q = 0; q < kCorrDepth; ++q) load_group(q * U, gd[q], gz[q], gy[q]);
+    __syncthreads();
+    constexpr int GPT = R / U;                    // groups per tile
+    static_assert(GPT % kCorrDepth == 0, "the in-flight slots cycle within a tile");
+    for (int tt = 0; tt < nrows; tt += R) {
+        const bool more = tt + R < nrows;
+        if (more) tile_fetch(tt + R);
+        const float* tile = &sC[buf][0][0];
+        // group k of the tile sits in slot k % kCorrDepth; once it is done the slot takes
+        // the group kCorrDepth further on (rows past the chunk end are clamped loads)
+#pragma unroll
+        for (int k = 0; k < GPT; ++k) {
+            const int q = k % kCorrDepth;
+            const int r0 = tt + k * U;
+            if (act && r0 < nrows) group(gd[q], gz[q], gy[q], tile + k * U * N, r0);
+            load_group(r0 + kCorrDepth * U, gd[q], gz[q], gy[q]);
+        }
+        if (more) tile_store(buf ^ 1);
+        const int parity = (tt / R) & 1;
+        if (all_done(parity)) return;             // (includes the barrier of the tile swap)
+        buf ^= 1;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Decode step. Four lanes (a quad) per (stream, channel): lane q holds state
 // entries [q*N/4, (q+1)*N/4), so every state load and store of a wave is one
 // contiguous, nontemporal vector access. The conv taps and the readout are
@@ -1552,6 +1870,17 @@ static void launch_k_agg(dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t e
     }
 }
 
+// The carry correction: general and, from kPowMinN states, power launches.
+template <typename T, int N, bool GATE, typename... Args>
+static void launch_k_corr(dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, Args... args) {
+    if constexpr (N >= kPowMinN) {
+        hipExtLaunchKernelGGL((k_corr<T, N, GATE, false>), grid, dim3(kScanThreads), 0, st, ev0, nullptr, 0, args...);
+        hipExtLaunchKernelGGL((k_corr<T, N, GATE, true>), grid, dim3(kScanThreads), 0, st, nullptr, ev1, 0, args...);
+    } else {
+        hipExtLaunchKernelGGL((k_corr<T, N, GATE, false>), grid, dim3(kScanThreads), 0, st, ev0, ev1, 0, args...);
+    }
+}
+
 template <typename T, int N, bool CONV, bool GATE, bool ZOH, bool REV = false, bool PART = false>
 static hipError_t launch_scan_t(const LaunchScan& p) {
     const T* x = static_cast<const T*>(p.x);
@@ -1580,8 +1909,32 @@ static hipError_t launch_scan_t(const LaunchScan& p) {
             return hipGetLastError();
         }
     }
-    // the aggregate pass sweeps whole B tiles of full chunks (no padding rows)
+    // the aggregate and correction passes take whole B/C tiles of full chunks (no padding
+    // rows) before the last chunk
     if (p.nchunks > 1 && (p.chunk_len % kScanTile != 0 || p.chunk_len < kScanTile)) return hipErrorInvalidValue;
+    if constexpr (!REV && !PART) {
+        if (p.nchunks > 1) {
+            // plain forward: every chunk in one pass (all but the first from zero), the
+            // fold of their end states into carries, then the carries added over each
+            // chunk's head
+            launch_k_scan<T, N, CONV, GATE, ZOH, false, false, false>(
+                dim3(gx, p.nchunks, (unsigned)p.batch), st, static_cast<hipEvent_t>(p.ev_main[0]),
+                static_cast<hipEvent_t>(p.ev_main[1]), x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
+                static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip, z, y, p.ssm_state, p.conv_state,
+                p.ws_S, p.ws_sdt, p.ws_h0, p.ws_c0, static_cast<float*>(nullptr), p.ypart, sa);
+            // one thread per (batch row, channel, state): chunking only happens with fewer
+            // than 256 x 256 channels in all, so the grid stays small
+            const int64_t nfold = p.batch * p.D * N;
+            hipExtLaunchKernelGGL((k_fold<T, N>), dim3((unsigned)((nfold + kScanThreads - 1) / kScanThreads)),
+                                  dim3(kScanThreads), 0, st, static_cast<hipEvent_t>(p.ev_agg[0]), nullptr, 0, x,
+                                  p.A, p.ssm_state, CONV ? p.conv_state : static_cast<float*>(nullptr), p.ws_S,
+                                  static_cast<const float*>(p.ws_sdt), p.batch, sa);
+            launch_k_corr<T, N, GATE>(dim3(gx, p.nchunks - 1, (unsigned)p.batch), st, nullptr,
+                                      static_cast<hipEvent_t>(p.ev_agg[1]), dl, p.delta_bias, p.A,
+                                      static_cast<const T*>(p.C), z, y, static_cast<const float*>(p.ws_S), sa);
+            return hipGetLastError();
+        }
+    }
     if (p.nchunks > 1) {
         launch_k_agg<T, N, CONV, ZOH, REV>(dim3(gx, p.nchunks - 1, (unsigned)p.batch), st,
                                            static_cast<hipEvent_t>(p.ev_agg[0]), static_cast<hipEvent_t>(p.ev_agg[1]),

@@ -38,12 +38,13 @@ struct LaunchScan {
     float* ssm_state; float* conv_state;
     // chunking and workspace (scan only)
     int nchunks; int64_t chunk_len;
-    float* ws_S;    // [B, nchunks-1, D, N]
-    float* ws_sdt;  // [B, nchunks-1, D]
+    float* ws_S;    // [B, nchunks, D, N] chunk end states (the aggregate pass: slots of all but the last)
+    float* ws_sdt;  // [B, nchunks, D] summed step sizes (likewise)
     float* ws_h0;   // [B, D, N]
     float* ws_c0;   // [B, D, K-1]
     void* stream;
-    void* ev_agg[2];   // optional hipEvent_t pair recorded around the aggregate kernel
+    void* ev_agg[2];   // optional hipEvent_t pair recorded around the aggregate kernel (the plain
+                       // forward over several chunks: around the carry-correction kernel)
     void* ev_main[2];  // optional hipEvent_t pair recorded around the main kernel
 };
 

@@ -149,12 +149,13 @@ def test_workspace_query_and_check():
 
 
 def _scan_ws(B, L, D, N, nc):
-    """Forward workspace for nc chunks: aggregates S [B, nc-1, D, N], summed steps
-    [B, nc-1, D], copies of the initial state [B, D, N] and conv history [B, D, 3]."""
+    """Forward workspace for nc chunks: a slot per chunk of end states S [B, nc, D, N]
+    and summed steps [B, nc, D], copies of the initial state [B, D, N] and conv history
+    [B, D, 3]."""
     a = lambda v: (v + 255) // 256 * 256  # noqa: E731
     if nc == 1:
         return 0
-    return a(B * (nc - 1) * D * N * 4) + a(B * (nc - 1) * D * 4) + a(B * D * N * 4) + a(B * D * 3 * 4)
+    return a(B * nc * D * N * 4) + a(B * nc * D * 4) + a(B * D * N * 4) + a(B * D * 3 * 4)
 
 
 def test_forward_chunk_rules():

@@ -196,6 +196,28 @@ def test_bidir_long_chunks_truncated_and_fallback(ss):
     check_bidir(ss, inp, "f32", dsel=dsel, label="bidir fallback")
 
 
+@pytest.mark.parametrize("zoh", [False, True])
+def test_bidir_forward_aggregate_bound_fallback(ss, zoh):
+    """The forward half's aggregate pass (the one the backward's checkpoint pass also
+    runs) at its exact fallback: constant step 0.1 drops the slowest state 278 tokens
+    before each chunk's end, and inputs 1e10 times larger sit 290-329 tokens before it,
+    where the weights are e^-29 to e^-33 (their part of the chunk's end state, about
+    2e-3 of it, is what the truncated sweep would miss). The reversed half meets them
+    about 700 tokens from its own chunk ends (weights below e^-69: its truncated sweep
+    stands). The gate is shut (z = -30) from 700 tokens before each chunk's end to 24
+    before it, over the rows that either direction's large state would dominate."""
+    from test_gpu_parity import one_lane_chunk_len
+    spec = W.ScanSpec("fbb", 2, 65536, 1024, 16, io_dtype="f32", delta_mode="direct", seed=130)
+    inp, _ = _inputs(spec)
+    cl = one_lane_chunk_len(ss, inp, "f32", zoh=zoh, pass_=ss.SS_PASS_BIDIR)
+    assert cl >= 1024 and 65536 % cl == 0, cl
+    inp["delta"][:] = np.float32(np.log(np.expm1(0.1)))
+    r = np.arange(65536) % cl
+    inp["x"][:, (r >= cl - 330) & (r < cl - 290), :] *= np.float32(1e10)
+    inp["z"][:, (r >= cl - 700) & (r < cl - 24), :] = np.float32(-30.0)
+    check_bidir(ss, inp, "f32", dsel=np.array([0, 3, 512, 1023]), zoh=zoh, label=f"bidir forward fallback zoh={zoh}")
+
+
 # ----------------------------------------------------------------------------- properties
 
 def test_bidir_mirror(ss):

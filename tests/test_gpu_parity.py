@@ -278,25 +278,24 @@ def _long_chunk_case(ss, inp, io, dsel, label, states=True):
 
 
 def test_long_chunks_fp32_truncated_aggregates(ss):
-    """Chunks of 1024 tokens with step sizes in [1e-3, 1e-1]: the aggregate pass drops
-    each state index once its weight is below 2^-40; fp32 parity must still hold."""
+    """Chunks of 1024 tokens with step sizes in [1e-3, 1e-1]: the carry-correction pass
+    drops each state index once its carry has decayed below 2^-28; fp32 parity must
+    still hold."""
     spec = W.ScanSpec("lc", 2, 65536, 1024, 16, io_dtype="f32", delta_mode="direct", seed=123)
     inp = W.gen_scan_inputs(spec)
     _long_chunk_case(ss, inp, "f32", np.array([0, 5, 511, 700, 1023]), "long chunks fp32")
 
 
 def test_aggregate_bound_fallback(ss):
-    """Constant step 0.1: the aggregate pass drops the slowest state (A = -1) 278
-    tokens before each chunk's end (0.1 * 278 > 40 ln 2). Inputs 1e10 times larger
-    sit just before that point (290-329 tokens before the chunk end), where the state
-    weights are e^-29 to e^-33: their contribution to the chunk's end state is about
-    2e-3 of it, which the truncated sweep would miss. The bound on the dropped part
-    (those rows' weights times the largest input) then exceeds one unit roundoff of
-    the aggregate, the exact recurrence takes over, and the next chunk's outputs and
-    the final state hold the fp32 bar. The gate is shut (z = -30) over the rows the
-    large inputs would otherwise dominate, so every output stays on the scale of the
-    others and the error metric stays sensitive to the carry. The rows are placed from
-    the chunk length the library reports for this shape."""
+    """Constant step 0.1 with inputs 1e10 times larger 290-329 tokens before each
+    chunk's end, where the state weights are e^-29 to e^-33: their part of the chunk's
+    end state is about 2e-3 of it. In the plain forward that end state is exact (the
+    main pass) and reaches the next chunk's outputs through the carry correction,
+    which these outputs check; the same inputs drive the aggregate pass's exact
+    fallback in the bidirectional scan (test_gpu_bidir). The gate is shut (z = -30)
+    over the rows the large inputs would otherwise dominate, so every output stays on
+    the scale of the others and the error metric stays sensitive to the carry. The
+    rows are placed from the chunk length the library reports for this shape."""
     spec = W.ScanSpec("fb", 2, 65536, 1024, 16, io_dtype="f32", delta_mode="direct", seed=124)
     inp = W.gen_scan_inputs(spec)
     inp["delta"][:] = np.float32(np.log(np.expm1(0.1)))
@@ -306,6 +305,31 @@ def test_aggregate_bound_fallback(ss):
     inp["x"][:, (r >= cl - 330) & (r < cl - 290), :] *= np.float32(1e10)
     inp["z"][:, (r >= cl - 330) & (r < cl - 24), :] = np.float32(-30.0)
     _long_chunk_case(ss, inp, "f32", np.array([0, 3, 512, 1023]), "bound fallback")
+
+
+def test_chunked_zero_carry(ss):
+    """x = 0 over the first half: every chunk there ends in a zero state, so the carry
+    correction has nothing to add (its workgroups stop at once) until the chunks after
+    the first nonzero input."""
+    spec = W.ScanSpec("zc", 1, 16384, 2048, 16, io_dtype="f32", delta_mode="direct", seed=129)
+    inp = W.gen_scan_inputs(spec)
+    one_lane_chunk_len(ss, inp, "f32")
+    inp["x"][:, :8192 + 5, :] = 0.0
+    check_inputs(ss, inp, "f32", states=False, dsel=np.array([0, 1, 1000, 2047]), label="zero carry",
+                 state_tol=TOL["f32"])
+
+
+def test_chunked_ragged_channels_last_channel(ss):
+    """d_inner 1800 on the one-lane chunked path (d_state 32, which never takes the
+    lane-quad kernels): the last workgroup's lanes past channel 1799 repeat it, three
+    whole waves of them. The carry correction reads, corrects and rewrites y, so only
+    the channel's own lane may store it (a repeated store would add the correction
+    again); the last channel is among those checked."""
+    spec = W.ScanSpec("rc", 1, 8192, 1800, 32, io_dtype="f32", delta_mode="direct", seed=131)
+    inp = W.gen_scan_inputs(spec)
+    one_lane_chunk_len(ss, inp, "f32")
+    check_inputs(ss, inp, "f32", states=True, dsel=np.array([0, 1791, 1792, 1798, 1799]), label="ragged channels",
+                 state_tol=TOL["f32"])
 
 
 def test_chunked_growing_state_channels(ss):

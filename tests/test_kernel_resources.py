@@ -37,7 +37,7 @@ def test_no_private_arrays_in_scratch(report):
 
 
 def test_aggregate_kernels_use_no_scratch(report):
-    bad = [demangle(n) for n, v in report.items() if "k_agg" in n and v.get("scratch", 0) > 0]
+    bad = [demangle(n) for n, v in report.items() if ("k_agg" in n or "k_corr" in n) and v.get("scratch", 0) > 0]
     assert not bad, bad
 
 
@@ -46,5 +46,5 @@ def test_benchmarked_kernels_do_not_spill(report):
     bidirectional, backward) keep everything in registers."""
     for n, v in report.items():
         d = demangle(n)
-        if "unsigned short, 16," in d and any(k in d for k in ("k_scan<", "k_agg<", "k_bwd<", "k_bagg<")):
+        if "unsigned short, 16," in d and any(k in d for k in ("k_scan<", "k_agg<", "k_corr<", "k_bwd<", "k_bagg<")):
             assert v.get("scratch", 0) == 0, d

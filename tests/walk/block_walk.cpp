@@ -130,12 +130,16 @@ void check_scan(const selscan::LaunchScan& p, bool step, bool bf16) {
     check("scan ssm_state", p.ssm_state, (size_t)p.batch * p.D * p.N * 4);
     check("scan conv_state", p.conv_state, (size_t)p.batch * p.D * 3 * 4);
     if (!step && p.nchunks > 1) {
-        const size_t na = (size_t)(p.nchunks - 1);
+        // the plain forward's main pass writes a slot per chunk (k_corr reads them back)
+        const size_t na = (size_t)p.nchunks;
         check("scan ws_S", p.ws_S, (size_t)p.batch * na * p.D * p.N * 4);
         check("scan ws_sdt", p.ws_sdt, (size_t)p.batch * na * p.D * 4);
         check("scan ws_h0", p.ws_h0, (size_t)p.batch * p.D * p.N * 4);
         check("scan ws_c0", p.ws_c0, (size_t)p.batch * p.D * 3 * 4);
         if ((int64_t)(p.nchunks - 1) * p.chunk_len >= p.L) fail("scan: last chunk empty");
+        // k_corr reads the last three rows of x for the final conv history
+        if (!p.quad && p.L < 3) fail("scan: sequence shorter than the conv history");
+        if (!p.quad && (p.chunk_len % selscan::kScanTile != 0)) fail("scan: chunk not whole tiles");
         if ((int64_t)p.nchunks * p.chunk_len < p.L) fail("scan: chunks do not cover L");
     }
     if (p.batch > 65535 || p.nchunks > 65535) fail("scan: grid extent");
