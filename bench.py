@@ -775,7 +775,7 @@ def main():
                                measured_counters("k_scan_main_general", digest), instr_per_row(N), trans_per_row(N),
                                issue),
         # the plain forward's second kernel: k_corr adds each chunk's carry over the head
-        # of the chunk where it has not yet decayed below 2^-28 (its bytes depend on the
+        # of the chunk where it has not yet decayed below 2^-24 (its bytes depend on the
         # decay, so it carries no roofline of its own)
         "carry_kernel_ms": round(r["agg_ms"], 4),
         "carry_share_of_step": round(r["agg_ms"] / ms_step, 4),

@@ -129,7 +129,11 @@ size_t ss_workspace_bytes(const ss_dims* dims);
  * (1: the call runs no chunk-aggregate pass); chunk_len, the tokens of every chunk
  * but the last (chunk c starts at token c * chunk_len); lane_quad, 1 when four lanes
  * share a channel (the forward on grids with few channels), 0 for one lane per
- * channel. Invalid dims or pass return SS_ERR_INVALID_ARG / SS_ERR_UNSUPPORTED as the
+ * channel; carry_correction, 1 when the forward runs its chunks from zero and adds
+ * each chunk's carry afterwards over the tokens where it has not yet decayed (one lane
+ * per channel, chunks of at least 1024 tokens), 0 when a chunk-aggregate pass gives
+ * the main pass its carries first (always 0 for the other passes).
+ * Invalid dims or pass return SS_ERR_INVALID_ARG / SS_ERR_UNSUPPORTED as the
  * calls themselves would, and leave *plan untouched. Host only; touches no device. */
 typedef enum { SS_PASS_FWD = 0, SS_PASS_BIDIR = 1, SS_PASS_BWD = 2 } ss_pass;
 
@@ -137,7 +141,7 @@ typedef struct {
     int64_t nchunks;
     int64_t chunk_len;
     int32_t lane_quad;
-    int32_t reserved;   /* 0 */
+    int32_t carry_correction;
 } ss_plan;
 
 ss_status ss_scan_plan(const ss_dims* dims, int32_t pass, ss_plan* plan);

@@ -41,7 +41,7 @@ class ss_args(ctypes.Structure):
 
 class ss_plan(ctypes.Structure):
     _fields_ = [("nchunks", ctypes.c_int64), ("chunk_len", ctypes.c_int64), ("lane_quad", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("carry_correction", ctypes.c_int32)]
 
 
 SS_PASS_FWD, SS_PASS_BIDIR, SS_PASS_BWD = 0, 1, 2
@@ -168,10 +168,11 @@ def ss_workspace_bytes(dims: ss_dims) -> int:
 
 def ss_scan_plan(dims: ss_dims, pass_: int = SS_PASS_FWD) -> dict:
     """How a call with these dims splits the sequence: {"nchunks", "chunk_len",
-    "lane_quad"} (pass_: SS_PASS_FWD, SS_PASS_BIDIR or SS_PASS_BWD)."""
+    "lane_quad", "carry_correction"} (pass_: SS_PASS_FWD, SS_PASS_BIDIR or SS_PASS_BWD)."""
     p = ss_plan()
     _check(lib.ss_scan_plan(ctypes.byref(dims), int(pass_), ctypes.byref(p)))
-    return {"nchunks": int(p.nchunks), "chunk_len": int(p.chunk_len), "lane_quad": bool(p.lane_quad)}
+    return {"nchunks": int(p.nchunks), "chunk_len": int(p.chunk_len), "lane_quad": bool(p.lane_quad),
+            "carry_correction": bool(p.carry_correction)}
 
 
 def _stream_handle(stream) -> Optional[int]:

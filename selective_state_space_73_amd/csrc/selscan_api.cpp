@@ -349,7 +349,8 @@ ss_status ss_scan_plan(const ss_dims* dims, int32_t pass, ss_plan* plan) {
     plan->nchunks = l.nchunks;
     plan->chunk_len = l.chunk_len;
     plan->lane_quad = l.quad ? 1 : 0;
-    plan->reserved = 0;
+    plan->carry_correction =
+        (pass == SS_PASS_FWD && l.nchunks > 1 && !l.quad && l.chunk_len >= selscan::kCorrMinChunk) ? 1 : 0;
     return SS_OK;
 }
 

@@ -239,7 +239,7 @@ template <int N, bool CONV, bool ZOH, bool CK, bool REV> constexpr int scan_wave
 // time-reversed sequence, so chunk-relative token r of chunk c is position
 // L-1-(c*chunk_len + r); it adds its gated output to ypart's and writes the sum to y.
 template <typename T, int N, bool CONV, bool GATE, bool ZOH, bool CK = false, bool REV = false, bool PART = false,
-          bool POW = false>
+          bool POW = false, bool LOC = false>
 __global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<N, CONV, ZOH, CK, REV>())))
 k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
        const T* __restrict__ delta, const float* __restrict__ delta_bias, const float* __restrict__ A,
@@ -257,8 +257,10 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
        ScanArgs sa) {
     static_assert(!(CK && GATE), "checkpoint mode has no gate");
     static_assert(!(CK && (REV || PART)) && !(REV && PART), "one mode per pass");
-    // the plain forward: several chunks run from zero and k_corr adds their carries
-    constexpr bool PLAIN = !CK && !REV && !PART;
+    // the plain forward with LOC: several chunks run from zero and k_corr adds their
+    // carries; without LOC it takes the aggregate pass's carries as the other passes do
+    constexpr bool PLAIN = !CK && !REV && !PART && LOC;
+    static_assert(!LOC || (!CK && !REV && !PART), "LOC is a plain forward mode");
     static_assert(!POW || N >= kPowMinN, "power path only from kPowMinN states");
     const int D = sa.D;
     const int d_raw = blockIdx.x * kScanThreads + threadIdx.x;
@@ -590,6 +592,17 @@ k_scan(const T* __restrict__ x, const float* __restrict__ conv_w, const float* _
         buf ^= 1;
     }
 
+    if constexpr (!CK && !REV && !PART && !LOC) {
+        if (c == sa.nchunks - 1) {
+            if (ssm_state) {
+#pragma unroll
+                for (int n = 0; n < N; ++n) ssm_state[bd * N + n] = h[n];
+            }
+            if (CONV && conv_state) {
+                conv_state[bd * 3 + 0] = x3; conv_state[bd * 3 + 1] = x2; conv_state[bd * 3 + 2] = x1;
+            }
+        }
+    }
     if constexpr (PLAIN) {
         if (!multi) {
             if (ssm_state) {
@@ -1111,15 +1124,16 @@ k_agg(const T* __restrict__ x, const float* __restrict__ conv_w, const float* __
 // which k_corr adds to y. Where A_n <= 0, E only shrinks as r grows: a state index
 // is dropped (wave-uniformly, in blocks as in k_agg) once exp(A_n R) <= 2^-kCorrCutLog2
 // on every lane whose carry is not exactly zero, and that leaves every later state of
-// the chunk off by at most 2^-kCorrCutLog2 |H_c[n]| (below the rounding already in
-// H_c). A workgroup stops once its waves have dropped every index, so the pass reads
+// the chunk off by at most 2^-kCorrCutLog2 |H_c[n]| (one fp32 unit roundoff of the
+// carry, the rounding H_c itself already holds). A workgroup stops once its waves have
+// dropped every index, so the pass reads
 // delta, z and y only over each chunk's head; channels whose states barely decay
 // (A_n > 0 or tiny steps) keep theirs to the chunk end.
 // POW: decays from exp(A_0 R)^(n+1); the per-row sum is then a polynomial in
 // exp(A_0 R), evaluated by Horner's rule over the states up to the highest one still
 // active (the drop order follows n, so dropped states below it add zero terms only
 // where their carry is exactly zero).
-constexpr int kCorrCutLog2 = 28;
+constexpr int kCorrCutLog2 = 24;
 constexpr int kCorrDepth = 8;                 // prefetched 4-row groups of delta, z and y
 
 // The fold of the plain forward's chunk end states, one thread per (batch row,
@@ -1842,16 +1856,17 @@ k_scan_q(const T* __restrict__ x, const float* __restrict__ conv_w, const float*
 // k_scan over `grid`: once with the general decays and, from kPowMinN states on, once
 // more with the power chain (each workgroup runs in one of the two, by its vote). The
 // optional start event is recorded before the first launch, the stop event after the last.
-template <typename T, int N, bool CONV, bool GATE, bool ZOH, bool CK, bool REV, bool PART, typename... Args>
+template <typename T, int N, bool CONV, bool GATE, bool ZOH, bool CK, bool REV, bool PART, bool LOC = false,
+          typename... Args>
 static void launch_k_scan(dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, Args... args) {
     if constexpr (N >= kPowMinN) {
-        hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, ZOH, CK, REV, PART, false>), grid, dim3(kScanThreads), 0, st,
-                              ev0, nullptr, 0, args...);
-        hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, ZOH, CK, REV, PART, true>), grid, dim3(kScanThreads), 0, st,
-                              nullptr, ev1, 0, args...);
+        hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, ZOH, CK, REV, PART, false, LOC>), grid, dim3(kScanThreads), 0,
+                              st, ev0, nullptr, 0, args...);
+        hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, ZOH, CK, REV, PART, true, LOC>), grid, dim3(kScanThreads), 0,
+                              st, nullptr, ev1, 0, args...);
     } else {
-        hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, ZOH, CK, REV, PART, false>), grid, dim3(kScanThreads), 0, st,
-                              ev0, ev1, 0, args...);
+        hipExtLaunchKernelGGL((k_scan<T, N, CONV, GATE, ZOH, CK, REV, PART, false, LOC>), grid, dim3(kScanThreads), 0,
+                              st, ev0, ev1, 0, args...);
     }
 }
 
@@ -1913,11 +1928,11 @@ static hipError_t launch_scan_t(const LaunchScan& p) {
     // rows) before the last chunk
     if (p.nchunks > 1 && (p.chunk_len % kScanTile != 0 || p.chunk_len < kScanTile)) return hipErrorInvalidValue;
     if constexpr (!REV && !PART) {
-        if (p.nchunks > 1) {
+        if (p.nchunks > 1 && p.chunk_len >= kCorrMinChunk) {
             // plain forward: every chunk in one pass (all but the first from zero), the
             // fold of their end states into carries, then the carries added over each
             // chunk's head
-            launch_k_scan<T, N, CONV, GATE, ZOH, false, false, false>(
+            launch_k_scan<T, N, CONV, GATE, ZOH, false, false, false, true>(
                 dim3(gx, p.nchunks, (unsigned)p.batch), st, static_cast<hipEvent_t>(p.ev_main[0]),
                 static_cast<hipEvent_t>(p.ev_main[1]), x, p.conv_w, p.conv_b, dl, p.delta_bias, p.A,
                 static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.Dskip, z, y, p.ssm_state, p.conv_state,

@@ -11,6 +11,11 @@ constexpr int kScanThreads = 256;   // channels per workgroup of the scan kernel
 constexpr int kStepThreads = 256;   // lanes per workgroup of the decode-step kernel (4 per channel)
 constexpr int kStepStreams = 4;     // streams each lane quad of the decode-step kernel handles
 constexpr int kScanTile = 64;       // tokens of B/C staged in LDS at a time
+// The plain forward over several chunks adds each chunk's carry afterwards (k_fold,
+// k_corr) when chunks hold at least kCorrMinChunk tokens: its cost follows the tokens
+// over which the carry has not yet decayed (about 800 with steps of 0.02 on average),
+// so shorter chunks take the aggregate pass (k_agg) before the main pass instead.
+constexpr int64_t kCorrMinChunk = 1024;
 // Lane-quad forward path (k_agg_q / k_scan_q), for d_state <= 16: taken when one lane
 // per channel, even with 64-token chunks, gives fewer than kQuadMaxTileWaves waves that
 // hold a channel (two per SIMD) and the quad layout at least doubles that count (its

@@ -183,17 +183,25 @@ def test_forward_chunk_rules():
 def test_scan_plan_matches_the_chunk_rules():
     """ss_scan_plan reports the chunking the workspace sizes above imply, per pass."""
     P = ss.ss_scan_plan
-    assert P(ss.make_dims(2, 1024, 1024, 16, ss.SS_F32)) == dict(nchunks=32, chunk_len=32, lane_quad=True)
-    assert P(ss.make_dims(2, 1024, 1024, 16, ss.SS_F32), ss.SS_PASS_BIDIR) == \
-        dict(nchunks=16, chunk_len=64, lane_quad=False)
-    assert P(ss.make_dims(2, 1024, 1024, 16, ss.SS_F32), ss.SS_PASS_BWD) == \
-        dict(nchunks=16, chunk_len=64, lane_quad=False)
-    assert P(ss.make_dims(1, 24576, 256, 16, ss.SS_BF16)) == dict(nchunks=384, chunk_len=64, lane_quad=False)
-    # the long workload: 2048 channels = 8 workgroups, 64 chunks of 2048 tokens
-    assert P(ss.make_dims(1, 131072, 2048, 16, ss.SS_BF16)) == dict(nchunks=64, chunk_len=2048, lane_quad=False)
+    F = dict(lane_quad=False, carry_correction=False)
+    assert P(ss.make_dims(2, 1024, 1024, 16, ss.SS_F32)) == dict(nchunks=32, chunk_len=32, lane_quad=True,
+                                                                 carry_correction=False)
+    assert P(ss.make_dims(2, 1024, 1024, 16, ss.SS_F32), ss.SS_PASS_BIDIR) == dict(nchunks=16, chunk_len=64, **F)
+    assert P(ss.make_dims(2, 1024, 1024, 16, ss.SS_F32), ss.SS_PASS_BWD) == dict(nchunks=16, chunk_len=64, **F)
+    assert P(ss.make_dims(1, 24576, 256, 16, ss.SS_BF16)) == dict(nchunks=384, chunk_len=64, **F)
+    # the long workload: 2048 channels = 8 workgroups, 64 chunks of 2048 tokens, whose
+    # carries are added after the main pass (chunks of at least 1024 tokens)
+    assert P(ss.make_dims(1, 131072, 2048, 16, ss.SS_BF16)) == dict(nchunks=64, chunk_len=2048, lane_quad=False,
+                                                                    carry_correction=True)
+    for pas in (ss.SS_PASS_BIDIR, ss.SS_PASS_BWD):
+        assert not P(ss.make_dims(1, 131072, 2048, 16, ss.SS_BF16), pas)["carry_correction"]
+    assert P(ss.make_dims(2, 65536, 1024, 16, ss.SS_F32)) == dict(nchunks=64, chunk_len=1024, lane_quad=False,
+                                                                  carry_correction=True)
+    assert P(ss.make_dims(1, 65536, 1024, 16, ss.SS_F32)) == dict(nchunks=128, chunk_len=512, **F)
+    # the train workload: 4 chunks of 512 tokens, aggregate pass first
+    assert P(ss.make_dims(8, 2048, 5120, 16, ss.SS_BF16)) == dict(nchunks=4, chunk_len=512, **F)
     # enough channels for the GPU: one chunk
-    assert P(ss.make_dims(8, 2048, 5120, 16, ss.SS_BF16))["nchunks"] == 4
-    assert P(ss.make_dims(64, 2048, 5120, 16, ss.SS_BF16)) == dict(nchunks=1, chunk_len=2048, lane_quad=False)
+    assert P(ss.make_dims(64, 2048, 5120, 16, ss.SS_BF16)) == dict(nchunks=1, chunk_len=2048, **F)
     for L, D, B in ((4096, 64, 1), (3001, 100, 2), (65536, 1024, 2), (65536, 1024, 1)):
         for pas in (ss.SS_PASS_FWD, ss.SS_PASS_BIDIR, ss.SS_PASS_BWD):
             p = P(ss.make_dims(B, L, D, 16, ss.SS_F32), pas)

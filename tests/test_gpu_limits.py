@@ -8,11 +8,13 @@ a large one forgets it.
   Delta_t (Euler) or -1/A (zero-order hold), independent of h_{t-1}.
 - a sequence that switches between the two (and ordinary steps) every few hundred
   tokens, so that some chunks' aggregate sweeps drop no state index and others drop
-  every index after their first group.
+  every index after their first group (and the carry correction runs to a chunk's
+  end or drops every carry at once).
 
 Every case runs on each forward path (one-lane chunked kernels with the aggregate
-pass, lane-quad kernels, the decode step, the zero-order hold, the bidirectional
-reversed pass), compared element by element with the fp64 oracle at the fp32 bar,
+pass, one-lane kernels with the carry correction, lane-quad kernels, the decode
+step, the zero-order hold, the bidirectional reversed pass), compared element by
+element with the fp64 oracle at the fp32 bar,
 and the two limits are also checked against their closed forms directly."""
 import numpy as np
 import pytest
@@ -27,9 +29,12 @@ pytestmark = pytest.mark.gpu
 
 SMALL, LARGE = np.float32(-30.0), np.float32(50.0)
 
-# (batch, seqlen, d_inner): a one-lane chunked shape and a lane-quad shape
+# (batch, seqlen, d_inner): one-lane chunked shapes with 256-token chunks (aggregate
+# pass first) and 1024-token chunks (carry correction after), and a lane-quad shape
 ONE_LANE = (2, 16384, 1024)
+CARRY = (2, 65536, 1024)
 QUAD = (1, 4096, 64)
+SHAPES = {"one_lane": ONE_LANE, "carry": CARRY, "quad": QUAD}
 
 
 @pytest.fixture(scope="module")
@@ -53,10 +58,11 @@ def _plan(ss, shape, io="f32", zoh=False, pass_=0):
     return ss.ss_scan_plan(dims, pass_)
 
 
-def _assert_path(ss, shape, quad, pass_=0):
+def _assert_path(ss, shape, quad, pass_=0, carry=False):
     p = _plan(ss, shape, pass_=pass_)
     assert p["nchunks"] > 1, p
     assert p["lane_quad"] == quad, p
+    assert p["carry_correction"] == carry, p
 
 
 def _mixed_delta(L):
@@ -70,10 +76,10 @@ DSEL = np.array([0, 1, 63, 64, 255, 256, 700, 1023])
 
 
 @pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
-@pytest.mark.parametrize("path", ["one_lane", "quad"])
+@pytest.mark.parametrize("path", ["one_lane", "carry", "quad"])
 def test_small_step_keeps_the_state(ss, path, zoh):
-    shape = ONE_LANE if path == "one_lane" else QUAD
-    _assert_path(ss, shape, path == "quad")
+    shape = SHAPES[path]
+    _assert_path(ss, shape, path == "quad", carry=path == "carry")
     inp = _inputs(shape, 301)
     inp["delta"][:] = SMALL
     Bsz, L, Dn = shape
@@ -107,10 +113,10 @@ def test_small_step_keeps_the_state(ss, path, zoh):
 
 
 @pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
-@pytest.mark.parametrize("path", ["one_lane", "quad"])
+@pytest.mark.parametrize("path", ["one_lane", "carry", "quad"])
 def test_large_step_forgets_the_state(ss, path, zoh):
-    shape = ONE_LANE if path == "one_lane" else QUAD
-    _assert_path(ss, shape, path == "quad")
+    shape = SHAPES[path]
+    _assert_path(ss, shape, path == "quad", carry=path == "carry")
     inp = _inputs(shape, 311)
     inp["delta"][:] = LARGE
     Bsz, L, Dn = shape
@@ -137,10 +143,10 @@ def test_large_step_forgets_the_state(ss, path, zoh):
 
 
 @pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
-@pytest.mark.parametrize("path", ["one_lane", "quad"])
+@pytest.mark.parametrize("path", ["one_lane", "carry", "quad"])
 def test_switching_steps(ss, path, zoh):
-    shape = ONE_LANE if path == "one_lane" else QUAD
-    _assert_path(ss, shape, path == "quad")
+    shape = SHAPES[path]
+    _assert_path(ss, shape, path == "quad", carry=path == "carry")
     inp = _inputs(shape, 321)
     mix = _mixed_delta(shape[1])
     keep = ~np.isnan(mix)

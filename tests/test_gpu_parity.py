@@ -260,15 +260,17 @@ def test_step_without_conv_or_gate(ss, S, Dn, N):
     assert maxrel(host(h), hr) <= TOL["f32"]
 
 
-def one_lane_chunk_len(ss, inp, io, zoh=False, pass_=0):
+def one_lane_chunk_len(ss, inp, io, zoh=False, pass_=0, carry=None):
     """Chunk length of the one-lane chunked kernels for these inputs' shape; fails when
     the shape would run unchunked or on the lane-quad kernels (whose aggregates are
-    exact, so a truncation test there would test nothing)."""
+    exact, so a truncation test there would test nothing), or when carry (True: the
+    forward's carry correction, False: the aggregate pass) is given and not taken."""
     Bsz, L, Dn = inp["x"].shape
     dims = ss.make_dims(Bsz, L, Dn, inp["A"].shape[1], 0 if io == "f32" else 1,
                         discretization=ss.SS_ZOH if zoh else ss.SS_EULER)
     p = ss.ss_scan_plan(dims, pass_)
     assert p["nchunks"] > 1 and not p["lane_quad"], ("shape does not select the one-lane chunked path", p)
+    assert carry is None or p["carry_correction"] == carry, ("carry scheme", p)
     return p["chunk_len"]
 
 
@@ -279,10 +281,11 @@ def _long_chunk_case(ss, inp, io, dsel, label, states=True):
 
 def test_long_chunks_fp32_truncated_aggregates(ss):
     """Chunks of 1024 tokens with step sizes in [1e-3, 1e-1]: the carry-correction pass
-    drops each state index once its carry has decayed below 2^-28; fp32 parity must
+    drops each state index once its carry has decayed below 2^-24; fp32 parity must
     still hold."""
     spec = W.ScanSpec("lc", 2, 65536, 1024, 16, io_dtype="f32", delta_mode="direct", seed=123)
     inp = W.gen_scan_inputs(spec)
+    one_lane_chunk_len(ss, inp, "f32", carry=True)
     _long_chunk_case(ss, inp, "f32", np.array([0, 5, 511, 700, 1023]), "long chunks fp32")
 
 
@@ -299,7 +302,7 @@ def test_aggregate_bound_fallback(ss):
     spec = W.ScanSpec("fb", 2, 65536, 1024, 16, io_dtype="f32", delta_mode="direct", seed=124)
     inp = W.gen_scan_inputs(spec)
     inp["delta"][:] = np.float32(np.log(np.expm1(0.1)))
-    cl = one_lane_chunk_len(ss, inp, "f32")
+    cl = one_lane_chunk_len(ss, inp, "f32", carry=True)
     assert cl >= 512, cl
     r = np.arange(65536) % cl
     inp["x"][:, (r >= cl - 330) & (r < cl - 290), :] *= np.float32(1e10)

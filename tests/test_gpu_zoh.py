@@ -121,17 +121,18 @@ def test_zoh_long_chunks_fp32_truncated_aggregates(ss):
 
 
 def test_zoh_aggregate_bound_fallback(ss):
-    """As for Euler: constant step 0.1, inputs 1e10 times larger 287-326 tokens before
-    each chunk's end (their part of the chunk's end state is 8e-3 of it), carried into
-    the next chunk's outputs by the carry correction; the gate is shut (z = -30) over
-    the rows the large inputs would otherwise dominate. The rows are placed from the
-    chunk length the library reports (512 tokens on this shape). The aggregate pass's
-    fallback under the same inputs runs in the bidirectional scan (test_gpu_bidir)."""
+    """Constant step 0.1 drops every state 278 tokens before a chunk's end, inputs 1e10
+    times larger sit just before that point (287-326 tokens before the chunk end; their
+    carry is 8e-3 of the chunk's end state, which the truncated sweep would miss), so
+    the aggregate pass's exact recurrence must take over; the gate is shut (z = -30)
+    over the rows the large inputs would otherwise dominate. The rows are placed from
+    the chunk length the library reports (512 tokens on this shape, which takes the
+    aggregate pass rather than the carry correction)."""
     from test_gpu_parity import one_lane_chunk_len
     spec = W.ScanSpec("zfb", 1, 65536, 1024, 16, io_dtype="f32", delta_mode="direct", seed=128)
     inp = W.gen_scan_inputs(spec)
     inp["delta"][:] = np.float32(np.log(np.expm1(0.1)))
-    cl = one_lane_chunk_len(ss, inp, "f32", zoh=True)
+    cl = one_lane_chunk_len(ss, inp, "f32", zoh=True, carry=False)
     assert cl >= 512, cl
     r = np.arange(65536) % cl
     inp["x"][:, (r >= cl - 327) & (r < cl - 287), :] *= np.float32(1e10)
