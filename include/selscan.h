@@ -126,7 +126,7 @@ size_t ss_workspace_bytes(const ss_dims* dims);
  * SS_PASS_FWD for ss_conv_scan_fwd, SS_PASS_BIDIR for each pass of
  * ss_conv_scan_bidir_fwd (the reversed pass counts chunks in reversed token order),
  * SS_PASS_BWD for ss_conv_scan_bwd. On SS_OK *plan holds: nchunks, the chunk count
- * (1: the call runs no chunk-aggregate pass); chunk_len, the tokens of every chunk
+ * (1: the call runs no carry pass); chunk_len, the tokens of every chunk
  * but the last (chunk c starts at token c * chunk_len); lane_quad, 1 when four lanes
  * share a channel (the forward on grids with few channels), 0 for one lane per
  * channel; carry_correction, 1 when the forward runs its chunks from zero and adds
@@ -314,9 +314,10 @@ ss_status ss_block_step(const ss_block_dims* dims, const ss_block_weights* weigh
  * caller) that the NEXT ss_conv_scan_fwd, ss_conv_scan_bidir_fwd, ss_conv_scan_bwd or
  * ss_step call made on this thread records around its kernels, at the kernels' own
  * start and end on the call's stream: agg_start/agg_stop around the forward's
- * chunk-aggregate kernel (left unrecorded when the call launches none, and by the
- * backward), main_start/main_stop around the main scan, backward-sweep or decode-step
- * kernel. For ss_conv_scan_bidir_fwd both pairs cover the reversed pass's kernels.
+ * carry kernels, i.e. the chunk-aggregate kernel before the main scan, or the
+ * carry fold and correction after it (see ss_scan_plan; left unrecorded when the call
+ * launches none, and by the backward), main_start/main_stop around the main scan,
+ * backward-sweep or decode-step kernel. For ss_conv_scan_bidir_fwd both pairs cover the reversed pass's kernels.
  * Any pointer may be NULL. The setting is consumed by that
  * next call, also when it fails. Always returns SS_OK. */
 ss_status ss_time_next_call(void* agg_start, void* agg_stop, void* main_start, void* main_stop);

@@ -22,10 +22,13 @@
 // GPU. The recurrence h_t = a_t h_{t-1} + b_t is associative in the pair (a, b)
 // (ai360xpert.com "Mamba", "Why this breaks the parallel form": the scan exploits
 // associativity; ozercemkelahmet.com "Deployment notes": chunks pass the state).
-// A first pass computes each chunk's end state from zero, S_c, and its summed
-// step size, so that the chunk's total decay is exp(A * sum Delta); the main pass
-// folds these aggregates of all earlier chunks into its carry-in and then runs
-// the chunk with the exact initial state.
+// A chunk's end state from zero, S_c, and its summed step size give its total
+// decay exp(A * sum Delta), and the carry-ins fold from them. Chunks of at least
+// kCorrMinChunk tokens of the plain forward run from zero in the main pass, which
+// records S_c; k_fold folds the carries and k_corr adds their decaying part to the
+// outputs afterwards. Otherwise (shorter chunks, the bidirectional and backward
+// passes) an aggregate pass computes S_c first and the main pass folds it into its
+// exact carry-in.
 #pragma once
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
