@@ -314,10 +314,10 @@ def test_chunked_zero_carry(ss):
     """x = 0 over the first half: every chunk there ends in a zero state, so the carry
     correction has nothing to add (its workgroups stop at once) until the chunks after
     the first nonzero input."""
-    spec = W.ScanSpec("zc", 1, 16384, 2048, 16, io_dtype="f32", delta_mode="direct", seed=129)
+    spec = W.ScanSpec("zc", 1, 65536, 2048, 16, io_dtype="f32", delta_mode="direct", seed=129)
     inp = W.gen_scan_inputs(spec)
-    one_lane_chunk_len(ss, inp, "f32")
-    inp["x"][:, :8192 + 5, :] = 0.0
+    one_lane_chunk_len(ss, inp, "f32", carry=True)
+    inp["x"][:, :32768 + 5, :] = 0.0
     check_inputs(ss, inp, "f32", states=False, dsel=np.array([0, 1, 1000, 2047]), label="zero carry",
                  state_tol=TOL["f32"])
 
@@ -328,11 +328,28 @@ def test_chunked_ragged_channels_last_channel(ss):
     whole waves of them. The carry correction reads, corrects and rewrites y, so only
     the channel's own lane may store it (a repeated store would add the correction
     again); the last channel is among those checked."""
-    spec = W.ScanSpec("rc", 1, 8192, 1800, 32, io_dtype="f32", delta_mode="direct", seed=131)
+    spec = W.ScanSpec("rc", 1, 65536, 1800, 32, io_dtype="f32", delta_mode="direct", seed=131)
     inp = W.gen_scan_inputs(spec)
-    one_lane_chunk_len(ss, inp, "f32")
+    one_lane_chunk_len(ss, inp, "f32", carry=True)
     check_inputs(ss, inp, "f32", states=True, dsel=np.array([0, 1791, 1792, 1798, 1799]), label="ragged channels",
                  state_tol=TOL["f32"])
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_carry_correction_general_decays(ss, io):
+    """The carry correction's general launch (each decay its own exponential): A drawn
+    as -exp(N(0, 1)) per (channel, state), so no channel has the form (n+1) A[d, 0],
+    with every 7th channel growing (A = +0.002, never dropped) and every 11th holding
+    four states at A = 0 (decay exactly 1, never dropped); 1024-token chunks."""
+    spec = W.ScanSpec("cg", 2, 65536, 1024, 16, io_dtype=io, delta_mode="direct", seed=132)
+    inp = W.gen_scan_inputs(spec)
+    one_lane_chunk_len(ss, inp, io, carry=True)
+    rng = np.random.default_rng(133)
+    inp["A"][:] = -np.exp(rng.standard_normal(inp["A"].shape)).astype(np.float32)
+    inp["A"][::7] = np.float32(0.002)
+    inp["A"][3::11, :4] = np.float32(0.0)
+    check_inputs(ss, inp, io, states=True, dsel=np.array([0, 3, 7, 14, 255, 256, 700, 1023]),
+                 label=f"carry general decays {io}", state_tol=TOL[io])
 
 
 def test_chunked_growing_state_channels(ss):
