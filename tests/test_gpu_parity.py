@@ -335,12 +335,14 @@ def test_chunked_ragged_channels_last_channel(ss):
                  state_tol=TOL["f32"])
 
 
+@pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_carry_correction_general_decays(ss, io):
-    """The carry correction's general launch (each decay its own exponential): A drawn
-    as -exp(N(0, 1)) per (channel, state), so no channel has the form (n+1) A[d, 0],
-    with every 7th channel growing (A = +0.002, never dropped) and every 11th holding
-    four states at A = 0 (decay exactly 1, never dropped); 1024-token chunks."""
+def test_carry_correction_general_decays(ss, io, zoh):
+    """The carry correction's general launch (each decay its own exponential), after
+    the main pass of either write term: A drawn as -exp(N(0, 1)) per (channel, state),
+    so no channel has the form (n+1) A[d, 0], with every 7th channel growing
+    (A = +0.002, never dropped) and every 11th holding four states at A = 0 (decay
+    exactly 1, never dropped); 1024-token chunks."""
     spec = W.ScanSpec("cg", 2, 65536, 1024, 16, io_dtype=io, delta_mode="direct", seed=132)
     inp = W.gen_scan_inputs(spec)
     one_lane_chunk_len(ss, inp, io, carry=True)
@@ -348,8 +350,8 @@ def test_carry_correction_general_decays(ss, io):
     inp["A"][:] = -np.exp(rng.standard_normal(inp["A"].shape)).astype(np.float32)
     inp["A"][::7] = np.float32(0.002)
     inp["A"][3::11, :4] = np.float32(0.0)
-    check_inputs(ss, inp, io, states=True, dsel=np.array([0, 3, 7, 14, 255, 256, 700, 1023]),
-                 label=f"carry general decays {io}", state_tol=TOL[io])
+    check_inputs(ss, inp, io, states=True, dsel=np.array([0, 3, 7, 14, 255, 256, 700, 1023]), zoh=zoh,
+                 label=f"carry general decays {io} zoh={zoh}", state_tol=TOL[io])
 
 
 def test_chunked_growing_state_channels(ss):
