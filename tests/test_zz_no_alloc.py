@@ -27,7 +27,9 @@ def _call(ss, fn, g, h=None, c=None, **kw):
               delta_bias=g["delta_bias"], D=g["D"], z=g["z"], ssm_state=h, conv_state=c, **kw)
 
 
-CASES = [  # (batch, seqlen, d_inner, io, states): one-lane chunked, then lane-quad, then with states
+CASES = [  # (batch, seqlen, d_inner, io, states): one-lane with the carry correction (1024-token
+           # chunks), one-lane with the aggregate pass, lane-quad, then the aggregate pass with states
+    (1, 65536, 2048, "bf16", True),
     (1, 65536, 1024, "bf16", False),
     (1, 8192, 256, "f32", False),
     (2, 6000, 512, "f32", True),
